@@ -1,0 +1,114 @@
+"""Plant plausible mistakes in the oracle (on the CPU, by monkeypatching) and
+check that at least one pin fails for each. This shows the pins can tell a
+wrong oracle from a right one."""
+
+import numpy as np
+import pytest
+
+import oracle.attention as A
+import oracle.blockmap as BM
+import oracle.tiles as T
+from tests import test_oracle_attention as ta
+from tests import test_oracle_paged as tp
+from tests import test_oracle_sparse as ts
+
+_orig_attend = A._attend
+_orig_causal = A._causal_allowed
+
+
+def _attend_no_scale(q, k, v, scale, allowed):
+    return _orig_attend(q, k, v, 1.0, allowed)
+
+
+def _attend_neg_scale(q, k, v, scale, allowed):
+    return _orig_attend(q, k, v, -scale, allowed)
+
+
+def _attend_log2_lse(q, k, v, scale, allowed):
+    o, l_ = _orig_attend(q, k, v, scale, allowed)
+    return o, l_ / np.log(2.0)
+
+
+def _attend_no_normalise(q, k, v, scale, allowed):
+    o, l_ = _orig_attend(q, k, v, scale, allowed)
+    return o * np.exp(l_ - l_.max() if np.isfinite(l_).any() else 0.0)[:, None] * 2.0, l_
+
+
+def _causal_top_left(rows, lq, lk):
+    return np.arange(lk)[None, :] <= rows[:, None]
+
+
+def _causal_off_by_one(rows, lq, lk):
+    return np.arange(lk)[None, :] < rows[:, None] + (lk - lq)
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except AssertionError:
+        return True
+    return False
+
+
+@pytest.mark.parametrize("mutant", [_attend_no_scale, _attend_neg_scale, _attend_log2_lse, _attend_no_normalise])
+def test_attend_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(A, "_attend", mutant)
+    caught = _fails(ta.test_closed_form_two_keys) or _fails(ta.test_closed_form_scale_and_sign)
+    caught = caught or _fails(ta.test_torch_sdpa_fp64, False)
+    assert caught
+
+
+@pytest.mark.parametrize("mutant", [_causal_top_left, _causal_off_by_one])
+def test_causal_mutants_are_caught(monkeypatch, mutant):
+    monkeypatch.setattr(A, "_causal_allowed", mutant)
+    assert _fails(ta.test_torch_sdpa_fp64, True) or _fails(ta.test_causal_row0_attends_only_itself)
+
+
+def test_paged_wrong_offset_is_caught(monkeypatch):
+    def paged_block_major(q, kv_cache, block_tables, context_lens, scale, seqs=None):
+        # plant: read the slots of every block in reverse order
+        cache = kv_cache.clone()
+        cache = cache.flip(2)  # equivalent to reading the block's slots backwards
+        return orig_paged(q, cache, block_tables, context_lens, scale, seqs)
+
+    orig_paged = A.paged_decode_attention
+    monkeypatch.setattr(tp.oracle, "paged_decode_attention", paged_block_major)
+    assert _fails(tp.test_paged_equals_contiguous_gather)
+
+
+def test_tile_order_mutant_is_caught(monkeypatch):
+    orig_boxes = T._boxes
+
+    def boxes_w_slowest(shape, tile):
+        boxes = list(orig_boxes(shape, tile))
+        return reversed(boxes)
+
+    monkeypatch.setattr(T, "_boxes", boxes_w_slowest)
+    assert _fails(ts.test_geometry_hand_example)
+
+
+def test_topk_smallest_mutant_is_caught(monkeypatch):
+    orig = BM.topk_block_map
+
+    def topk_smallest(scores, topk):
+        return orig(-np.asarray(scores), topk)
+
+    monkeypatch.setattr(ts.oracle, "topk_block_map", topk_smallest)
+    assert _fails(ts.test_topk_map_properties)
+
+
+def test_gqa_modulo_mutant_is_caught(monkeypatch):
+    orig_varlen = A.varlen_attention
+
+    def varlen_mod(q, k, v, cu_q, cu_k, scale, causal, rows=None):
+        # plant: query head h reads kv head h % Hkv
+        import torch
+
+        hq, hkv = q.shape[1], k.shape[1]
+        idx = torch.tensor([h % hkv for h in range(hq)])
+        kk = (k if isinstance(k, torch.Tensor) else torch.from_numpy(k)).index_select(1, idx)
+        vv = (v if isinstance(v, torch.Tensor) else torch.from_numpy(v)).index_select(1, idx)
+        return orig_varlen(q, kk, vv, cu_q, cu_k, scale, causal, rows)
+
+    monkeypatch.setattr(ta.oracle, "varlen_attention", varlen_mod)
+    assert _fails(ta.test_torch_sdpa_fp64, False)

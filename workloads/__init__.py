@@ -1,0 +1,233 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU parity tests and
+the benchmark. This module holds no attention arithmetic: it only draws
+lengths, permutations and N(0, 1) tensors.
+
+Recipe (same for every case):
+* integer structure (lengths, block permutation) comes from
+  ``numpy.random.default_rng(seed)``: lengths first, then the permutation;
+* float tensors are ``torch.randn(..., float32)`` from a CPU generator seeded
+  ``1000 * seed + j`` (j = 0 for Q, 1 for K, 2 for V or the KV cache), rounded
+  to bf16 on the host (round-to-nearest-even);
+* the five named workloads follow the shapes of the pages' use cases: a tiny
+  two-document varlen prefill, DiT-style dense self-attention, causal GQA
+  varlen prefill, paged-KV decode with a shuffled block pool, and 3-D video
+  block-sparse attention with 64-token (4, 4, 4) tiles.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+BF16 = torch.bfloat16
+
+
+def randn_bf16(shape, seed: int) -> torch.Tensor:
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    return torch.randn(tuple(shape), dtype=torch.float32, generator=g).to(BF16)
+
+
+def cumulative(lengths) -> np.ndarray:
+    """[0, l0, l0+l1, ...] as int32 (the cu_seqlens layout)."""
+    out = np.zeros(len(lengths) + 1, dtype=np.int64)
+    out[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return out.astype(np.int32)
+
+
+@dataclass
+class VarlenCase:
+    name: str
+    q: torch.Tensor  # [Tq, Hq, D] bf16
+    k: torch.Tensor  # [Tk, Hkv, D]
+    v: torch.Tensor  # [Tk, Hkv, D]
+    cu_seqlens_q: np.ndarray  # int32 [B+1]
+    cu_seqlens_k: np.ndarray
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    causal: bool
+    scale: float
+    seed: int
+
+    @property
+    def batch(self) -> int:
+        return len(self.cu_seqlens_q) - 1
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(np.diff(self.cu_seqlens_q).max()) if self.batch else 0
+
+    @property
+    def max_seqlen_k(self) -> int:
+        return int(np.diff(self.cu_seqlens_k).max()) if self.batch else 0
+
+
+def varlen_case(lengths_q, lengths_k=None, *, num_heads, num_kv_heads, head_dim, causal, seed,
+                scale=None, name="varlen") -> VarlenCase:
+    lengths_k = lengths_q if lengths_k is None else lengths_k
+    cu_q, cu_k = cumulative(lengths_q), cumulative(lengths_k)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    return VarlenCase(
+        name=name,
+        q=randn_bf16((tq, num_heads, head_dim), 1000 * seed + 0),
+        k=randn_bf16((tk, num_kv_heads, head_dim), 1000 * seed + 1),
+        v=randn_bf16((tk, num_kv_heads, head_dim), 1000 * seed + 2),
+        cu_seqlens_q=cu_q,
+        cu_seqlens_k=cu_k,
+        num_heads=num_heads,
+        num_kv_heads=num_kv_heads,
+        head_dim=head_dim,
+        causal=causal,
+        scale=float(scale) if scale is not None else head_dim ** -0.5,
+        seed=seed,
+    )
+
+
+def config1() -> VarlenCase:
+    """Tiny varlen prefill: cu_seqlens [0, 100, 256], 4 heads, D 64, non-causal."""
+    return varlen_case([100, 156], num_heads=4, num_kv_heads=4, head_dim=64, causal=False, seed=1,
+                       scale=1.0 / 8.0, name="tiny-varlen-2doc-h4-d64")
+
+
+def config2() -> VarlenCase:
+    """DiT-style dense self-attention: batch 2 x seq 4096 as uniform varlen, 24 heads, D 128."""
+    return varlen_case([4096, 4096], num_heads=24, num_kv_heads=24, head_dim=128, causal=False, seed=2,
+                       name="dit-dense-b2-s4096-h24-d128")
+
+
+def config3_lengths() -> np.ndarray:
+    return np.random.default_rng(3).integers(512, 4097, 8)
+
+
+def config3() -> VarlenCase:
+    """Causal GQA varlen prefill: 8 docs, lengths uniform in [512, 4096], 32/8 heads, D 128."""
+    return varlen_case(config3_lengths().tolist(), num_heads=32, num_kv_heads=8, head_dim=128, causal=True,
+                       seed=3, name="causal-gqa-varlen-8doc-h32kv8-d128")
+
+
+@dataclass
+class PagedCase:
+    name: str
+    q: torch.Tensor  # [S, Hq, D] bf16
+    kv_cache: torch.Tensor  # [2, NB, BS, Hkv, D] bf16
+    block_tables: np.ndarray  # int32 [S, MB], unused tail = -1
+    context_lens: np.ndarray  # int32 [S]
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    scale: float
+    seed: int
+
+    @property
+    def num_seqs(self) -> int:
+        return int(self.q.shape[0])
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.kv_cache.shape[1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.num_seqs else 0
+
+
+def paged_case(context_lens, *, num_heads, num_kv_heads, head_dim, seed, block_size=128,
+               max_blocks_per_seq=None, spare_blocks=0, rng=None, scale=None, name="paged",
+               chunk_blocks=512) -> PagedCase:
+    """Blocks of a shuffled pool are dealt to sequences in order; table tails are -1.
+
+    ``rng`` continues the integer stream that drew ``context_lens`` (the block
+    permutation is drawn after the lengths)."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    need = [math.ceil(c / block_size) for c in ctx]
+    num_blocks = int(sum(need)) + int(spare_blocks)
+    rng = np.random.default_rng(seed) if rng is None else rng
+    perm = rng.permutation(num_blocks)
+    mb = max(need) if max_blocks_per_seq is None else int(max_blocks_per_seq)
+    mb = max(mb, 1)
+    tables = np.full((len(ctx), mb), -1, dtype=np.int32)
+    pos = 0
+    for s, n in enumerate(need):
+        tables[s, :n] = perm[pos:pos + n]
+        pos += n
+    cache = torch.empty((2, num_blocks, block_size, num_kv_heads, head_dim), dtype=BF16)
+    g = torch.Generator("cpu").manual_seed(1000 * seed + 2)
+    for b0 in range(0, num_blocks, chunk_blocks):
+        b1 = min(num_blocks, b0 + chunk_blocks)
+        cache[:, b0:b1] = torch.randn((2, b1 - b0, block_size, num_kv_heads, head_dim), dtype=torch.float32,
+                                      generator=g).to(BF16)
+    return PagedCase(
+        name=name,
+        q=randn_bf16((len(ctx), num_heads, head_dim), 1000 * seed + 0),
+        kv_cache=cache,
+        block_tables=tables,
+        context_lens=ctx.astype(np.int32),
+        num_heads=num_heads,
+        num_kv_heads=num_kv_heads,
+        head_dim=head_dim,
+        block_size=block_size,
+        scale=float(scale) if scale is not None else head_dim ** -0.5,
+        seed=seed,
+    )
+
+
+def config4_lengths(rng=None) -> np.ndarray:
+    rng = np.random.default_rng(4) if rng is None else rng
+    return rng.integers(1024, 32769, 64)
+
+
+def config4() -> PagedCase:
+    """Paged decode: 64 seqs, contexts uniform in [1024, 32768], cache (2, NB, 128, 8, 128), 32 q heads."""
+    rng = np.random.default_rng(4)
+    ctx = config4_lengths(rng)
+    return paged_case(ctx, num_heads=32, num_kv_heads=8, head_dim=128, seed=4, block_size=128,
+                      max_blocks_per_seq=256, rng=rng, name="paged-decode-64seq-ctx1k-32k-h32kv8-d128")
+
+
+@dataclass
+class VideoCase:
+    name: str
+    q: torch.Tensor  # raster [B, N, H, D] bf16
+    k: torch.Tensor
+    v: torch.Tensor
+    video_shape: tuple = (16, 32, 32)
+    tile_shape: tuple = (4, 4, 4)
+    block: int = 64
+    topk: int = 32
+    num_heads: int = 12
+    head_dim: int = 128
+    scale: float = 128 ** -0.5
+    seed: int = 5
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_tiles(self) -> int:
+        return math.prod(math.ceil(s / t) for s, t in zip(self.video_shape, self.tile_shape))
+
+
+def video_case(video_shape, *, num_heads, head_dim, topk, seed, tile_shape=(4, 4, 4), batch=1,
+               name="video") -> VideoCase:
+    n = math.prod(video_shape)
+    return VideoCase(
+        name=name,
+        q=randn_bf16((batch, n, num_heads, head_dim), 1000 * seed + 0),
+        k=randn_bf16((batch, n, num_heads, head_dim), 1000 * seed + 1),
+        v=randn_bf16((batch, n, num_heads, head_dim), 1000 * seed + 2),
+        video_shape=tuple(video_shape),
+        tile_shape=tuple(tile_shape),
+        topk=topk,
+        num_heads=num_heads,
+        head_dim=head_dim,
+        scale=head_dim ** -0.5,
+        seed=seed,
+    )
+
+
+def config5() -> VideoCase:
+    """Video block-sparse: 16x32x32 latent, (4,4,4) tiles (256 tiles of 64), 12 heads, D 128, top-32."""
+    return video_case((16, 32, 32), num_heads=12, head_dim=128, topk=32, seed=5,
+                      name="video-block-sparse-16x32x32-t444-h12-d128-top32")
