@@ -1,0 +1,187 @@
+/*
+ * attn_mi355x.h - C ABI of the MI355X (gfx950) attention forward library.
+ *
+ * Operation (all entry points): fused scaled-dot-product attention forward
+ *
+ *     O_i   = sum_j exp(z_ij) v_j / sum_j exp(z_ij),   z_ij = scale * <q_i, k_j>
+ *     LSE_i = ln sum_j exp(z_ij)
+ *
+ * over the keys j allowed for query i. This is the contract of the fused kernels
+ * that the vLLM-Omni diffusion backend page (flash_attn.py, FlashAttentionImpl)
+ * calls with a softmax scale and a causal flag and that return out or
+ * (out, lse); its laser-attention note names S = Q K^T, and the fastvideo_vsa.py
+ * page writes tile attention as softmax(scale * q k^T) v. A query row with no
+ * allowed key gets O = 0 and LSE = -inf.
+ *
+ * Conventions shared by every call:
+ *   - Pointers are DEVICE pointers unless marked (host). Tensors are dense,
+ *     row-major, with no padding between rows. Q/K/V/O and the KV cache are
+ *     bf16 (passed as void*), index arrays int32, LSE fp32.
+ *   - Output buffers belong to the caller (the pages' backends all declare
+ *     accept_output_buffer and the Ascend forward requires an output tensor).
+ *     The library allocates nothing, never synchronises the host, keeps no
+ *     state besides cached launch parameters, and enqueues its kernels on
+ *     `stream` (a hipStream_t; NULL = the default stream). Every call is
+ *     therefore capturable in a HIP graph.
+ *   - Host-side sizes (batch, totals, max lengths) plan the launch; device-side
+ *     index arrays are never read by the host (the pages pass max_seqlen as host
+ *     ints so no device sync is needed).
+ *   - Validation: every argument the host can check is checked before any HIP
+ *     call; on failure nothing is enqueued and an ATTN_ERR_* code is returned.
+ *     Device-resident index values (cu_seqlens, block tables, context lengths,
+ *     tile sizes) are preconditions; the kernels clamp them into the buffers
+ *     they index, so a bad value yields wrong numbers, never an out-of-bounds
+ *     access.
+ *   - Determinism: results are bitwise identical run to run (fixed reduction
+ *     order, no atomics).
+ *   - softmax_scale must be finite and > 0 (the pages use head_dim^-0.5).
+ *   - head_dim must be one of 64, 96, 128, 192, 256 (the flash backend's
+ *     get_supported_head_sizes list).
+ *   - Grouped-query heads: num_heads % num_kv_heads == 0; query head h reads kv
+ *     head h / (num_heads / num_kv_heads) (the Ascend backend's
+ *     num_queries_per_kv grouping).
+ */
+#ifndef ATTN_MI355X_H
+#define ATTN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_ABI_VERSION 1
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,          /* null pointer, negative size, inconsistent shape */
+  ATTN_ERR_UNSUPPORTED = 2,          /* head_dim, block_size or GQA ratio not supported */
+  ATTN_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the size query's answer */
+  ATTN_ERR_LAUNCH = 4                /* the HIP runtime rejected a kernel launch */
+} attn_status_t;
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+/* ATTN_ABI_VERSION of the built library. */
+int attn_abi_version(void);
+
+/*
+ * Packed variable-length prefill (vLLM-Omni flash_attn.py page:
+ * FlashAttentionImpl._forward_varlen_packed and _forward_varlen_dense, which
+ * flatten [B, S, H, D] to [total, H, D] and pass cumulative cu_seqlens;
+ * vLLM-Ascend attention_v1.py page: _forward_encoder_attention / TND layout).
+ *
+ *   q            [total_q, num_heads, head_dim]     bf16
+ *   k, v         [total_k, num_kv_heads, head_dim]  bf16
+ *   cu_seqlens_q [batch + 1] int32, cu_seqlens_q[0] = 0, non-decreasing,
+ *                cu_seqlens_q[batch] = total_q; document b owns rows
+ *                [cu_seqlens_q[b], cu_seqlens_q[b+1]). Same for cu_seqlens_k.
+ *   max_seqlen_q (host) >= every document's query length; sizes the grid.
+ *   max_seqlen_k (host) >= every document's key length.
+ *   causal       0 = every key of the document; 1 = bottom-right aligned causal
+ *                (key j is allowed for query i iff j <= i + Lk - Lq, the
+ *                alignment the flash backend's NPU causal branch spells out).
+ *   out          [total_q, num_heads, head_dim] bf16 (caller-owned)
+ *   lse          nullable; [num_heads, total_q] fp32 natural-log LSE.
+ * A query never attends a key of another document. batch == 0 or
+ * total_q == 0 is a no-op returning ATTN_OK.
+ */
+attn_status_t attn_varlen_fwd(const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t batch, int32_t total_q, int32_t total_k,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              float softmax_scale, int32_t causal,
+                              void* out, float* lse, void* stream);
+
+/*
+ * Workspace bytes that attn_paged_decode needs for these host sizes
+ * (the Ascend page sizes its paged-attention workspace with a query call,
+ * _npu_paged_attention_get_workspace). Written to *bytes (host pointer).
+ */
+attn_status_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t max_context_len, size_t* bytes);
+
+/*
+ * Single-token decode over a paged KV cache (vLLM-Ascend attention_v1.py page:
+ * get_kv_cache_shape, get_supported_block_size, AscendMetadata.block_tables /
+ * seq_lens, forward_paged_attention).
+ *
+ *   q             [num_seqs, num_heads, head_dim] bf16, one query token per sequence
+ *   kv_cache      [2, num_blocks, block_size, num_kv_heads, head_dim] bf16;
+ *                 [0] = K, [1] = V
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32 physical block ids;
+ *                 token t of sequence b lives in block block_tables[b][t / block_size]
+ *                 at offset t % block_size. Entries at or past
+ *                 ceil(context_lens[b] / block_size) are never read.
+ *   context_lens  [num_seqs] int32, 0 <= len <= max_blocks_per_seq * block_size
+ *                 (the cache already holds the new token: the query attends all
+ *                 context_lens[b] keys). len 0 gives O = 0, LSE = -inf.
+ *   max_context_len (host) >= every context_lens[b]; plans the KV split.
+ *   block_size    must be 128.
+ *   out           [num_seqs, num_heads, head_dim] bf16
+ *   lse           nullable; [num_heads, num_seqs] fp32
+ *   workspace     device buffer of at least attn_paged_decode_workspace_size()
+ *                 bytes (split partials; contents on return are unspecified).
+ * Long contexts are split over workgroups; partial (O, LSE) pairs are merged in
+ * ascending split order by a second kernel, so the result is deterministic.
+ * num_seqs == 0 is a no-op.
+ */
+attn_status_t attn_paged_decode(const void* q, const void* kv_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, float softmax_scale,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
+ * Block map -> ascending index lists (vLLM-Omni fastvideo_vsa.py page: the
+ * native route converts the boolean block map with map_to_index into per-row
+ * kept key-tile indices and counts).
+ *
+ *   block_map [rows, n_cols] uint8, nonzero = keep
+ *   idx       [rows, n_cols] int32: row r's kept columns in ascending order in
+ *             idx[r][0 .. num[r]-1]; entries past num[r] are left untouched
+ *   num       [rows] int32
+ * Bit-exact. rows == 0 is a no-op.
+ */
+attn_status_t attn_block_map_to_index(const uint8_t* block_map, int32_t rows, int32_t n_cols,
+                                      int32_t* idx, int32_t* num, void* stream);
+
+/* Workspace bytes for attn_block_sparse_fwd (the index lists it builds). */
+attn_status_t attn_block_sparse_workspace_size(int32_t batch, int32_t num_heads, int32_t num_tiles,
+                                               size_t* bytes);
+
+/*
+ * 64-token-tile block-sparse attention (vLLM-Omni fastvideo_vsa.py page:
+ * _fastvideo_h3_vsa_bhsd_op / block_sparse_attn with block_map and
+ * variable_block_sizes; FastVideoVSAImpl._forward_h3 prepares tile order).
+ *
+ *   q            [batch, num_tiles * 64, num_heads, head_dim]    bf16, tile order
+ *   k, v         [batch, num_tiles * 64, num_kv_heads, head_dim] bf16, tile order
+ *   block_map    [batch, num_heads, num_tiles, num_tiles] uint8; nonzero = query
+ *                tile a attends key tile c
+ *   tile_sizes   [num_tiles] int32 in [0, 64]: rows >= tile_sizes[c] of tile c
+ *                are padding (neither queries nor keys)
+ *   out          [batch, num_tiles * 64, num_heads, head_dim] bf16; padding rows
+ *                and rows whose map row is empty are written 0
+ *   lse          nullable; [batch, num_heads, num_tiles * 64] fp32 (-inf there)
+ *   workspace    >= attn_block_sparse_workspace_size() bytes
+ * Non-causal only and Sq == Skv, as the page's VSA preconditions require;
+ * the same tile_sizes serve queries and keys.
+ */
+attn_status_t attn_block_sparse_fwd(const void* q, const void* k, const void* v,
+                                    const uint8_t* block_map, const int32_t* tile_sizes,
+                                    int32_t batch, int32_t num_tiles, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                                    void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_MI355X_H */

@@ -202,7 +202,7 @@ def paged_decode_attention(q, kv_cache, block_tables, context_lens, scale: float
     return out, lse
 
 
-def block_sparse_attention(q, k, v, block_map, tile_sizes, scale: float, tile: int = 64, heads=None):
+def block_sparse_attention(q, k, v, block_map, tile_sizes, scale: float, tile: int = 64, heads=None, q_tiles=None):
     """Tile-granular block-sparse attention ([VSA] fastvideo_h3_vsa_bhsd op and
     FastVideoVSAImpl._forward_h3: q/k/v are in tile order with ``tile`` rows per
     tile, of which the first ``tile_sizes[c]`` are real; ``block_map[b, h, a, c]``
@@ -212,6 +212,8 @@ def block_sparse_attention(q, k, v, block_map, tile_sizes, scale: float, tile: i
     tile a: the valid rows of every key tile c with block_map[b, h, a, c].
 
     q [B, S, H, D], k/v [B, S, Hkv, D] with S = n_tiles * tile.
+    ``heads`` / ``q_tiles`` restrict the computed (head, query tile) pairs;
+    rows outside them are left at O = 0, LSE = -inf.
     Returns out [B, S, H, D] and lse [B, H, S] in float64.
 
     Pinned: full map == dense, brute force, token-mask equivalence.
@@ -233,7 +235,7 @@ def block_sparse_attention(q, k, v, block_map, tile_sizes, scale: float, tile: i
     for b in range(bsz):
         for h in heads:
             hk = h // group
-            for a in range(n_tiles):
+            for a in (range(n_tiles) if q_tiles is None else q_tiles):
                 qrows = np.arange(a * tile, a * tile + sizes[a])
                 if qrows.size == 0:
                     continue

@@ -55,14 +55,14 @@ def topk_block_map(scores, topk: int) -> np.ndarray:
 
 
 def map_to_index(block_map):
-    """Ascending kept key-tile indices per row, int32 [B, H, nQ, nK] padded with -1,
-    and the kept count per row, int32 [B, H, nQ]."""
+    """Ascending kept key-tile indices per row, int32 [..., nK] padded with -1,
+    and the kept count per row, int32 [...] (any number of leading dims)."""
     m = np.asarray(block_map).astype(bool)
     num = m.sum(axis=-1).astype(np.int32)
     idx = np.full(m.shape, -1, dtype=np.int32)
     # stable sort of "not kept" puts kept columns first, in ascending order
     order = np.argsort(~m, axis=-1, kind="stable").astype(np.int32)
     pos = np.arange(m.shape[-1])
-    valid = pos[None, None, None, :] < num[..., None]
+    valid = pos < num[..., None]
     idx[valid] = order[valid]
     return idx, num

@@ -1,0 +1,259 @@
+"""MI355X (gfx950) attention forward: Python binding of the C ABI in
+``include/attn_mi355x.h``.
+
+The functions here carry the C entry points' names and do argument marshalling
+only: they check dtype, device, shape and contiguity of torch tensors, pass
+their device pointers and the current HIP stream to ``libattn_mi355x.so``, and
+raise :class:`AttnError` on a non-zero status. Every step of the computation
+runs in the library's HIP kernels; there is no other code path. If the library
+has not been built, importing works but every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = [
+    "AttnError",
+    "load_library",
+    "exported_symbols",
+    "attn_abi_version",
+    "attn_status_string",
+    "attn_varlen_fwd",
+    "attn_paged_decode_workspace_size",
+    "attn_paged_decode",
+    "attn_block_map_to_index",
+    "attn_block_sparse_workspace_size",
+    "attn_block_sparse_fwd",
+    "SUPPORTED_HEAD_DIMS",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn_mi355x.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "attn_mi355x.h")
+SUPPORTED_HEAD_DIMS = (64, 96, 128, 192, 256)
+
+_i32, _f32, _sz, _p = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+_SIGS = {
+    "attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "attn_abi_version": (ctypes.c_int, []),
+    "attn_varlen_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                       _i32, _p, _p, _p]),
+    "attn_paged_decode_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "attn_paged_decode": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p,
+                                         _p, _p, _sz, _p]),
+    "attn_block_map_to_index": (ctypes.c_int, [_p, _i32, _i32, _p, _p, _p]),
+    "attn_block_sparse_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "attn_block_sparse_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
+                                             _sz, _p]),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A library call returned a non-zero attn_status_t."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed with status {status}: {message}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built HIP library once; raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build the HIP library first "
+                "(python -c 'import __graft_entry__ as e; e.build()')")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def exported_symbols(header: str = HEADER) -> list[str]:
+    """Names of the functions the C header declares."""
+    with open(header) as f:
+        text = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def attn_status_string(status: int) -> str:
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_abi_version() -> int:
+    return int(load_library().attn_abi_version())
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise AttnError(fn, status, attn_status_string(status))
+
+
+def _stream_ptr(t: torch.Tensor, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, device=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _shape(t: torch.Tensor, name: str, shape):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def attn_varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+                    softmax_scale: float, causal: bool, out=None, lse=None, return_lse: bool = False, stream=None):
+    """Packed varlen attention forward. q [Tq, Hq, D], k/v [Tk, Hkv, D] bf16;
+    cu_seqlens int32 [B+1]. Returns out (and lse [Hq, Tq] fp32 if requested)."""
+    dev = q.device
+    tq, hq, d = q.shape
+    tk, hkv, dk = k.shape
+    batch = cu_seqlens_q.numel() - 1
+    if cu_seqlens_k.numel() != batch + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    _shape(v, "v", (tk, hkv, dk))
+    if dk != d:
+        raise ValueError("q and k head sizes differ")
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, tq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _shape(lse, "lse", (hq, tq))
+    lib = load_library()
+    st = lib.attn_varlen_fwd(
+        _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16, dev), _dev(v, "v", torch.bfloat16, dev),
+        _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev), _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, dev),
+        batch, tq, tk, int(max_seqlen_q), int(max_seqlen_k), hq, hkv, d, float(softmax_scale), int(bool(causal)),
+        _dev(out, "out", torch.bfloat16, dev), _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
+        _stream_ptr(q, stream))
+    _check("attn_varlen_fwd", st)
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def attn_paged_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                                     max_context_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("attn_paged_decode_workspace_size",
+           load_library().attn_paged_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                           max_context_len, ctypes.byref(n)))
+    return int(n.value)
+
+
+def attn_paged_decode(q, kv_cache, block_tables, context_lens, max_context_len: int, softmax_scale: float,
+                      out=None, lse=None, return_lse: bool = False, workspace=None, stream=None):
+    """Single-token decode over a paged cache [2, NB, 128, Hkv, D]. q [S, Hq, D]."""
+    dev = q.device
+    nseq, hq, d = q.shape
+    two, nblocks, bs, hkv, dk = kv_cache.shape
+    if two != 2 or dk != d:
+        raise ValueError("kv_cache must be [2, num_blocks, block_size, num_kv_heads, head_dim]")
+    mbps = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    _shape(block_tables, "block_tables", (nseq, mbps))
+    _shape(context_lens, "context_lens", (nseq,))
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, nseq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _shape(lse, "lse", (hq, nseq))
+    need = attn_paged_decode_workspace_size(nseq, hq, hkv, d, int(max_context_len))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    lib = load_library()
+    st = lib.attn_paged_decode(
+        _dev(q, "q", torch.bfloat16), _dev(kv_cache, "kv_cache", torch.bfloat16, dev),
+        _dev(block_tables, "block_tables", torch.int32, dev), _dev(context_lens, "context_lens", torch.int32, dev),
+        nseq, nblocks, mbps, int(max_context_len), hq, hkv, d, bs, float(softmax_scale),
+        _dev(out, "out", torch.bfloat16, dev), _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
+        _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(), _stream_ptr(q, stream))
+    _check("attn_paged_decode", st)
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def attn_block_map_to_index(block_map, idx=None, num=None, stream=None):
+    """uint8/bool [..., n_cols] map -> (idx int32 [..., n_cols], num int32 [...])."""
+    if block_map.dtype == torch.bool:
+        block_map = block_map.view(torch.uint8)
+    n_cols = block_map.shape[-1]
+    rows = block_map.numel() // n_cols if n_cols else 0
+    dev = block_map.device
+    if idx is None:
+        idx = torch.full(block_map.shape, -1, dtype=torch.int32, device=dev)
+    if num is None:
+        num = torch.empty(block_map.shape[:-1], dtype=torch.int32, device=dev)
+    _shape(idx, "idx", block_map.shape)
+    _shape(num, "num", block_map.shape[:-1])
+    st = load_library().attn_block_map_to_index(
+        _dev(block_map, "block_map", torch.uint8), rows, n_cols, _dev(idx, "idx", torch.int32, dev),
+        _dev(num, "num", torch.int32, dev), _stream_ptr(block_map, stream))
+    _check("attn_block_map_to_index", st)
+    return idx, num
+
+
+def attn_block_sparse_workspace_size(batch: int, num_heads: int, num_tiles: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("attn_block_sparse_workspace_size",
+           load_library().attn_block_sparse_workspace_size(batch, num_heads, num_tiles, ctypes.byref(n)))
+    return int(n.value)
+
+
+def attn_block_sparse_fwd(q, k, v, block_map, tile_sizes, softmax_scale: float, out=None, lse=None,
+                          return_lse: bool = False, workspace=None, stream=None):
+    """Block-sparse attention over 64-row tiles in tile order. q [B, T*64, H, D]."""
+    dev = q.device
+    b, s, hq, d = q.shape
+    hkv = k.shape[2]
+    if s % 64 != 0:
+        raise ValueError("sequence length must be a multiple of the 64-row tile")
+    nt = s // 64
+    _shape(k, "k", (b, s, hkv, d))
+    _shape(v, "v", (b, s, hkv, d))
+    if block_map.dtype == torch.bool:
+        block_map = block_map.view(torch.uint8)
+    _shape(block_map, "block_map", (b, hq, nt, nt))
+    _shape(tile_sizes, "tile_sizes", (nt,))
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((b, hq, s), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _shape(lse, "lse", (b, hq, s))
+    need = attn_block_sparse_workspace_size(b, hq, nt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load_library().attn_block_sparse_fwd(
+        _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16, dev), _dev(v, "v", torch.bfloat16, dev),
+        _dev(block_map, "block_map", torch.uint8, dev), _dev(tile_sizes, "tile_sizes", torch.int32, dev),
+        b, nt, hq, hkv, d, float(softmax_scale), _dev(out, "out", torch.bfloat16, dev),
+        _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
+        _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(), _stream_ptr(q, stream))
+    _check("attn_block_sparse_fwd", st)
+    return (out, lse) if (return_lse or lse is not None) else out

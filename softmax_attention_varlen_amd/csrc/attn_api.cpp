@@ -1,0 +1,145 @@
+// C ABI entry points: host-side validation, launch planning and dispatch.
+// Nothing here reads device memory, allocates, or synchronises.
+#include "../../include/attn_mi355x.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "launch.hpp"
+
+namespace {
+
+bool supported_head_dim(int d) { return d == 64 || d == 96 || d == 128 || d == 192 || d == 256; }
+
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+// Signed byte counts stay far inside size_t; this guards 32-bit index math in
+// the kernels, which address tensors with 64-bit offsets but 32-bit row ids.
+constexpr long long kMaxRows = 0x7fffffffLL;
+
+attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_INVALID_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case ATTN_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int attn_abi_version(void) { return ATTN_ABI_VERSION; }
+
+attn_status_t attn_varlen_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                              const int32_t* cu_seqlens_k, int32_t batch, int32_t total_q, int32_t total_k,
+                              int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
+                              void* out, float* lse, void* stream) {
+  if (batch < 0 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 || max_seqlen_k < 0) return ATTN_ERR_INVALID_ARG;
+  if (num_heads <= 0 || num_kv_heads <= 0) return ATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
+  if (max_seqlen_q > total_q || max_seqlen_k > total_k) return ATTN_ERR_INVALID_ARG;
+  if (batch == 0 || total_q == 0) return ATTN_OK;
+  if (max_seqlen_q == 0) return ATTN_ERR_INVALID_ARG;  // rows exist but no document could own them
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  if (total_k > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_INVALID_ARG;
+  if ((long long)total_q * num_heads > kMaxRows || (long long)total_k * num_kv_heads > kMaxRows) {
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (attn::varlen_grid_size(batch, max_seqlen_q, num_heads) > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  attn::VarlenArgs a{q, k, v, cu_seqlens_q, cu_seqlens_k, batch, total_q, total_k, max_seqlen_q, max_seqlen_k,
+                     num_heads, num_kv_heads, head_dim, softmax_scale, causal, out, lse};
+  return from_hip(attn::launch_varlen_fwd(a, (hipStream_t)stream));
+}
+
+attn_status_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t max_context_len, size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) return ATTN_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
+  *bytes = attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len).workspace_bytes;
+  return ATTN_OK;
+}
+
+attn_status_t attn_paged_decode(const void* q, const void* kv_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float softmax_scale,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0) return ATTN_ERR_INVALID_ARG;
+  if (num_heads <= 0 || num_kv_heads <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
+  if (block_size != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * block_size) return ATTN_ERR_INVALID_ARG;
+  if (num_seqs == 0) return ATTN_OK;
+  if (q == nullptr || out == nullptr || context_lens == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (max_context_len > 0 && (kv_cache == nullptr || block_tables == nullptr || num_blocks == 0)) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  if ((long long)num_blocks * block_size * num_kv_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  const attn::DecodePlan plan = attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len);
+  if (workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (plan.workspace_bytes > 0 && workspace == nullptr) return ATTN_ERR_INVALID_ARG;
+  attn::DecodeArgs a{q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
+                     max_context_len, num_heads, num_kv_heads, head_dim, block_size, softmax_scale, out, lse,
+                     workspace};
+  return from_hip(attn::launch_paged_decode(a, plan, (hipStream_t)stream));
+}
+
+attn_status_t attn_block_map_to_index(const uint8_t* block_map, int32_t rows, int32_t n_cols, int32_t* idx,
+                                      int32_t* num, void* stream) {
+  if (rows < 0 || n_cols <= 0) return ATTN_ERR_INVALID_ARG;
+  if (rows == 0) return ATTN_OK;
+  if (block_map == nullptr || idx == nullptr || num == nullptr) return ATTN_ERR_INVALID_ARG;
+  if ((long long)rows * n_cols > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  return from_hip(attn::launch_map_to_index(block_map, rows, n_cols, idx, num, (hipStream_t)stream));
+}
+
+attn_status_t attn_block_sparse_workspace_size(int32_t batch, int32_t num_heads, int32_t num_tiles, size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (batch < 0 || num_heads <= 0 || num_tiles < 0) return ATTN_ERR_INVALID_ARG;
+  *bytes = attn::sparse_workspace_bytes(batch, num_heads, num_tiles);
+  return ATTN_OK;
+}
+
+attn_status_t attn_block_sparse_fwd(const void* q, const void* k, const void* v, const uint8_t* block_map,
+                                    const int32_t* tile_sizes, int32_t batch, int32_t num_tiles, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, float softmax_scale, void* out,
+                                    float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || num_tiles < 0 || num_heads <= 0 || num_kv_heads <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0 || num_tiles == 0) return ATTN_OK;
+  if (q == nullptr || k == nullptr || v == nullptr || block_map == nullptr || tile_sizes == nullptr ||
+      out == nullptr) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  if ((long long)batch * num_tiles * 64 * num_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)batch * num_heads * num_tiles * num_tiles > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn::sparse_workspace_bytes(batch, num_heads, num_tiles);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return ATTN_ERR_INVALID_ARG;
+  const size_t rows = (size_t)batch * num_heads * num_tiles;
+  int32_t* idx = (int32_t*)workspace;
+  int32_t* num = idx + rows * (size_t)num_tiles;
+  attn::SparseArgs a{q, k, v, block_map, tile_sizes, batch, num_tiles, num_heads, num_kv_heads, head_dim,
+                     softmax_scale, out, lse, idx, num};
+  return from_hip(attn::launch_block_sparse_fwd(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,78 @@
+// Host-side launch plans shared between the C ABI layer and the kernel files.
+// Every struct holds already-validated arguments; the launchers only enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct VarlenArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int batch, total_q, total_k, max_seqlen_q, max_seqlen_k;
+  int num_heads, num_kv_heads, head_dim;
+  float scale;
+  int causal;
+  void* out;
+  float* lse;
+};
+
+hipError_t launch_varlen_fwd(const VarlenArgs& a, hipStream_t stream);
+long varlen_grid_size(int batch, int max_seqlen_q, int num_heads);
+
+// Paged decode: the context of each sequence is cut into splits of
+// split_tokens (a multiple of the 128-token block); split s of a sequence
+// writes a normalised fp32 partial (O_s, LSE_s) that a second kernel merges.
+struct DecodePlan {
+  int split_tokens;  // tokens per split
+  int max_splits;    // ceil(max_context_len / split_tokens)
+  int q_chunks;      // ceil(group / 16): query heads of one kv head per pass
+  size_t o_bytes;    // partial O   [num_seqs][max_splits][num_heads][head_dim] fp32
+  size_t lse_bytes;  // partial LSE [num_seqs][max_splits][num_heads] fp32
+  size_t workspace_bytes;
+};
+
+DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len);
+
+struct DecodeArgs {
+  const void* q;
+  const void* kv_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs, num_blocks, max_blocks_per_seq, max_context_len;
+  int num_heads, num_kv_heads, head_dim, block_size;
+  float scale;
+  void* out;
+  float* lse;
+  void* workspace;
+};
+
+hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+// Block map -> ascending index lists.
+hipError_t launch_map_to_index(const uint8_t* map, int rows, int n_cols, int32_t* idx, int32_t* num,
+                               hipStream_t stream);
+
+struct SparseArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const uint8_t* block_map;
+  const int32_t* tile_sizes;
+  int batch, num_tiles, num_heads, num_kv_heads, head_dim;
+  float scale;
+  void* out;
+  float* lse;
+  int32_t* idx;  // workspace: [batch*num_heads*num_tiles][num_tiles]
+  int32_t* num;  // workspace: [batch*num_heads*num_tiles]
+};
+
+size_t sparse_workspace_bytes(int batch, int num_heads, int num_tiles);
+hipError_t launch_block_sparse_fwd(const SparseArgs& a, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,134 @@
+"""The C-ABI library loads, exports every symbol the header declares, and its
+host-side validation rejects bad arguments before any HIP call. No call here
+reaches a kernel launch, so these run without a GPU."""
+
+import ctypes
+import os
+
+import pytest
+
+import softmax_attention_varlen_amd as sav
+
+LIB = sav.LIB_PATH
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="library not built")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def lib():
+    return sav.load_library()
+
+
+def test_exports_every_declared_symbol():
+    names = sav.exported_symbols()
+    assert {"attn_varlen_fwd", "attn_paged_decode", "attn_block_sparse_fwd"} <= set(names)
+    raw = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in the header but not exported"
+
+
+def test_abi_version_and_status_strings():
+    assert sav.attn_abi_version() == 1
+    assert sav.attn_status_string(0) == "ok"
+    assert sav.attn_status_string(1) == "invalid argument"
+    assert sav.attn_status_string(3) == "workspace too small"
+    assert sav.attn_status_string(99) == "unknown status"
+
+
+def _varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, cuq=FAKE, cuk=FAKE, batch=2, tq=256, tk=256, mq=156, mk=156, hq=4, hkv=4, d=64,
+             scale=0.125, causal=0, out=FAKE, lse=None)
+    a.update(kw)
+    return lib().attn_varlen_fwd(a["q"], a["k"], a["v"], a["cuq"], a["cuk"], a["batch"], a["tq"], a["tk"], a["mq"],
+                                 a["mk"], a["hq"], a["hkv"], a["d"], a["scale"], a["causal"], a["out"], a["lse"],
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=80), UNSUPPORTED), (dict(d=512), UNSUPPORTED), (dict(d=0), UNSUPPORTED),
+    (dict(hq=6, hkv=4), UNSUPPORTED),
+    (dict(hq=0), INVALID), (dict(hkv=0), INVALID), (dict(batch=-1), INVALID), (dict(tq=-5), INVALID),
+    (dict(scale=0.0), INVALID), (dict(scale=-0.1), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(causal=2), INVALID),
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(cuq=None), INVALID), (dict(cuk=None), INVALID),
+    (dict(k=None), INVALID), (dict(mq=300), INVALID), (dict(mk=300), INVALID), (dict(mq=0), INVALID),
+])
+def test_varlen_validation(kw, code):
+    assert _varlen(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(tq=0, mq=0)])
+def test_varlen_empty_is_noop(kw):
+    # nothing to do: returns before any HIP call, even with null buffers
+    assert _varlen(q=None, out=None, **kw) == OK
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, ctx=FAKE, nseq=4, nblocks=10, mbps=4, maxctx=500, hq=8, hkv=2, d=128,
+             bs=128, scale=0.1, out=FAKE, lse=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib().attn_paged_decode(a["q"], a["kv"], a["bt"], a["ctx"], a["nseq"], a["nblocks"], a["mbps"],
+                                   a["maxctx"], a["hq"], a["hkv"], a["d"], a["bs"], a["scale"], a["out"], a["lse"],
+                                   a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=64), UNSUPPORTED), (dict(bs=16), UNSUPPORTED), (dict(d=100), UNSUPPORTED), (dict(hq=6, hkv=4), UNSUPPORTED),
+    (dict(maxctx=513), INVALID), (dict(nseq=-1), INVALID), (dict(q=None), INVALID), (dict(kv=None), INVALID),
+    (dict(bt=None), INVALID), (dict(ctx=None), INVALID), (dict(out=None), INVALID), (dict(scale=0.0), INVALID),
+    (dict(wsb=0), WS_SMALL), (dict(ws=None), INVALID), (dict(nblocks=0), INVALID),
+])
+def test_decode_validation(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_empty_is_noop():
+    assert _decode(nseq=0, q=None, out=None, ws=None, wsb=0) == OK
+
+
+def test_decode_workspace_query_is_monotone_and_covers_partials():
+    small = sav.attn_paged_decode_workspace_size(64, 32, 8, 128, 1024)
+    big = sav.attn_paged_decode_workspace_size(64, 32, 8, 128, 32768)
+    assert 0 < small <= big
+    # at least one fp32 partial (O and LSE) per (seq, head) whenever a split is possible
+    assert big >= 64 * 32 * (128 + 1) * 4
+    with pytest.raises(sav.AttnError):
+        sav.attn_paged_decode_workspace_size(64, 32, 8, 100, 1024)
+
+
+def _sparse(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, m=FAKE, ts=FAKE, b=1, nt=4, hq=2, hkv=2, d=128, scale=0.1, out=FAKE, lse=None,
+             ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return lib().attn_block_sparse_fwd(a["q"], a["k"], a["v"], a["m"], a["ts"], a["b"], a["nt"], a["hq"], a["hkv"],
+                                       a["d"], a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=32), UNSUPPORTED), (dict(hq=3, hkv=2), UNSUPPORTED), (dict(m=None), INVALID), (dict(ts=None), INVALID),
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(wsb=10), WS_SMALL), (dict(ws=None), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(nt=-1), INVALID),
+])
+def test_sparse_validation(kw, code):
+    assert _sparse(**kw) == code
+
+
+def test_sparse_workspace_query():
+    assert sav.attn_block_sparse_workspace_size(1, 12, 256) == 12 * 256 * 256 * 4 + 12 * 256 * 4
+
+
+def test_map_to_index_validation():
+    L = lib()
+    assert L.attn_block_map_to_index(FAKE, 4, 0, FAKE, FAKE, None) == INVALID
+    assert L.attn_block_map_to_index(None, 4, 8, FAKE, FAKE, None) == INVALID
+    assert L.attn_block_map_to_index(None, 0, 8, None, None, None) == OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+
+    q = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sav.attn_varlen_fwd(q, q, q, cu, cu, 4, 4, 0.125, False, out=torch.empty_like(q))

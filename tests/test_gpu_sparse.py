@@ -1,0 +1,156 @@
+"""GPU parity of attn_block_map_to_index (bit-exact) and attn_block_sparse_fwd
+against the fp64 oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import softmax_attention_varlen_amd as sav
+from tests._gpu_helpers import LSE_TOL, OUT_TOL, announce, assert_close, dev, guard_intact, guarded_empty, host
+from workloads import config5, randn_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("rows,cols,density", [(48, 256, 0.125), (17, 17, 0.5), (9, 100, 0.0), (9, 130, 1.0),
+                                               (3072, 256, 0.125)])
+def test_map_to_index_bit_exact(rows, cols, density):
+    rng = np.random.default_rng(rows + cols)
+    m = rng.random((rows, cols)) < density
+    if rows > 2:
+        m[1] = False  # an empty row
+        m[2] = True   # a full row
+    announce("map_to_index", rows, cols, density)
+    idx, num = sav.attn_block_map_to_index(dev(m.astype(np.uint8)))
+    torch.cuda.synchronize()
+    ref_idx, ref_num = oracle.map_to_index(m)
+    num = num.cpu().numpy()
+    idx = idx.cpu().numpy()
+    assert np.array_equal(num, ref_num)
+    for r in range(rows):
+        assert np.array_equal(idx[r, :num[r]], ref_idx[r, :ref_num[r]])
+
+
+def _tiled(shape, tile, b, hq, hkv, d, seed):
+    n = int(np.prod(shape))
+    part, sizes, non_pad, untile = oracle.tile_metadata(shape, tile, 64)
+    nt = sizes.size
+    raster = [randn_bf16((b, n, h, d), 1000 * seed + j) for j, h in enumerate((hq, hkv, hkv))]
+    tiled = []
+    for x in raster:
+        t = torch.zeros((b, nt * 64) + tuple(x.shape[2:]), dtype=x.dtype)
+        t[:, torch.from_numpy(non_pad)] = x[:, torch.from_numpy(part)]
+        tiled.append(t)
+    return tiled, sizes
+
+
+def run(qt, kt, vt, bmap, sizes, scale, with_lse=True):
+    res = sav.attn_block_sparse_fwd(dev(qt), dev(kt), dev(vt), dev(bmap.astype(np.uint8)),
+                                    dev(sizes.astype(np.int32)), scale, return_lse=with_lse)
+    torch.cuda.synchronize()
+    return res
+
+
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 1)])
+def test_partial_tiles_random_map(d, hq, hkv):
+    shape, tile = (5, 7, 9), (4, 4, 4)  # 2x2x3 = 12 boxes, clipped edges of 16..64 tokens
+    (qt, kt, vt), sizes = _tiled(shape, tile, 2, hq, hkv, d, seed=300 + d)
+    nt = sizes.size
+    rng = np.random.default_rng(d + hq)
+    bmap = rng.random((2, hq, nt, nt)) < 0.4
+    bmap[0, 0, 3] = False  # an empty row
+    bmap[1, -1, 5] = True  # a full row
+    scale = d ** -0.5
+    announce("sparse", d, hq, hkv, sizes.tolist())
+    out, lse = run(qt, kt, vt, bmap, sizes, scale)
+    ref_o, ref_l = oracle.block_sparse_attention(qt, kt, vt, bmap, sizes, scale)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("lse", host(lse), ref_l, LSE_TOL)
+
+
+def test_full_map_matches_dense_oracle_and_is_deterministic():
+    b, nt, h, d = 1, 5, 3, 128
+    q, k, v = (randn_bf16((b, nt * 64, h, d), 320 + j) for j in range(3))
+    bmap = np.ones((b, h, nt, nt), dtype=bool)
+    sizes = np.full(nt, 64, dtype=np.int32)
+    announce("sparse full map")
+    out, lse = run(q, k, v, bmap, sizes, d ** -0.5)
+    out2, _ = run(q, k, v, bmap, sizes, d ** -0.5)
+    ref_o, ref_l = oracle.dense_attention(q, k, v, d ** -0.5, False)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("lse", host(lse), ref_l, LSE_TOL)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_guards_and_pad_rows_zero():
+    shape, tile = (3, 5, 6), (2, 2, 3)
+    (qt, kt, vt), sizes = _tiled(shape, tile, 1, 2, 2, 64, seed=330)
+    nt = sizes.size
+    bmap = np.random.default_rng(1).random((1, 2, nt, nt)) < 0.5
+    announce("sparse guards")
+    q, k, v = dev(qt), dev(kt), dev(vt)
+    out, og = guarded_empty(q.shape, torch.bfloat16)
+    lse, lg = guarded_empty((1, 2, nt * 64), torch.float32)
+    sav.attn_block_sparse_fwd(q, k, v, dev(bmap.astype(np.uint8)), dev(sizes), 0.125, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert guard_intact(og) and guard_intact(lg)
+    pad = (np.arange(nt * 64) % 64) >= np.repeat(sizes, 64)
+    assert torch.all(out[:, torch.from_numpy(pad)] == 0)
+    assert torch.all(torch.isneginf(lse[:, :, torch.from_numpy(pad)]))
+
+
+def test_kept_tile_probe_bit_exact():
+    """K = 0 except one selected key per head with a logit 512 above the rest;
+    every query tile whose map keeps the selected key's tile must return that
+    key's V bit-exactly (V encodes tile and row)."""
+    nt, h, d = 9, 3, 64
+    q = torch.full((1, nt * 64, h, d), 8.0, dtype=torch.bfloat16)
+    k = torch.zeros_like(q)
+    v = torch.zeros_like(q)
+    v[0, :, :, 0] = (torch.arange(nt * 64) // 64).view(-1, 1).to(torch.bfloat16)
+    v[0, :, :, 1] = (torch.arange(nt * 64) % 64).view(-1, 1).to(torch.bfloat16)
+    sel = [5 * 64 + 17, 0, nt * 64 - 1]
+    for hh, j in enumerate(sel):
+        k[0, j, hh] = 8.0
+    rng = np.random.default_rng(5)
+    bmap = rng.random((1, h, nt, nt)) < 0.5
+    sizes = np.full(nt, 64, dtype=np.int32)
+    announce("sparse probe")
+    out = run(q, k, v, bmap, sizes, 0.125, with_lse=False).cpu()
+    hits = 0
+    for hh, j in enumerate(sel):
+        for a in range(nt):
+            if bmap[0, hh, a, j // 64]:
+                assert torch.equal(out[0, a * 64:(a + 1) * 64, hh], v[0, j, hh].expand(64, d))
+                hits += 1
+    assert hits >= 6
+
+
+def test_config5_full_size_with_oracle_map_sampled_tiles():
+    case = config5()
+    part, sizes, non_pad, untile = oracle.tile_metadata(case.video_shape, case.tile_shape, 64)
+    nt = sizes.size
+
+    def tile_order(x):
+        t = torch.zeros((x.shape[0], nt * 64) + tuple(x.shape[2:]), dtype=x.dtype)
+        t[:, torch.from_numpy(non_pad)] = x[:, torch.from_numpy(part)]
+        return t
+
+    qt, kt, vt = tile_order(case.q), tile_order(case.k), tile_order(case.v)
+    scores = oracle.pooled_scores(oracle.pool_tiles(qt, sizes), oracle.pool_tiles(kt, sizes), case.scale)
+    bmap = oracle.topk_block_map(scores, case.topk)
+    assert np.all(bmap.sum(-1) == 32)
+    announce("sparse config5")
+    out, lse = run(qt, kt, vt, bmap, sizes, case.scale)
+    tiles = [0, 1, 63, 64, 127, 128, 200, 255]
+    heads = [0, 5, 11]
+    ref_o, ref_l = oracle.block_sparse_attention(qt, kt, vt, bmap, sizes, case.scale, heads=heads, q_tiles=tiles)
+    rows = np.concatenate([np.arange(a * 64, a * 64 + 64) for a in tiles])
+    rt = torch.from_numpy(rows).cuda()
+    got_o = host(out.index_select(1, rt))[:, :, heads]
+    got_l = host(lse.index_select(2, rt))[:, heads]
+    assert_close("out", got_o, ref_o[:, rows][:, :, heads], OUT_TOL, bf16_output=True)
+    assert_close("lse", got_l, ref_l[:, heads][:, :, rows], LSE_TOL)
+    assert torch.isfinite(lse).all()

@@ -1,0 +1,152 @@
+"""GPU parity of attn_varlen_fwd against the fp64 oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import softmax_attention_varlen_amd as sav
+from tests._gpu_helpers import (LSE_TOL, OUT_TOL, announce, assert_close, dev, guard_intact, guarded_empty, host)
+from workloads import config1, config2, config3, varlen_case
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(case, with_lse=True):
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    cu_q, cu_k = dev(case.cu_seqlens_q), dev(case.cu_seqlens_k)
+    res = sav.attn_varlen_fwd(q, k, v, cu_q, cu_k, case.max_seqlen_q, case.max_seqlen_k, case.scale, case.causal,
+                              return_lse=with_lse)
+    torch.cuda.synchronize()
+    return res
+
+
+def check_full(case):
+    announce("varlen", case.name, case.cu_seqlens_q.tolist()[:8], case.num_heads, case.num_kv_heads,
+             case.head_dim, case.causal)
+    out, lse = run_case(case)
+    ref_o, ref_l = oracle.varlen_attention(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k, case.scale,
+                                           case.causal)
+    e_o = assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    e_l = assert_close("lse", host(lse), ref_l, LSE_TOL)
+    return e_o, e_l
+
+
+def test_config1_tiny_full_parity():
+    check_full(config1())
+
+
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 2), (6, 1)])
+def test_sweep_ragged(d, causal, hq, hkv):
+    # several 128-row query tiles and 64-key tiles, ragged tails, a 1-row doc
+    lens = [1, 129, 300, 64, 190]
+    case = varlen_case(lens, num_heads=hq, num_kv_heads=hkv, head_dim=d, causal=causal, seed=100 + d + hq + causal)
+    check_full(case)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_cross_lengths_bottom_right(causal):
+    # Lq != Lk per document, including Lq > Lk (rows with no key under causal)
+    case = varlen_case([5, 200, 130, 70], [77, 150, 130, 1], num_heads=4, num_kv_heads=2, head_dim=128,
+                       causal=causal, seed=41)
+    check_full(case)
+
+
+def test_empty_documents():
+    case = varlen_case([0, 70, 0, 33], [0, 70, 5, 0], num_heads=2, num_kv_heads=2, head_dim=64, causal=False,
+                       seed=42)
+    check_full(case)
+
+
+def test_no_lse_and_determinism():
+    case = varlen_case([300, 77], num_heads=4, num_kv_heads=2, head_dim=128, causal=True, seed=43)
+    announce("varlen determinism")
+    o1 = run_case(case, with_lse=False)
+    o2 = run_case(case, with_lse=False)
+    o3, l3 = run_case(case, with_lse=True)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+
+
+def test_guard_canaries():
+    case = varlen_case([130, 257], num_heads=4, num_kv_heads=4, head_dim=64, causal=False, seed=44)
+    announce("varlen guards")
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    out, og = guarded_empty(q.shape, torch.bfloat16)
+    lse, lg = guarded_empty((4, q.shape[0]), torch.float32)
+    sav.attn_varlen_fwd(q, k, v, dev(case.cu_seqlens_q), dev(case.cu_seqlens_k), case.max_seqlen_q,
+                        case.max_seqlen_k, case.scale, False, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert guard_intact(og) and guard_intact(lg)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_indexing_probe_bit_exact(causal):
+    """K = 0 except one selected key per (doc, head) with a logit 512 above the
+    rest; every row that can see it must return that key's V bit-exactly, and V
+    encodes (doc, token) so a wrong cu_seqlens offset is visible."""
+    lens = [3, 129, 64, 250, 1]
+    hq = hkv = 3
+    d = 64
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q = torch.full((T, hq, d), 8.0, dtype=torch.bfloat16)
+    k = torch.zeros((T, hkv, d), dtype=torch.bfloat16)
+    v = torch.zeros((T, hkv, d), dtype=torch.bfloat16)
+    sel = {}
+    for b, L in enumerate(lens):
+        for h in range(hkv):
+            j = [0, L - 1, L // 2][h]  # first, last, middle key of the document
+            sel[(b, h)] = j
+            k[cu[b] + j, h] = 8.0
+        for t in range(L):
+            v[cu[b] + t, :, 0] = b
+            v[cu[b] + t, :, 1] = t % 128
+            v[cu[b] + t, :, 2] = t // 128
+            v[cu[b] + t, :, 3] = torch.arange(hkv)
+    announce("varlen probe", causal)
+    out = sav.attn_varlen_fwd(dev(q), dev(k), dev(v), dev(cu), dev(cu), max(lens), max(lens), 0.125, causal)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    checked = 0
+    for b, L in enumerate(lens):
+        for h in range(hq):
+            j = sel[(b, h)]
+            for i in range(L):
+                if causal and j > i:
+                    continue
+                assert torch.equal(out[cu[b] + i, h], v[cu[b] + j, h]), (b, h, i, j)
+                checked += 1
+    assert checked > 500
+
+
+def _sample_rows(case, rng, extra=24):
+    rows = []
+    cu = case.cu_seqlens_q
+    for b in range(case.batch):
+        L = int(cu[b + 1] - cu[b])
+        cand = {0, 1, 31, 32, 63, 64, 127, 128, 129, L // 2, L - 129, L - 128, L - 2, L - 1}
+        cand |= set(rng.integers(0, L, extra).tolist())
+        rows += [int(cu[b]) + r for r in sorted(cand) if 0 <= r < L]
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("make", [config2, config3])
+def test_full_size_config_sampled_rows(make):
+    case = make()
+    announce("varlen full-size", case.name)
+    out, lse = run_case(case)
+    rng = np.random.default_rng(7)
+    rows = _sample_rows(case, rng)
+    ref_o, ref_l = oracle.varlen_attention(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k, case.scale,
+                                           case.causal, rows=rows)
+    rows_t = torch.from_numpy(rows).cuda()
+    assert_close("out", host(out.index_select(0, rows_t)), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("lse", host(lse.index_select(1, rows_t)), ref_l, LSE_TOL)
+    # properties over every row: finite, inside the value range of V
+    assert torch.isfinite(lse).all()
+    vmax = case.v.float().abs().max().item()
+    assert out.float().abs().max().item() <= vmax + 1e-2
