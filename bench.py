@@ -1,0 +1,266 @@
+"""Attention forward throughput on one MI355X.
+
+Default run (no flags): the DiT-style dense self-attention workload (batch 2 x
+seq 4096 packed as uniform varlen, 24 heads, head_dim 128, non-causal, fp32 LSE)
+is the headline line (TFLOP/s). The causal GQA varlen prefill, paged decode
+and video block-sparse workloads are timed too and reported under "secondary".
+Inputs are seeded synthetic bf16 tensors already resident in HBM when the
+timed region starts; each step is one call of the entry point (every kernel it
+launches). Timing uses HIP events on the stream the kernels run on.
+
+Prints ONE JSON line. `--gpus N` with N > 1 is refused: this library runs on
+one GPU and nothing here shards across devices.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import softmax_attention_varlen_amd as sav  # noqa: E402
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work (only what the method must do)
+# ----------------------------------------------------------------------------
+
+def varlen_flops(case) -> float:
+    """4 * D flops per allowed (query, key) pair and query head (QK^T and PV)."""
+    lq = np.diff(case.cu_seqlens_q).astype(np.int64)
+    lk = np.diff(case.cu_seqlens_k).astype(np.int64)
+    pairs = 0
+    for a, b in zip(lq, lk):
+        if case.causal:
+            i = np.arange(a)
+            pairs += int(np.clip(i + (b - a) + 1, 0, b).sum())
+        else:
+            pairs += int(a * b)
+    return 4.0 * case.head_dim * case.num_heads * pairs
+
+
+def paged_bytes(case) -> float:
+    """K and V bytes of every context token, plus Q, O, block tables and lengths."""
+    kv = float(case.context_lens.astype(np.int64).sum()) * case.num_kv_heads * case.head_dim * 2 * 2
+    qo = 2.0 * case.num_seqs * case.num_heads * case.head_dim * 2
+    return kv + qo + case.block_tables.nbytes + case.context_lens.nbytes
+
+
+def sparse_flops(bmap: np.ndarray, sizes: np.ndarray, head_dim: int) -> float:
+    """4 * D flops per (valid query row, valid key row) pair of every kept tile pair."""
+    sz = sizes.astype(np.float64)
+    per_pair = np.outer(sz, sz)  # [nQ, nK] valid row pairs
+    return 4.0 * head_dim * float((bmap.astype(np.float64) * per_pair[None, None]).sum())
+
+
+# ----------------------------------------------------------------------------
+# timing
+# ----------------------------------------------------------------------------
+
+def time_steps(step, steps: int, warmup: int) -> float:
+    """Average milliseconds per step over `steps` timed steps (HIP events)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def bench_varlen(case, steps, warmup, with_lse=True):
+    dev = torch.device("cuda")
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    cu_q = torch.from_numpy(case.cu_seqlens_q).to(dev)
+    cu_k = torch.from_numpy(case.cu_seqlens_k).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((case.num_heads, q.shape[0]), dtype=torch.float32, device=dev) if with_lse else None
+
+    def step():
+        sav.attn_varlen_fwd(q, k, v, cu_q, cu_k, case.max_seqlen_q, case.max_seqlen_k, case.scale, case.causal,
+                            out=out, lse=lse)
+
+    ms = time_steps(step, steps, warmup)
+    return ms, varlen_flops(case)
+
+
+def bench_paged(case, steps, warmup):
+    dev = torch.device("cuda")
+    q, kv = case.q.to(dev), case.kv_cache.to(dev)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cl = torch.from_numpy(case.context_lens).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((case.num_heads, case.num_seqs), dtype=torch.float32, device=dev)
+    ws = torch.empty(sav.attn_paged_decode_workspace_size(case.num_seqs, case.num_heads, case.num_kv_heads,
+                                                          case.head_dim, case.max_context_len),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        sav.attn_paged_decode(q, kv, bt, cl, case.max_context_len, case.scale, out=out, lse=lse, workspace=ws)
+
+    ms = time_steps(step, steps, warmup)
+    del kv
+    return ms, paged_bytes(case)
+
+
+def bench_sparse(case, steps, warmup):
+    """Tile order, pooled-score top-k map and the block-sparse call all run in the
+    library's kernels; only the block-sparse call is in the timed step."""
+    dev = torch.device("cuda")
+    prep = sav.vsa_prepare(case.q.to(dev), case.k.to(dev), case.v.to(dev), case.video_shape, case.tile_shape,
+                           case.topk, case.scale)
+    qt, kt, vt, bmap, sizes = prep["q"], prep["k"], prep["v"], prep["block_map"], prep["tile_sizes"]
+    out = torch.empty_like(qt)
+    lse = torch.empty((qt.shape[0], case.num_heads, qt.shape[1]), dtype=torch.float32, device=dev)
+    ws = torch.empty(sav.attn_block_sparse_workspace_size(qt.shape[0], case.num_heads, sizes.numel()),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        sav.attn_block_sparse_fwd(qt, kt, vt, bmap, sizes, case.scale, out=out, lse=lse, workspace=ws)
+
+    ms = time_steps(step, steps, warmup)
+    flops = sparse_flops(bmap.cpu().numpy(), sizes.cpu().numpy(), case.head_dim)
+    prep_ms = time_steps(lambda: sav.vsa_prepare(case.q.to(dev), case.k.to(dev), case.v.to(dev), case.video_shape,
+                                                 case.tile_shape, case.topk, case.scale), 3, 1)
+    return ms, flops, prep_ms
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle on a bounded sample of the headline workload
+# ----------------------------------------------------------------------------
+
+def cpu_baseline(case, budget_s=10.0):
+    import oracle  # test infrastructure: used only for this reported baseline
+    from threadpoolctl import threadpool_info
+
+    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    rows_per_doc = 128
+    lq = np.diff(case.cu_seqlens_q)
+    while True:
+        rows = np.concatenate([case.cu_seqlens_q[b] + np.arange(min(rows_per_doc, lq[b]))
+                               for b in range(case.batch)])
+        t0 = time.perf_counter()
+        oracle.varlen_attention(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k, case.scale,
+                                case.causal, rows=rows)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or rows_per_doc >= int(lq.max()):
+            break
+        rows_per_doc *= 2
+    lk = np.diff(case.cu_seqlens_k)
+    flops = 4.0 * case.head_dim * case.num_heads * float(sum(min(rows_per_doc, lq[b]) * lk[b]
+                                                             for b in range(case.batch)))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {rows_per_doc} query rows of each of the {case.batch} documents, all {case.num_heads} "
+                      f"heads, fp64 numpy ({dt:.1f} s)",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse"], default=None,
+                    help="time one workload only (for profiling runs)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (no multi-GPU path exists)"}))
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(2)
+    sav.load_library()
+    torch.cuda.set_device(0)
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    secondary = []
+    head = None
+    if args.only in (None, "dense"):
+        case = workloads.config2()
+        ms, flops = bench_varlen(case, args.steps, args.warmup)
+        tf = flops / (ms * 1e-3) / 1e12
+        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s")
+        head = (case, ms, flops, tf)
+    if args.only in (None, "causal") and not (args.only is None and args.no_secondary):
+        case = workloads.config3()
+        ms, flops = bench_varlen(case, args.steps, args.warmup)
+        tf = flops / (ms * 1e-3) / 1e12
+        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s")
+        secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+                          "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
+                          "algorithmic_gflop": round(flops / 1e9, 3)})
+    if args.only in (None, "paged") and not (args.only is None and args.no_secondary):
+        case = workloads.config4()
+        ms, nbytes = bench_paged(case, args.steps, args.warmup)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"{case.name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+        secondary.append({"workload": case.name, "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
+                          "frac_of_peak": round(gbs / PEAK_HBM_GBPS, 4), "bound": "hbm",
+                          "algorithmic_gb": round(nbytes / 1e9, 4)})
+        del case
+        torch.cuda.empty_cache()
+    if args.only in (None, "sparse") and not (args.only is None and args.no_secondary):
+        case = workloads.config5()
+        ms, flops, prep_ms = bench_sparse(case, args.steps, args.warmup)
+        tf = flops / (ms * 1e-3) / 1e12
+        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s (map build {prep_ms * 1e3:.0f} us)")
+        secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+                          "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
+                          "algorithmic_gflop": round(flops / 1e9, 3),
+                          "tile_prep_and_map_ms": round(prep_ms, 4)})
+
+    if head is None:  # a single secondary workload was asked for
+        print(json.dumps({"metric": "attention throughput", "secondary": secondary}))
+        return
+    case, ms, flops, tf = head
+    line = {
+        "metric": "attention TFLOP/s (prefill, sparse) and HBM GB/s (paged decode), 1 MI355X",
+        "value": round(tf, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, resident in HBM)",
+        "config": {"workload": case.name, "batch": 2, "seq_len": 4096, "num_heads": case.num_heads,
+                   "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "causal": case.causal,
+                   "layout": "packed varlen [total, heads, dim], cu_seqlens [0, 4096, 8192]", "lse": "fp32"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "varlen_fwd_kernel<128,false>",
+                     "algorithmic_gflop_per_launch": round(flops / 1e9, 3)},
+        "secondary": secondary,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a sample (cpu baseline)")
+        line["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

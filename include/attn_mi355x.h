@@ -180,6 +180,53 @@ attn_status_t attn_block_sparse_fwd(const void* q, const void* k, const void* v,
                                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                                     void* stream);
 
+/*
+ * Raster -> padded tile order (vLLM-Omni fastvideo_vsa.py page:
+ * _get_tile_partition_indices, _construct_variable_block_sizes,
+ * _get_non_pad_index; FastVideoVSAImpl._forward_h3 gathers q/k/v this way).
+ * A raster (t, h, w) latent is cut into (tile_t, tile_h, tile_w) boxes,
+ * enumerated t-box slowest, then h, then w, tokens inside a box in raster
+ * order, edge boxes clipped; box c owns rows [64c, 64c + 64).
+ *   x          [batch, t*h*w, row_elems] bf16 in raster order
+ *              (row_elems = heads * head_dim, a multiple of 8)
+ *   x_tiled    [batch, num_tiles * 64, row_elems] bf16; rows past a box's size
+ *              are written 0
+ *   tile_sizes nullable; [num_tiles] int32, real rows of each box
+ * num_tiles = ceil(t/tile_t) * ceil(h/tile_h) * ceil(w/tile_w);
+ * tile_t * tile_h * tile_w must be <= 64. Pure data movement (bit-exact).
+ */
+attn_status_t attn_vsa_tile_gather(const void* x, int32_t batch, int32_t t, int32_t h, int32_t w, int32_t tile_t,
+                                   int32_t tile_h, int32_t tile_w, int32_t row_elems, void* x_tiled,
+                                   int32_t* tile_sizes, void* stream);
+
+/* Inverse of attn_vsa_tile_gather: padded tile order -> raster order (the
+ * page's untile gather, non_pad[argsort(partition)]). Padding rows are
+ * dropped. Same argument meaning; x [batch, t*h*w, row_elems] is written. */
+attn_status_t attn_vsa_untile(const void* x_tiled, int32_t batch, int32_t t, int32_t h, int32_t w, int32_t tile_t,
+                              int32_t tile_h, int32_t tile_w, int32_t row_elems, void* x, void* stream);
+
+/* Workspace bytes for attn_vsa_block_map (fp32 tile means of q and k). */
+attn_status_t attn_vsa_block_map_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                                int32_t num_tiles, int32_t head_dim, size_t* bytes);
+
+/*
+ * Per-query-tile top-k block map from tile means (vLLM-Omni fastvideo_vsa.py
+ * page: _pool_h3_tiles, the pooled score matmul and _build_h3_block_map in
+ * FastVideoVSAImpl._forward_h3).
+ *   q_tiled     [batch, num_tiles * 64, num_heads, head_dim] bf16 tile order
+ *   k_tiled     [batch, num_tiles * 64, num_kv_heads, head_dim] bf16 tile order
+ *   tile_sizes  [num_tiles] int32 in [0, 64]
+ *   block_map   [batch, num_heads, num_tiles, num_tiles] uint8 (1 = keep)
+ * Each tile's mean is taken in fp32 over its real rows (divided by
+ * max(size, 1)); score[a][c] = scale * qmean_a . kmean_c in fp32; row a keeps
+ * the min(topk, num_tiles) largest scores, a tie going to the lower tile index;
+ * topk >= num_tiles keeps every tile. num_tiles <= 16384, topk >= 1.
+ */
+attn_status_t attn_vsa_block_map(const void* q_tiled, const void* k_tiled, const int32_t* tile_sizes,
+                                 int32_t batch, int32_t num_tiles, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float softmax_scale, int32_t topk, uint8_t* block_map,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -29,6 +29,12 @@ __all__ = [
     "attn_block_map_to_index",
     "attn_block_sparse_workspace_size",
     "attn_block_sparse_fwd",
+    "attn_vsa_tile_gather",
+    "attn_vsa_untile",
+    "attn_vsa_block_map_workspace_size",
+    "attn_vsa_block_map",
+    "vsa_num_tiles",
+    "vsa_prepare",
     "SUPPORTED_HEAD_DIMS",
 ]
 
@@ -50,6 +56,10 @@ _SIGS = {
     "attn_block_sparse_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "attn_block_sparse_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
                                              _sz, _p]),
+    "attn_vsa_tile_gather": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p, _p]),
+    "attn_vsa_untile": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]),
+    "attn_vsa_block_map_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "attn_vsa_block_map": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _sz, _p]),
 }
 
 _lib = None
@@ -257,3 +267,97 @@ def attn_block_sparse_fwd(q, k, v, block_map, tile_sizes, softmax_scale: float, 
         _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(), _stream_ptr(q, stream))
     _check("attn_block_sparse_fwd", st)
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def vsa_num_tiles(video_shape, tile_shape) -> int:
+    """Number of (clipped) boxes a raster shape is cut into."""
+    n = 1
+    for s_, t_ in zip(video_shape, tile_shape):
+        n *= -(-int(s_) // int(t_))
+    return n
+
+
+def attn_vsa_tile_gather(x, video_shape, tile_shape, x_tiled=None, tile_sizes=None, stream=None):
+    """Raster [B, t*h*w, H, D] bf16 -> padded tile order [B, n_tiles*64, H, D] (+ int32 tile sizes)."""
+    b, n = x.shape[:2]
+    row = int(x[0, 0].numel()) if n else int(torch.tensor(x.shape[2:]).prod())
+    nt = vsa_num_tiles(video_shape, tile_shape)
+    dev = x.device
+    if x_tiled is None:
+        x_tiled = torch.empty((b, nt * 64) + tuple(x.shape[2:]), dtype=x.dtype, device=dev)
+    _shape(x_tiled, "x_tiled", (b, nt * 64) + tuple(x.shape[2:]))
+    if tile_sizes is None:
+        tile_sizes = torch.empty(nt, dtype=torch.int32, device=dev)
+    _shape(tile_sizes, "tile_sizes", (nt,))
+    t, h, w = (int(v) for v in video_shape)
+    if n != t * h * w:
+        raise ValueError("x's sequence length must equal t*h*w")
+    st = load_library().attn_vsa_tile_gather(
+        _dev(x, "x", torch.bfloat16), b, t, h, w, *(int(v) for v in tile_shape), row,
+        _dev(x_tiled, "x_tiled", torch.bfloat16, dev), _dev(tile_sizes, "tile_sizes", torch.int32, dev),
+        _stream_ptr(x, stream))
+    _check("attn_vsa_tile_gather", st)
+    return x_tiled, tile_sizes
+
+
+def attn_vsa_untile(x_tiled, video_shape, tile_shape, out=None, stream=None):
+    """Padded tile order [B, n_tiles*64, H, D] -> raster [B, t*h*w, H, D]."""
+    b = x_tiled.shape[0]
+    t, h, w = (int(v) for v in video_shape)
+    nt = vsa_num_tiles(video_shape, tile_shape)
+    _shape(x_tiled, "x_tiled", (b, nt * 64) + tuple(x_tiled.shape[2:]))
+    row = 1
+    for v_ in x_tiled.shape[2:]:
+        row *= int(v_)
+    dev = x_tiled.device
+    if out is None:
+        out = torch.empty((b, t * h * w) + tuple(x_tiled.shape[2:]), dtype=x_tiled.dtype, device=dev)
+    _shape(out, "out", (b, t * h * w) + tuple(x_tiled.shape[2:]))
+    st = load_library().attn_vsa_untile(
+        _dev(x_tiled, "x_tiled", torch.bfloat16), b, t, h, w, *(int(v) for v in tile_shape), row,
+        _dev(out, "out", torch.bfloat16, dev), _stream_ptr(x_tiled, stream))
+    _check("attn_vsa_untile", st)
+    return out
+
+
+def attn_vsa_block_map_workspace_size(batch: int, num_heads: int, num_kv_heads: int, num_tiles: int,
+                                      head_dim: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("attn_vsa_block_map_workspace_size",
+           load_library().attn_vsa_block_map_workspace_size(batch, num_heads, num_kv_heads, num_tiles, head_dim,
+                                                            ctypes.byref(n)))
+    return int(n.value)
+
+
+def attn_vsa_block_map(q_tiled, k_tiled, tile_sizes, softmax_scale: float, topk: int, block_map=None,
+                       workspace=None, stream=None):
+    """Top-k per query tile of scale * mean(q_tile) . mean(k_tile) -> uint8 [B, H, nT, nT]."""
+    b, s, hq, d = q_tiled.shape
+    hkv = k_tiled.shape[2]
+    nt = s // 64
+    _shape(k_tiled, "k_tiled", (b, s, hkv, d))
+    _shape(tile_sizes, "tile_sizes", (nt,))
+    dev = q_tiled.device
+    if block_map is None:
+        block_map = torch.empty((b, hq, nt, nt), dtype=torch.uint8, device=dev)
+    _shape(block_map, "block_map", (b, hq, nt, nt))
+    need = attn_vsa_block_map_workspace_size(b, hq, hkv, nt, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load_library().attn_vsa_block_map(
+        _dev(q_tiled, "q_tiled", torch.bfloat16), _dev(k_tiled, "k_tiled", torch.bfloat16, dev),
+        _dev(tile_sizes, "tile_sizes", torch.int32, dev), b, nt, hq, hkv, d, float(softmax_scale), int(topk),
+        _dev(block_map, "block_map", torch.uint8, dev), _dev(workspace, "workspace", torch.uint8, dev),
+        workspace.numel(), _stream_ptr(q_tiled, stream))
+    _check("attn_vsa_block_map", st)
+    return block_map
+
+
+def vsa_prepare(q, k, v, video_shape, tile_shape, topk: int, softmax_scale: float, stream=None):
+    """Raster q/k/v -> tile order plus the top-k block map, all in the library's
+    kernels. Returns a dict with q, k, v (tile order), block_map and tile_sizes."""
+    qt, sizes = attn_vsa_tile_gather(q, video_shape, tile_shape, stream=stream)
+    kt, _ = attn_vsa_tile_gather(k, video_shape, tile_shape, stream=stream)
+    vt, _ = attn_vsa_tile_gather(v, video_shape, tile_shape, stream=stream)
+    bmap = attn_vsa_block_map(qt, kt, sizes, softmax_scale, topk, stream=stream)
+    return {"q": qt, "k": kt, "v": vt, "block_map": bmap, "tile_sizes": sizes}

@@ -142,4 +142,70 @@ attn_status_t attn_block_sparse_fwd(const void* q, const void* k, const void* v,
   return from_hip(attn::launch_block_sparse_fwd(a, (hipStream_t)stream));
 }
 
+static attn_status_t check_vsa_geometry(int32_t batch, int32_t t, int32_t h, int32_t w, int32_t tile_t,
+                                        int32_t tile_h, int32_t tile_w, int32_t row_elems) {
+  if (batch < 0 || t < 0 || h < 0 || w < 0 || row_elems <= 0) return ATTN_ERR_INVALID_ARG;
+  if (tile_t <= 0 || tile_h <= 0 || tile_w <= 0) return ATTN_ERR_INVALID_ARG;
+  if ((long long)tile_t * tile_h * tile_w > 64) return ATTN_ERR_UNSUPPORTED;
+  if (row_elems % 8 != 0) return ATTN_ERR_UNSUPPORTED;
+  const long long n = (long long)t * h * w;
+  const long long tiles = (long long)((t + tile_t - 1) / tile_t) * ((h + tile_h - 1) / tile_h) *
+                          ((w + tile_w - 1) / tile_w);
+  if ((long long)batch * (n > tiles * 64 ? n : tiles * 64) > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status_t attn_vsa_tile_gather(const void* x, int32_t batch, int32_t t, int32_t h, int32_t w, int32_t tile_t,
+                                   int32_t tile_h, int32_t tile_w, int32_t row_elems, void* x_tiled,
+                                   int32_t* tile_sizes, void* stream) {
+  const attn_status_t st = check_vsa_geometry(batch, t, h, w, tile_t, tile_h, tile_w, row_elems);
+  if (st != ATTN_OK) return st;
+  if (batch == 0 || (long long)t * h * w == 0) return ATTN_OK;
+  if (x == nullptr || x_tiled == nullptr) return ATTN_ERR_INVALID_ARG;
+  const attn::VsaGeometry g{t, h, w, tile_t, tile_h, tile_w};
+  return from_hip(attn::launch_tile_gather(x, g, batch, row_elems, x_tiled, tile_sizes, (hipStream_t)stream));
+}
+
+attn_status_t attn_vsa_untile(const void* x_tiled, int32_t batch, int32_t t, int32_t h, int32_t w, int32_t tile_t,
+                              int32_t tile_h, int32_t tile_w, int32_t row_elems, void* x, void* stream) {
+  const attn_status_t st = check_vsa_geometry(batch, t, h, w, tile_t, tile_h, tile_w, row_elems);
+  if (st != ATTN_OK) return st;
+  if (batch == 0 || (long long)t * h * w == 0) return ATTN_OK;
+  if (x == nullptr || x_tiled == nullptr) return ATTN_ERR_INVALID_ARG;
+  const attn::VsaGeometry g{t, h, w, tile_t, tile_h, tile_w};
+  return from_hip(attn::launch_untile(x_tiled, g, batch, row_elems, x, (hipStream_t)stream));
+}
+
+attn_status_t attn_vsa_block_map_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                                int32_t num_tiles, int32_t head_dim, size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_tiles < 0 || head_dim <= 0) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  *bytes = attn::vsa_map_workspace_bytes(batch, num_heads, num_kv_heads, num_tiles, head_dim);
+  return ATTN_OK;
+}
+
+attn_status_t attn_vsa_block_map(const void* q_tiled, const void* k_tiled, const int32_t* tile_sizes,
+                                 int32_t batch, int32_t num_tiles, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float softmax_scale, int32_t topk, uint8_t* block_map,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || num_tiles < 0 || num_heads <= 0 || num_kv_heads <= 0 || topk < 1) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
+  if (num_tiles > 16384) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0 || num_tiles == 0) return ATTN_OK;
+  if (q_tiled == nullptr || k_tiled == nullptr || tile_sizes == nullptr || block_map == nullptr) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  if ((long long)batch * num_heads * num_tiles * num_tiles > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn::vsa_map_workspace_bytes(batch, num_heads, num_kv_heads, num_tiles, head_dim);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_vsa_block_map(q_tiled, k_tiled, tile_sizes, batch, num_tiles, num_heads, num_kv_heads,
+                                             head_dim, softmax_scale, topk, block_map, workspace,
+                                             (hipStream_t)stream));
+}
+
 }  // extern "C"

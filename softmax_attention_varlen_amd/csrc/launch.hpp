@@ -75,4 +75,18 @@ struct SparseArgs {
 size_t sparse_workspace_bytes(int batch, int num_heads, int num_tiles);
 hipError_t launch_block_sparse_fwd(const SparseArgs& a, hipStream_t stream);
 
+// Video tile geometry (raster (t, h, w) cut into (tile_t, tile_h, tile_w) boxes).
+struct VsaGeometry {
+  int t, h, w, tile_t, tile_h, tile_w;
+};
+
+int vsa_num_tiles(const VsaGeometry& g);
+hipError_t launch_tile_gather(const void* x, const VsaGeometry& g, int batch, int row_elems, void* y,
+                              int32_t* sizes, hipStream_t stream);
+hipError_t launch_untile(const void* y, const VsaGeometry& g, int batch, int row_elems, void* x, hipStream_t stream);
+size_t vsa_map_workspace_bytes(int batch, int heads, int kv_heads, int n_tiles, int head_dim);
+hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const int32_t* sizes, int batch,
+                                int n_tiles, int heads, int kv_heads, int head_dim, float scale, int topk,
+                                uint8_t* map, void* workspace, hipStream_t stream);
+
 }  // namespace attn

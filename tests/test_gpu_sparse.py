@@ -154,3 +154,98 @@ def test_config5_full_size_with_oracle_map_sampled_tiles():
     assert_close("out", got_o, ref_o[:, rows][:, :, heads], OUT_TOL, bf16_output=True)
     assert_close("lse", got_l, ref_l[:, heads][:, :, rows], LSE_TOL)
     assert torch.isfinite(lse).all()
+
+
+# --------------------------------------------------------------------------
+# tile geometry and block map built on the GPU
+# --------------------------------------------------------------------------
+
+def check_map_is_valid_topk(gpu_map, scores, topk, eps=1e-6):
+    """Where the fp64 oracle's k-th and (k+1)-th scores of a row are apart by
+    more than eps the kept set is unique and must match exactly; otherwise every
+    kept score must be >= the k-th largest - eps and every dropped one <= it + eps."""
+    s = np.asarray(scores, dtype=np.float64)
+    g = np.asarray(gpu_map).astype(bool)
+    n = s.shape[-1]
+    keep = min(topk, n)
+    assert np.all(g.sum(-1) == keep)
+    if keep == n:
+        return 0
+    srt = -np.sort(-s, axis=-1)
+    kth, nxt = srt[..., keep - 1], srt[..., keep]
+    unique = (kth - nxt) > eps
+    ref = oracle.topk_block_map(s, topk)
+    assert np.array_equal(g[unique], ref[unique])
+    kept_min = np.where(g, s, np.inf).min(-1)
+    drop_max = np.where(~g, s, -np.inf).max(-1)
+    assert np.all(kept_min >= kth - eps) and np.all(drop_max <= kth + eps)
+    return int((~unique).sum())
+
+
+@pytest.mark.parametrize("shape,tile", [((5, 7, 9), (4, 4, 4)), ((3, 2, 5), (2, 2, 3)), ((16, 32, 32), (4, 4, 4)),
+                                        ((1, 1, 3), (4, 4, 4))])
+def test_tile_gather_untile_bit_exact(shape, tile):
+    n = int(np.prod(shape))
+    x = randn_bf16((2, n, 3, 64), 77)
+    announce("tile gather", shape, tile)
+    xt, sizes = sav.attn_vsa_tile_gather(dev(x), shape, tile)
+    back = sav.attn_vsa_untile(xt, shape, tile)
+    torch.cuda.synchronize()
+    part, ref_sizes, non_pad, untile = oracle.tile_metadata(shape, tile, 64)
+    ref_t = oracle.to_tile_order(x.view(torch.int16).numpy(), shape, tile)  # integer view: exact bytes
+    assert np.array_equal(sizes.cpu().numpy(), ref_sizes)
+    assert np.array_equal(xt.cpu().view(torch.int16).numpy(), ref_t)
+    assert torch.equal(back.cpu().view(torch.int16), x.view(torch.int16))
+
+
+@pytest.mark.parametrize("topk", [1, 4, 12, 20])
+def test_block_map_matches_oracle_topk(topk):
+    shape, tile = (5, 7, 9), (4, 4, 4)
+    (qt, kt, vt), sizes = _tiled(shape, tile, 2, 4, 2, 128, seed=340)
+    announce("vsa block map", topk)
+    gmap = sav.attn_vsa_block_map(dev(qt), dev(kt), dev(sizes), 128 ** -0.5, topk)
+    torch.cuda.synchronize()
+    scores = oracle.pooled_scores(oracle.pool_tiles(qt, sizes),
+                                  np.repeat(oracle.pool_tiles(kt, sizes), 2, axis=1), 128 ** -0.5)
+    check_map_is_valid_topk(gmap.cpu().numpy(), scores, topk)
+
+
+def test_raster_pipeline_end_to_end():
+    """raster q/k/v -> tile order -> GPU block map -> block-sparse -> untile, against
+    raster-order oracle attention with the same (GPU-built, validated) map."""
+    shape, tile, hq, d, topk = (5, 7, 9), (4, 4, 4), 2, 64, 5
+    n = int(np.prod(shape))
+    q, k, v = (randn_bf16((1, n, hq, d), 350 + j) for j in range(3))
+    announce("vsa pipeline")
+    prep = sav.vsa_prepare(dev(q), dev(k), dev(v), shape, tile, topk, d ** -0.5)
+    out_t = sav.attn_block_sparse_fwd(prep["q"], prep["k"], prep["v"], prep["block_map"], prep["tile_sizes"],
+                                      d ** -0.5)
+    out = sav.attn_vsa_untile(out_t, shape, tile)
+    torch.cuda.synchronize()
+    bmap = prep["block_map"].cpu().numpy().astype(bool)
+    _, sizes, _, _ = oracle.tile_metadata(shape, tile, 64)
+    qt = oracle.to_tile_order(q.double().numpy(), shape, tile)
+    kt = oracle.to_tile_order(k.double().numpy(), shape, tile)
+    vt = oracle.to_tile_order(v.double().numpy(), shape, tile)
+    scores = oracle.pooled_scores(oracle.pool_tiles(qt, sizes), oracle.pool_tiles(kt, sizes), d ** -0.5)
+    check_map_is_valid_topk(bmap, scores, topk)
+    ref_t, _ = oracle.block_sparse_attention(qt, kt, vt, bmap, sizes, d ** -0.5)
+    assert_close("out", host(out), oracle.from_tile_order(ref_t, shape, tile), OUT_TOL, bf16_output=True)
+
+
+def test_config5_gpu_map_matches_oracle_map():
+    case = config5()
+    announce("config5 gpu map")
+    prep = sav.vsa_prepare(dev(case.q), dev(case.k), dev(case.v), case.video_shape, case.tile_shape, case.topk,
+                           case.scale)
+    torch.cuda.synchronize()
+    part, sizes, non_pad, _ = oracle.tile_metadata(case.video_shape, case.tile_shape, 64)
+    nt = sizes.size
+    qt = torch.zeros((1, nt * 64, 12, 128), dtype=torch.bfloat16)
+    kt = torch.zeros_like(qt)
+    qt[:, torch.from_numpy(non_pad)] = case.q[:, torch.from_numpy(part)]
+    kt[:, torch.from_numpy(non_pad)] = case.k[:, torch.from_numpy(part)]
+    assert torch.equal(prep["q"].cpu().view(torch.int16), qt.view(torch.int16))
+    scores = oracle.pooled_scores(oracle.pool_tiles(qt, sizes), oracle.pool_tiles(kt, sizes), case.scale)
+    near_ties = check_map_is_valid_topk(prep["block_map"].cpu().numpy(), scores, case.topk)
+    print(f"[parity] config5 map: rows with a near-tie at the cut: {near_ties} of {scores.shape[2] * 12}")
