@@ -177,8 +177,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse"], default=None,
-                    help="time one workload only (for profiling runs)")
+    ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse", "copy"], default=None,
+                    help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
+                         "copy, the reference that scales the HBM byte counters")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -193,6 +194,15 @@ def main():
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        ms = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
+        print(json.dumps({"metric": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                          "ms": round(ms, 5), "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
+        return
 
     secondary = []
     head = None
