@@ -23,6 +23,9 @@ struct VarlenArgs {
 };
 
 hipError_t launch_varlen_fwd(const VarlenArgs& a, hipStream_t stream);
+// head_dim 128: pipelined direct-to-LDS prefill (prefill_d128.hip)
+bool prefill_d128_supported(const VarlenArgs& a);
+hipError_t launch_prefill_d128(const VarlenArgs& a, hipStream_t stream);
 long varlen_grid_size(int batch, int max_seqlen_q, int num_heads);
 
 // Paged decode: the context of each sequence is cut into splits of

@@ -119,6 +119,7 @@ static hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_varlen_fwd(const VarlenArgs& a, hipStream_t stream) {
+  if (prefill_d128_supported(a)) return launch_prefill_d128(a, stream);
   const bool causal = a.causal != 0;
 #define ATTN_VARLEN_CASE(DIM)                                                              \
   case DIM:                                                                                \
