@@ -6,10 +6,11 @@
 //   * global -> LDS with direct-to-LDS 16-byte loads (no VGPR staging, no
 //     transpose on the way in). Load block b (16 per tile) is one contiguous
 //     1 KB holding the four keys κ(b) + {0, 16, 32, 48}; blocks sit 1040 bytes
-//     apart. Key k%16 = (b3 b2 b1 b0) lives in block (b3 b1 b0 b2): then 8 (or
-//     16) consecutive keys of a K read sit in distinct 4-bank groups, and the
-//     4 keys x 32 bytes of a transposing V read sit in disjoint 8-bank groups,
-//     for 32- and 64-bank LDS alike; every LDS address is a per-lane base
+//     apart (16 bytes = 4 banks of pad). Key k%16 = (b3 b2 b1 b0) lives in
+//     block (b1 b0 b3 b2). A 16-lane slice of a K read then covers the 16
+//     blocks (all 64 banks once), and a 32-lane slice of a transposing V read
+//     (4 keys x 64 bytes) puts its 4 rows 16 banks apart: both conflict-free on
+//     gfx950's 64-bank LDS, as measured. Every LDS address is a per-lane base
 //     plus a compile-time offset.
 //   * K is read row-wise (ds_read_b128) as the A operand of S^T = K Q^T.
 //   * V stays row-major and is read with the transposing ds_read_b64_tr_b16,
@@ -38,14 +39,10 @@ constexpr float kRescaleThreshold = 8.f;      // log2 units
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-// LDS block of key k (0..15 within its group of 16): bits (b3 b2 b1 b0) -> (b3 b1 b0 b2).
-__device__ __forceinline__ uint32_t key_block(uint32_t k) {
-  return (k & 8u) | ((k & 3u) << 1) | ((k >> 2) & 1u);
-}
-// The key held by LDS block b (inverse of key_block).
-__device__ __forceinline__ uint32_t block_key(uint32_t b) {
-  return (b & 8u) | ((b & 1u) << 2) | ((b >> 1) & 3u);
-}
+// LDS block of key k (0..15 within its group of 16): bits (b3 b2 b1 b0) -> (b1 b0 b3 b2).
+__device__ __forceinline__ uint32_t key_block(uint32_t k) { return ((k & 3u) << 2) | ((k >> 2) & 3u); }
+// The key held by LDS block b (the same 2-bit rotation undoes itself).
+__device__ __forceinline__ uint32_t block_key(uint32_t b) { return ((b & 3u) << 2) | ((b >> 2) & 3u); }
 // Byte offset of 16-byte chunk `ch` of key `key` inside a K or V tile.
 __device__ __forceinline__ uint32_t tile_off(uint32_t key, uint32_t ch) {
   return key_block(key & 15u) * kBlockBytes + (key >> 4) * kRowBytes + ch * 16u;
@@ -104,7 +101,7 @@ struct Ring {
 // Per-lane LDS read bases.
 struct Lane {
   uint32_t k_base;  // K A operand for key 32kb + n, d = 16db + 8g: k_base + 512kb + 32db
-  uint32_t v_base;  // transposing read (c, h, b): v_base + 8320h + 256c + 64b
+  uint32_t v_base;  // transposing read (c, h, b): v_base + 2080h + 256c + 64b
   int n, g;
 };
 
@@ -122,16 +119,16 @@ __device__ __forceinline__ Lane make_lane(int lane) {
 
 // O^T (128 d x 32 queries) += V^T P^T for one tile. P chunk c holds keys
 // 16c + 8*(i/4) + 4g + i%4 in k-slot (g, i); the transposing reads deliver the
-// matching V columns (key + 8 is LDS block + 8: 8*1040 bytes further).
+// matching V columns (key + 8 sits two LDS blocks further: + 2080 bytes).
 __device__ __forceinline__ void pv(uint32_t vt, const Lane& L, const bf16x8 (&p)[4], f32x16 (&o)[4]) {
   const lds_bf16x4* base = (const lds_bf16x4*)(vt + L.v_base);
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      // byte offsets 8320h + 256c + 64b, in 8-byte units
+      // byte offsets 2080h + 256c + 64b, in 8-byte units
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 32 * c + 8 * b));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 1040 + 32 * c + 8 * b));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 260 + 32 * c + 8 * b));
       const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       o[b] = mfma32x32x16(a, p[c], o[b]);
     }
@@ -162,9 +159,11 @@ struct Softmax {
 };
 
 // One tile: masking of `s` when some key of the tile is hidden from some row
-// of the wave (a wave-uniform branch, before the straight-line part), then the
-// S^T of the next tile (read from `nk`; its result is ignored after the last
-// tile) interleaved with the softmax of `s`, then O += V^T P^T.
+// of the wave (a wave-uniform branch), the row maximum, then 16 steps that
+// each issue one S^T MFMA of the next tile (K operand prefetched four steps
+// ahead; after the last tile the result is not used) next to two exp2 of this
+// tile, so the transcendental/VALU work runs under the matrix unit; a
+// scheduling fence between steps keeps that order. Then O += V^T P^T.
 __device__ __forceinline__ void tile_step(f32x16 (&s)[2], f32x16 (&sn)[2], const char* nk, uint32_t vt,
                                           const Lane& L, const bf16x8 (&q)[8], f32x16 (&o)[4], Softmax& st,
                                           float c, bool mask, int key0, int len_k, int lim) {
@@ -178,7 +177,6 @@ __device__ __forceinline__ void tile_step(f32x16 (&s)[2], f32x16 (&sn)[2], const
       }
     }
   }
-  qk(nk, L, q, sn);
   // row maximum over the lane's 32 keys, four independent chains
   float mx4[4];
 #pragma unroll
@@ -194,32 +192,42 @@ __device__ __forceinline__ void tile_step(f32x16 (&s)[2], f32x16 (&sn)[2], const
   const float alpha = need ? hw_exp2((st.m - m_new) * c) : 1.f;
   const float m_ref = need ? m_new : st.m;
   const float ms = (m_ref == kNegInf ? 0.f : m_ref) * c;
+
+  // step i: MFMA (db = i/2, kb = i%2) of the next tile, and elements 2i, 2i+1
+  // of this tile (P chunk t = i/4 collects 8 of them)
+  const char* kbase = nk + L.k_base;
+  bf16x8 kr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kr[i] = ld_lds16(kbase, (i & 1) * 2 * kRowBytes + (i >> 1) * 32);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sn[kb][r] = 0.f;
+  }
   bf16x8 p[4];
-  float rs4[4];
+  f32x8 e;
+  float rs0 = 0.f, rs1 = 0.f;
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    f32x8 e;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) e[i] = hw_exp2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + i], c, -ms));
-    rs4[t] = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-    p[t] = to_bf16x8(e);
+  for (int i = 0; i < 16; ++i) {
+    const int db = i >> 1, kb = i & 1;
+    sn[kb] = mfma32x32x16(kr[i & 3], q[db], sn[kb]);
+    if (i + 4 < 16) kr[i & 3] = ld_lds16(kbase, ((i + 4) & 1) * 2 * kRowBytes + ((i + 4) >> 1) * 32);
+    const int t = i >> 2, u = 2 * (i & 3);
+    e[u] = hw_exp2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + u], c, -ms));
+    e[u + 1] = hw_exp2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + u + 1], c, -ms));
+    rs0 += e[u];
+    rs1 += e[u + 1];
+    if ((i & 3) == 3) p[t] = to_bf16x8(e);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  st.l = st.l * alpha + ((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));
+  const float rs = rs0 + rs1;
+  st.l = st.l * alpha + rs;
   st.m = m_ref;
-  // thread the softmax VALU work between the next tile's S^T MFMAs
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // 4 K reads ahead
-#pragma unroll
-  for (int i = 0; i < 12; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
-  }
-  if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+  // Rare rescale of O. The row sum takes part in the condition (it is never
+  // NaN for finite inputs) so that the exp2 above stay interleaved with the
+  // MFMAs instead of being sunk past the branch.
+  if (__builtin_amdgcn_ballot_w64(need || rs != rs) != 0ull) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) o[b] *= alpha;
   }
