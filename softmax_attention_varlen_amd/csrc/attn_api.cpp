@@ -106,7 +106,7 @@ attn_status_t attn_block_map_to_index(const uint8_t* block_map, int32_t rows, in
   if (rows == 0) return ATTN_OK;
   if (block_map == nullptr || idx == nullptr || num == nullptr) return ATTN_ERR_INVALID_ARG;
   if ((long long)rows * n_cols > kMaxRows) return ATTN_ERR_UNSUPPORTED;
-  return from_hip(attn::launch_map_to_index(block_map, rows, n_cols, idx, num, (hipStream_t)stream));
+  return from_hip(attn::launch_map_to_index(block_map, rows, n_cols, nullptr, idx, num, (hipStream_t)stream));
 }
 
 attn_status_t attn_block_sparse_workspace_size(int32_t batch, int32_t num_heads, int32_t num_tiles, size_t* bytes) {

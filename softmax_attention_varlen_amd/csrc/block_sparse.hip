@@ -3,7 +3,8 @@
 // Step 1 (map -> index): each map row (batch, head, query tile) becomes the
 // ascending list of kept key tiles plus a count, built with a wave ballot and
 // a prefix popcount (bit-exact, no atomics).
-// Step 2 (attention): one workgroup of 2 waves owns one (batch, head, query
+// Step 2 (attention, head_dim other than 128; head_dim 128 has its own
+// pipelined kernel): one workgroup of 2 waves owns one (batch, head, query
 // tile); each wave owns 32 query rows. It walks only the kept key tiles, each
 // staged through LDS exactly as in the varlen prefill (K row-major, V
 // transposed), with the same S^T = K Q^T MFMA / online softmax / O^T += V^T P^T
@@ -17,7 +18,11 @@ namespace attn {
 constexpr int kSparseTile = 64;
 constexpr int kSparseThreads = 128;
 
+// With `sizes` (the launch of the head_dim-128 kernel) tiles of size 0 are
+// dropped and each entry is packed as (size << 24) | tile, so the attention
+// loop reads one word per kept tile.
 __global__ __launch_bounds__(256) void map_to_index_kernel(const uint8_t* __restrict__ map, int rows, int n_cols,
+                                                           const int32_t* __restrict__ sizes,
                                                            int32_t* __restrict__ idx, int32_t* __restrict__ num) {
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -28,18 +33,24 @@ __global__ __launch_bounds__(256) void map_to_index_kernel(const uint8_t* __rest
   int base = 0;
   for (int c0 = 0; c0 < n_cols; c0 += 64) {
     const int col = c0 + lane;
-    const bool keep = col < n_cols && mrow[col] != 0;
+    bool keep = col < n_cols && mrow[col] != 0;
+    int32_t val = col;
+    if (sizes != nullptr && keep) {
+      const int sz = clampi(sizes[col], 0, kSparseTile);
+      keep = sz > 0;
+      val = (sz << 24) | col;
+    }
     const unsigned long long bits = __ballot(keep);
-    if (keep) irow[base + __popcll(bits & below)] = col;
+    if (keep) irow[base + __popcll(bits & below)] = val;
     base += __popcll(bits);
   }
   if (lane == 0) num[row] = base;
 }
 
-hipError_t launch_map_to_index(const uint8_t* map, int rows, int n_cols, int32_t* idx, int32_t* num,
-                               hipStream_t stream) {
+hipError_t launch_map_to_index(const uint8_t* map, int rows, int n_cols, const int32_t* sizes, int32_t* idx,
+                               int32_t* num, hipStream_t stream) {
   hipLaunchKernelGGL(map_to_index_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, map, rows,
-                     n_cols, idx, num);
+                     n_cols, sizes, idx, num);
   return hipGetLastError();
 }
 
@@ -154,12 +165,14 @@ static hipError_t launch_sparse_d(const SparseArgs& a, hipStream_t stream) {
 
 hipError_t launch_block_sparse_fwd(const SparseArgs& a, hipStream_t stream) {
   const int rows = a.batch * a.num_heads * a.num_tiles;
-  hipError_t e = launch_map_to_index(a.block_map, rows, a.num_tiles, a.idx, a.num, stream);
+  const bool d128 = a.head_dim == 128;
+  hipError_t e = launch_map_to_index(a.block_map, rows, a.num_tiles, d128 ? a.tile_sizes : nullptr, a.idx, a.num,
+                                     stream);
   if (e != hipSuccess) return e;
   switch (a.head_dim) {
     case 64: return launch_sparse_d<64>(a, stream);
     case 96: return launch_sparse_d<96>(a, stream);
-    case 128: return launch_sparse_d<128>(a, stream);
+    case 128: return launch_block_sparse_d128(a, stream);
     case 192: return launch_sparse_d<192>(a, stream);
     case 256: return launch_sparse_d<256>(a, stream);
     default: return hipErrorInvalidValue;

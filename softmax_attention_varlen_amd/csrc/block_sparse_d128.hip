@@ -1,0 +1,202 @@
+// Pipelined block-sparse attention over 64-token tiles, head_dim 128, gfx950.
+//
+// Work unit: one workgroup of 4 waves owns one (batch, head, query tile).
+// Wave w owns query rows 32*(w%2) .. +31 of the tile and key half w/2 (keys
+// 32*(w/2) .. +31 of every kept key tile), so all four waves consume each K/V
+// tile the ring brings in, and the two key halves of a row are merged once at
+// the end, through LDS, with the usual max/rescale combination of partial
+// softmax sums.
+//
+// The kept key tiles come from the block map as ascending lists with empty
+// tiles dropped, each entry packed as (size << 24) | tile. K and V stream
+// through separate two-stage LDS rings (direct-to-LDS loads, the
+// conflict-free layout of pipe_d128.hpp): step j reads K of tile j+1 (the S^T
+// MFMAs of the next tile run under this tile's softmax) and V of tile j, while
+// K of tile j+2 and V of tile j+1 are in flight. With two workgroups per CU
+// (66.5 KB of LDS each) a SIMD holds two waves.
+//
+// Padding keys (at or past a tile's size) are masked; padding query rows are
+// written as zeros with LSE = -inf; a query tile with no kept key gets zeros
+// and -inf as well.
+#include "launch.hpp"
+#include "pipe_d128.hpp"
+
+namespace attn {
+namespace {
+
+using namespace pipe;
+
+constexpr int kSW = 4;                       // waves per workgroup
+constexpr int kSIPW = 16 / kSW;              // load blocks per wave per K (or V) tile
+constexpr int kSparseLds = 4 * kTileBytes;   // K stages 0, 1, then V stages 0, 1
+constexpr int kMergeOBytes = 32 * 128 * 4;   // one wave's fp32 O^T block
+static_assert(2 * kMergeOBytes + 2 * 512 <= kSparseLds, "merge area must fit in the ring");
+
+struct Entry {
+  int tile, size;
+};
+
+__device__ __forceinline__ Entry unpack(int32_t v, int num_tiles) {
+  Entry e;
+  e.tile = clampi(v & 0xffffff, 0, num_tiles - 1);
+  e.size = clampi((int)((uint32_t)v >> 24), 1, kBN);
+  return e;
+}
+
+__global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ tile_sizes, const int32_t* __restrict__ kidx, const int32_t* __restrict__ knum,
+    int num_tiles, int hq, int hkv, int n_items, int per_xcd, float c, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSparseLds];
+
+  // XCD-aware order: XCD x runs logical items [x*per_xcd, (x+1)*per_xcd); query
+  // tiles run fastest, so one XCD's L2 serves the K/V of few heads.
+  const int hw = blockIdx.x;
+  const int item = (hw & 7) * per_xcd + (hw >> 3);
+  if (item >= n_items) return;
+  const int a = item % num_tiles;
+  const int bh = item / num_tiles;
+  const int h = bh % hq;
+  const int b = bh / hq;
+  const int hk = h / (hq / hkv);
+  const long seq = (long)num_tiles * kBN;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rh = w & 1, kh = w >> 1;
+  const Lane L = make_lane(lane, 32 * kh);
+  const int qsize = clampi(tile_sizes[a], 0, kBN);
+  const int r = 32 * rh + L.n;
+  const int r_c = r < qsize ? r : (qsize > 0 ? qsize - 1 : 0);
+  const bool wave_live = 32 * rh < qsize;
+  const int32_t* list = kidx + (long)item * num_tiles;
+  const int count = qsize > 0 ? clampi(knum[item], 0, num_tiles) : 0;
+
+  const long kv_stride = (long)hkv * kD;
+  const uint32_t stride_bytes = (uint32_t)kv_stride * 2u;
+  const uint16_t* kbatch = k + (long)b * seq * kv_stride + hk * kD;
+  const uint16_t* vbatch = v + (long)b * seq * kv_stride + hk * kD;
+  const uint32_t ring = lds_u32(smem);
+  const long qrow0 = (long)b * seq + (long)a * kBN;
+
+  bf16x8 qr[8];
+  {
+    const uint16_t* qp = q + ((qrow0 + r_c) * hq + h) * kD + L.g * 8;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) qr[db] = as_bf16x8(ld_global16(qp + db * 16));
+  }
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+  }
+  Softmax st{kNegInf, 0.f};
+  f32x16 sa[1], sb[1];
+
+  auto issue_k = [&](const Entry& t, int stage) {
+    issue_tile<kSIPW>(kbatch + (long)t.tile * kBN * kv_stride, stride_bytes, t.size, ring + stage * kTileBytes,
+                      w * kSIPW, lane);
+  };
+  auto issue_v = [&](const Entry& t, int stage) {
+    issue_tile<kSIPW>(vbatch + (long)t.tile * kBN * kv_stride, stride_bytes, t.size,
+                      ring + (2 + stage) * kTileBytes, w * kSIPW, lane);
+  };
+
+  // entry of tile j (unpacked) and raw entries of tiles j+1, j+2: each list
+  // word is read one step before its first use
+  Entry e0{0, 1};
+  int32_t n1 = 0, n2 = 0;
+  if (count > 0) e0 = unpack(list[0], num_tiles);
+  if (count > 1) n1 = list[1];
+  if (count > 2) n2 = list[2];
+
+  if (count > 0) {
+    issue_k(e0, 0);
+    issue_v(e0, 0);
+    if (count > 1) {
+      issue_k(unpack(n1, num_tiles), 1);
+      wait_loads_barrier<2 * kSIPW>();  // K of tile 0 has landed
+    } else {
+      wait_loads_barrier<kSIPW>();
+    }
+    if (wave_live) qk<1>(smem, L, qr, sa);
+  }
+  settle_q(qr);
+
+  // step j: K of tile j+1 and V of tile j must have landed (everything issued
+  // so far); all waves are done with K of tile j and V of tile j-1, whose
+  // stages receive K of tile j+2 and V of tile j+1.
+  auto iteration = [&](int j, f32x16 (&s)[1], f32x16 (&sn)[1]) {
+    wait_loads_barrier<0>();
+    if (j + 2 < count) issue_k(unpack(n2, num_tiles), j & 1);
+    const Entry e1 = unpack(n1, num_tiles);
+    if (j + 1 < count) issue_v(e1, (j + 1) & 1);
+    const int size = e0.size;
+    e0 = e1;
+    n1 = n2;
+    if (j + 3 < count) n2 = list[j + 3];
+    if (wave_live) {
+      // after the last tile the "next" K stage holds stale data; its S^T is unused
+      const char* nk = smem + ((j + 1) & 1) * kTileBytes;
+      const uint32_t vt = ring + (2 + (j & 1)) * kTileBytes;
+      tile_step<1>(s, sn, nk, vt, L, qr, o, st, c, size < 32 * kh + 32, 32 * kh, size, 0x7fffffff);
+    }
+  };
+  for (int j = 0; j < count; j += 2) {
+    iteration(j, sa, sb);
+    if (j + 1 < count) iteration(j + 1, sb, sa);
+  }
+
+  // merge the two key halves of each row: wave (rh, 1) hands its O^T block,
+  // reference maximum and lane-partial sum to wave (rh, 0) through LDS
+  wait_loads_barrier<0>();
+  f32x4* mo = reinterpret_cast<f32x4*>(smem + rh * kMergeOBytes) + lane;
+  float2* mml = reinterpret_cast<float2*>(smem + 2 * kMergeOBytes + rh * 512) + lane;
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        f32x4 t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = o[i][4 * grp + e];
+        mo[(4 * i + grp) * 64] = t;
+      }
+    }
+    *mml = make_float2(st.m, st.l);
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  const float2 ml = *mml;
+  const float mm = fmaxf(st.m, ml.x);
+  const float a0 = st.m == kNegInf ? 0.f : hw_exp2((st.m - mm) * c);
+  const float a1 = ml.x == kNegInf ? 0.f : hw_exp2((ml.x - mm) * c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int grp = 0; grp < 4; ++grp) {
+      const f32x4 t = mo[(4 * i + grp) * 64];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[i][4 * grp + e] = o[i][4 * grp + e] * a0 + t[e] * a1;
+    }
+  }
+  st.m = mm;
+  st.l = r < qsize ? st.l * a0 + ml.y * a1 : 0.f;  // padding rows: zeros, LSE = -inf
+  store_rows(o, st, L, c, true, out + ((qrow0 + r) * hq + h) * kD,
+             lse != nullptr ? lse + ((long)b * hq + h) * seq + (long)a * kBN + r : nullptr);
+}
+
+}  // namespace
+
+hipError_t launch_block_sparse_d128(const SparseArgs& a, hipStream_t stream) {
+  const long n_items = (long)a.batch * a.num_heads * a.num_tiles;
+  const long per_xcd = (n_items + 7) / 8;
+  hipLaunchKernelGGL(block_sparse_d128_kernel, dim3((unsigned)(per_xcd * 8)), dim3(64 * kSW), 0, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.tile_sizes, a.idx, a.num,
+                     a.num_tiles, a.num_heads, a.num_kv_heads, (int)n_items, (int)per_xcd, a.scale * kLog2e,
+                     (uint16_t*)a.out, a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace attn

@@ -58,8 +58,9 @@ struct DecodeArgs {
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 
 // Block map -> ascending index lists.
-hipError_t launch_map_to_index(const uint8_t* map, int rows, int n_cols, int32_t* idx, int32_t* num,
-                               hipStream_t stream);
+// With sizes != nullptr: tiles of size 0 are dropped, entries are (size << 24) | tile.
+hipError_t launch_map_to_index(const uint8_t* map, int rows, int n_cols, const int32_t* sizes, int32_t* idx,
+                               int32_t* num, hipStream_t stream);
 
 struct SparseArgs {
   const void* q;
@@ -77,6 +78,8 @@ struct SparseArgs {
 
 size_t sparse_workspace_bytes(int batch, int num_heads, int num_tiles);
 hipError_t launch_block_sparse_fwd(const SparseArgs& a, hipStream_t stream);
+// head_dim 128; expects the packed, size-filtered lists in a.idx / a.num.
+hipError_t launch_block_sparse_d128(const SparseArgs& a, hipStream_t stream);
 
 // Video tile geometry (raster (t, h, w) cut into (tile_t, tile_h, tile_w) boxes).
 struct VsaGeometry {

@@ -2,78 +2,19 @@
 //
 // Work unit: one workgroup of NW waves owns NW*32 query rows of one document
 // and one query head; wave w owns rows [32w, 32w+32). K/V tiles of 64 keys
-// stream through an NS-stage LDS ring:
-//   * global -> LDS with direct-to-LDS 16-byte loads (no VGPR staging, no
-//     transpose on the way in). Load block b (16 per tile) is one contiguous
-//     1 KB holding the four keys κ(b) + {0, 16, 32, 48}; blocks sit 1040 bytes
-//     apart (16 bytes = 4 banks of pad). Key k%16 = (b3 b2 b1 b0) lives in
-//     block (b1 b0 b3 b2). A 16-lane slice of a K read then covers the 16
-//     blocks (all 64 banks once), and a 32-lane slice of a transposing V read
-//     (4 keys x 64 bytes) puts its 4 rows 16 banks apart: both conflict-free on
-//     gfx950's 64-bank LDS, as measured. Every LDS address is a per-lane base
-//     plus a compile-time offset.
-//   * K is read row-wise (ds_read_b128) as the A operand of S^T = K Q^T.
-//   * V stays row-major and is read with the transposing ds_read_b64_tr_b16,
-//     which hands each lane four keys of one column: exactly the k-slot layout
-//     of the A operand of O^T += V^T P^T.
-// Per tile a wave issues the S^T MFMAs of the next tile interleaved with the
-// softmax of the current one (the scheduler is asked for that interleave), so
-// the VALU/transcendental work runs while the matrix unit is busy; then it
-// issues the PV MFMAs of the current tile. One barrier per tile guards the
-// ring. The output accumulator is only rescaled when some row maximum grows by
-// more than 2^8 (in exp2 units); until then the stale maximum keeps every exp2
-// argument <= 8, exact up to rounding.
-#include "attn_common.hpp"
+// stream through an NS-stage LDS ring filled by direct-to-LDS loads (no VGPR
+// staging, no transpose on the way in), in the bank-conflict-free layout of
+// pipe_d128.hpp. Per tile a wave issues the S^T MFMAs of the next tile
+// interleaved with the softmax of the current one, then the PV MFMAs of the
+// current tile. One barrier per tile guards the ring.
 #include "launch.hpp"
+#include "pipe_d128.hpp"
 
 namespace attn {
 namespace {
 
-constexpr int kD = 128;
-constexpr int kBN = 64;
-constexpr int kRowBytes = kD * 2;             // 256 B per K/V row
-constexpr int kBlockBytes = 1040;             // one 1 KB load block + 16 B pad
-constexpr int kTileBytes = 16 * kBlockBytes;  // 16 blocks of 4 rows per K (or V) tile
-constexpr int kStageBytes = 2 * kTileBytes;   // K tile, then V tile
-constexpr float kRescaleThreshold = 8.f;      // log2 units
-
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-
-// LDS block of key k (0..15 within its group of 16): bits (b3 b2 b1 b0) -> (b1 b0 b3 b2).
-__device__ __forceinline__ uint32_t key_block(uint32_t k) { return ((k & 3u) << 2) | ((k >> 2) & 3u); }
-// The key held by LDS block b (the same 2-bit rotation undoes itself).
-__device__ __forceinline__ uint32_t block_key(uint32_t b) { return ((b & 3u) << 2) | ((b >> 2) & 3u); }
-// Byte offset of 16-byte chunk `ch` of key `key` inside a K or V tile.
-__device__ __forceinline__ uint32_t tile_off(uint32_t key, uint32_t ch) {
-  return key_block(key & 15u) * kBlockBytes + (key >> 4) * kRowBytes + ch * 16u;
-}
-
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// One 16-byte-per-lane direct-to-LDS load: lane l's bytes land at lds + 16*l.
-__device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
-               : "memory", "m0");
-}
-
-// Wait until at most N of this wave's direct-to-LDS loads are in flight, drain
-// its LDS reads, and meet the other waves.
-template <int N>
-__device__ __forceinline__ void wait_loads_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
-}
-
-// max / sum of a lane's value and lane (l ^ 32)'s, via one lane swap.
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
+using namespace pipe;
+constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile
 
 template <int NW>
 struct Ring {
@@ -85,154 +26,10 @@ struct Ring {
   // tile (this kv head); rows >= nvalid re-read row nvalid-1.
   __device__ __forceinline__ static void issue(const uint16_t* kbase, const uint16_t* vbase, uint32_t stride_bytes,
                                                int nvalid, uint32_t stage_lds, int w, int lane) {
-#pragma unroll
-    for (int t = 0; t < IPW; ++t) {
-      const int blk = w * IPW + t;
-      const int key = (int)block_key((uint32_t)blk) + 16 * (lane >> 4);
-      const int kc = key < nvalid ? key : nvalid - 1;
-      const uint32_t voff = (uint32_t)kc * stride_bytes + (uint32_t)(lane & 15) * 16u;
-      const uint32_t lds = __builtin_amdgcn_readfirstlane(stage_lds + blk * kBlockBytes);
-      load_lds16(kbase, voff, lds);
-      load_lds16(vbase, voff, lds + kTileBytes);
-    }
+    issue_tile<IPW>(kbase, stride_bytes, nvalid, stage_lds, w * IPW, lane);
+    issue_tile<IPW>(vbase, stride_bytes, nvalid, stage_lds + kTileBytes, w * IPW, lane);
   }
 };
-
-// Per-lane LDS read bases.
-struct Lane {
-  uint32_t k_base;  // K A operand for key 32kb + n, d = 16db + 8g: k_base + 512kb + 32db
-  uint32_t v_base;  // transposing read (c, h, b): v_base + 2080h + 256c + 64b
-  int n, g;
-};
-
-__device__ __forceinline__ Lane make_lane(int lane) {
-  Lane L;
-  L.n = lane & 31;
-  L.g = lane >> 5;
-  L.k_base = tile_off((uint32_t)L.n, (uint32_t)L.g);
-  // source lane (G, s) of a transposing read points at key 16c + 8h + 4(G/2) + s/4,
-  // columns 32b + 16(G%2) + 4(s%4) .. +3
-  const uint32_t G = (uint32_t)lane >> 4, s = (uint32_t)lane & 15u;
-  L.v_base = tile_off(4u * (G >> 1) + (s >> 2), 2u * (G & 1u) + ((s & 3u) >> 1)) + (s & 1u) * 8u;
-  return L;
-}
-
-// O^T (128 d x 32 queries) += V^T P^T for one tile. P chunk c holds keys
-// 16c + 8*(i/4) + 4g + i%4 in k-slot (g, i); the transposing reads deliver the
-// matching V columns (key + 8 sits two LDS blocks further: + 2080 bytes).
-__device__ __forceinline__ void pv(uint32_t vt, const Lane& L, const bf16x8 (&p)[4], f32x16 (&o)[4]) {
-  const lds_bf16x4* base = (const lds_bf16x4*)(vt + L.v_base);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      // byte offsets 2080h + 256c + 64b, in 8-byte units
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 32 * c + 8 * b));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 260 + 32 * c + 8 * b));
-      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[b] = mfma32x32x16(a, p[c], o[b]);
-    }
-  }
-}
-
-// S^T for one tile: s[kb] = keys 32kb..32kb+31 x the wave's 32 queries.
-__device__ __forceinline__ void qk(const char* kt, const Lane& L, const bf16x8 (&q)[8], f32x16 (&s)[2]) {
-  const char* base = kt + L.k_base;
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-  }
-#pragma unroll
-  for (int db = 0; db < 8; ++db) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const bf16x8 a = ld_lds16(base, kb * 2 * kRowBytes + db * 32);
-      s[kb] = mfma32x32x16(a, q[db], s[kb]);
-    }
-  }
-}
-
-struct Softmax {
-  float m;  // reference maximum of the raw scores (the exp2 shift is m * c)
-  float l;  // lane-partial sum of the unrounded probabilities
-};
-
-// One tile: masking of `s` when some key of the tile is hidden from some row
-// of the wave (a wave-uniform branch), the row maximum, then 16 steps that
-// each issue one S^T MFMA of the next tile (K operand prefetched four steps
-// ahead; after the last tile the result is not used) next to two exp2 of this
-// tile, so the transcendental/VALU work runs under the matrix unit; a
-// scheduling fence between steps keeps that order. Then O += V^T P^T.
-__device__ __forceinline__ void tile_step(f32x16 (&s)[2], f32x16 (&sn)[2], const char* nk, uint32_t vt,
-                                          const Lane& L, const bf16x8 (&q)[8], f32x16 (&o)[4], Softmax& st,
-                                          float c, bool mask, int key0, int len_k, int lim) {
-  if (mask) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * L.g + (r & 3);
-        if (key >= len_k || key > lim) s[kb][r] = kNegInf;
-      }
-    }
-  }
-  // row maximum over the lane's 32 keys, four independent chains
-  float mx4[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) mx4[t] = fmaxf(s[t >> 1][8 * (t & 1)], s[t >> 1][8 * (t & 1) + 1]);
-#pragma unroll
-  for (int i = 2; i < 8; ++i) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) mx4[t] = fmaxf(mx4[t], s[t >> 1][8 * (t & 1) + i]);
-  }
-  const float mx = pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
-  const float m_new = fmaxf(st.m, mx);
-  const bool need = (m_new - st.m) * c > kRescaleThreshold;  // true on the first finite maximum
-  const float alpha = need ? hw_exp2((st.m - m_new) * c) : 1.f;
-  const float m_ref = need ? m_new : st.m;
-  const float ms = (m_ref == kNegInf ? 0.f : m_ref) * c;
-
-  // step i: MFMA (db = i/2, kb = i%2) of the next tile, and elements 2i, 2i+1
-  // of this tile (P chunk t = i/4 collects 8 of them)
-  const char* kbase = nk + L.k_base;
-  bf16x8 kr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) kr[i] = ld_lds16(kbase, (i & 1) * 2 * kRowBytes + (i >> 1) * 32);
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sn[kb][r] = 0.f;
-  }
-  bf16x8 p[4];
-  f32x8 e;
-  float rs0 = 0.f, rs1 = 0.f;
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int db = i >> 1, kb = i & 1;
-    sn[kb] = mfma32x32x16(kr[i & 3], q[db], sn[kb]);
-    if (i + 4 < 16) kr[i & 3] = ld_lds16(kbase, ((i + 4) & 1) * 2 * kRowBytes + ((i + 4) >> 1) * 32);
-    const int t = i >> 2, u = 2 * (i & 3);
-    e[u] = hw_exp2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + u], c, -ms));
-    e[u + 1] = hw_exp2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + u + 1], c, -ms));
-    rs0 += e[u];
-    rs1 += e[u + 1];
-    if ((i & 3) == 3) p[t] = to_bf16x8(e);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const float rs = rs0 + rs1;
-  st.l = st.l * alpha + rs;
-  st.m = m_ref;
-  // Rare rescale of O. The row sum takes part in the condition (it is never
-  // NaN for finite inputs) so that the exp2 above stay interleaved with the
-  // MFMAs instead of being sunk past the branch.
-  if (__builtin_amdgcn_ballot_w64(need || rs != rs) != 0ull) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) o[b] *= alpha;
-  }
-  pv(vt, L, p, o);
-}
 
 template <bool CAUSAL, int NW, int NS>
 __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
@@ -335,8 +132,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
     } else {
       wait_loads_barrier<0>();
     }
-    if (ntiles_w > 0) qk(smem, L, qr, sa);
+    if (ntiles_w > 0) qk<2>(smem, L, qr, sa);
   }
+  settle_q(qr);
 
   // one iteration of the ring: refill, then this wave's compute for tile j
   auto iteration = [&](int j, f32x16 (&s)[2], f32x16 (&sn)[2]) {
@@ -359,31 +157,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
     const uint32_t vt = ring + (j % NS) * kStageBytes + kTileBytes;
     const int key0 = j * kBN;
     const bool mask = !(j < nomask_w && key0 + kBN <= len_k);
-    tile_step(s, sn, nk, vt, L, qr, o, st, c, mask, key0, len_k, CAUSAL ? row + diag : 0x7fffffff);
+    tile_step<2>(s, sn, nk, vt, L, qr, o, st, c, mask, key0, len_k, CAUSAL ? row + diag : 0x7fffffff);
   };
   for (int j = 0; j < ntiles; j += 2) {
     iteration(j, sa, sb);
     if (j + 1 < ntiles) iteration(j + 1, sb, sa);
   }
 
-  const float lt = pair_sum(st.l);
-  if (row < len_q) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* orow = out + ((long)(q0 + row) * hq + h) * kD;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-#pragma unroll
-      for (int grp = 0; grp < 4; ++grp) {
-        f32x4 t;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] = o[b][4 * grp + i] * inv;
-        *reinterpret_cast<bf16x4*>(orow + b * 32 + 8 * grp + 4 * L.g) = to_bf16x4(t);
-      }
-    }
-    if (lse != nullptr && L.g == 0) {
-      lse[(long)h * total_q + q0 + row] = lt > 0.f ? (st.m * c + hw_log2(lt)) * kLn2 : kNegInf;
-    }
-  }
+  store_rows(o, st, L, c, row < len_q, out + ((long)(q0 + row_c) * hq + h) * kD,
+             lse != nullptr ? lse + (long)h * total_q + q0 + row_c : nullptr);
 }
 
 }  // namespace
