@@ -91,6 +91,7 @@ attn_status_t attn_paged_decode(const void* q, const void* kv_cache, const int32
     return ATTN_ERR_INVALID_ARG;
   }
   if ((long long)num_blocks * block_size * num_kv_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)num_seqs * max_context_len >= (1LL << 30)) return ATTN_ERR_UNSUPPORTED;  // int32 token prefix
   const attn::DecodePlan plan = attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len);
   if (workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (plan.workspace_bytes > 0 && workspace == nullptr) return ATTN_ERR_INVALID_ARG;

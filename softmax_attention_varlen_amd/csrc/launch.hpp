@@ -57,6 +57,20 @@ struct DecodeArgs {
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 
+// head_dim 128: balanced streaming decode (paged_decode_stream.hip). The
+// token stream of all sequences is cut into n_seg equal segments per kv head
+// (and query-head chunk); one wave streams one segment.
+constexpr int kDecodeStreamWaves = 1024;  // 4 waves on each of MI355X's 256 CUs
+struct DecodeStreamPlan {
+  int q_chunks, n_seg;
+  size_t prefix_bytes;  // int32 [num_seqs + 1] token prefix sums
+  size_t lse_bytes;     // fp32 [n_seg + num_seqs][num_heads] partial LSE
+  size_t o_bytes;       // fp32 [n_seg + num_seqs][num_heads][128] partial O
+  size_t workspace_bytes;
+};
+DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads);
+hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, hipStream_t stream);
+
 // Block map -> ascending index lists.
 // With sizes != nullptr: tiles of size 0 are dropped, entries are (size << 24) | tile.
 hipError_t launch_map_to_index(const uint8_t* map, int rows, int n_cols, const int32_t* sizes, int32_t* idx,

@@ -1,0 +1,409 @@
+// Streaming single-token decode over a paged KV cache, head_dim 128, gfx950.
+//
+// Work balance. The contexts of all sequences, laid end to end, form one token
+// stream of T = sum(context_lens) positions. For each kv head (and chunk of
+// <= 16 query heads of its group) the stream is cut into n_seg segments of
+// L = max(ceil(T / n_seg), kMinSeg) positions; one wave owns one segment, so
+// every wave reads the same number of K/V bytes whatever the mix of lengths.
+// A segment may cover the end of one sequence, whole sequences and the start
+// of another: each such piece is finished separately. A sequence that lies in
+// one segment gets its final bf16 output from that wave; otherwise each piece
+// writes a normalised fp32 partial (O, LSE) to slot (segment + sequence),
+// which is unique because segments and sequences are both contiguous ranges
+// of the stream, and the combine kernel merges the pieces of each sequence in
+// ascending segment order. The token prefix sums come from a one-workgroup
+// scan kernel, so the host never reads the lengths.
+//
+// Streaming. Each wave keeps a two-stage LDS ring of 32-token chunks (K and V
+// of its kv head, 8 KB each) filled by direct-to-LDS loads, and issues chunk
+// j+2 as soon as chunk j is consumed: one chunk is always in flight, which is
+// what keeps HBM busy (a wave that waits for its whole chunk before issuing
+// the next leaves gaps). Load block b of a chunk holds tokens b, b+8, b+16,
+// b+24 (4 rows x 256 B); blocks sit 1056 bytes apart, which makes the
+// transposing V reads conflict-free and the K reads at most 2-way.
+//
+// Math per chunk (16x16x32 bf16 MFMA): S^T = K Q^T with K from LDS (A) and the
+// query heads as the 16 columns (B); online softmax per column; O^T += V^T P^T
+// with V^T from transposing LDS reads (A) and P straight from the S^T
+// accumulator (B): the lane's 8 tokens 4G..4G+3 and 16+4G..16+4G+3 are the
+// k-slots of its B operand, and the two transposing reads fetch exactly those
+// V rows.
+#include "attn_common.hpp"
+#include "launch.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int kSD = 128;
+constexpr int kSChunk = 32;
+constexpr int kSBlk = 1056;                  // 4 token rows (1 KB) + 32 B pad
+constexpr int kSHalf = 8 * kSBlk;            // K (or V) of one chunk
+constexpr int kSStage = 2 * kSHalf;          // K, then V
+constexpr int kSWaves = 4;                   // waves per workgroup (one workgroup per CU by LDS)
+constexpr int kSWaveLds = 2 * kSStage;       // two-stage ring per wave
+constexpr int kSLoads = 16;                  // direct-to-LDS loads per chunk per wave
+constexpr int kMinSeg = 256;                 // shortest segment (positions)
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ uint32_t tok_off(uint32_t t) { return (t & 7u) * kSBlk + (t >> 3) * 256u; }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+__device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Index of the sequence holding stream position pos: the largest s with
+// prefix[s] <= pos (prefix non-decreasing, prefix[0] = 0 <= pos < prefix[n]).
+// A 64-way search: each round the lanes probe 64 evenly spaced entries.
+__device__ __forceinline__ int find_seq(const int32_t* prefix, int n, int pos, int lane) {
+  int lo = 0, hi = n;  // answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int step = (hi - lo + 63) / 64;
+    const int idx = lo + lane * step;
+    const bool ok = idx < hi && prefix[idx] <= pos;
+    const int cnt = __popcll(__ballot(ok));  // >= 1: prefix[lo] <= pos
+    lo = lo + (cnt - 1) * step;
+    hi = lo + step < hi ? lo + step : hi;
+  }
+  return lo;
+}
+
+// Exclusive prefix sums of the clamped context lengths, prefix[num_seqs] = T.
+__global__ __launch_bounds__(1024) void decode_prefix_kernel(const int32_t* __restrict__ context_lens, int num_seqs,
+                                                             int max_context_len, int32_t* __restrict__ prefix) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (num_seqs + 1023) / 1024;
+  const int b = t * per < num_seqs ? t * per : num_seqs;
+  const int e = b + per < num_seqs ? b + per : num_seqs;
+  int sum = 0;
+  for (int i = b; i < e; ++i) sum += clampi(context_lens[i], 0, max_context_len);
+  part[t] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int add = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += add;
+    __syncthreads();
+  }
+  int run = part[t] - sum;
+  for (int i = b; i < e; ++i) {
+    prefix[i] = run;
+    run += clampi(context_lens[i], 0, max_context_len);
+  }
+  if (t == 1023) prefix[num_seqs] = part[1023];
+}
+
+__device__ __forceinline__ int seg_len(int total, int n_seg) {
+  const int l = (total + n_seg - 1) / n_seg;
+  return l > kMinSeg ? l : kMinSeg;
+}
+
+__global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ prefix, int num_seqs, int num_blocks, int max_blocks_per_seq, int hq, int hkv,
+    int q_chunks, int n_seg, float c, uint16_t* __restrict__ out, float* __restrict__ lse,
+    float* __restrict__ part_o, float* __restrict__ part_lse) {
+  __shared__ __attribute__((aligned(1024))) char smem[kSWaves * kSWaveLds];
+  // every cursor below is wave-uniform (scalar registers, scalar loads): no
+  // compiler-visible vector load may sit in the streaming loop, since the
+  // compiler's wait for it would also drain the ring
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = blockIdx.x * kSWaves + wv;
+  if (w >= n_seg * hkv * q_chunks) return;  // no workgroup barriers below
+  const int qc = w % q_chunks;
+  const int hk = (w / q_chunks) % hkv;
+  const int g = w / (q_chunks * hkv);
+
+  const int total = prefix[num_seqs];
+  if (total <= 0) return;
+  const int L = seg_len(total, n_seg);
+  const int seg_begin = g * L;
+  if (seg_begin >= total) return;
+  const int seg_end = total - seg_begin < L ? total : seg_begin + L;
+
+  const int group = hq / hkv;
+  const int n16 = lane & 15, G = lane >> 4;
+  const int qh_local = qc * 16 + n16;
+  const bool q_real = qh_local < group;
+  const int h = hk * group + (q_real ? qh_local : 0);
+
+  const long row_elems = (long)hkv * kSD;                // elements between tokens of a block
+  const long blk_elems = 128L * row_elems;
+  const long v_plane = (long)num_blocks * blk_elems;
+  const uint32_t row_bytes = (uint32_t)row_elems * 2u;
+  const uint32_t ring = lds_addr(smem + wv * kSWaveLds);
+  const char* ring_p = smem + wv * kSWaveLds;
+
+  // per-lane LDS offsets: K A operand (token 16kb + n16, d = 32b + 8G) and the
+  // transposing V reads (token 4G + s/4, columns 16db + 4(s%4))
+  const uint32_t k_lane = tok_off((uint32_t)n16) + (uint32_t)G * 16u;
+  const uint32_t v_lane = tok_off(4u * (uint32_t)G + ((uint32_t)n16 >> 2)) + ((uint32_t)n16 & 3u) * 8u;
+
+  const int s0 = __builtin_amdgcn_readfirstlane(find_seq(prefix, num_seqs, seg_begin, lane));
+  // the loader's cursor: sequence ls, chunk lc (32 tokens), its last chunk lc_end
+  int ls = s0;
+  int lbase = prefix[ls];
+  int lctx = prefix[ls + 1] - lbase;
+  int lc = (seg_begin - lbase) / kSChunk;
+  int lc_end = ((seg_end < lbase + lctx ? seg_end : lbase + lctx) - lbase - 1) / kSChunk;
+  bool lvalid = true;
+
+  // issue the loader's chunk into `stage` and advance the cursor
+  auto issue = [&](int stage) {
+    const int t0 = lc * kSChunk;
+    int blk = block_tables[(long)ls * max_blocks_per_seq + (t0 >> 7)];
+    blk = clampi(blk, 0, num_blocks - 1);
+    const uint16_t* kb = kv + (long)blk * blk_elems + (long)hk * kSD;
+    const uint32_t st = ring + stage * kSStage;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      int t = t0 + b + 8 * (lane >> 4);
+      t = t < lctx ? t : lctx - 1;  // rows past the context re-read the last one (same block)
+      const uint32_t voff = (uint32_t)(t & 127) * row_bytes + (uint32_t)(lane & 15) * 16u;
+      load_lds16(kb, voff, st + b * kSBlk);
+      load_lds16(kb + v_plane, voff, st + kSHalf + b * kSBlk);
+    }
+    if (lc < lc_end) {
+      ++lc;
+    } else {
+      // next non-empty sequence starting before the segment end
+      do {
+        ls = __builtin_amdgcn_readfirstlane(ls + 1);
+        lbase = prefix[ls];
+        lctx = ls < num_seqs ? prefix[ls + 1] - lbase : 0;
+      } while (ls < num_seqs && lctx == 0 && lbase < seg_end);
+      lvalid = ls < num_seqs && lbase < seg_end;
+      if (lvalid) {
+        lc = 0;
+        lc_end = ((seg_end < lbase + lctx ? seg_end : lbase + lctx) - lbase - 1) / kSChunk;
+      }
+    }
+  };
+
+  issue(0);
+  bool second = lvalid;
+  if (second) issue(1);
+
+  // the consumer's cursor mirrors the loader's
+  int cs = s0;
+  int cbase = prefix[cs];
+  int cctx = prefix[cs + 1] - cbase;
+  int cc = (seg_begin - cbase) / kSChunk;
+  int t_lo = seg_begin - cbase;                                               // first token of the piece
+  int t_hi = (seg_end < cbase + cctx ? seg_end : cbase + cctx) - cbase;       // one past its last
+  int cc_end = (t_hi - 1) / kSChunk;
+  bool fresh = true;
+
+  bf16x8 qb[4];
+  f32x4 o[8];
+  float m = kNegInf, l = 0.f;
+  for (int j = 0;; ++j) {
+    if (fresh) {
+      // a new piece: its query heads (the compiler's wait for these loads also
+      // drains the ring, once per piece), and a reset softmax state
+      const uint16_t* qrow = q + ((long)cs * hq + h) * kSD;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        u32x4 x = ld_global16(qrow + b * 32 + G * 8);
+        if (!q_real) x = u32x4{0u, 0u, 0u, 0u};
+        qb[b] = as_bf16x8(x);
+      }
+      asm volatile("" : : "v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
+#pragma unroll
+      for (int b = 0; b < 8; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m = kNegInf;
+      l = 0.f;
+      fresh = false;
+    }
+    // chunk j has landed once at most the next chunk's loads are in flight
+    if (second) {
+      wait_vm<kSLoads>();
+    } else {
+      wait_vm<0>();
+    }
+    const int stage = j & 1;
+    const char* kt = ring_p + stage * kSStage;
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const bf16x8 a = ld_lds16(kt, (int)(k_lane + (uint32_t)kb * 512u + (uint32_t)b * 64u));
+        s[kb] = mfma16x16x32(a, qb[b], s[kb]);
+      }
+    }
+    const int t0 = cc * kSChunk;
+    if (t0 < t_lo || t0 + kSChunk > t_hi) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + kb * 16 + 4 * G + r;
+          if (t < t_lo || t >= t_hi) s[kb][r] = kNegInf;
+        }
+      }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    mx = wave_xor_max(mx, 16);
+    mx = wave_xor_max(mx, 32);
+    const float m_new = fmaxf(m, mx);  // finite: every chunk holds a token of the piece
+    const float alpha = hw_exp2((m - m_new) * c);
+    const float ms = m_new * c;
+    f32x8 pt;
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pt[r] = hw_exp2(__builtin_fmaf(s[0][r], c, -ms));
+      pt[4 + r] = hw_exp2(__builtin_fmaf(s[1][r], c, -ms));
+      rs += pt[r] + pt[4 + r];
+    }
+    const bf16x8 p = to_bf16x8(pt);
+    l = l * alpha + rs;
+    m = m_new;
+    const lds_bf16x4* vb = (const lds_bf16x4*)(ring + stage * kSStage + kSHalf + v_lane);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      // byte offsets 32db (columns) and tok_off(16) = 512 for tokens 16..31, in 8-byte units
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 4 * db));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 64 + 4 * db));
+      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      o[db] = o[db] * alpha;
+      o[db] = mfma16x16x32(a, p, o[db]);
+    }
+
+    if (cc == cc_end) {
+      // piece done: the lane's column sum lives in 4 lanes (G = 0..3)
+      float lt = wave_xor_sum(l, 16);
+      lt = wave_xor_sum(lt, 32);
+      const float inv = 1.f / lt;
+      const float lse_p = (m * c + hw_log2(lt)) * kLn2;
+      if (q_real) {
+        if (t_lo == 0 && t_hi == cctx) {
+          uint16_t* orow = out + ((long)cs * hq + h) * kSD;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) {
+            const f32x4 t = o[db] * inv;
+            *reinterpret_cast<bf16x4*>(orow + db * 16 + 4 * G) = to_bf16x4(t);
+          }
+          if (lse != nullptr && G == 0) lse[(long)h * num_seqs + cs] = lse_p;
+        } else {
+          const long slot = (long)(g + cs) * hq + h;
+          float* orow = part_o + slot * kSD;
+#pragma unroll
+          for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * G) = o[db] * inv;
+          if (G == 0) part_lse[slot] = lse_p;
+        }
+      }
+      // next non-empty sequence of the segment
+      do {
+        cs = __builtin_amdgcn_readfirstlane(cs + 1);
+        cbase = prefix[cs];
+        cctx = cs < num_seqs ? prefix[cs + 1] - cbase : 0;
+      } while (cs < num_seqs && cctx == 0 && cbase < seg_end);
+      if (cs >= num_seqs || cbase >= seg_end) break;
+      cc = 0;
+      t_lo = 0;
+      t_hi = (seg_end < cbase + cctx ? seg_end : cbase + cctx) - cbase;
+      cc_end = (t_hi - 1) / kSChunk;
+      fresh = true;
+    } else {
+      ++cc;
+    }
+    // this chunk's LDS reads are done before its stage is refilled
+    asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+    second = lvalid;
+    if (lvalid) issue(stage);
+  }
+}
+
+// Merge the pieces of each (sequence, head) in ascending segment order:
+// LSE = ln sum_i exp(LSE_i), O = sum_i exp(LSE_i - LSE) O_i. A sequence that
+// lies in one segment was finished by the streaming kernel; an empty one gets
+// zeros and LSE = -inf.
+__global__ __launch_bounds__(256) void paged_decode_stream_combine_kernel(
+    const int32_t* __restrict__ prefix, int num_seqs, int hq, int n_seg, const float* __restrict__ part_o,
+    const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
+  const int lane = threadIdx.x & 63;
+  const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= (long)num_seqs * hq) return;
+  const int s = (int)(pair / hq), h = (int)(pair % hq);
+  const int total = prefix[num_seqs];
+  const int b0 = prefix[s], b1 = prefix[s + 1];
+  uint16_t* orow = out + pair * kSD;
+  if (b1 <= b0) {
+    for (int d = lane; d < kSD; d += 64) orow[d] = 0;
+    if (lse != nullptr && lane == 0) lse[(long)h * num_seqs + s] = kNegInf;
+    return;
+  }
+  const int L = seg_len(total, n_seg);
+  const int first = b0 / L, last = (b1 - 1) / L;
+  if (first == last) return;
+  float mx = kNegInf;
+  for (int gg = first; gg <= last; ++gg) mx = fmaxf(mx, part_lse[(long)(gg + s) * hq + h]);
+  float tot = 0.f;
+  for (int gg = first; gg <= last; ++gg) tot += hw_exp2((part_lse[(long)(gg + s) * hq + h] - mx) * kLog2e);
+  const float lse_all = mx + hw_log2(tot) * kLn2;
+  for (int d = lane; d < kSD; d += 64) {
+    float acc = 0.f;
+    for (int gg = first; gg <= last; ++gg) {
+      const long slot = (long)(gg + s) * hq + h;
+      acc += hw_exp2((part_lse[slot] - lse_all) * kLog2e) * part_o[slot * kSD + d];
+    }
+    orow[d] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+  }
+  if (lse != nullptr && lane == 0) lse[(long)h * num_seqs + s] = lse_all;
+}
+
+}  // namespace
+
+DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads) {
+  DecodeStreamPlan p{};
+  const int group = num_heads / num_kv_heads;
+  p.q_chunks = (group + 15) / 16;
+  const int lanes = num_kv_heads * p.q_chunks;
+  p.n_seg = kDecodeStreamWaves / lanes > 1 ? kDecodeStreamWaves / lanes : 1;
+  p.prefix_bytes = ((size_t)(num_seqs + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  const size_t slots = (size_t)(p.n_seg + num_seqs) * num_heads;
+  p.lse_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
+  p.o_bytes = slots * kSD * sizeof(float);
+  p.workspace_bytes = p.prefix_bytes + p.lse_bytes + p.o_bytes;
+  return p;
+}
+
+hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, hipStream_t stream) {
+  int32_t* prefix = (int32_t*)a.workspace;
+  float* part_lse = (float*)((char*)a.workspace + p.prefix_bytes);
+  float* part_o = (float*)((char*)a.workspace + p.prefix_bytes + p.lse_bytes);
+  hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens, a.num_seqs,
+                     a.max_context_len, prefix);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long waves = (long)p.n_seg * a.num_kv_heads * p.q_chunks;
+  hipLaunchKernelGGL(paged_decode_stream_kernel, dim3((unsigned)((waves + kSWaves - 1) / kSWaves)),
+                     dim3(64 * kSWaves), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.kv_cache,
+                     a.block_tables, prefix, a.num_seqs, a.num_blocks, a.max_blocks_per_seq, a.num_heads,
+                     a.num_kv_heads, p.q_chunks, p.n_seg, a.scale * kLog2e, (uint16_t*)a.out, a.lse, part_o,
+                     part_lse);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long pairs = (long)a.num_seqs * a.num_heads;
+  hipLaunchKernelGGL(paged_decode_stream_combine_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream,
+                     prefix, a.num_seqs, a.num_heads, p.n_seg, part_o, part_lse, (uint16_t*)a.out, a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace attn
