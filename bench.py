@@ -124,8 +124,8 @@ def bench_sparse(case, steps, warmup):
     """Tile order, pooled-score top-k map and the block-sparse call all run in the
     library's kernels; only the block-sparse call is in the timed step."""
     dev = torch.device("cuda")
-    prep = sav.vsa_prepare(case.q.to(dev), case.k.to(dev), case.v.to(dev), case.video_shape, case.tile_shape,
-                           case.topk, case.scale)
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)  # raster inputs, resident before any timing
+    prep = sav.vsa_prepare(q, k, v, case.video_shape, case.tile_shape, case.topk, case.scale)
     qt, kt, vt, bmap, sizes = prep["q"], prep["k"], prep["v"], prep["block_map"], prep["tile_sizes"]
     out = torch.empty_like(qt)
     lse = torch.empty((qt.shape[0], case.num_heads, qt.shape[1]), dtype=torch.float32, device=dev)
@@ -137,8 +137,8 @@ def bench_sparse(case, steps, warmup):
 
     ms = time_steps(step, steps, warmup)
     flops = sparse_flops(bmap.cpu().numpy(), sizes.cpu().numpy(), case.head_dim)
-    prep_ms = time_steps(lambda: sav.vsa_prepare(case.q.to(dev), case.k.to(dev), case.v.to(dev), case.video_shape,
-                                                 case.tile_shape, case.topk, case.scale), 3, 1)
+    prep_ms = time_steps(lambda: sav.vsa_prepare(q, k, v, case.video_shape, case.tile_shape, case.topk, case.scale),
+                         steps, warmup)
     return ms, flops, prep_ms
 
 

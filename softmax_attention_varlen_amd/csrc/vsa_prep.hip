@@ -80,68 +80,105 @@ __global__ __launch_bounds__(256) void untile_kernel(const uint16_t* __restrict_
   for (int j = lane; j < chunks; j += 64) *reinterpret_cast<u32x4*>(xrow + j * 8) = ld_global16(yrow + j * 8);
 }
 
-// Tile means: pooled[b][h][c][d] = sum of the size(c) real rows / max(size, 1).
-// One 64-thread block per (batch, tile, head); lane owns d = lane, lane+64, ...
-__global__ __launch_bounds__(64) void tile_pool_kernel(const uint16_t* __restrict__ x,
+// Tile means: pooled[b][h][c][d] = (sum of the size(c) real rows) / max(size, 1),
+// fp32, rows summed in ascending order. One workgroup per (batch, tile); a
+// thread owns one 16-byte chunk (8 columns of one head) of the tile's rows, so
+// a row is read by consecutive threads.
+__global__ __launch_bounds__(256) void tile_pool_kernel(const uint16_t* __restrict__ x,
                                                        const int32_t* __restrict__ sizes, float* __restrict__ pooled,
                                                        int n_tiles, int heads, int head_dim) {
-  const int lane = threadIdx.x;
-  const long id = blockIdx.x;  // ((b * n_tiles) + c) * heads + h
-  const int h = (int)(id % heads);
-  const int c = (int)((id / heads) % n_tiles);
-  const int b = (int)(id / ((long)heads * n_tiles));
+  const int c = (int)(blockIdx.x % n_tiles);
+  const long b = blockIdx.x / n_tiles;
   const int size = clampi(sizes[c], 0, 64);
   const float inv = 1.f / (float)(size > 1 ? size : 1);
-  const uint16_t* base = x + (((long)b * n_tiles + c) * 64 * heads + h) * head_dim;
-  float* prow = pooled + (((long)b * heads + h) * n_tiles + c) * head_dim;
-  for (int d = lane; d < head_dim; d += 64) {
-    float s = 0.f;
+  const long row_elems = (long)heads * head_dim;
+  const uint16_t* base = x + (b * n_tiles + c) * 64 * row_elems;
+  const int chunks = (int)(row_elems / 8);
+  for (int j = threadIdx.x; j < chunks; j += blockDim.x) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     for (int r = 0; r < size; ++r) {
-      s += (float)__builtin_bit_cast(__bf16, base[(long)r * heads * head_dim + d]);
+      const u32x4 v = ld_global16(base + (long)r * row_elems + j * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += __uint_as_float(v[i] << 16);
+        acc[2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
+      }
     }
-    prow[d] = s * inv;
+    const int h = (j * 8) / head_dim, d = (j * 8) % head_dim;
+    float* prow = pooled + ((b * heads + h) * n_tiles + c) * (long)head_dim + d;
+    *reinterpret_cast<f32x4*>(prow) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+    *reinterpret_cast<f32x4*>(prow + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
   }
 }
 
-// Scores of one query tile against every key tile, then a top-k mask.
-// One 256-thread block per (batch, head, query tile); LDS holds the query mean
-// and all n_tiles scores.
+constexpr int kMapRows = 8;  // query tiles per workgroup of the top-k kernel (at most)
+
+// Scores of up to qg query tiles of one (batch, head) against every key tile,
+// then a top-k mask per query tile. LDS holds the qg query means and the
+// qg x n_tiles scores. Thread c computes key tile c's scores (one pass over
+// its mean); a score is fp32 scale * sum_d qbar[d] kbar[d], d ascending.
+// Selection: tile c is kept when fewer than k tiles beat it (a higher score,
+// or an equal score at a lower index), or when k reaches the tile count.
 __global__ __launch_bounds__(256) void topk_map_kernel(const float* __restrict__ qpool,
                                                        const float* __restrict__ kpool, uint8_t* __restrict__ map,
                                                        int n_tiles, int heads, int kv_heads, int head_dim, float scale,
-                                                       int keep) {
-  extern __shared__ float sh[];  // [head_dim] query mean, then [n_tiles] scores
+                                                       int keep, int qg) {
+  extern __shared__ float sh[];  // [qg][head_dim] query means, then [qg][n_tiles] scores
   float* qs = sh;
-  float* sc = sh + head_dim;
-  const long row = blockIdx.x;  // (b * heads + h) * n_tiles + a
-  const int a = (int)(row % n_tiles);
-  const long bh = row / n_tiles;
+  float* sc = sh + qg * head_dim;
+  const int groups = (n_tiles + qg - 1) / qg;
+  const int a0 = (int)(blockIdx.x % groups) * qg;
+  const long bh = blockIdx.x / groups;
   const int h = (int)(bh % heads), b = (int)(bh / heads);
   const int hk = h / (heads / kv_heads);
-  const float* qrow = qpool + (bh * n_tiles + a) * (long)head_dim;
+  const int nq = n_tiles - a0 < qg ? n_tiles - a0 : qg;
   const float* kbase = kpool + ((long)b * kv_heads + hk) * n_tiles * (long)head_dim;
-  for (int d = threadIdx.x; d < head_dim; d += blockDim.x) qs[d] = qrow[d];
-  __syncthreads();
-  for (int c = threadIdx.x; c < n_tiles; c += blockDim.x) {
-    const float* krow = kbase + (long)c * head_dim;
-    float s = 0.f;
-    for (int d = 0; d < head_dim; ++d) s = __builtin_fmaf(qs[d], krow[d], s);
-    sc[c] = s * scale;
+  for (int i = threadIdx.x; i < nq * head_dim; i += blockDim.x) {
+    qs[i] = qpool[(bh * n_tiles + a0) * (long)head_dim + i];
   }
   __syncthreads();
-  uint8_t* mrow = map + row * n_tiles;
   for (int c = threadIdx.x; c < n_tiles; c += blockDim.x) {
-    uint8_t kept = 1;
-    if (keep < n_tiles) {
-      const float s = sc[c];
-      int rank = 0;
-      for (int j = 0; j < n_tiles; ++j) {
-        const float t = sc[j];
-        rank += (t > s) || (t == s && j < c);
+    const f32x4* krow = reinterpret_cast<const f32x4*>(kbase + (long)c * head_dim);
+    float s[kMapRows];
+#pragma unroll
+    for (int qi = 0; qi < kMapRows; ++qi) s[qi] = 0.f;
+    for (int d4 = 0; d4 < head_dim / 4; ++d4) {
+      const f32x4 kv = krow[d4];
+#pragma unroll
+      for (int qi = 0; qi < kMapRows; ++qi) {
+        if (qi < nq) {
+          const float* qrow = qs + qi * head_dim + 4 * d4;
+          s[qi] = __builtin_fmaf(qrow[0], kv[0], s[qi]);
+          s[qi] = __builtin_fmaf(qrow[1], kv[1], s[qi]);
+          s[qi] = __builtin_fmaf(qrow[2], kv[2], s[qi]);
+          s[qi] = __builtin_fmaf(qrow[3], kv[3], s[qi]);
+        }
       }
-      kept = rank < keep;
     }
-    mrow[c] = kept;
+#pragma unroll
+    for (int qi = 0; qi < kMapRows; ++qi) {
+      if (qi < nq) sc[qi * n_tiles + c] = s[qi] * scale;
+    }
+  }
+  __syncthreads();
+  for (int qi = 0; qi < nq; ++qi) {
+    const float* srow = sc + qi * n_tiles;
+    uint8_t* mrow = map + (bh * n_tiles + a0 + qi) * n_tiles;
+    for (int c = threadIdx.x; c < n_tiles; c += blockDim.x) {
+      uint8_t kept = 1;
+      if (keep < n_tiles) {
+        const float v = srow[c];
+        int rank = 0;
+        for (int j = 0; j < n_tiles; ++j) {
+          const float t = srow[j];
+          rank += (t > v) || (t == v && j < c);
+        }
+        kept = rank < keep;
+      }
+      mrow[c] = kept;
+    }
   }
 }
 
@@ -188,18 +225,22 @@ hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const 
                                 uint8_t* map, void* workspace, hipStream_t stream) {
   float* qpool = (float*)workspace;
   float* kpool = qpool + (size_t)batch * heads * n_tiles * head_dim;
-  hipLaunchKernelGGL(tile_pool_kernel, dim3((unsigned)((long)batch * n_tiles * heads)), dim3(64), 0, stream,
+  hipLaunchKernelGGL(tile_pool_kernel, dim3((unsigned)((long)batch * n_tiles)), dim3(256), 0, stream,
                      (const uint16_t*)q_tiled, sizes, qpool, n_tiles, heads, head_dim);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(tile_pool_kernel, dim3((unsigned)((long)batch * n_tiles * kv_heads)), dim3(64), 0, stream,
+  hipLaunchKernelGGL(tile_pool_kernel, dim3((unsigned)((long)batch * n_tiles)), dim3(256), 0, stream,
                      (const uint16_t*)k_tiled, sizes, kpool, n_tiles, kv_heads, head_dim);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int keep = topk < n_tiles ? topk : n_tiles;
-  const size_t lds = (size_t)(head_dim + n_tiles) * sizeof(float);
-  hipLaunchKernelGGL(topk_map_kernel, dim3((unsigned)((long)batch * heads * n_tiles)), dim3(256), lds, stream,
-                     qpool, kpool, map, n_tiles, heads, kv_heads, head_dim, scale, keep);
+  // as many query tiles per workgroup as keep the scores within 64 KB of LDS
+  int qg = (int)((64 * 1024 / sizeof(float) - (size_t)kMapRows * head_dim) / (size_t)n_tiles);
+  qg = qg < 1 ? 1 : (qg > kMapRows ? kMapRows : qg);
+  const size_t lds = (size_t)qg * (head_dim + n_tiles) * sizeof(float);
+  const long groups = (n_tiles + qg - 1) / qg;
+  hipLaunchKernelGGL(topk_map_kernel, dim3((unsigned)((long)batch * heads * groups)), dim3(256), lds, stream,
+                     qpool, kpool, map, n_tiles, heads, kv_heads, head_dim, scale, keep, qg);
   return hipGetLastError();
 }
 
