@@ -32,6 +32,56 @@ import workloads  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 
+# HBM traffic of each workload's main kernel, per launch: rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE (KiB per dispatch, one pass each), scaled by what
+# the same counters read for a plain 1 GiB device copy (bench.py --only copy):
+# FETCH_SIZE reports half the bytes read, WRITE_SIZE all the bytes written.
+# A record holds only while the kernel sources it was taken from are unchanged:
+# their sha256 is stored with it and a mismatch reports null.
+FETCH_SCALE = 2.0
+WRITE_SCALE = 1.0
+CSRC = os.path.join(ROOT, "softmax_attention_varlen_amd", "csrc")
+_PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "launch.hpp"]
+TRAFFIC = {
+    "dense": {"kernel": "prefill_d128_kernel<false,8,3>", "fetch_kib": 73808.8, "write_kib": 49923.7,
+              "sources": _PREFILL_SRC, "sha256": "c08464c1eabe9f53"},
+    "causal": {"kernel": "prefill_d128_kernel<true,8,3>", "fetch_kib": 110343.0, "write_kib": 142436.5,
+               "sources": _PREFILL_SRC, "sha256": "c08464c1eabe9f53"},
+    "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443446.2, "write_kib": 3040.1,
+              "sources": ["paged_decode_stream.hip", "attn_common.hpp", "launch.hpp"], "sha256": "da55d4286999fe7c"},
+    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 430233.7, "write_kib": 49920.1,
+               "sources": ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "launch.hpp"],
+               "sha256": "93ddc01b0ae2456d"},
+}
+
+
+def sources_sha256(files) -> str:
+    import hashlib
+    m = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            m.update(fh.read())
+    return m.hexdigest()[:16]
+
+
+def traffic_bytes(workload: str):
+    """Measured HBM bytes per launch of the workload's main kernel, or None when
+    the kernel sources changed since the counters were taken."""
+    rec = TRAFFIC[workload]
+    if sources_sha256(rec["sources"]) != rec["sha256"]:
+        return None
+    return int(round((rec["fetch_kib"] * FETCH_SCALE + rec["write_kib"] * WRITE_SCALE) * 1024))
+
+
+def roofline(workload: str, bound: str, achieved: float, work: float):
+    """Roofline object: achieved rate of the step against the MI355X peak."""
+    peak, unit = (PEAK_BF16_TFLOPS, "TFLOP/s") if bound == "mfma" else (PEAK_HBM_GBPS, "GB/s")
+    rec = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+           "frac": round(achieved / peak, 4), "traffic": traffic_bytes(workload),
+           "kernel": TRAFFIC[workload]["kernel"]}
+    rec["algorithmic_gflop_per_launch" if bound == "mfma" else "algorithmic_gb_per_launch"] = round(work / 1e9, 4)
+    return rec
+
 
 # ----------------------------------------------------------------------------
 # algorithmic work (only what the method must do)
@@ -218,16 +268,14 @@ def main():
         tf = flops / (ms * 1e-3) / 1e12
         log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s")
         secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
-                          "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
-                          "algorithmic_gflop": round(flops / 1e9, 3)})
+                          "roofline": roofline("causal", "mfma", tf, flops)})
     if args.only in (None, "paged") and not (args.only is None and args.no_secondary):
         case = workloads.config4()
         ms, nbytes = bench_paged(case, args.steps, args.warmup)
         gbs = nbytes / (ms * 1e-3) / 1e9
         log(f"{case.name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
         secondary.append({"workload": case.name, "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
-                          "frac_of_peak": round(gbs / PEAK_HBM_GBPS, 4), "bound": "hbm",
-                          "algorithmic_gb": round(nbytes / 1e9, 4)})
+                          "roofline": roofline("paged", "hbm", gbs, nbytes)})
         del case
         torch.cuda.empty_cache()
     if args.only in (None, "sparse") and not (args.only is None and args.no_secondary):
@@ -236,8 +284,7 @@ def main():
         tf = flops / (ms * 1e-3) / 1e12
         log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s (map build {prep_ms * 1e3:.0f} us)")
         secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
-                          "frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4), "bound": "mfma",
-                          "algorithmic_gflop": round(flops / 1e9, 3),
+                          "roofline": roofline("sparse", "mfma", tf, flops),
                           "tile_prep_and_map_ms": round(prep_ms, 4)})
 
     if head is None:  # a single secondary workload was asked for
@@ -260,10 +307,7 @@ def main():
         "config": {"workload": case.name, "batch": 2, "seq_len": 4096, "num_heads": case.num_heads,
                    "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim, "causal": case.causal,
                    "layout": "packed varlen [total, heads, dim], cu_seqlens [0, 4096, 8192]", "lse": "fp32"},
-        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "varlen_fwd_kernel<128,false>",
-                     "algorithmic_gflop_per_launch": round(flops / 1e9, 3)},
+        "roofline": roofline("dense", "mfma", tf, flops),
         "secondary": secondary,
     }
     if not args.no_cpu_baseline:

@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256) void tile_pool_kernel(const uint16_t* __restri
   }
 }
 
-constexpr int kMapRows = 8;  // query tiles per workgroup of the top-k kernel (at most)
+constexpr int kMapRows = 4;  // query tiles per workgroup of the top-k kernel (at most)
 
 // Scores of up to qg query tiles of one (batch, head) against every key tile,
 // then a top-k mask per query tile. LDS holds the qg query means and the
@@ -125,7 +125,8 @@ __global__ __launch_bounds__(256) void topk_map_kernel(const float* __restrict__
                                                        const float* __restrict__ kpool, uint8_t* __restrict__ map,
                                                        int n_tiles, int heads, int kv_heads, int head_dim, float scale,
                                                        int keep, int qg) {
-  extern __shared__ float sh[];  // [qg][head_dim] query means, then [qg][n_tiles] scores
+  extern __shared__ float sh[];  // [qg][head_dim] query means, then [qg][stride] scores
+  const int stride = (n_tiles + 3) & ~3;  // score rows padded to whole 16-byte groups
   float* qs = sh;
   float* sc = sh + qg * head_dim;
   const int groups = (n_tiles + qg - 1) / qg;
@@ -135,11 +136,16 @@ __global__ __launch_bounds__(256) void topk_map_kernel(const float* __restrict__
   const int hk = h / (heads / kv_heads);
   const int nq = n_tiles - a0 < qg ? n_tiles - a0 : qg;
   const float* kbase = kpool + ((long)b * kv_heads + hk) * n_tiles * (long)head_dim;
-  for (int i = threadIdx.x; i < nq * head_dim; i += blockDim.x) {
-    qs[i] = qpool[(bh * n_tiles + a0) * (long)head_dim + i];
-  }
+  for (int i = threadIdx.x; i < nq * head_dim; i += blockDim.x) qs[i] = qpool[(bh * n_tiles + a0) * (long)head_dim + i];
   __syncthreads();
-  for (int c = threadIdx.x; c < n_tiles; c += blockDim.x) {
+  for (int c = threadIdx.x; c < stride; c += blockDim.x) {
+    if (c >= n_tiles) {  // padding: never beats a real score
+#pragma unroll
+      for (int qi = 0; qi < kMapRows; ++qi) {
+        if (qi < nq) sc[qi * stride + c] = kNegInf;
+      }
+      continue;
+    }
     const f32x4* krow = reinterpret_cast<const f32x4*>(kbase + (long)c * head_dim);
     float s[kMapRows];
 #pragma unroll
@@ -159,23 +165,27 @@ __global__ __launch_bounds__(256) void topk_map_kernel(const float* __restrict__
     }
 #pragma unroll
     for (int qi = 0; qi < kMapRows; ++qi) {
-      if (qi < nq) sc[qi * n_tiles + c] = s[qi] * scale;
+      if (qi < nq) sc[qi * stride + c] = s[qi] * scale;
     }
   }
   __syncthreads();
   for (int qi = 0; qi < nq; ++qi) {
-    const float* srow = sc + qi * n_tiles;
+    const float* srow = sc + qi * stride;
     uint8_t* mrow = map + (bh * n_tiles + a0 + qi) * n_tiles;
     for (int c = threadIdx.x; c < n_tiles; c += blockDim.x) {
       uint8_t kept = 1;
       if (keep < n_tiles) {
         const float v = srow[c];
-        int rank = 0;
-        for (int j = 0; j < n_tiles; ++j) {
-          const float t = srow[j];
-          rank += (t > v) || (t == v && j < c);
+        // tiles beating c: a higher score, or an equal one at a lower index
+        int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+        for (int j = 0; j < stride; j += 4) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(srow + j);
+          r0 += (t[0] > v) || (t[0] == v && j < c);
+          r1 += (t[1] > v) || (t[1] == v && j + 1 < c);
+          r2 += (t[2] > v) || (t[2] == v && j + 2 < c);
+          r3 += (t[3] > v) || (t[3] == v && j + 3 < c);
         }
-        kept = rank < keep;
+        kept = (r0 + r1 + r2 + r3) < keep;
       }
       mrow[c] = kept;
     }
@@ -235,9 +245,10 @@ hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const 
   if (e != hipSuccess) return e;
   const int keep = topk < n_tiles ? topk : n_tiles;
   // as many query tiles per workgroup as keep the scores within 64 KB of LDS
-  int qg = (int)((64 * 1024 / sizeof(float) - (size_t)kMapRows * head_dim) / (size_t)n_tiles);
+  const int stride = (n_tiles + 3) & ~3;
+  int qg = (int)((64 * 1024 / sizeof(float) - (size_t)kMapRows * head_dim) / (size_t)stride);
   qg = qg < 1 ? 1 : (qg > kMapRows ? kMapRows : qg);
-  const size_t lds = (size_t)qg * (head_dim + n_tiles) * sizeof(float);
+  const size_t lds = (size_t)qg * (head_dim + stride) * sizeof(float);
   const long groups = (n_tiles + qg - 1) / qg;
   hipLaunchKernelGGL(topk_map_kernel, dim3((unsigned)((long)batch * heads * groups)), dim3(256), lds, stream,
                      qpool, kpool, map, n_tiles, heads, kv_heads, head_dim, scale, keep, qg);
