@@ -56,6 +56,28 @@ def test_zero_context_gives_zero_and_neg_inf():
     check(case)
 
 
+# head_dim 128 streams equal segments of the concatenated token stream (at
+# least 256 positions each), so a segment can hold many sequences, start or end
+# exactly on a sequence boundary, start inside a 32-token chunk, or cover one
+# long sequence among many others
+STREAM_CASES = {
+    "zeros-between": [0, 5, 0, 300, 0, 0, 1, 0],
+    "aligned-32s": [32] * 100,
+    "ones-then-long": [1] * 50 + [257, 0, 513],
+    "odd-mix": [7, 250, 3, 1000, 0, 33, 31, 129, 2, 600],
+    "one-long": [40000],
+}
+
+
+@pytest.mark.parametrize("name", list(STREAM_CASES))
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (8, 1), (40, 2)])
+def test_stream_segments_d128(name, hq, hkv):
+    ctx = STREAM_CASES[name]
+    case = paged_case(ctx, num_heads=hq, num_kv_heads=hkv, head_dim=128, seed=230 + len(ctx) + hq, spare_blocks=3,
+                      name=f"stream-{name}-h{hq}kv{hkv}")
+    check(case)
+
+
 def test_host_max_context_len_larger_than_needed():
     # a generous host bound only changes the split plan, not the result
     case = paged_case([300, 2000, 17], num_heads=8, num_kv_heads=2, head_dim=128, seed=212, max_blocks_per_seq=64,
