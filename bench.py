@@ -41,17 +41,16 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 CSRC = os.path.join(ROOT, "softmax_attention_varlen_amd", "csrc")
-_PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "launch.hpp"]
+_PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp"]
 TRAFFIC = {
     "dense": {"kernel": "prefill_d128_kernel<false,8,3>", "fetch_kib": 73808.8, "write_kib": 49923.7,
-              "sources": _PREFILL_SRC, "sha256": "c08464c1eabe9f53"},
+              "sources": _PREFILL_SRC, "sha256": "d84e76cbb930b4ff"},
     "causal": {"kernel": "prefill_d128_kernel<true,8,3>", "fetch_kib": 110343.0, "write_kib": 142436.5,
-               "sources": _PREFILL_SRC, "sha256": "c08464c1eabe9f53"},
+               "sources": _PREFILL_SRC, "sha256": "d84e76cbb930b4ff"},
     "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443446.2, "write_kib": 3040.1,
-              "sources": ["paged_decode_stream.hip", "attn_common.hpp", "launch.hpp"], "sha256": "da55d4286999fe7c"},
-    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 430233.7, "write_kib": 49920.1,
-               "sources": ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "launch.hpp"],
-               "sha256": "93ddc01b0ae2456d"},
+              "sources": ["paged_decode_stream.hip", "attn_common.hpp"], "sha256": "386540a926c11f8c"},
+    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 428675.5, "write_kib": 49920.1,
+               "sources": ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"], "sha256": "0189fa2bd092cb4f"},
 }
 
 

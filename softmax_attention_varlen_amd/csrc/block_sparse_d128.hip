@@ -30,6 +30,7 @@ constexpr int kSW = 4;                       // waves per workgroup
 constexpr int kSIPW = 16 / kSW;              // load blocks per wave per K (or V) tile
 constexpr int kSparseLds = 4 * kTileBytes;   // K stages 0, 1, then V stages 0, 1
 constexpr int kMergeOBytes = 32 * 128 * 4;   // one wave's fp32 O^T block
+constexpr int kListCap = kSparseD128MaxTiles;  // the whole kept-tile list is staged in LDS
 static_assert(2 * kMergeOBytes + 2 * 512 <= kSparseLds, "merge area must fit in the ring");
 
 struct Entry {
@@ -49,6 +50,7 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
     int num_tiles, int hq, int hkv, int n_items, int per_xcd, float c, uint16_t* __restrict__ out,
     float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) char smem[kSparseLds];
+  __shared__ int32_t lst[kListCap];
 
   // XCD-aware order: XCD x runs logical items [x*per_xcd, (x+1)*per_xcd); query
   // tiles run fastest, so one XCD's L2 serves the K/V of few heads.
@@ -103,13 +105,20 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
                       ring + (2 + stage) * kTileBytes, w * kSIPW, lane);
   };
 
+  // The kept-tile list goes to LDS first: a list word read from memory inside
+  // the loop would be a scalar load, and on this architecture every later wait
+  // for LDS data also waits for outstanding scalar loads. (The launcher only
+  // sends tile counts up to kListCap here.)
+  for (int i = tid; i < count; i += 64 * kSW) lst[i] = list[i];
+  __syncthreads();
+  auto entry = [&](int j) -> int32_t { return lst[j]; };
   // entry of tile j (unpacked) and raw entries of tiles j+1, j+2: each list
   // word is read one step before its first use
   Entry e0{0, 1};
   int32_t n1 = 0, n2 = 0;
-  if (count > 0) e0 = unpack(list[0], num_tiles);
-  if (count > 1) n1 = list[1];
-  if (count > 2) n2 = list[2];
+  if (count > 0) e0 = unpack(entry(0), num_tiles);
+  if (count > 1) n1 = entry(1);
+  if (count > 2) n2 = entry(2);
 
   if (count > 0) {
     issue_k(e0, 0);
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
     const int size = e0.size;
     e0 = e1;
     n1 = n2;
-    if (j + 3 < count) n2 = list[j + 3];
+    if (j + 3 < count) n2 = entry(j + 3);
     if (wave_live) {
       // after the last tile the "next" K stage holds stale data; its S^T is unused
       const char* nk = smem + ((j + 1) & 1) * kTileBytes;

@@ -92,7 +92,9 @@ struct SparseArgs {
 
 size_t sparse_workspace_bytes(int batch, int num_heads, int num_tiles);
 hipError_t launch_block_sparse_fwd(const SparseArgs& a, hipStream_t stream);
-// head_dim 128; expects the packed, size-filtered lists in a.idx / a.num.
+// head_dim 128 with at most kSparseD128MaxTiles tiles (its kept-tile list is
+// staged in LDS); expects the packed, size-filtered lists in a.idx / a.num.
+constexpr int kSparseD128MaxTiles = 3072;
 hipError_t launch_block_sparse_d128(const SparseArgs& a, hipStream_t stream);
 
 // Video tile geometry (raster (t, h, w) cut into (tile_t, tile_h, tile_w) boxes).

@@ -70,6 +70,28 @@ def test_partial_tiles_random_map(d, hq, hkv):
     assert_close("lse", host(lse), ref_l, LSE_TOL)
 
 
+def test_head_dim_128_beyond_staged_list_capacity():
+    # head_dim 128 stages each query tile's kept-tile list in LDS for up to
+    # 3072 tiles; a longer tile axis takes the general kernel
+    b, nt, h, d = 1, 3100, 1, 128
+    q, k, v = (randn_bf16((b, nt * 64, h, d), 340 + j) for j in range(3))
+    rng = np.random.default_rng(34)
+    sizes = np.full(nt, 64, dtype=np.int32)
+    sizes[rng.choice(nt, 40, replace=False)] = rng.integers(1, 64, 40)
+    bmap = np.zeros((b, h, nt, nt), dtype=bool)
+    for a in range(nt):
+        bmap[0, 0, a, rng.choice(nt, 3, replace=False)] = True
+    bmap[0, 0, nt - 1, rng.choice(nt, 200, replace=False)] = True  # one long kept list
+    scale = d ** -0.5
+    announce("sparse beyond list capacity", nt)
+    out, lse = run(q, k, v, bmap, sizes, scale)
+    sample = sorted({0, 1, 1500, 3071, 3072, 3073, nt - 2, nt - 1} | set(rng.choice(nt, 8, replace=False).tolist()))
+    ref_o, ref_l = oracle.block_sparse_attention(q, k, v, bmap, sizes, scale, q_tiles=sample)
+    rows = np.concatenate([np.arange(a * 64, a * 64 + 64) for a in sample])
+    assert_close("out", host(out)[:, rows], ref_o[:, rows], OUT_TOL, bf16_output=True)
+    assert_close("lse", host(lse)[:, :, rows], ref_l[:, :, rows], LSE_TOL)
+
+
 def test_full_map_matches_dense_oracle_and_is_deterministic():
     b, nt, h, d = 1, 5, 3, 128
     q, k, v = (randn_bf16((b, nt * 64, h, d), 320 + j) for j in range(3))
