@@ -31,6 +31,8 @@ from .attention import (  # noqa: F401
     varlen_attention,
     dense_attention,
     paged_decode_attention,
+    paged_kv_write,
+    paged_prefill_attention,
     block_sparse_attention,
     merge_partials,
     slot_to_block_offset,

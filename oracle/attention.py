@@ -249,6 +249,90 @@ def block_sparse_attention(q, k, v, block_map, tile_sizes, scale: float, tile: i
     return out, lse
 
 
+def _gather_paged(kv_cache, plane: int, blk: np.ndarray, off: np.ndarray) -> np.ndarray:
+    """Rows (blk[i], off[i]) of one cache plane as float64 [N, Hkv, D]."""
+    if isinstance(kv_cache, np.ndarray):
+        return kv_cache[plane][blk, off].astype(np.float64)
+    import torch
+
+    return kv_cache[plane][torch.from_numpy(blk), torch.from_numpy(off)].to(torch.float64).numpy()
+
+
+def paged_kv_write(kv_cache, k, v, slot_mapping):
+    """[ASC] AscendAttentionImpl.reshape_and_cache with AscendMetadata.slot_mapping:
+    new token i's K and V rows go to the cache slot slot_mapping[i], i.e. block
+    slot // block_size at offset slot % block_size (slot_to_block_offset).
+    Reading: a negative slot marks a token that is not stored (padding).
+
+    kv_cache [2, NB, BS, Hkv, D]; k, v [N, Hkv, D]. Returns a new cache (same
+    dtype and container type); the input is not modified.
+
+    Pinned: worked slot example, write-then-gather round trip, untouched slots.
+    """
+    slots = _ints(slot_mapping)
+    bs = kv_cache.shape[2]
+    keep = np.nonzero(slots >= 0)[0]
+    blk, off = slot_to_block_offset(slots[keep], bs)
+    if isinstance(kv_cache, np.ndarray):
+        cache = kv_cache.copy()
+        cache[0][blk, off] = np.asarray(k)[keep]
+        cache[1][blk, off] = np.asarray(v)[keep]
+        return cache
+    import torch
+
+    cache = kv_cache.clone()
+    ki, bi, oi = torch.from_numpy(keep), torch.from_numpy(blk), torch.from_numpy(off)
+    cache[0][bi, oi] = k[ki].to(cache.dtype)
+    cache[1][bi, oi] = v[ki].to(cache.dtype)
+    return cache
+
+
+def paged_prefill_attention(q, kv_cache, block_tables, cu_seqlens_q, context_lens, scale: float, rows=None):
+    """Multi-token attention over a paged cache ([ASC] _get_fia_params for
+    PrefillCacheHit / ChunkedPrefill / SpecDecoding: keys and values come from
+    the paged cache through ``block_table`` with ``actual_seq_lengths_kv`` =
+    seq_lens, the queries are packed by cumulative query lengths). The cache
+    already holds the sequence's new tokens (reshape_and_cache runs first), so
+    sequence b has Lk = context_lens[b] keys, its Lq = cu_q[b+1] - cu_q[b]
+    queries are the last Lq positions, and bottom-right causal applies: key j
+    is visible to query i iff j <= i + (Lk - Lq). Key t of sequence b is cache
+    row (block_tables[b, t // BS], t % BS).
+
+    q [Tq, Hq, D]; kv_cache [2, NB, BS, Hkv, D]. Returns out [R, Hq, D] and
+    lse [Hq, R] (float64) for the selected packed rows (all by default).
+
+    Pinned: contiguous varlen equivalence, decode (Lq = 1) equivalence, chunk
+    split identity, physical block relabelling.
+    """
+    qf = _f64(q)
+    bt = _ints(block_tables)
+    cu = _ints(cu_seqlens_q)
+    ctx = _ints(context_lens)
+    total_q, hq, _ = qf.shape
+    bs = kv_cache.shape[2]
+    hkv = kv_cache.shape[3]
+    group = hq // hkv
+    sel = np.arange(total_q) if rows is None else _ints(rows)
+    out = np.zeros((sel.size, hq, kv_cache.shape[4]))
+    lse = np.full((hq, sel.size), NEG_INF)
+    for b in range(cu.size - 1):
+        q0, q1 = int(cu[b]), int(cu[b + 1])
+        pick = np.nonzero((sel >= q0) & (sel < q1))[0]
+        if pick.size == 0:
+            continue
+        lk = int(ctx[b])
+        t = np.arange(lk)
+        keys = _gather_paged(kv_cache, 0, bt[b, t // bs], t % bs)
+        vals = _gather_paged(kv_cache, 1, bt[b, t // bs], t % bs)
+        local = sel[pick] - q0
+        allowed = _causal_allowed(local, q1 - q0, lk)
+        for h in range(hq):
+            o, l_ = _attend(qf[sel[pick], h], keys[:, h // group], vals[:, h // group], scale, allowed)
+            out[pick, h] = o
+            lse[h, pick] = l_
+    return out, lse
+
+
 def merge_partials(outs, lses):
     """Combine attention results over disjoint key subsets into the result over
     their union (the definition split over keys: each part carries its normalised

@@ -53,10 +53,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
   int rest = item;
   const int qh = rest % group;
   rest /= group;
-  const int tile = tiles_per_doc - 1 - rest % tiles_per_doc;  // heaviest (last) tiles first
-  rest /= tiles_per_doc;
   const int doc = rest % batch;
-  const int hk = rest / batch;
+  rest /= batch;
+  // query tiles from the last (heaviest under a causal mask) to the first,
+  // across all documents, within a kv head
+  const int tile = tiles_per_doc - 1 - rest % tiles_per_doc;
+  const int hk = rest / tiles_per_doc;
   const int h = hk * group + qh;
 
   const int q0 = clampi(cu_q[doc], 0, total_q);

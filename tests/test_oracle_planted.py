@@ -112,3 +112,31 @@ def test_gqa_modulo_mutant_is_caught(monkeypatch):
 
     monkeypatch.setattr(ta.oracle, "varlen_attention", varlen_mod)
     assert _fails(ta.test_torch_sdpa_fp64, False)
+
+
+def test_paged_prefill_mutants_are_caught(monkeypatch):
+    from tests import test_oracle_paged_prefill as tpp
+
+    orig_gather = A._gather_paged
+
+    def gather_reversed_slots(kv_cache, plane, blk, off):
+        # plant: read each block's slots back to front
+        return orig_gather(kv_cache, plane, blk, kv_cache.shape[2] - 1 - off)
+
+    monkeypatch.setattr(A, "_gather_paged", gather_reversed_slots)
+    assert _fails(tpp.test_brute_force_tiny)
+    monkeypatch.setattr(A, "_gather_paged", orig_gather)
+
+    # plant: top-left causal alignment (new queries treated as the first positions)
+    monkeypatch.setattr(A, "_causal_allowed", _causal_top_left)
+    assert _fails(tpp.test_brute_force_tiny)
+    monkeypatch.setattr(A, "_causal_allowed", _orig_causal)
+
+    orig_write = A.paged_kv_write
+
+    def write_swapped(kv_cache, k, v, slot_mapping):
+        # plant: K and V planes exchanged
+        return orig_write(kv_cache, v, k, slot_mapping)
+
+    monkeypatch.setattr(tpp.oracle, "paged_kv_write", write_swapped)
+    assert _fails(tpp.test_kv_write_worked_example)

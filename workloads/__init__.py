@@ -175,6 +175,63 @@ def paged_case(context_lens, *, num_heads, num_kv_heads, head_dim, seed, block_s
     )
 
 
+@dataclass
+class PagedPrefillCase:
+    name: str
+    q: torch.Tensor  # packed [Tq, Hq, D] bf16
+    cu_seqlens_q: np.ndarray  # int32 [B + 1]
+    kv_cache: torch.Tensor  # [2, NB, BS, Hkv, D] bf16 (already holds every sequence's new tokens)
+    block_tables: np.ndarray  # int32 [B, MB], unused tail = -1
+    context_lens: np.ndarray  # int32 [B]: keys per sequence, new tokens included
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    scale: float
+    seed: int
+
+    @property
+    def batch(self) -> int:
+        return int(self.context_lens.size)
+
+    @property
+    def max_seqlen_q(self) -> int:
+        return int(np.diff(self.cu_seqlens_q).max()) if self.batch else 0
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.batch else 0
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.kv_cache.shape[1])
+
+
+def paged_prefill_case(q_lens, context_lens, *, num_heads, num_kv_heads, head_dim, seed, block_size=128,
+                       max_blocks_per_seq=None, spare_blocks=0, rng=None, scale=None,
+                       name="paged-prefill") -> PagedPrefillCase:
+    """Multi-token queries over a paged cache: cache and tables as in paged_case
+    (same seed, same streams), queries drawn with generator seed 1000*seed + 3."""
+    base = paged_case(context_lens, num_heads=num_heads, num_kv_heads=num_kv_heads, head_dim=head_dim, seed=seed,
+                      block_size=block_size, max_blocks_per_seq=max_blocks_per_seq, spare_blocks=spare_blocks,
+                      rng=rng, scale=scale, name=name)
+    ql = np.asarray(q_lens, dtype=np.int64)
+    return PagedPrefillCase(
+        name=name,
+        q=randn_bf16((int(ql.sum()), num_heads, head_dim), 1000 * seed + 3),
+        cu_seqlens_q=cumulative(ql),
+        kv_cache=base.kv_cache,
+        block_tables=base.block_tables,
+        context_lens=base.context_lens,
+        num_heads=num_heads,
+        num_kv_heads=num_kv_heads,
+        head_dim=head_dim,
+        block_size=block_size,
+        scale=base.scale,
+        seed=seed,
+    )
+
+
 def config4_lengths(rng=None) -> np.ndarray:
     rng = np.random.default_rng(4) if rng is None else rng
     return rng.integers(1024, 32769, 64)
