@@ -138,6 +138,57 @@ attn_status_t attn_paged_decode(const void* q, const void* kv_cache,
                                 void* stream);
 
 /*
+ * Paged KV cache write (vLLM-Ascend attention_v1.py page:
+ * AscendAttentionImpl.reshape_and_cache with AscendMetadata.slot_mapping).
+ * New token i's K and V rows are stored at cache slot slot_mapping[i]: block
+ * slot / block_size, offset slot % block_size, in both planes.
+ *
+ *   k, v          [num_tokens, num_kv_heads, head_dim] bf16
+ *   slot_mapping  [num_tokens] int32; a negative slot (a padding token) or one
+ *                 at or past num_blocks * block_size is skipped. Slots must be
+ *                 unique (two tokens writing one slot race).
+ *   kv_cache      [2, num_blocks, block_size, num_kv_heads, head_dim] bf16,
+ *                 written in place (only the named slots change)
+ *   block_size    must be 128.
+ * num_tokens == 0 is a no-op.
+ */
+attn_status_t attn_paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping,
+                                  int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t num_blocks, int32_t block_size, void* kv_cache, void* stream);
+
+/*
+ * Multi-token attention over a paged KV cache: prefix-cache-hit prefill,
+ * chunked prefill and speculative decoding (vLLM-Ascend attention_v1.py page:
+ * AscendAttentionState and _get_fia_params, which read keys and values from
+ * the paged cache through block_table with actual_seq_lengths_kv = seq_lens and
+ * take the queries packed by cumulative query lengths). The cache already
+ * holds each sequence's new tokens (reshape_and_cache runs first), so the
+ * Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] queries of sequence b are its last
+ * Lq positions among Lk = context_lens[b] keys, with bottom-right causal
+ * masking: key j is visible to query i iff j <= i + Lk - Lq. A query that sees
+ * no key gets O = 0, LSE = -inf.
+ *
+ *   q             [total_q, num_heads, head_dim] bf16, packed by cu_seqlens_q
+ *   kv_cache      [2, num_blocks, block_size, num_kv_heads, head_dim] bf16
+ *   block_tables  [batch, max_blocks_per_seq] int32, as for attn_paged_decode
+ *   cu_seqlens_q  [batch + 1] int32, leading 0, non-decreasing
+ *   context_lens  [batch] int32 keys per sequence (new tokens included),
+ *                 0 <= len <= max_context_len
+ *   max_seqlen_q, max_context_len (host) bound the lengths; they size the grid.
+ *   block_size    must be 128.
+ *   out           [total_q, num_heads, head_dim] bf16
+ *   lse           nullable; [num_heads, total_q] fp32
+ * batch == 0 or total_q == 0 is a no-op. No workspace.
+ */
+attn_status_t attn_paged_prefill(const void* q, const void* kv_cache, const int32_t* block_tables,
+                                 const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                 int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                 int32_t max_context_len, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                 int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, float softmax_scale, void* out, float* lse,
+                                 void* stream);
+
+/*
  * Block map -> ascending index lists (vLLM-Omni fastvideo_vsa.py page: the
  * native route converts the boolean block map with map_to_index into per-row
  * kept key-tile indices and counts).

@@ -26,6 +26,8 @@ __all__ = [
     "attn_varlen_fwd",
     "attn_paged_decode_workspace_size",
     "attn_paged_decode",
+    "attn_paged_kv_write",
+    "attn_paged_prefill",
     "attn_block_map_to_index",
     "attn_block_sparse_workspace_size",
     "attn_block_sparse_fwd",
@@ -52,6 +54,9 @@ _SIGS = {
     "attn_paged_decode_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "attn_paged_decode": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p,
                                          _p, _p, _sz, _p]),
+    "attn_paged_kv_write": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p]),
+    "attn_paged_prefill": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                          _i32, _f32, _p, _p, _p]),
     "attn_block_map_to_index": (ctypes.c_int, [_p, _i32, _i32, _p, _p, _p]),
     "attn_block_sparse_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "attn_block_sparse_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
@@ -204,6 +209,56 @@ def attn_paged_decode(q, kv_cache, block_tables, context_lens, max_context_len: 
         _dev(out, "out", torch.bfloat16, dev), _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
         _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(), _stream_ptr(q, stream))
     _check("attn_paged_decode", st)
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def attn_paged_kv_write(k, v, slot_mapping, kv_cache, stream=None):
+    """Store new tokens' K/V [N, Hkv, D] at their cache slots (negative slots are
+    skipped); kv_cache [2, NB, 128, Hkv, D] is written in place and returned."""
+    dev = kv_cache.device
+    n, hkv, d = k.shape
+    two, nblocks, bs, hkv_c, dk = kv_cache.shape
+    if two != 2 or hkv_c != hkv or dk != d:
+        raise ValueError("kv_cache must be [2, num_blocks, block_size, num_kv_heads, head_dim] matching k")
+    _shape(v, "v", (n, hkv, d))
+    _shape(slot_mapping, "slot_mapping", (n,))
+    st = load_library().attn_paged_kv_write(
+        _dev(k, "k", torch.bfloat16, dev), _dev(v, "v", torch.bfloat16, dev),
+        _dev(slot_mapping, "slot_mapping", torch.int32, dev), n, hkv, d, nblocks, bs,
+        _dev(kv_cache, "kv_cache", torch.bfloat16), _stream_ptr(kv_cache, stream))
+    _check("attn_paged_kv_write", st)
+    return kv_cache
+
+
+def attn_paged_prefill(q, kv_cache, block_tables, cu_seqlens_q, context_lens, max_seqlen_q: int,
+                       max_context_len: int, softmax_scale: float, out=None, lse=None, return_lse: bool = False,
+                       stream=None):
+    """Multi-token queries (packed [Tq, Hq, D] by cu_seqlens_q) over a paged
+    cache [2, NB, 128, Hkv, D], bottom-right causal against context_lens keys."""
+    dev = q.device
+    total_q, hq, d = q.shape
+    two, nblocks, bs, hkv, dk = kv_cache.shape
+    if two != 2 or dk != d:
+        raise ValueError("kv_cache must be [2, num_blocks, block_size, num_kv_heads, head_dim]")
+    batch = cu_seqlens_q.numel() - 1
+    mbps = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    _shape(block_tables, "block_tables", (batch, mbps))
+    _shape(context_lens, "context_lens", (batch,))
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, total_q), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _shape(lse, "lse", (hq, total_q))
+    st = load_library().attn_paged_prefill(
+        _dev(q, "q", torch.bfloat16), _dev(kv_cache, "kv_cache", torch.bfloat16, dev),
+        _dev(block_tables, "block_tables", torch.int32, dev), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev),
+        _dev(context_lens, "context_lens", torch.int32, dev), batch, total_q, int(max_seqlen_q),
+        int(max_context_len), nblocks, mbps, hq, hkv, d, bs, float(softmax_scale),
+        _dev(out, "out", torch.bfloat16, dev), _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
+        _stream_ptr(q, stream))
+    _check("attn_paged_prefill", st)
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -101,6 +101,57 @@ attn_status_t attn_paged_decode(const void* q, const void* kv_cache, const int32
   return from_hip(attn::launch_paged_decode(a, plan, (hipStream_t)stream));
 }
 
+attn_status_t attn_paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens,
+                                  int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                                  void* kv_cache, void* stream) {
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks < 0) return ATTN_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (block_size != 128) return ATTN_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return ATTN_OK;
+  if (k == nullptr || v == nullptr || slot_mapping == nullptr || kv_cache == nullptr || num_blocks == 0) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  if ((long long)num_blocks * block_size * num_kv_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  return from_hip(attn::launch_paged_kv_write(k, v, slot_mapping, num_tokens, num_kv_heads * head_dim, num_blocks,
+                                              kv_cache, (hipStream_t)stream));
+}
+
+attn_status_t attn_paged_prefill(const void* q, const void* kv_cache, const int32_t* block_tables,
+                                 const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t batch,
+                                 int32_t total_q, int32_t max_seqlen_q, int32_t max_context_len, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, float softmax_scale, void* out, float* lse,
+                                 void* stream) {
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_context_len < 0) return ATTN_ERR_INVALID_ARG;
+  if (num_blocks < 0 || max_blocks_per_seq < 0 || num_heads <= 0 || num_kv_heads <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
+  if (block_size != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)max_context_len > (long long)max_blocks_per_seq * block_size) return ATTN_ERR_INVALID_ARG;
+  if (max_seqlen_q > total_q) return ATTN_ERR_INVALID_ARG;
+  if (batch == 0 || total_q == 0) return ATTN_OK;
+  if (max_seqlen_q == 0) return ATTN_ERR_INVALID_ARG;  // rows exist but no sequence could own them
+  if (q == nullptr || out == nullptr || cu_seqlens_q == nullptr || context_lens == nullptr) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  if (max_context_len > 0 && (kv_cache == nullptr || block_tables == nullptr || num_blocks == 0)) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  if ((long long)total_q * num_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)num_blocks * block_size * num_kv_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  if (attn::varlen_grid_size(batch, max_seqlen_q, num_heads) > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  const long long plane = (long long)num_blocks * block_size * num_kv_heads * head_dim;  // elements
+  attn::VarlenArgs a{q, kv_cache, (const uint16_t*)kv_cache + plane, cu_seqlens_q, nullptr, batch, total_q, 0,
+                     max_seqlen_q, max_context_len, num_heads, num_kv_heads, head_dim, softmax_scale, 1, out, lse};
+  a.paged = true;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  return from_hip(attn::launch_varlen_fwd(a, (hipStream_t)stream));
+}
+
 attn_status_t attn_block_map_to_index(const uint8_t* block_map, int32_t rows, int32_t n_cols, int32_t* idx,
                                       int32_t* num, void* stream) {
   if (rows < 0 || n_cols <= 0) return ATTN_ERR_INVALID_ARG;

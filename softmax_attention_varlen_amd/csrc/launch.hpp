@@ -10,16 +10,23 @@ namespace attn {
 
 struct VarlenArgs {
   const void* q;
-  const void* k;
-  const void* v;
+  const void* k;  // contiguous: [total_k][Hkv][D]; paged: the K plane of the cache
+  const void* v;  // contiguous: [total_k][Hkv][D]; paged: the V plane of the cache
   const int32_t* cu_q;
-  const int32_t* cu_k;
+  const int32_t* cu_k;  // contiguous only
   int batch, total_q, total_k, max_seqlen_q, max_seqlen_k;
   int num_heads, num_kv_heads, head_dim;
   float scale;
   int causal;
   void* out;
   float* lse;
+  // paged keys (multi-token attention over a paged cache): key t of document b
+  // is cache row (block_tables[b][t / 128], t % 128); its length is
+  // context_lens[b] clamped to max_seqlen_k
+  bool paged = false;
+  const int32_t* block_tables = nullptr;
+  const int32_t* context_lens = nullptr;
+  int max_blocks_per_seq = 0, num_blocks = 0;
 };
 
 hipError_t launch_varlen_fwd(const VarlenArgs& a, hipStream_t stream);
@@ -70,6 +77,11 @@ struct DecodeStreamPlan {
 };
 DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads);
 hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, hipStream_t stream);
+
+// Scatter new tokens' K/V rows into the paged cache by slot (negative or
+// out-of-range slots are skipped). row_elems = Hkv * D.
+hipError_t launch_paged_kv_write(const void* k, const void* v, const int32_t* slots, int num_tokens, int row_elems,
+                                 int num_blocks, void* kv_cache, hipStream_t stream);
 
 // Block map -> ascending index lists.
 // With sizes != nullptr: tiles of size 0 are dropped, entries are (size << 24) | tile.

@@ -7,6 +7,7 @@
 // pipe_d128.hpp. Per tile a wave issues the S^T MFMAs of the next tile
 // interleaved with the softmax of the current one, then the PV MFMAs of the
 // current tile. One barrier per tile guards the ring.
+#include "key_rows.hpp"
 #include "launch.hpp"
 #include "pipe_d128.hpp"
 
@@ -31,12 +32,16 @@ struct Ring {
   }
 };
 
-template <bool CAUSAL, int NW, int NS>
+// PAGED: keys come from a paged cache (k, v = its K and V planes) through
+// block_tables, with context_lens[doc] (clamped to max_len_k) keys per
+// document; otherwise from contiguous rows delimited by cu_k.
+template <bool CAUSAL, bool PAGED, int NW, int NS>
 __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int total_q, int total_k,
     int tiles_per_doc, int hq, int hkv, int n_items, int per_xcd, float c, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    int max_blocks_per_seq, int num_blocks, int max_len_k) {
   using R = Ring<NW>;
   constexpr int BM = 32 * NW;
   static_assert(NS == 3 || NS == 4, "the load-count waits below cover 3- and 4-stage rings");
@@ -63,9 +68,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
 
   const int q0 = clampi(cu_q[doc], 0, total_q);
   const int q1 = clampi(cu_q[doc + 1], q0, total_q);
-  const int k0 = clampi(cu_k[doc], 0, total_k);
-  const int k1 = clampi(cu_k[doc + 1], k0, total_k);
-  const int len_q = q1 - q0, len_k = k1 - k0;
+  int k0 = 0, len_k;
+  if (PAGED) {
+    len_k = clampi(context_lens[doc], 0, max_len_k);
+  } else {
+    k0 = clampi(cu_k[doc], 0, total_k);
+    len_k = clampi(cu_k[doc + 1], k0, total_k) - k0;
+  }
+  const int len_q = q1 - q0;
   const int m0 = tile * BM;
   if (m0 >= len_q) return;
 
@@ -97,6 +107,8 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
   const uint32_t stride_bytes = (uint32_t)hkv * kD * 2u;
   const uint16_t* kb0 = k + ((long)k0 * hkv + hk) * kD;
   const uint16_t* vb0 = v + ((long)k0 * hkv + hk) * kD;
+  const KeyRows<PAGED> rows{(long)hkv * kD, PAGED ? block_tables + (long)doc * max_blocks_per_seq : nullptr,
+                            num_blocks};
   const uint32_t ring = lds_u32(smem);
 
   // Q into registers first (the compiler's wait for these also covers the
@@ -111,7 +123,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s) {
     if (s < ntiles) {
-      const long off = (long)s * kBN * hkv * kD;
+      const long off = rows.row(s * kBN);
       R::issue(kb0 + off, vb0 + off, stride_bytes, len_k - s * kBN, ring + s * kStageBytes, w, lane);
     }
   }
@@ -148,7 +160,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
       }
       const int jn = j + NS - 1;
       if (jn < ntiles) {
-        const long off = (long)jn * kBN * hkv * kD;
+        const long off = rows.row(jn * kBN);
         R::issue(kb0 + off, vb0 + off, stride_bytes, len_k - jn * kBN, ring + (jn % NS) * kStageBytes, w, lane);
       }
     }
@@ -177,23 +189,31 @@ constexpr int kPrefillStages = 3;
 
 bool prefill_d128_supported(const VarlenArgs& a) { return a.head_dim == 128; }
 
+template <bool CAUSAL, bool PAGED>
+static void launch_prefill_d128_t(const VarlenArgs& a, int tiles, long n_items, long per_xcd, hipStream_t stream) {
+  const float c = a.scale * kLog2e;
+  hipLaunchKernelGGL((prefill_d128_kernel<CAUSAL, PAGED, kPrefillWaves, kPrefillStages>), dim3((unsigned)(per_xcd * 8)),
+                     dim3(64 * kPrefillWaves), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch, a.total_q, a.total_k, tiles, a.num_heads,
+                     a.num_kv_heads, (int)n_items, (int)per_xcd, c, (uint16_t*)a.out, a.lse, a.block_tables,
+                     a.context_lens, a.max_blocks_per_seq, a.num_blocks, a.max_seqlen_k);
+}
+
 hipError_t launch_prefill_d128(const VarlenArgs& a, hipStream_t stream) {
   constexpr int BM = 32 * kPrefillWaves;
   const int tiles = (a.max_seqlen_q + BM - 1) / BM;
   const long n_items = (long)tiles * a.batch * a.num_heads;
   const long per_xcd = (n_items + 7) / 8;
-  const float c = a.scale * kLog2e;
-  const dim3 grid((unsigned)(per_xcd * 8)), block(64 * kPrefillWaves);
-  if (a.causal) {
-    hipLaunchKernelGGL((prefill_d128_kernel<true, kPrefillWaves, kPrefillStages>), grid, block, 0, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch,
-                       a.total_q, a.total_k, tiles, a.num_heads, a.num_kv_heads, (int)n_items, (int)per_xcd, c,
-                       (uint16_t*)a.out, a.lse);
+  if (a.paged) {
+    if (a.causal) {
+      launch_prefill_d128_t<true, true>(a, tiles, n_items, per_xcd, stream);
+    } else {
+      launch_prefill_d128_t<false, true>(a, tiles, n_items, per_xcd, stream);
+    }
+  } else if (a.causal) {
+    launch_prefill_d128_t<true, false>(a, tiles, n_items, per_xcd, stream);
   } else {
-    hipLaunchKernelGGL((prefill_d128_kernel<false, kPrefillWaves, kPrefillStages>), grid, block, 0, stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch,
-                       a.total_q, a.total_k, tiles, a.num_heads, a.num_kv_heads, (int)n_items, (int)per_xcd, c,
-                       (uint16_t*)a.out, a.lse);
+    launch_prefill_d128_t<false, false>(a, tiles, n_items, per_xcd, stream);
   }
   return hipGetLastError();
 }

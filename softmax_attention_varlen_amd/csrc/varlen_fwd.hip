@@ -10,6 +10,7 @@
 // j <= i + Lk - Lq) and applied only on tiles that straddle the diagonal or the
 // document end; tiles wholly above the diagonal are never loaded.
 #include "attn_common.hpp"
+#include "key_rows.hpp"
 #include "launch.hpp"
 
 namespace attn {
@@ -18,11 +19,16 @@ constexpr int kVarlenBM = 128;
 constexpr int kVarlenBN = 64;
 constexpr int kVarlenThreads = 256;
 
-template <int D, bool CAUSAL>
+// PAGED: keys come from a paged cache (k, v = its K and V planes) through
+// block_tables, with context_lens[doc] (clamped to max_len_k) keys per
+// document; otherwise from contiguous rows delimited by cu_k.
+template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kVarlenThreads, (D <= 128 ? 2 : 1)) void varlen_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int total_q, int total_k,
-    int tiles_per_doc, int hq, int hkv, float c, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    int tiles_per_doc, int hq, int hkv, float c, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, int max_blocks_per_seq,
+    int num_blocks, int max_len_k) {
   using Tile = KVTile<D, kVarlenBN, kVarlenThreads>;
   __shared__ __attribute__((aligned(16))) char smem[Tile::BYTES];
 
@@ -36,9 +42,14 @@ __global__ __launch_bounds__(kVarlenThreads, (D <= 128 ? 2 : 1)) void varlen_fwd
 
   const int q0 = clampi(cu_q[doc], 0, total_q);
   const int q1 = clampi(cu_q[doc + 1], q0, total_q);
-  const int k0 = clampi(cu_k[doc], 0, total_k);
-  const int k1 = clampi(cu_k[doc + 1], k0, total_k);
-  const int len_q = q1 - q0, len_k = k1 - k0;
+  int k0 = 0, len_k;
+  if (PAGED) {
+    len_k = clampi(context_lens[doc], 0, max_len_k);
+  } else {
+    k0 = clampi(cu_k[doc], 0, total_k);
+    len_k = clampi(cu_k[doc + 1], k0, total_k) - k0;
+  }
+  const int len_q = q1 - q0;
   const int m0 = tile * kVarlenBM;
   if (m0 >= len_q) return;
 
@@ -65,9 +76,10 @@ __global__ __launch_bounds__(kVarlenThreads, (D <= 128 ? 2 : 1)) void varlen_fwd
   const long kv_stride = (long)hkv * D;
   const uint16_t* kb0 = k + (long)k0 * kv_stride + hk * D;
   const uint16_t* vb0 = v + (long)k0 * kv_stride + hk * D;
+  const KeyRows<PAGED> rows{kv_stride, PAGED ? block_tables + (long)doc * max_blocks_per_seq : nullptr, num_blocks};
 
   Tile tl;
-  if (ntiles > 0) tl.load(kb0, vb0, kv_stride, len_k, tid);
+  if (ntiles > 0) tl.load(kb0 + rows.row(0), vb0 + rows.row(0), kv_stride, len_k, tid);
 
   for (int j = 0; j < ntiles; ++j) {
     const int n0 = j * kVarlenBN;
@@ -76,7 +88,7 @@ __global__ __launch_bounds__(kVarlenThreads, (D <= 128 ? 2 : 1)) void varlen_fwd
     __syncthreads();
     if (j + 1 < ntiles) {
       const int n1 = n0 + kVarlenBN;
-      tl.load(kb0 + (long)n1 * kv_stride, vb0 + (long)n1 * kv_stride, kv_stride, len_k - n1, tid);
+      tl.load(kb0 + rows.row(n1), vb0 + rows.row(n1), kv_stride, len_k - n1, tid);
     }
     // waves whose rows are all past the end or all above this tile's keys skip it
     bool active = wave_live;
@@ -112,9 +124,17 @@ static hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream) {
   const int tiles = (a.max_seqlen_q + kVarlenBM - 1) / kVarlenBM;
   const long grid = (long)tiles * a.batch * a.num_heads;
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((varlen_fwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kVarlenThreads), 0, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch,
-                     a.total_q, a.total_k, tiles, a.num_heads, a.num_kv_heads, c, (uint16_t*)a.out, a.lse);
+  if (a.paged) {
+    hipLaunchKernelGGL((varlen_fwd_kernel<D, CAUSAL, true>), dim3((unsigned)grid), dim3(kVarlenThreads), 0, stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch,
+                       a.total_q, a.total_k, tiles, a.num_heads, a.num_kv_heads, c, (uint16_t*)a.out, a.lse,
+                       a.block_tables, a.context_lens, a.max_blocks_per_seq, a.num_blocks, a.max_seqlen_k);
+  } else {
+    hipLaunchKernelGGL((varlen_fwd_kernel<D, CAUSAL, false>), dim3((unsigned)grid), dim3(kVarlenThreads), 0,
+                       stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.cu_q, a.cu_k,
+                       a.batch, a.total_q, a.total_k, tiles, a.num_heads, a.num_kv_heads, c, (uint16_t*)a.out,
+                       a.lse, nullptr, nullptr, 0, 0, 0);
+  }
   return hipGetLastError();
 }
 

@@ -132,3 +132,48 @@ def test_binding_rejects_cpu_tensors():
     cu = torch.tensor([0, 4], dtype=torch.int32)
     with pytest.raises(ValueError):
         sav.attn_varlen_fwd(q, q, q, cu, cu, 4, 4, 0.125, False, out=torch.empty_like(q))
+
+
+def _kv_write(**kw):
+    a = dict(k=FAKE, v=FAKE, slots=FAKE, n=16, hkv=2, d=128, nblocks=10, bs=128, cache=FAKE)
+    a.update(kw)
+    return lib().attn_paged_kv_write(a["k"], a["v"], a["slots"], a["n"], a["hkv"], a["d"], a["nblocks"], a["bs"],
+                                     a["cache"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=64), UNSUPPORTED), (dict(d=100), UNSUPPORTED), (dict(n=-1), INVALID), (dict(hkv=0), INVALID),
+    (dict(k=None), INVALID), (dict(v=None), INVALID), (dict(slots=None), INVALID), (dict(cache=None), INVALID),
+    (dict(nblocks=0), INVALID), (dict(nblocks=-3), INVALID),
+])
+def test_kv_write_validation(kw, code):
+    assert _kv_write(**kw) == code
+
+
+def test_kv_write_empty_is_noop():
+    assert _kv_write(n=0, k=None, v=None, slots=None, cache=None) == OK
+
+
+def _paged_prefill(**kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, cuq=FAKE, ctx=FAKE, batch=3, tq=300, mq=200, maxctx=500, nblocks=12, mbps=4,
+             hq=8, hkv=2, d=128, bs=128, scale=0.1, out=FAKE, lse=None)
+    a.update(kw)
+    return lib().attn_paged_prefill(a["q"], a["kv"], a["bt"], a["cuq"], a["ctx"], a["batch"], a["tq"], a["mq"],
+                                    a["maxctx"], a["nblocks"], a["mbps"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                    a["scale"], a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=64), UNSUPPORTED), (dict(d=100), UNSUPPORTED), (dict(hq=6, hkv=4), UNSUPPORTED),
+    (dict(maxctx=513), INVALID), (dict(mq=301), INVALID), (dict(mq=0), INVALID), (dict(batch=-1), INVALID),
+    (dict(tq=-1), INVALID), (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(cuq=None), INVALID),
+    (dict(ctx=None), INVALID), (dict(kv=None), INVALID), (dict(bt=None), INVALID), (dict(nblocks=0), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(hkv=0), INVALID),
+])
+def test_paged_prefill_validation(kw, code):
+    assert _paged_prefill(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(batch=0), dict(tq=0, mq=0)])
+def test_paged_prefill_empty_is_noop(kw):
+    assert _paged_prefill(q=None, out=None, **kw) == OK
