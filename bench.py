@@ -41,16 +41,19 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 CSRC = os.path.join(ROOT, "softmax_attention_varlen_amd", "csrc")
-_PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp"]
+_PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "key_rows.hpp"]
 TRAFFIC = {
-    "dense": {"kernel": "prefill_d128_kernel<false,8,3>", "fetch_kib": 73808.8, "write_kib": 49923.7,
-              "sources": _PREFILL_SRC, "sha256": "d84e76cbb930b4ff"},
-    "causal": {"kernel": "prefill_d128_kernel<true,8,3>", "fetch_kib": 110343.0, "write_kib": 142436.5,
-               "sources": _PREFILL_SRC, "sha256": "d84e76cbb930b4ff"},
+    "dense": {"kernel": "prefill_d128_kernel<false,false,8,3>", "fetch_kib": 73808.8, "write_kib": 49923.7,
+              "sources": _PREFILL_SRC, "sha256": "7b72c5eccb5c4b2b"},
+    "causal": {"kernel": "prefill_d128_kernel<true,false,8,3>", "fetch_kib": 110361.6, "write_kib": 142436.7,
+               "sources": _PREFILL_SRC, "sha256": "7b72c5eccb5c4b2b"},
     "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443446.2, "write_kib": 3040.1,
               "sources": ["paged_decode_stream.hip", "attn_common.hpp"], "sha256": "386540a926c11f8c"},
     "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 428675.5, "write_kib": 49920.1,
                "sources": ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"], "sha256": "0189fa2bd092cb4f"},
+    "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,3>", "fetch_kib": 704107.8,
+                      "write_kib": 87201.8, "sources": _PREFILL_SRC, "sha256": "7b72c5eccb5c4b2b"},
+    "spec": {"kernel": "prefill_d128_kernel<true,true,8,3>"},
 }
 
 
@@ -65,8 +68,10 @@ def sources_sha256(files) -> str:
 
 def traffic_bytes(workload: str):
     """Measured HBM bytes per launch of the workload's main kernel, or None when
-    the kernel sources changed since the counters were taken."""
-    rec = TRAFFIC[workload]
+    none was measured or the kernel sources changed since the counters were taken."""
+    rec = TRAFFIC.get(workload)
+    if rec is None or "fetch_kib" not in rec:
+        return None
     if sources_sha256(rec["sources"]) != rec["sha256"]:
         return None
     return int(round((rec["fetch_kib"] * FETCH_SCALE + rec["write_kib"] * WRITE_SCALE) * 1024))
@@ -105,6 +110,24 @@ def paged_bytes(case) -> float:
     kv = float(case.context_lens.astype(np.int64).sum()) * case.num_kv_heads * case.head_dim * 2 * 2
     qo = 2.0 * case.num_seqs * case.num_heads * case.head_dim * 2
     return kv + qo + case.block_tables.nbytes + case.context_lens.nbytes
+
+
+def paged_prefill_flops(case) -> float:
+    """4 * D flops per visible (query, key) pair and query head, bottom-right causal."""
+    lq = np.diff(case.cu_seqlens_q).astype(np.int64)
+    lk = case.context_lens.astype(np.int64)
+    pairs = 0
+    for a, b in zip(lq, lk):
+        i = np.arange(a)
+        pairs += int(np.clip(i + (b - a) + 1, 0, b).sum())
+    return 4.0 * case.head_dim * case.num_heads * pairs
+
+
+def paged_prefill_bytes(case) -> float:
+    """K and V bytes of every context token, plus Q, O, tables and lengths."""
+    kv = float(case.context_lens.astype(np.int64).sum()) * case.num_kv_heads * case.head_dim * 2 * 2
+    qo = 2.0 * case.q.shape[0] * case.num_heads * case.head_dim * 2
+    return kv + qo + case.block_tables.nbytes + case.context_lens.nbytes + case.cu_seqlens_q.nbytes
 
 
 def sparse_flops(bmap: np.ndarray, sizes: np.ndarray, head_dim: int) -> float:
@@ -169,6 +192,41 @@ def bench_paged(case, steps, warmup):
     return ms, paged_bytes(case)
 
 
+def bench_paged_prefill(case, steps, warmup):
+    dev = torch.device("cuda")
+    q, kv = case.q.to(dev), case.kv_cache.to(dev)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    cu = torch.from_numpy(case.cu_seqlens_q).to(dev)
+    cl = torch.from_numpy(case.context_lens).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((case.num_heads, q.shape[0]), dtype=torch.float32, device=dev)
+
+    def step():
+        sav.attn_paged_prefill(q, kv, bt, cu, cl, case.max_seqlen_q, case.max_context_len, case.scale, out=out,
+                               lse=lse)
+
+    ms = time_steps(step, steps, warmup)
+    del kv
+    return ms
+
+
+def bench_kv_write(case, steps, warmup):
+    """Store every sequence's new tokens (the last Lq positions) into the cache."""
+    dev = torch.device("cuda")
+    kv = case.kv_cache.to(dev)
+    n = case.q.shape[0]
+    k_new = workloads.randn_bf16((n, case.num_kv_heads, case.head_dim), 1000 * case.seed + 4).to(dev)
+    v_new = workloads.randn_bf16((n, case.num_kv_heads, case.head_dim), 1000 * case.seed + 5).to(dev)
+    lq = np.diff(case.cu_seqlens_q)
+    slots = np.concatenate([case.block_tables[b, t // 128].astype(np.int64) * 128 + t % 128
+                            for b in range(case.batch)
+                            for t in [np.arange(case.context_lens[b] - lq[b], case.context_lens[b])]])
+    sl = torch.from_numpy(slots.astype(np.int32)).to(dev)
+    ms = time_steps(lambda: sav.attn_paged_kv_write(k_new, v_new, sl, kv), steps, warmup)
+    del kv
+    return ms, 2.0 * 2 * n * case.num_kv_heads * case.head_dim + 4 * n  # read + write of K and V, slots
+
+
 def bench_sparse(case, steps, warmup):
     """Tile order, pooled-score top-k map and the block-sparse call all run in the
     library's kernels; only the block-sparse call is in the timed step."""
@@ -226,7 +284,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse", "copy"], default=None,
+    ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse", "paged_prefill", "spec", "copy"],
+                    default=None,
                     help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
                          "copy, the reference that scales the HBM byte counters")
     ap.add_argument("--no-secondary", action="store_true")
@@ -285,6 +344,30 @@ def main():
         secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
                           "roofline": roofline("sparse", "mfma", tf, flops),
                           "tile_prep_and_map_ms": round(prep_ms, 4)})
+
+    if args.only in (None, "paged_prefill") and not (args.only is None and args.no_secondary):
+        case = workloads.config6()
+        ms = bench_paged_prefill(case, args.steps, args.warmup)
+        flops = paged_prefill_flops(case)
+        tf = flops / (ms * 1e-3) / 1e12
+        wms, wbytes = bench_kv_write(case, args.steps, args.warmup)
+        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s (kv write {wms * 1e3:.1f} us)")
+        secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+                          "roofline": roofline("paged_prefill", "mfma", tf, flops),
+                          "kv_write": {"ms": round(wms, 5), "GB/s": round(wbytes / (wms * 1e-3) / 1e9, 1),
+                                       "tokens": int(case.q.shape[0])}})
+        del case
+        torch.cuda.empty_cache()
+    if args.only in (None, "spec") and not (args.only is None and args.no_secondary):
+        case = workloads.config7()
+        ms = bench_paged_prefill(case, args.steps, args.warmup)
+        nbytes = paged_prefill_bytes(case)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"{case.name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+        secondary.append({"workload": case.name, "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
+                          "roofline": roofline("spec", "hbm", gbs, nbytes)})
+        del case
+        torch.cuda.empty_cache()
 
     if head is None:  # a single secondary workload was asked for
         print(json.dumps({"metric": "attention throughput", "secondary": secondary}))

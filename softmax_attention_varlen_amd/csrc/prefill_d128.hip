@@ -49,8 +49,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
 
   // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs, so
   // XCD x receives logical items [x*per_xcd, (x+1)*per_xcd), laid out
-  // kv-head-major so that one XCD's L2 serves the K/V of its kv heads, and
-  // every XCD gets the same mix of documents.
+  // kv-head-major so that one XCD's L2 serves the K/V of its kv heads.
   const int hw = blockIdx.x;
   const int item = (hw & 7) * per_xcd + (hw >> 3);
   if (item >= n_items) return;
@@ -58,12 +57,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
   int rest = item;
   const int qh = rest % group;
   rest /= group;
-  const int doc = rest % batch;
-  rest /= batch;
-  // query tiles from the last (heaviest under a causal mask) to the first,
-  // across all documents, within a kv head
+  // within a kv head, documents one after the other (the workgroups running at
+  // once on an XCD then share one document's K/V in its L2), and in each
+  // document the query tiles from the last (heaviest under a causal mask) to
+  // the first
   const int tile = tiles_per_doc - 1 - rest % tiles_per_doc;
-  const int hk = rest / tiles_per_doc;
+  rest /= tiles_per_doc;
+  const int doc = rest % batch;
+  const int hk = rest / batch;
   const int h = hk * group + qh;
 
   const int q0 = clampi(cu_q[doc], 0, total_q);

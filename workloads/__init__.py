@@ -245,6 +245,25 @@ def config4() -> PagedCase:
                       max_blocks_per_seq=256, rng=rng, name="paged-decode-64seq-ctx1k-32k-h32kv8-d128")
 
 
+def config6() -> PagedPrefillCase:
+    """Chunked / cache-hit prefill over a paged cache: 16 sequences, 256..1024 new
+    tokens each over contexts of 2048..16384 keys (new tokens included), 32/8 heads, D=128."""
+    rng = np.random.default_rng(6)
+    ql = rng.integers(256, 1025, 16)
+    ctx = rng.integers(2048, 16385, 16)
+    return paged_prefill_case(ql, ctx, num_heads=32, num_kv_heads=8, head_dim=128, seed=6, rng=rng,
+                              name="paged-prefill-16seq-q256-1k-ctx2k-16k-h32kv8-d128")
+
+
+def config7() -> PagedPrefillCase:
+    """Speculative decoding over a paged cache: the 64 contexts of the decode
+    workload, each with 4 new query tokens (the last 4 positions), 32/8 heads, D=128."""
+    rng = np.random.default_rng(4)
+    ctx = config4_lengths(rng)
+    return paged_prefill_case(np.full(ctx.size, 4), ctx, num_heads=32, num_kv_heads=8, head_dim=128, seed=7,
+                              max_blocks_per_seq=256, name="spec-decode-64seq-q4-ctx1k-32k-h32kv8-d128")
+
+
 @dataclass
 class VideoCase:
     name: str
