@@ -47,13 +47,14 @@ TRAFFIC = {
               "sources": _PREFILL_SRC, "sha256": "7b72c5eccb5c4b2b"},
     "causal": {"kernel": "prefill_d128_kernel<true,false,8,3>", "fetch_kib": 110361.6, "write_kib": 142436.7,
                "sources": _PREFILL_SRC, "sha256": "7b72c5eccb5c4b2b"},
-    "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443446.2, "write_kib": 3040.1,
-              "sources": ["paged_decode_stream.hip", "attn_common.hpp"], "sha256": "386540a926c11f8c"},
+    "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443507.5, "write_kib": 3040.1,
+              "sources": ["paged_decode_stream.hip", "attn_common.hpp"], "sha256": "e954fcbfba207e55"},
     "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 428675.5, "write_kib": 49920.1,
                "sources": ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"], "sha256": "0189fa2bd092cb4f"},
     "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,3>", "fetch_kib": 704107.8,
                       "write_kib": 87201.8, "sources": _PREFILL_SRC, "sha256": "7b72c5eccb5c4b2b"},
-    "spec": {"kernel": "prefill_d128_kernel<true,true,8,3>"},
+    "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445745.0, "write_kib": 12148.7,
+             "sources": ["paged_decode_stream.hip", "attn_common.hpp"], "sha256": "e954fcbfba207e55"},
 }
 
 

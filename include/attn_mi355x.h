@@ -178,7 +178,12 @@ attn_status_t attn_paged_kv_write(const void* k, const void* v, const int32_t* s
  *   block_size    must be 128.
  *   out           [total_q, num_heads, head_dim] bf16
  *   lse           nullable; [num_heads, total_q] fp32
- * batch == 0 or total_q == 0 is a no-op. No workspace.
+ *   workspace     device buffer of at least attn_paged_prefill_workspace_size()
+ *                 bytes (nullable when that is 0). Short query runs (speculative
+ *                 decoding: head_dim 128 and max_seqlen_q * num_heads/num_kv_heads
+ *                 <= 64) stream the cache once per kv head like decode and keep
+ *                 fp32 partials there; longer ones need none.
+ * batch == 0 or total_q == 0 is a no-op.
  */
 attn_status_t attn_paged_prefill(const void* q, const void* kv_cache, const int32_t* block_tables,
                                  const int32_t* cu_seqlens_q, const int32_t* context_lens,
@@ -186,7 +191,13 @@ attn_status_t attn_paged_prefill(const void* q, const void* kv_cache, const int3
                                  int32_t max_context_len, int32_t num_blocks, int32_t max_blocks_per_seq,
                                  int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t block_size, float softmax_scale, void* out, float* lse,
-                                 void* stream);
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes that attn_paged_prefill needs for these host sizes (0 when
+ * the call runs the prefill kernels). Written to *bytes (host pointer). */
+attn_status_t attn_paged_prefill_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t max_seqlen_q,
+                                                int32_t max_context_len, size_t* bytes);
 
 /*
  * Block map -> ascending index lists (vLLM-Omni fastvideo_vsa.py page: the

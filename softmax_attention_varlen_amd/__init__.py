@@ -28,6 +28,7 @@ __all__ = [
     "attn_paged_decode",
     "attn_paged_kv_write",
     "attn_paged_prefill",
+    "attn_paged_prefill_workspace_size",
     "attn_block_map_to_index",
     "attn_block_sparse_workspace_size",
     "attn_block_sparse_fwd",
@@ -56,7 +57,8 @@ _SIGS = {
                                          _p, _p, _sz, _p]),
     "attn_paged_kv_write": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p]),
     "attn_paged_prefill": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
-                                          _i32, _f32, _p, _p, _p]),
+                                          _i32, _f32, _p, _p, _p, _sz, _p]),
+    "attn_paged_prefill_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "attn_block_map_to_index": (ctypes.c_int, [_p, _i32, _i32, _p, _p, _p]),
     "attn_block_sparse_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "attn_block_sparse_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _p,
@@ -230,9 +232,18 @@ def attn_paged_kv_write(k, v, slot_mapping, kv_cache, stream=None):
     return kv_cache
 
 
+def attn_paged_prefill_workspace_size(batch: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                                      max_seqlen_q: int, max_context_len: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("attn_paged_prefill_workspace_size",
+           load_library().attn_paged_prefill_workspace_size(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q,
+                                                            max_context_len, ctypes.byref(n)))
+    return n.value
+
+
 def attn_paged_prefill(q, kv_cache, block_tables, cu_seqlens_q, context_lens, max_seqlen_q: int,
                        max_context_len: int, softmax_scale: float, out=None, lse=None, return_lse: bool = False,
-                       stream=None):
+                       workspace=None, stream=None):
     """Multi-token queries (packed [Tq, Hq, D] by cu_seqlens_q) over a paged
     cache [2, NB, 128, Hkv, D], bottom-right causal against context_lens keys."""
     dev = q.device
@@ -251,13 +262,17 @@ def attn_paged_prefill(q, kv_cache, block_tables, cu_seqlens_q, context_lens, ma
         lse = torch.empty((hq, total_q), dtype=torch.float32, device=dev)
     if lse is not None:
         _shape(lse, "lse", (hq, total_q))
+    need = attn_paged_prefill_workspace_size(batch, hq, hkv, d, int(max_seqlen_q), int(max_context_len))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     st = load_library().attn_paged_prefill(
         _dev(q, "q", torch.bfloat16), _dev(kv_cache, "kv_cache", torch.bfloat16, dev),
         _dev(block_tables, "block_tables", torch.int32, dev), _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, dev),
         _dev(context_lens, "context_lens", torch.int32, dev), batch, total_q, int(max_seqlen_q),
         int(max_context_len), nblocks, mbps, hq, hkv, d, bs, float(softmax_scale),
         _dev(out, "out", torch.bfloat16, dev), _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
-        _stream_ptr(q, stream))
+        _dev(workspace, "workspace", torch.uint8, dev) if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream_ptr(q, stream))
     _check("attn_paged_prefill", st)
     return (out, lse) if (return_lse or lse is not None) else out
 

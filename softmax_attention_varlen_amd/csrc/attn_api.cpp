@@ -116,12 +116,41 @@ attn_status_t attn_paged_kv_write(const void* k, const void* v, const int32_t* s
                                               kv_cache, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
+namespace {
+// Short multi-token queries (speculative decoding) stream the paged cache like
+// decode, with (query token, head) columns; longer ones run the prefill kernels.
+bool paged_prefill_streams(int batch, int num_heads, int num_kv_heads, int head_dim, int max_seqlen_q,
+                           int max_context_len) {
+  return head_dim == 128 && (long long)max_seqlen_q * (num_heads / num_kv_heads) <= attn::kSpecMaxCols &&
+         (long long)batch * max_context_len < (1LL << 30);
+}
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_paged_prefill_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t max_seqlen_q, int32_t max_context_len,
+                                                size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_seqlen_q < 0 || max_context_len < 0) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
+  *bytes = paged_prefill_streams(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q, max_context_len)
+               ? attn::plan_decode_stream(batch, num_heads, num_kv_heads, max_seqlen_q).workspace_bytes
+               : 0;
+  return ATTN_OK;
+}
+
 attn_status_t attn_paged_prefill(const void* q, const void* kv_cache, const int32_t* block_tables,
                                  const int32_t* cu_seqlens_q, const int32_t* context_lens, int32_t batch,
                                  int32_t total_q, int32_t max_seqlen_q, int32_t max_context_len, int32_t num_blocks,
                                  int32_t max_blocks_per_seq, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, float softmax_scale, void* out, float* lse,
-                                 void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream) {
   if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_context_len < 0) return ATTN_ERR_INVALID_ARG;
   if (num_blocks < 0 || max_blocks_per_seq < 0 || num_heads <= 0 || num_kv_heads <= 0) return ATTN_ERR_INVALID_ARG;
   if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
@@ -141,6 +170,17 @@ attn_status_t attn_paged_prefill(const void* q, const void* kv_cache, const int3
   if ((long long)total_q * num_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
   if ((long long)num_blocks * block_size * num_kv_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
   if (attn::varlen_grid_size(batch, max_seqlen_q, num_heads) > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  if (paged_prefill_streams(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q, max_context_len)) {
+    const attn::DecodeStreamPlan plan = attn::plan_decode_stream(batch, num_heads, num_kv_heads, max_seqlen_q);
+    if (workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace == nullptr) return ATTN_ERR_INVALID_ARG;
+    attn::DecodeArgs d{q, kv_cache, block_tables, context_lens, batch, num_blocks, max_blocks_per_seq,
+                       max_context_len, num_heads, num_kv_heads, head_dim, block_size, softmax_scale, out, lse,
+                       workspace};
+    d.cu_q = cu_seqlens_q;
+    d.total_q = total_q;
+    return from_hip(attn::launch_decode_stream(d, plan, (hipStream_t)stream));
+  }
   const long long plane = (long long)num_blocks * block_size * num_kv_heads * head_dim;  // elements
   attn::VarlenArgs a{q, kv_cache, (const uint16_t*)kv_cache + plane, cu_seqlens_q, nullptr, batch, total_q, 0,
                      max_seqlen_q, max_context_len, num_heads, num_kv_heads, head_dim, softmax_scale, 1, out, lse};

@@ -60,6 +60,10 @@ struct DecodeArgs {
   void* out;
   float* lse;
   void* workspace;
+  // multi-token queries (streaming path only): q is packed by cu_q, sequence b
+  // has cu_q[b+1] - cu_q[b] <= max_q new tokens; nullptr = one token each
+  const int32_t* cu_q = nullptr;
+  int total_q = 0;
 };
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
@@ -69,13 +73,17 @@ hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipS
 // (and query-head chunk); one wave streams one segment.
 constexpr int kDecodeStreamWaves = 1024;  // 4 waves on each of MI355X's 256 CUs
 struct DecodeStreamPlan {
-  int q_chunks, n_seg;
+  int max_q, q_chunks, n_seg;
   size_t prefix_bytes;  // int32 [num_seqs + 1] token prefix sums
-  size_t lse_bytes;     // fp32 [n_seg + num_seqs][num_heads] partial LSE
-  size_t o_bytes;       // fp32 [n_seg + num_seqs][num_heads][128] partial O
+  size_t lse_bytes;     // fp32 [n_seg + num_seqs][max_q][num_heads] partial LSE
+  size_t o_bytes;       // fp32 [n_seg + num_seqs][max_q][num_heads][128] partial O
   size_t workspace_bytes;
 };
-DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads);
+// max_q: new query tokens per sequence at most (1 for decode)
+DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads, int max_q = 1);
+// multi-token queries take the streaming path when their (token, head)
+// columns per kv head fit in kSpecMaxCols (at most that many / 16 passes over K/V)
+constexpr int kSpecMaxCols = 64;
 hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, hipStream_t stream);
 
 // Scatter new tokens' K/V rows into the paged cache by slot (negative or

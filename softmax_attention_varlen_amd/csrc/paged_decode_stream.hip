@@ -22,8 +22,14 @@
 // b+24 (4 rows x 256 B); blocks sit 1056 bytes apart, which makes the
 // transposing V reads conflict-free and the K reads at most 2-way.
 //
+// Queries. The 16 MFMA columns of a wave are (query token, head) pairs of its
+// kv head's group: column n of chunk qc is token (16qc + n) / group, head
+// (16qc + n) % group, so a sequence's max_q new tokens (speculative decoding:
+// the last max_q positions, bottom-right causal) share one pass over its K/V;
+// plain decode is max_q = 1.
+//
 // Math per chunk (16x16x32 bf16 MFMA): S^T = K Q^T with K from LDS (A) and the
-// query heads as the 16 columns (B); online softmax per column; O^T += V^T P^T
+// (token, head) columns (B); online softmax per column; O^T += V^T P^T
 // with V^T from transposing LDS reads (A) and P straight from the S^T
 // accumulator (B): the lane's 8 tokens 4G..4G+3 and 16+4G..16+4G+3 are the
 // k-slots of its B operand, and the two transposing reads fetch exactly those
@@ -113,7 +119,8 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ prefix, int num_seqs, int num_blocks, int max_blocks_per_seq, int hq, int hkv,
     int q_chunks, int n_seg, float c, uint16_t* __restrict__ out, float* __restrict__ lse,
-    float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ part_o, float* __restrict__ part_lse, const int32_t* __restrict__ cu_q, int max_q,
+    int total_q) {
   __shared__ __attribute__((aligned(1024))) char smem[kSWaves * kSWaveLds];
   // every cursor below is wave-uniform (scalar registers, scalar loads): no
   // compiler-visible vector load may sit in the streaming loop, since the
@@ -135,9 +142,10 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
 
   const int group = hq / hkv;
   const int n16 = lane & 15, G = lane >> 4;
-  const int qh_local = qc * 16 + n16;
-  const bool q_real = qh_local < group;
-  const int h = hk * group + (q_real ? qh_local : 0);
+  const int col = qc * 16 + n16;           // (query token, head) column of this kv head
+  const bool col_real = col < max_q * group;
+  const int qi = col_real ? col / group : 0;
+  const int h = hk * group + (col_real ? col % group : 0);
 
   const long row_elems = (long)hkv * kSD;                // elements between tokens of a block
   const long blk_elems = 128L * row_elems;
@@ -209,16 +217,28 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
   bf16x8 qb[4];
   f32x4 o[8];
   float m = kNegInf, l = 0.f;
+  int q_row = 0, lim = 0, lim_min = 0;
+  bool live = false;
   for (int j = 0;; ++j) {
     if (fresh) {
-      // a new piece: its query heads (the compiler's wait for these loads also
-      // drains the ring, once per piece), and a reset softmax state
-      const uint16_t* qrow = q + ((long)cs * hq + h) * kSD;
+      // a new piece: its queries (the compiler's wait for these loads also
+      // drains the ring, once per piece), and a reset softmax state. Query
+      // token qi of the sequence's lq sees keys t <= qi + cctx - lq.
+      int q_first = cs, lq = 1;
+      if (cu_q != nullptr) {
+        q_first = clampi(cu_q[cs], 0, total_q);
+        lq = clampi(cu_q[cs + 1], q_first, total_q) - q_first;
+        lq = lq > max_q ? max_q : lq;
+      }
+      live = col_real && qi < lq;
+      q_row = live ? q_first + qi : 0;  // row 0 exists whenever this kernel runs
+      lim = qi + cctx - lq;
+      lim_min = cctx - lq;
+      const uint16_t* qrow = q + ((long)q_row * hq + h) * kSD;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        u32x4 x = ld_global16(qrow + b * 32 + G * 8);
-        if (!q_real) x = u32x4{0u, 0u, 0u, 0u};
-        qb[b] = as_bf16x8(x);
+        const u32x4 x = ld_global16(qrow + b * 32 + G * 8);  // unconditional: no branch per load
+        qb[b] = as_bf16x8(live ? x : u32x4{0u, 0u, 0u, 0u});
       }
       asm volatile("" : : "v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
 #pragma unroll
@@ -246,13 +266,13 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
       }
     }
     const int t0 = cc * kSChunk;
-    if (t0 < t_lo || t0 + kSChunk > t_hi) {
+    if (t0 < t_lo || t0 + kSChunk > t_hi || t0 + kSChunk - 1 > lim_min) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = t0 + kb * 16 + 4 * G + r;
-          if (t < t_lo || t >= t_hi) s[kb][r] = kNegInf;
+          if (t < t_lo || t >= t_hi || t > lim) s[kb][r] = kNegInf;
         }
       }
     }
@@ -260,9 +280,10 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     mx = wave_xor_max(mx, 16);
     mx = wave_xor_max(mx, 32);
-    const float m_new = fmaxf(m, mx);  // finite: every chunk holds a token of the piece
-    const float alpha = hw_exp2((m - m_new) * c);
-    const float ms = m_new * c;
+    // a column may see no key of this chunk (causal limit) or of the piece yet
+    const float m_new = fmaxf(m, mx);
+    const float alpha = m_new == kNegInf ? 1.f : hw_exp2((m - m_new) * c);
+    const float ms = m_new == kNegInf ? 0.f : m_new * c;
     f32x8 pt;
     float rs = 0.f;
 #pragma unroll
@@ -289,19 +310,19 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
       // piece done: the lane's column sum lives in 4 lanes (G = 0..3)
       float lt = wave_xor_sum(l, 16);
       lt = wave_xor_sum(lt, 32);
-      const float inv = 1.f / lt;
-      const float lse_p = (m * c + hw_log2(lt)) * kLn2;
-      if (q_real) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      const float lse_p = lt > 0.f ? (m * c + hw_log2(lt)) * kLn2 : kNegInf;
+      if (live) {
         if (t_lo == 0 && t_hi == cctx) {
-          uint16_t* orow = out + ((long)cs * hq + h) * kSD;
+          uint16_t* orow = out + ((long)q_row * hq + h) * kSD;
 #pragma unroll
           for (int db = 0; db < 8; ++db) {
             const f32x4 t = o[db] * inv;
             *reinterpret_cast<bf16x4*>(orow + db * 16 + 4 * G) = to_bf16x4(t);
           }
-          if (lse != nullptr && G == 0) lse[(long)h * num_seqs + cs] = lse_p;
+          if (lse != nullptr && G == 0) lse[(long)h * total_q + q_row] = lse_p;
         } else {
-          const long slot = (long)(g + cs) * hq + h;
+          const long slot = ((long)(g + cs) * max_q + qi) * hq + h;
           float* orow = part_o + slot * kSD;
 #pragma unroll
           for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * G) = o[db] * inv;
@@ -330,54 +351,71 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
   }
 }
 
-// Merge the pieces of each (sequence, head) in ascending segment order:
-// LSE = ln sum_i exp(LSE_i), O = sum_i exp(LSE_i - LSE) O_i. A sequence that
-// lies in one segment was finished by the streaming kernel; an empty one gets
-// zeros and LSE = -inf.
+// Merge the pieces of each (sequence, query token, head) in ascending segment
+// order: LSE = ln sum_i exp(LSE_i), O = sum_i exp(LSE_i - LSE) O_i. A sequence
+// that lies in one segment was finished by the streaming kernel; an empty one
+// gets zeros and LSE = -inf.
 __global__ __launch_bounds__(256) void paged_decode_stream_combine_kernel(
     const int32_t* __restrict__ prefix, int num_seqs, int hq, int n_seg, const float* __restrict__ part_o,
-    const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse) {
+    const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse,
+    const int32_t* __restrict__ cu_q, int max_q, int total_q) {
   const int lane = threadIdx.x & 63;
-  const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= (long)num_seqs * hq) return;
-  const int s = (int)(pair / hq), h = (int)(pair % hq);
+  const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // (s * max_q + qi) * hq + h
+  if (pair >= (long)num_seqs * max_q * hq) return;
+  const int h = (int)(pair % hq);
+  const int qi = (int)((pair / hq) % max_q);
+  const int s = (int)(pair / ((long)hq * max_q));
+  int q_first = s, lq = 1;
+  if (cu_q != nullptr) {
+    q_first = clampi(cu_q[s], 0, total_q);
+    lq = clampi(cu_q[s + 1], q_first, total_q) - q_first;
+    lq = lq > max_q ? max_q : lq;
+  }
+  if (qi >= lq) return;
+  const long row = q_first + qi;
   const int total = prefix[num_seqs];
   const int b0 = prefix[s], b1 = prefix[s + 1];
-  uint16_t* orow = out + pair * kSD;
+  uint16_t* orow = out + (row * hq + h) * kSD;
   if (b1 <= b0) {
     for (int d = lane; d < kSD; d += 64) orow[d] = 0;
-    if (lse != nullptr && lane == 0) lse[(long)h * num_seqs + s] = kNegInf;
+    if (lse != nullptr && lane == 0) lse[(long)h * total_q + row] = kNegInf;
     return;
   }
   const int L = seg_len(total, n_seg);
   const int first = b0 / L, last = (b1 - 1) / L;
   if (first == last) return;
+  auto slot = [&](int gg) { return ((long)(gg + s) * max_q + qi) * hq + h; };
   float mx = kNegInf;
-  for (int gg = first; gg <= last; ++gg) mx = fmaxf(mx, part_lse[(long)(gg + s) * hq + h]);
+  for (int gg = first; gg <= last; ++gg) mx = fmaxf(mx, part_lse[slot(gg)]);
+  if (mx == kNegInf) {  // no key visible to this query in any piece
+    for (int d = lane; d < kSD; d += 64) orow[d] = 0;
+    if (lse != nullptr && lane == 0) lse[(long)h * total_q + row] = kNegInf;
+    return;
+  }
   float tot = 0.f;
-  for (int gg = first; gg <= last; ++gg) tot += hw_exp2((part_lse[(long)(gg + s) * hq + h] - mx) * kLog2e);
+  for (int gg = first; gg <= last; ++gg) tot += hw_exp2((part_lse[slot(gg)] - mx) * kLog2e);
   const float lse_all = mx + hw_log2(tot) * kLn2;
   for (int d = lane; d < kSD; d += 64) {
     float acc = 0.f;
     for (int gg = first; gg <= last; ++gg) {
-      const long slot = (long)(gg + s) * hq + h;
-      acc += hw_exp2((part_lse[slot] - lse_all) * kLog2e) * part_o[slot * kSD + d];
+      acc += hw_exp2((part_lse[slot(gg)] - lse_all) * kLog2e) * part_o[slot(gg) * kSD + d];
     }
     orow[d] = __builtin_bit_cast(uint16_t, (__bf16)acc);
   }
-  if (lse != nullptr && lane == 0) lse[(long)h * num_seqs + s] = lse_all;
+  if (lse != nullptr && lane == 0) lse[(long)h * total_q + row] = lse_all;
 }
 
 }  // namespace
 
-DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads) {
+DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads, int max_q) {
   DecodeStreamPlan p{};
   const int group = num_heads / num_kv_heads;
-  p.q_chunks = (group + 15) / 16;
+  p.max_q = max_q > 1 ? max_q : 1;
+  p.q_chunks = (p.max_q * group + 15) / 16;
   const int lanes = num_kv_heads * p.q_chunks;
   p.n_seg = kDecodeStreamWaves / lanes > 1 ? kDecodeStreamWaves / lanes : 1;
   p.prefix_bytes = ((size_t)(num_seqs + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
-  const size_t slots = (size_t)(p.n_seg + num_seqs) * num_heads;
+  const size_t slots = (size_t)(p.n_seg + num_seqs) * p.max_q * num_heads;
   p.lse_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
   p.o_bytes = slots * kSD * sizeof(float);
   p.workspace_bytes = p.prefix_bytes + p.lse_bytes + p.o_bytes;
@@ -388,6 +426,7 @@ hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, 
   int32_t* prefix = (int32_t*)a.workspace;
   float* part_lse = (float*)((char*)a.workspace + p.prefix_bytes);
   float* part_o = (float*)((char*)a.workspace + p.prefix_bytes + p.lse_bytes);
+  const int total_q = a.cu_q != nullptr ? a.total_q : a.num_seqs;
   hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens, a.num_seqs,
                      a.max_context_len, prefix);
   hipError_t e = hipGetLastError();
@@ -397,12 +436,13 @@ hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, 
                      dim3(64 * kSWaves), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.kv_cache,
                      a.block_tables, prefix, a.num_seqs, a.num_blocks, a.max_blocks_per_seq, a.num_heads,
                      a.num_kv_heads, p.q_chunks, p.n_seg, a.scale * kLog2e, (uint16_t*)a.out, a.lse, part_o,
-                     part_lse);
+                     part_lse, a.cu_q, p.max_q, total_q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long pairs = (long)a.num_seqs * a.num_heads;
+  const long pairs = (long)a.num_seqs * p.max_q * a.num_heads;
   hipLaunchKernelGGL(paged_decode_stream_combine_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream,
-                     prefix, a.num_seqs, a.num_heads, p.n_seg, part_o, part_lse, (uint16_t*)a.out, a.lse);
+                     prefix, a.num_seqs, a.num_heads, p.n_seg, part_o, part_lse, (uint16_t*)a.out, a.lse, a.cu_q,
+                     p.max_q, total_q);
   return hipGetLastError();
 }
 

@@ -156,11 +156,11 @@ def test_kv_write_empty_is_noop():
 
 def _paged_prefill(**kw):
     a = dict(q=FAKE, kv=FAKE, bt=FAKE, cuq=FAKE, ctx=FAKE, batch=3, tq=300, mq=200, maxctx=500, nblocks=12, mbps=4,
-             hq=8, hkv=2, d=128, bs=128, scale=0.1, out=FAKE, lse=None)
+             hq=8, hkv=2, d=128, bs=128, scale=0.1, out=FAKE, lse=None, ws=None, wsb=0)
     a.update(kw)
     return lib().attn_paged_prefill(a["q"], a["kv"], a["bt"], a["cuq"], a["ctx"], a["batch"], a["tq"], a["mq"],
                                     a["maxctx"], a["nblocks"], a["mbps"], a["hq"], a["hkv"], a["d"], a["bs"],
-                                    a["scale"], a["out"], a["lse"], None)
+                                    a["scale"], a["out"], a["lse"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -169,6 +169,8 @@ def _paged_prefill(**kw):
     (dict(tq=-1), INVALID), (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(cuq=None), INVALID),
     (dict(ctx=None), INVALID), (dict(kv=None), INVALID), (dict(bt=None), INVALID), (dict(nblocks=0), INVALID),
     (dict(scale=float("nan")), INVALID), (dict(hkv=0), INVALID),
+    # 4 new tokens x group 4 = 16 columns: the streaming path, which needs a workspace
+    (dict(mq=4, tq=12), WS_SMALL), (dict(mq=4, tq=12, wsb=1 << 30), INVALID),
 ])
 def test_paged_prefill_validation(kw, code):
     assert _paged_prefill(**kw) == code
@@ -177,3 +179,13 @@ def test_paged_prefill_validation(kw, code):
 @pytest.mark.parametrize("kw", [dict(batch=0), dict(tq=0, mq=0)])
 def test_paged_prefill_empty_is_noop(kw):
     assert _paged_prefill(q=None, out=None, **kw) == OK
+
+
+def test_paged_prefill_workspace_query():
+    # long query runs use the prefill kernels (no workspace); short ones stream like decode
+    assert sav.attn_paged_prefill_workspace_size(16, 32, 8, 128, 1024, 16384) == 0
+    assert sav.attn_paged_prefill_workspace_size(16, 32, 8, 64, 4, 16384) == 0
+    n4 = sav.attn_paged_prefill_workspace_size(64, 32, 8, 128, 4, 32768)
+    n1 = sav.attn_paged_prefill_workspace_size(64, 32, 8, 128, 1, 32768)
+    assert n4 > n1 > 0
+    assert n1 == sav.attn_paged_decode_workspace_size(64, 32, 8, 128, 32768)

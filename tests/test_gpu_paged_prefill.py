@@ -130,3 +130,15 @@ def test_chunked_prefill_full_size_sampled_rows():
     rows = sorted({int(cu[b]) for b in range(16)} | {int(cu[b + 1]) - 1 for b in range(16)}
                   | set(rng.choice(int(cu[-1]), 48, replace=False).tolist()))
     check(case, rows=rows)
+
+
+def test_spec_decode_full_size_sampled():
+    # the decode workload's 64 contexts (1k..32k) with 4 new tokens each: the
+    # streaming path, (token, head) columns, segments crossing sequences
+    from workloads import config7
+
+    case = config7()
+    rng = np.random.default_rng(81)
+    seqs = sorted(rng.choice(case.batch, 8, replace=False).tolist())
+    rows = [int(case.cu_seqlens_q[b]) + i for b in seqs for i in range(4)]
+    check(case, rows=rows)
