@@ -51,4 +51,5 @@ from .blockmap import (  # noqa: F401
     pooled_scores,
     topk_block_map,
     map_to_index,
+    compressed_branch,
 )

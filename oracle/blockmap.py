@@ -66,3 +66,34 @@ def map_to_index(block_map):
     valid = pos < num[..., None]
     idx[valid] = order[valid]
     return idx, num
+
+
+def compressed_branch(q_tiled, k_tiled, v_tiled, sizes, scale: float, gate_tiled, out_tiled=None, block: int = 64):
+    """[VSA] FastVideoVSAImpl._forward_h3, gate branch: with the tile means of
+    q, k and v (pool_tiles) and the pooled scores S = scale * q_pool k_pool^T
+    (the same scores the block map is built from), every query tile gets
+    c = softmax(S, over all key tiles) @ v_pool; each of its rows then adds
+    c * gate to the attention output: out + broadcast_rows(c) * gate, in tile
+    order (the page's gate_tiled is zero on padding rows). With grouped heads
+    query head h reads kv head h // (H / Hkv).
+
+    q_tiled [B, T*block, H, D]; k/v_tiled [B, T*block, Hkv, D]; gate_tiled like
+    q_tiled; out_tiled like q_tiled or None (zeros). Returns (out + c * gate,
+    c [B, H, T, D]) in float64.
+
+    Pinned: brute force on tiny inputs, uniform scores give the mean of the
+    value means, a zero gate leaves the output, grouped = repeated heads.
+    """
+    qp = pool_tiles(q_tiled, sizes, block)
+    kp = pool_tiles(k_tiled, sizes, block)
+    vp = pool_tiles(v_tiled, sizes, block)
+    group = qp.shape[1] // kp.shape[1]
+    kp = np.repeat(kp, group, axis=1)
+    vp = np.repeat(vp, group, axis=1)
+    s = pooled_scores(qp, kp, scale)
+    w = np.exp(s - s.max(axis=-1, keepdims=True))
+    w /= w.sum(axis=-1, keepdims=True)
+    comp = w @ vp  # [B, H, T, D]
+    rows = np.repeat(comp.transpose(0, 2, 1, 3), block, axis=1)  # [B, T*block, H, D]
+    base = np.zeros(rows.shape) if out_tiled is None else _f64(out_tiled)
+    return base + rows * _f64(gate_tiled), comp

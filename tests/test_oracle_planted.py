@@ -140,3 +140,26 @@ def test_paged_prefill_mutants_are_caught(monkeypatch):
 
     monkeypatch.setattr(tpp.oracle, "paged_kv_write", write_swapped)
     assert _fails(tpp.test_kv_write_worked_example)
+
+
+def test_compressed_branch_mutants_are_caught(monkeypatch):
+    from tests import test_oracle_compressed as tc
+
+    orig_pool = BM.pool_tiles
+
+    def pool_sum_not_mean(x, sizes, block=64):
+        # plant: tile sums instead of tile means
+        return orig_pool(x, np.ones_like(np.asarray(sizes)), block)
+
+    monkeypatch.setattr(BM, "pool_tiles", pool_sum_not_mean)
+    assert _fails(tc.test_brute_force_tiny)
+    monkeypatch.setattr(BM, "pool_tiles", orig_pool)
+
+    orig_scores = BM.pooled_scores
+
+    def scores_transposed(qp, kp, scale):
+        # plant: key tiles scored against query tiles the other way round
+        return np.swapaxes(orig_scores(qp, kp, scale), -1, -2)
+
+    monkeypatch.setattr(BM, "pooled_scores", scores_transposed)
+    assert _fails(tc.test_brute_force_tiny)
