@@ -247,7 +247,15 @@ def bench_sparse(case, steps, warmup):
     flops = sparse_flops(bmap.cpu().numpy(), sizes.cpu().numpy(), case.head_dim)
     prep_ms = time_steps(lambda: sav.vsa_prepare(q, k, v, case.video_shape, case.tile_shape, case.topk, case.scale),
                          steps, warmup)
-    return ms, flops, prep_ms
+    # the gate branch on the same tiles, with a synthetic gate (a trained one
+    # comes from a checkpoint's projection)
+    gate = workloads.randn_bf16(tuple(qt.shape), 1000 * case.seed + 6).to(dev)
+    cws = torch.empty(sav.attn_vsa_compressed_workspace_size(qt.shape[0], case.num_heads, kt.shape[2],
+                                                             sizes.numel(), case.head_dim), dtype=torch.uint8,
+                      device=dev)
+    comp_ms = time_steps(lambda: sav.attn_vsa_compressed_add(qt, kt, vt, sizes, gate, case.scale, out, workspace=cws),
+                         steps, warmup)
+    return ms, flops, prep_ms, comp_ms
 
 
 # ----------------------------------------------------------------------------
@@ -339,12 +347,13 @@ def main():
         torch.cuda.empty_cache()
     if args.only in (None, "sparse") and not (args.only is None and args.no_secondary):
         case = workloads.config5()
-        ms, flops, prep_ms = bench_sparse(case, args.steps, args.warmup)
+        ms, flops, prep_ms, comp_ms = bench_sparse(case, args.steps, args.warmup)
         tf = flops / (ms * 1e-3) / 1e12
-        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s (map build {prep_ms * 1e3:.0f} us)")
+        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s (map build {prep_ms * 1e3:.0f} us, "
+            f"compressed branch {comp_ms * 1e3:.0f} us)")
         secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
                           "roofline": roofline("sparse", "mfma", tf, flops),
-                          "tile_prep_and_map_ms": round(prep_ms, 4)})
+                          "tile_prep_and_map_ms": round(prep_ms, 4), "compressed_branch_ms": round(comp_ms, 4)})
 
     if args.only in (None, "paged_prefill") and not (args.only is None and args.no_secondary):
         case = workloads.config6()

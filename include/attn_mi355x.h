@@ -289,6 +289,35 @@ attn_status_t attn_vsa_block_map(const void* q_tiled, const void* k_tiled, const
                                  int32_t head_dim, float softmax_scale, int32_t topk, uint8_t* block_map,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes for attn_vsa_compressed_add (fp32 tile means of q, k, v and
+ * the per-tile compressed rows). Written to *bytes (host pointer). */
+attn_status_t attn_vsa_compressed_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                                 int32_t num_tiles, int32_t head_dim, size_t* bytes);
+
+/*
+ * VSA compressed branch (vLLM-Omni fastvideo_vsa.py page:
+ * FastVideoVSAImpl._forward_h3, the gate branch): with the fp32 tile means of
+ * q, k and v (as attn_vsa_block_map pools them) and the pooled scores
+ * S = softmax_scale * qbar kbar^T, each query tile a gets
+ * c_a = softmax(S[a, :]) @ vbar over all key tiles, and every row r of the
+ * tile adds c_a * gate: out[b][64a + r][h][:] += c_a[:] * gate[b][64a + r][h][:]
+ * (computed in fp32, rounded to bf16 once). The page's gate is zero on padding
+ * rows, which then stay unchanged.
+ *
+ *   q_tiled     [batch, num_tiles * 64, num_heads, head_dim] bf16, tile order
+ *   k/v_tiled   [batch, num_tiles * 64, num_kv_heads, head_dim] bf16
+ *   tile_sizes  [num_tiles] int32 in [0, 64]
+ *   gate_tiled  like q_tiled (the gate in tile order)
+ *   out         like q_tiled, updated in place (the block-sparse output)
+ *   workspace   >= attn_vsa_compressed_workspace_size() bytes
+ * batch == 0 or num_tiles == 0 is a no-op.
+ */
+attn_status_t attn_vsa_compressed_add(const void* q_tiled, const void* k_tiled, const void* v_tiled,
+                                      const int32_t* tile_sizes, const void* gate_tiled, int32_t batch,
+                                      int32_t num_tiles, int32_t num_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, float softmax_scale, void* out, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,8 @@ __all__ = [
     "attn_vsa_untile",
     "attn_vsa_block_map_workspace_size",
     "attn_vsa_block_map",
+    "attn_vsa_compressed_workspace_size",
+    "attn_vsa_compressed_add",
     "vsa_num_tiles",
     "vsa_prepare",
     "SUPPORTED_HEAD_DIMS",
@@ -67,6 +69,9 @@ _SIGS = {
     "attn_vsa_untile": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]),
     "attn_vsa_block_map_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "attn_vsa_block_map": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _sz, _p]),
+    "attn_vsa_compressed_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "attn_vsa_compressed_add": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _sz,
+                                               _p]),
 }
 
 _lib = None
@@ -421,6 +426,42 @@ def attn_vsa_block_map(q_tiled, k_tiled, tile_sizes, softmax_scale: float, topk:
         workspace.numel(), _stream_ptr(q_tiled, stream))
     _check("attn_vsa_block_map", st)
     return block_map
+
+
+def attn_vsa_compressed_workspace_size(batch: int, num_heads: int, num_kv_heads: int, num_tiles: int,
+                                       head_dim: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("attn_vsa_compressed_workspace_size",
+           load_library().attn_vsa_compressed_workspace_size(batch, num_heads, num_kv_heads, num_tiles, head_dim,
+                                                             ctypes.byref(n)))
+    return n.value
+
+
+def attn_vsa_compressed_add(q_tiled, k_tiled, v_tiled, tile_sizes, gate_tiled, softmax_scale: float, out,
+                            workspace=None, stream=None):
+    """out (tile order) += broadcast_rows(softmax(pooled scores) @ value tile means) * gate; returns out."""
+    dev = q_tiled.device
+    b, s, hq, d = q_tiled.shape
+    hkv = k_tiled.shape[2]
+    if s % 64 != 0:
+        raise ValueError("sequence length must be a multiple of the 64-row tile")
+    nt = s // 64
+    _shape(k_tiled, "k_tiled", (b, s, hkv, d))
+    _shape(v_tiled, "v_tiled", (b, s, hkv, d))
+    _shape(gate_tiled, "gate_tiled", q_tiled.shape)
+    _shape(out, "out", q_tiled.shape)
+    _shape(tile_sizes, "tile_sizes", (nt,))
+    need = attn_vsa_compressed_workspace_size(b, hq, hkv, nt, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load_library().attn_vsa_compressed_add(
+        _dev(q_tiled, "q_tiled", torch.bfloat16), _dev(k_tiled, "k_tiled", torch.bfloat16, dev),
+        _dev(v_tiled, "v_tiled", torch.bfloat16, dev), _dev(tile_sizes, "tile_sizes", torch.int32, dev),
+        _dev(gate_tiled, "gate_tiled", torch.bfloat16, dev), b, nt, hq, hkv, d, float(softmax_scale),
+        _dev(out, "out", torch.bfloat16, dev), _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(),
+        _stream_ptr(q_tiled, stream))
+    _check("attn_vsa_compressed_add", st)
+    return out
 
 
 def vsa_prepare(q, k, v, video_shape, tile_shape, topk: int, softmax_scale: float, stream=None):

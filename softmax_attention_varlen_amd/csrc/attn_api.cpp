@@ -300,4 +300,38 @@ attn_status_t attn_vsa_block_map(const void* q_tiled, const void* k_tiled, const
                                              (hipStream_t)stream));
 }
 
+attn_status_t attn_vsa_compressed_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
+                                                 int32_t num_tiles, int32_t head_dim, size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_tiles < 0 || head_dim <= 0) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  *bytes = attn::vsa_compressed_workspace_bytes(batch, num_heads, num_kv_heads, num_tiles, head_dim);
+  return ATTN_OK;
+}
+
+attn_status_t attn_vsa_compressed_add(const void* q_tiled, const void* k_tiled, const void* v_tiled,
+                                      const int32_t* tile_sizes, const void* gate_tiled, int32_t batch,
+                                      int32_t num_tiles, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (batch < 0 || num_tiles < 0 || num_heads <= 0 || num_kv_heads <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
+  if (num_tiles > 16384) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0 || num_tiles == 0) return ATTN_OK;
+  if (q_tiled == nullptr || k_tiled == nullptr || v_tiled == nullptr || tile_sizes == nullptr ||
+      gate_tiled == nullptr || out == nullptr) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  if ((long long)batch * num_tiles * 64 * num_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn::vsa_compressed_workspace_bytes(batch, num_heads, num_kv_heads, num_tiles, head_dim);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_vsa_compressed_add(q_tiled, k_tiled, v_tiled, tile_sizes, gate_tiled, batch,
+                                                  num_tiles, num_heads, num_kv_heads, head_dim, softmax_scale, out,
+                                                  workspace, (hipStream_t)stream));
+}
+
 }  // extern "C"

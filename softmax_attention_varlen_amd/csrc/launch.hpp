@@ -131,4 +131,12 @@ hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const 
                                 int n_tiles, int heads, int kv_heads, int head_dim, float scale, int topk,
                                 uint8_t* map, void* workspace, hipStream_t stream);
 
+// VSA compressed branch: out (tile order, bf16) += broadcast_rows(softmax(pooled
+// scores) @ value tile means) * gate. Workspace: fp32 means of q, k, v and c.
+size_t vsa_compressed_workspace_bytes(int batch, int heads, int kv_heads, int n_tiles, int head_dim);
+hipError_t launch_vsa_compressed_add(const void* q_tiled, const void* k_tiled, const void* v_tiled,
+                                     const int32_t* sizes, const void* gate, int batch, int n_tiles, int heads,
+                                     int kv_heads, int head_dim, float scale, void* out, void* workspace,
+                                     hipStream_t stream);
+
 }  // namespace attn

@@ -271,3 +271,56 @@ def test_config5_gpu_map_matches_oracle_map():
     scores = oracle.pooled_scores(oracle.pool_tiles(qt, sizes), oracle.pool_tiles(kt, sizes), case.scale)
     near_ties = check_map_is_valid_topk(prep["block_map"].cpu().numpy(), scores, case.topk)
     print(f"[parity] config5 map: rows with a near-tie at the cut: {near_ties} of {scores.shape[2] * 12}")
+
+
+def _gate_tiled(shape, tile, b, hq, d, seed):
+    """A synthetic gate in tile order, zero on padding rows (as the page builds it)."""
+    n = int(np.prod(shape))
+    part, sizes, non_pad, _ = oracle.tile_metadata(shape, tile, 64)
+    g = randn_bf16((b, n, hq, d), seed)
+    t = torch.zeros((b, sizes.size * 64, hq, d), dtype=g.dtype)
+    t[:, torch.from_numpy(non_pad)] = g[:, torch.from_numpy(part)]
+    return t
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 1)])
+def test_compressed_branch_partial_tiles(d, hq, hkv):
+    shape, tile = (5, 7, 9), (4, 4, 4)
+    (qt, kt, vt), sizes = _tiled(shape, tile, 2, hq, hkv, d, seed=350 + d)
+    gate = _gate_tiled(shape, tile, 2, hq, d, 360 + d)
+    base = randn_bf16(qt.shape, 370 + d)
+    scale = d ** -0.5
+    announce("compressed branch", d, hq, hkv, sizes.tolist())
+    out = dev(base)
+    sav.attn_vsa_compressed_add(dev(qt), dev(kt), dev(vt), dev(sizes.astype(np.int32)), dev(gate), scale, out)
+    torch.cuda.synchronize()
+    ref, _ = oracle.compressed_branch(qt, kt, vt, sizes, scale, gate, base)
+    assert_close("out", host(out), ref, OUT_TOL, bf16_output=True)
+
+
+def test_compressed_branch_zero_gate_keeps_output():
+    shape, tile = (4, 8, 8), (4, 4, 4)
+    (qt, kt, vt), sizes = _tiled(shape, tile, 1, 3, 3, 128, seed=380)
+    base = randn_bf16(qt.shape, 381)
+    out = dev(base)
+    sav.attn_vsa_compressed_add(dev(qt), dev(kt), dev(vt), dev(sizes.astype(np.int32)), dev(torch.zeros_like(qt)),
+                                128 ** -0.5, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), base)
+
+
+def test_compressed_branch_config5():
+    case = config5()
+    prep = sav.vsa_prepare(dev(case.q), dev(case.k), dev(case.v), case.video_shape, case.tile_shape, case.topk,
+                           case.scale)
+    qt, kt, vt, sizes = prep["q"], prep["k"], prep["v"], prep["tile_sizes"]
+    gate = dev(_gate_tiled(case.video_shape, case.tile_shape, 1, case.num_heads, case.head_dim, 390))
+    base = dev(randn_bf16(tuple(qt.shape), 391))
+    out = base.clone()
+    announce("compressed branch config5")
+    sav.attn_vsa_compressed_add(qt, kt, vt, sizes, gate, case.scale, out)
+    torch.cuda.synchronize()
+    ref, _ = oracle.compressed_branch(qt.cpu(), kt.cpu(), vt.cpu(), sizes.cpu().numpy(), case.scale, gate.cpu(),
+                                      base.cpu())
+    assert_close("out", host(out), ref, OUT_TOL, bf16_output=True)
