@@ -85,109 +85,211 @@ __global__ __launch_bounds__(256) void untile_kernel(const uint16_t* __restrict_
 }
 
 // Tile means: pooled[b][h][c][d] = (sum of the size(c) real rows) / max(size, 1),
-// fp32, rows summed in ascending order. One workgroup per (batch, tile); a
-// thread owns one 16-byte chunk (8 columns of one head) of the tile's rows, so
-// a row is read by consecutive threads.
-__global__ __launch_bounds__(256) void tile_pool_kernel(const uint16_t* __restrict__ x,
-                                                       const int32_t* __restrict__ sizes, float* __restrict__ pooled,
-                                                       int n_tiles, int heads, int head_dim) {
+// fp32. One workgroup per (batch, tile, source tensor); the tensors of one
+// launch (q, k, v) may differ in head count. Wave g sums rows 16g .. 16g + 15
+// (rows at or past the size count as zero) of 64 consecutive 16-byte chunks,
+// all 16 loads in flight at once; the four wave partials are then added in
+// ascending wave order through LDS.
+struct PoolSrc {
+  const uint16_t* x;
+  float* pooled;
+  int heads;
+};
+struct PoolArgs {
+  PoolSrc s[3];
+};
+
+__global__ __launch_bounds__(256) void tile_pool_kernel(PoolArgs pa, const int32_t* __restrict__ sizes, int n_tiles,
+                                                       int head_dim) {
+  __shared__ f32x4 part[4][64][2];
+  const PoolSrc src = pa.s[blockIdx.y];
   const int c = (int)(blockIdx.x % n_tiles);
   const long b = blockIdx.x / n_tiles;
   const int size = clampi(sizes[c], 0, 64);
   const float inv = 1.f / (float)(size > 1 ? size : 1);
-  const long row_elems = (long)heads * head_dim;
-  const uint16_t* base = x + (b * n_tiles + c) * 64 * row_elems;
+  const long row_elems = (long)src.heads * head_dim;
+  const uint16_t* base = src.x + (b * n_tiles + c) * 64 * row_elems;
   const int chunks = (int)(row_elems / 8);
-  for (int j = threadIdx.x; j < chunks; j += blockDim.x) {
-    float acc[8];
+  const int tid = threadIdx.x, g = tid >> 6, jl = tid & 63;
+  for (int j0 = 0; j0 < chunks; j0 += 64) {
+    const int j = j0 + jl;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    if (j < chunks) {
+      u32x4 v[16];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll 8
-    for (int r = 0; r < size; ++r) {
-      const u32x4 v = ld_global16(base + (long)r * row_elems + j * 8);
+      for (int i = 0; i < 16; ++i) v[i] = ld_global16(base + (long)(16 * g + i) * row_elems + j * 8);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] += __uint_as_float(v[i] << 16);
-        acc[2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
+      for (int i = 0; i < 16; ++i) {
+        if (16 * g + i < size) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            lo[2 * e] += __uint_as_float(v[i][e] << 16);
+            lo[2 * e + 1] += __uint_as_float(v[i][e] & 0xffff0000u);
+            hi[2 * e] += __uint_as_float(v[i][2 + e] << 16);
+            hi[2 * e + 1] += __uint_as_float(v[i][2 + e] & 0xffff0000u);
+          }
+        }
       }
     }
-    const int h = (j * 8) / head_dim, d = (j * 8) % head_dim;
-    float* prow = pooled + ((b * heads + h) * n_tiles + c) * (long)head_dim + d;
-    *reinterpret_cast<f32x4*>(prow) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-    *reinterpret_cast<f32x4*>(prow + 4) = f32x4{acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+    part[g][jl][0] = lo;
+    part[g][jl][1] = hi;
+    __syncthreads();
+    if (tid < 128) {
+      const int jj = j0 + (tid >> 1), half = tid & 1;
+      if (jj < chunks) {
+        f32x4 t = part[0][tid >> 1][half];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) t += part[w][tid >> 1][half];
+        const int h = (jj * 8) / head_dim, d = (jj * 8) % head_dim + 4 * half;
+        float* prow = src.pooled + ((b * src.heads + h) * n_tiles + c) * (long)head_dim + d;
+        *reinterpret_cast<f32x4*>(prow) = t * inv;
+      }
+    }
+    __syncthreads();
   }
 }
 
 // Batched fp32 GEMM for the pooled scores and the compressed rows:
-// C[z] = alpha * A[z] B'[z], A [M][K] row-major; B' = B^T with B stored [N][K]
-// (TRANS_B), else B' = B stored [K][N]. The launch covers batch entries
-// z0 + z = b * heads + h; A and C are indexed by z (the caller offsets them),
-// B by b * kv_heads + h / (heads / kv_heads) (grouped heads). A
-// 256-thread workgroup owns a 64 x 64 tile of C, each thread 4 x 4 of it;
-// K advances 16 at a time through LDS. Sums run over k in ascending order.
+// C[z] = alpha * A[z] B'[z], A [M][K] (row stride lda); B' = B^T with B stored
+// [N][K] (TRANS_B), else B' = B stored [K][N]; C row stride ldc. The launch
+// covers batch entries z0 + z = b * heads + h; A and C are indexed by z (the
+// caller offsets them), B by b * kv_heads + h / (heads / kv_heads) (grouped
+// heads). lda and ldb are multiples of 4 and cover K (resp. N) rounded up to 4.
+//
+// A workgroup of 4 waves owns a 32 x 32 tile of C. K runs in chunks of kKC:
+// each chunk of A and B is loaded whole (every thread's loads in flight at
+// once, the next chunk's issued before this one is consumed) and staged in
+// LDS; wave w multiplies the w-th quarter of the chunk, so each wave keeps a
+// partial 32 x 32 tile (lane (tx, ty): rows ty + 8i, columns tx + 8j, or
+// 4 tx + j for a row-major B), and the four partials are added in wave order.
+// k past K reads as zero.
+constexpr int kKC = 128;
+
+template <bool TRANS_B>
+struct GemmStage {
+  f32x4 a[4], b[4];
+};
+
+template <bool TRANS_B>
+__device__ __forceinline__ GemmStage<TRANS_B> gemm_fetch(const float* Az, const float* Bz, int m0, int n0, int M,
+                                                         int N, int K, int lda, int ldb, int kc, int tid) {
+  GemmStage<TRANS_B> g;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int idx = p * 256 + tid;  // 32 rows x 32 four-wide k groups
+    const int r = idx >> 5, k = kc + (idx & 31) * 4;
+    const int m = min(m0 + r, M - 1);
+    const int kk = min(k, ((K - 1) & ~3));
+    f32x4 t = *reinterpret_cast<const f32x4*>(Az + (long)m * lda + kk);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) t[e] = (k + e < K) ? t[e] : 0.f;
+    g.a[p] = t;
+  }
+  if (TRANS_B) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int idx = p * 256 + tid;
+      const int r = idx >> 5, k = kc + (idx & 31) * 4;
+      const int n = min(n0 + r, N - 1);
+      const int kk = min(k, ((K - 1) & ~3));
+      f32x4 t = *reinterpret_cast<const f32x4*>(Bz + (long)n * ldb + kk);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (k + e < K) ? t[e] : 0.f;
+      g.b[p] = t;
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int idx = p * 256 + tid;  // kKC rows x 8 four-wide column groups
+      const int k = kc + (idx >> 3), c = n0 + (idx & 7) * 4;
+      const int kr = min(k, K - 1);
+      const int cc = min(c, (N - 1) & ~3);
+      f32x4 t = *reinterpret_cast<const f32x4*>(Bz + (long)kr * ldb + cc);
+      g.b[p] = k < K ? t : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  return g;
+}
+
 template <bool TRANS_B>
 __global__ __launch_bounds__(256) void sgemm_kernel(const float* __restrict__ A, const float* __restrict__ B,
-                                                    float* __restrict__ C, int M, int N, int K, int z0,
-                                                    int heads, int kv_heads, float alpha) {
-  __shared__ float As[16][64 + 4];
-  __shared__ float Bs[16][64 + 4];
-  const int tiles_n = (N + 63) / 64;
-  const int m0 = (int)(blockIdx.x / tiles_n) * 64, n0 = (int)(blockIdx.x % tiles_n) * 64;
+                                                    float* __restrict__ C, int M, int N, int K, int lda, int ldb,
+                                                    int ldc, int z0, int heads, int kv_heads, float alpha) {
+  __shared__ __attribute__((aligned(16))) float As[32][kKC + 4];
+  __shared__ __attribute__((aligned(16))) float Bs[TRANS_B ? 32 : kKC][TRANS_B ? kKC + 4 : 36];
+  __shared__ f32x4 red[3][4][64];
+  const int tiles_n = (N + 31) / 32;
+  const int m0 = (int)(blockIdx.x / tiles_n) * 32, n0 = (int)(blockIdx.x % tiles_n) * 32;
   const long z = blockIdx.y, za = z0 + z;
   const long zb = (za / heads) * kv_heads + (za % heads) / (heads / kv_heads);
-  const float* Az = A + z * (long)M * K;
-  const float* Bz = B + zb * (long)N * K;
-  float* Cz = C + z * (long)M * N;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    {  // A tile [64 rows][16 k] -> As[k][row]
-      const int r = tid >> 2, c = (tid & 3) * 4;
+  const float* Az = A + z * (long)M * lda;
+  const float* Bz = B + zb * (TRANS_B ? (long)N * ldb : (long)K * ldb);
+  float* Cz = C + z * (long)M * ldc;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tx = lane & 7, ty = lane >> 3;
+  float acc[4][4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = m0 + r, k = k0 + c + i;
-        As[c + i][r] = (m < M && k < K) ? Az[(long)m * K + k] : 0.f;
-      }
-    }
-    if (TRANS_B) {  // B stored [N][K]: tile [64 n][16 k] -> Bs[k][n]
-      const int r = tid >> 2, c = (tid & 3) * 4;
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + r, k = k0 + c + i;
-        Bs[c + i][r] = (n < N && k < K) ? Bz[(long)n * K + k] : 0.f;
-      }
-    } else {  // B stored [K][N]: tile [16 k][64 n] -> Bs[k][n]
-      const int r = tid >> 4, c = (tid & 15) * 4;
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  }
+  GemmStage<TRANS_B> g = gemm_fetch<TRANS_B>(Az, Bz, m0, n0, M, N, K, lda, ldb, 0, tid);
+  for (int kc = 0; kc < K; kc += kKC) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int k = k0 + r, n = n0 + c + i;
-        Bs[r][c + i] = (n < N && k < K) ? Bz[(long)k * N + n] : 0.f;
+    for (int p = 0; p < 4; ++p) {
+      const int idx = p * 256 + tid;
+      *reinterpret_cast<f32x4*>(&As[idx >> 5][(idx & 31) * 4]) = g.a[p];
+      if (TRANS_B) {
+        *reinterpret_cast<f32x4*>(&Bs[idx >> 5][(idx & 31) * 4]) = g.b[p];
+      } else {
+        *reinterpret_cast<f32x4*>(&Bs[idx >> 3][(idx & 7) * 4]) = g.b[p];
       }
     }
     __syncthreads();
+    if (kc + kKC < K) g = gemm_fetch<TRANS_B>(Az, Bz, m0, n0, M, N, K, lda, ldb, kc + kKC, tid);
+#pragma unroll 2
+    for (int k = w * (kKC / 4); k < (w + 1) * (kKC / 4); k += 4) {
+      f32x4 av[4], bv[4];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float av[4], bv[4];
+      for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const f32x4*>(&As[ty + 8 * i][k]);
+      if (TRANS_B) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+        for (int j = 0; j < 4; ++j) bv[j] = *reinterpret_cast<const f32x4*>(&Bs[tx + 8 * j][k]);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
+        for (int kk = 0; kk < 4; ++kk) bv[kk] = *reinterpret_cast<const f32x4*>(&Bs[k + kk][4 * tx]);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(av[i], bv[j], acc[i][j]);
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float bb = TRANS_B ? bv[j][kk] : bv[kk][j];
+            acc[i][j] = __builtin_fmaf(av[i][kk], bb, acc[i][j]);
+          }
+        }
       }
     }
     __syncthreads();
   }
+  if (w > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[w - 1][i][lane] = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+  }
+  __syncthreads();
+  if (w > 0) return;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty * 4 + i;
+    f32x4 t = f32x4{acc[i][0], acc[i][1], acc[i][2], acc[i][3]};
+#pragma unroll
+    for (int p = 0; p < 3; ++p) t += red[p][i][lane];
+    const int m = m0 + ty + 8 * i;
     if (m >= M) continue;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx * 4 + j;
-      if (n < N) Cz[(long)m * N + n] = acc[i][j] * alpha;
+      const int n = TRANS_B ? n0 + tx + 8 * j : n0 + 4 * tx + j;
+      if (n < N) Cz[(long)m * ldc + n] = t[j] * alpha;
     }
   }
 }
@@ -214,11 +316,11 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
 // when fewer than k tiles beat it (a higher score, or an equal score at a
 // lower index), or when k reaches the tile count.
 __global__ __launch_bounds__(256) void topk_map_kernel(const float* __restrict__ scores, uint8_t* __restrict__ map,
-                                                       int n_tiles, int keep) {
+                                                       int n_tiles, int ld, int keep) {
   extern __shared__ float srow[];  // [stride]
   const int stride = (n_tiles + 3) & ~3;
   const long row = blockIdx.x;
-  const float* in = scores + row * n_tiles;
+  const float* in = scores + row * ld;
   for (int c = threadIdx.x; c < stride; c += blockDim.x) srow[c] = c < n_tiles ? in[c] : kNegInf;
   __syncthreads();
   uint8_t* mrow = map + row * n_tiles;
@@ -240,10 +342,61 @@ __global__ __launch_bounds__(256) void topk_map_kernel(const float* __restrict__
   }
 }
 
-// Row softmax in place (fp32, exp2 of (s - max) * log2 e): one row per workgroup.
-__global__ __launch_bounds__(256) void softmax_rows_kernel(float* __restrict__ x, int n) {
+// Order-preserving map of a float to an unsigned key (larger float, larger
+// key; -0 sorts just below +0). Key 0 is below every finite score.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// One map row per wave, for rows of at most 64 R tiles (lane l holds tiles
+// l, l + 64, ...). The keep-th largest key T is found bit by bit from the top
+// (the largest T with at least keep keys >= T, counted with wave ballots);
+// then every key above T is kept, and of the keys equal to T the lowest-index
+// ones until keep is reached.
+template <int R>
+__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ scores, uint8_t* __restrict__ map,
+                                                        int n_tiles, int ld, int keep, long rows) {
+  const int lane = threadIdx.x & 63;
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* in = scores + row * ld;
+  uint32_t key[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int idx = r * 64 + lane;
+    key[r] = idx < n_tiles ? order_key(in[idx]) : 0u;
+  }
+  uint32_t t = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = t | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) cnt += __popcll(__ballot(key[r] >= cand));
+    if (cnt >= keep) t = cand;
+  }
+  int above = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) above += __popcll(__ballot(key[r] > t));
+  const int quota = keep - above;
+  int eq_before = 0;
+  uint8_t* mrow = map + row * n_tiles;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int idx = r * 64 + lane;
+    const unsigned long long eq = __ballot(idx < n_tiles && key[r] == t);
+    const int rank = eq_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
+    eq_before += __popcll(eq);
+    if (idx < n_tiles) mrow[idx] = (uint8_t)(key[r] > t || (key[r] == t && rank < quota));
+  }
+}
+
+// Row softmax in place (fp32, exp2 of (s - max) * log2 e) over the first n
+// entries of rows ld apart: one row per workgroup.
+__global__ __launch_bounds__(256) void softmax_rows_kernel(float* __restrict__ x, int n, int ld) {
   __shared__ float red[4];
-  float* row = x + (long)blockIdx.x * n;
+  float* row = x + (long)blockIdx.x * ld;
   float mx = kNegInf;
   for (int c = threadIdx.x; c < n; c += blockDim.x) mx = fmaxf(mx, row[c]);
   mx = block_max(mx, red);
@@ -258,11 +411,11 @@ __global__ __launch_bounds__(256) void softmax_rows_kernel(float* __restrict__ x
 }
 
 template <bool TRANS_B>
-static hipError_t launch_sgemm(const float* A, const float* B, float* C, int M, int N, int K, int z0, int nz,
-                               int heads, int kv_heads, float alpha, hipStream_t stream) {
-  const dim3 grid((unsigned)(((M + 63) / 64) * ((N + 63) / 64)), (unsigned)nz);
-  hipLaunchKernelGGL((sgemm_kernel<TRANS_B>), grid, dim3(256), 0, stream, A, B, C, M, N, K, z0, heads, kv_heads,
-                     alpha);
+static hipError_t launch_sgemm(const float* A, const float* B, float* C, int M, int N, int K, int lda, int ldb,
+                               int ldc, int z0, int nz, int heads, int kv_heads, float alpha, hipStream_t stream) {
+  const dim3 grid((unsigned)(((M + 31) / 32) * ((N + 31) / 32)), (unsigned)nz);
+  hipLaunchKernelGGL((sgemm_kernel<TRANS_B>), grid, dim3(256), 0, stream, A, B, C, M, N, K, lda, ldb, ldc, z0, heads,
+                     kv_heads, alpha);
   return hipGetLastError();
 }
 
@@ -271,8 +424,10 @@ static hipError_t launch_sgemm(const float* A, const float* B, float* C, int M, 
 // pair's matrix, when that is larger).
 constexpr size_t kScoreChunkBytes = (size_t)64 << 20;
 
+static int score_ld(int n_tiles) { return (n_tiles + 3) & ~3; }
+
 static int score_chunk(int batch, int heads, int n_tiles) {
-  const size_t one = (size_t)n_tiles * n_tiles * sizeof(float);
+  const size_t one = (size_t)n_tiles * score_ld(n_tiles) * sizeof(float);
   size_t c = kScoreChunkBytes / (one > 0 ? one : 1);
   const size_t total = (size_t)batch * heads;
   c = c < 1 ? 1 : (c > total ? total : c);
@@ -281,13 +436,13 @@ static int score_chunk(int batch, int heads, int n_tiles) {
 }
 
 static size_t score_bytes(int batch, int heads, int n_tiles) {
-  return (size_t)score_chunk(batch, heads, n_tiles) * n_tiles * n_tiles * sizeof(float);
+  return (size_t)score_chunk(batch, heads, n_tiles) * n_tiles * score_ld(n_tiles) * sizeof(float);
 }
 
-static hipError_t launch_pool(const void* x, const int32_t* sizes, float* pooled, int batch, int n_tiles, int heads,
+static hipError_t launch_pool(const PoolArgs& pa, int n_src, const int32_t* sizes, int batch, int n_tiles,
                               int head_dim, hipStream_t stream) {
-  hipLaunchKernelGGL(tile_pool_kernel, dim3((unsigned)((long)batch * n_tiles)), dim3(256), 0, stream,
-                     (const uint16_t*)x, sizes, pooled, n_tiles, heads, head_dim);
+  hipLaunchKernelGGL(tile_pool_kernel, dim3((unsigned)((long)batch * n_tiles), (unsigned)n_src), dim3(256), 0, stream,
+                     pa, sizes, n_tiles, head_dim);
   return hipGetLastError();
 }
 
@@ -362,6 +517,33 @@ hipError_t launch_untile(const void* y, const VsaGeometry& g, int batch, int row
   return hipGetLastError();
 }
 
+template <int R>
+static void launch_topk_wave(const float* scores, uint8_t* map, int n_tiles, int ld, int keep, long rows,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(topk_wave_kernel<R>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, scores, map,
+                     n_tiles, ld, keep, rows);
+}
+
+// Rows of up to 1024 tiles take the one-wave radix select; longer rows (and
+// k >= the tile count) the workgroup-per-row ranking.
+static hipError_t launch_topk(const float* scores, uint8_t* map, int n_tiles, int ld, int keep, long rows, size_t lds,
+                              hipStream_t stream) {
+  if (keep >= n_tiles || n_tiles > 1024) {
+    hipLaunchKernelGGL(topk_map_kernel, dim3((unsigned)rows), dim3(256), lds, stream, scores, map, n_tiles, ld, keep);
+  } else if (n_tiles <= 64) {
+    launch_topk_wave<1>(scores, map, n_tiles, ld, keep, rows, stream);
+  } else if (n_tiles <= 128) {
+    launch_topk_wave<2>(scores, map, n_tiles, ld, keep, rows, stream);
+  } else if (n_tiles <= 256) {
+    launch_topk_wave<4>(scores, map, n_tiles, ld, keep, rows, stream);
+  } else if (n_tiles <= 512) {
+    launch_topk_wave<8>(scores, map, n_tiles, ld, keep, rows, stream);
+  } else {
+    launch_topk_wave<16>(scores, map, n_tiles, ld, keep, rows, stream);
+  }
+  return hipGetLastError();
+}
+
 size_t vsa_map_workspace_bytes(int batch, int heads, int kv_heads, int n_tiles, int head_dim) {
   return ((size_t)batch * heads * n_tiles * head_dim + (size_t)batch * kv_heads * n_tiles * head_dim) * sizeof(float) +
          score_bytes(batch, heads, n_tiles);
@@ -373,21 +555,22 @@ hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const 
   float* qpool = (float*)workspace;
   float* kpool = qpool + (size_t)batch * heads * n_tiles * head_dim;
   float* scores = kpool + (size_t)batch * kv_heads * n_tiles * head_dim;
-  hipError_t e = launch_pool(q_tiled, sizes, qpool, batch, n_tiles, heads, head_dim, stream);
-  if (e == hipSuccess) e = launch_pool(k_tiled, sizes, kpool, batch, n_tiles, kv_heads, head_dim, stream);
+  PoolArgs pa{};
+  pa.s[0] = PoolSrc{(const uint16_t*)q_tiled, qpool, heads};
+  pa.s[1] = PoolSrc{(const uint16_t*)k_tiled, kpool, kv_heads};
+  hipError_t e = launch_pool(pa, 2, sizes, batch, n_tiles, head_dim, stream);
   if (e != hipSuccess) return e;
   const int keep = topk < n_tiles ? topk : n_tiles;
-  const int total = batch * heads, chunk = score_chunk(batch, heads, n_tiles);
+  const int total = batch * heads, chunk = score_chunk(batch, heads, n_tiles), ld = score_ld(n_tiles);
   const size_t lds = (size_t)((n_tiles + 3) & ~3) * sizeof(float);
   const size_t mat = (size_t)n_tiles * head_dim;
   for (int z0 = 0; z0 < total; z0 += chunk) {
     const int nz = total - z0 < chunk ? total - z0 : chunk;
-    e = launch_sgemm<true>(qpool + z0 * mat, kpool, scores, n_tiles, n_tiles, head_dim, z0, nz, heads, kv_heads,
-                           scale, stream);
+    e = launch_sgemm<true>(qpool + z0 * mat, kpool, scores, n_tiles, n_tiles, head_dim, head_dim, head_dim, ld, z0,
+                           nz, heads, kv_heads, scale, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_map_kernel, dim3((unsigned)((long)nz * n_tiles)), dim3(256), lds, stream, scores,
-                       map + (size_t)z0 * n_tiles * n_tiles, n_tiles, keep);
-    e = hipGetLastError();
+    e = launch_topk(scores, map + (size_t)z0 * n_tiles * n_tiles, n_tiles, ld, keep, (long)nz * n_tiles, lds,
+                    stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -412,23 +595,25 @@ hipError_t launch_vsa_compressed_add(const void* q_tiled, const void* k_tiled, c
   float* kpool = comp + (size_t)batch * heads * n_tiles * head_dim;
   float* vpool = kpool + (size_t)batch * kv_heads * n_tiles * head_dim;
   float* scores = vpool + (size_t)batch * kv_heads * n_tiles * head_dim;
-  hipError_t e = launch_pool(q_tiled, sizes, qpool, batch, n_tiles, heads, head_dim, stream);
-  if (e == hipSuccess) e = launch_pool(k_tiled, sizes, kpool, batch, n_tiles, kv_heads, head_dim, stream);
-  if (e == hipSuccess) e = launch_pool(v_tiled, sizes, vpool, batch, n_tiles, kv_heads, head_dim, stream);
+  PoolArgs pa{};
+  pa.s[0] = PoolSrc{(const uint16_t*)q_tiled, qpool, heads};
+  pa.s[1] = PoolSrc{(const uint16_t*)k_tiled, kpool, kv_heads};
+  pa.s[2] = PoolSrc{(const uint16_t*)v_tiled, vpool, kv_heads};
+  hipError_t e = launch_pool(pa, 3, sizes, batch, n_tiles, head_dim, stream);
   if (e != hipSuccess) return e;
-  const int total = batch * heads, chunk = score_chunk(batch, heads, n_tiles);
+  const int total = batch * heads, chunk = score_chunk(batch, heads, n_tiles), ld = score_ld(n_tiles);
   const size_t mat = (size_t)n_tiles * head_dim;
   for (int z0 = 0; z0 < total; z0 += chunk) {
     const int nz = total - z0 < chunk ? total - z0 : chunk;
-    e = launch_sgemm<true>(qpool + z0 * mat, kpool, scores, n_tiles, n_tiles, head_dim, z0, nz, heads, kv_heads,
-                           scale, stream);
+    e = launch_sgemm<true>(qpool + z0 * mat, kpool, scores, n_tiles, n_tiles, head_dim, head_dim, head_dim, ld, z0,
+                           nz, heads, kv_heads, scale, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(softmax_rows_kernel, dim3((unsigned)((long)nz * n_tiles)), dim3(256), 0, stream, scores,
-                       n_tiles);
+                       n_tiles, ld);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_sgemm<false>(scores, vpool, comp + z0 * mat, n_tiles, head_dim, n_tiles, z0, nz, heads, kv_heads, 1.f,
-                            stream);
+    e = launch_sgemm<false>(scores, vpool, comp + z0 * mat, n_tiles, head_dim, n_tiles, ld, head_dim, head_dim, z0, nz,
+                            heads, kv_heads, 1.f, stream);
     if (e != hipSuccess) return e;
   }
   const long rows = (long)batch * n_tiles * 64;

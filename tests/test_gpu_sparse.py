@@ -299,6 +299,57 @@ def test_compressed_branch_partial_tiles(d, hq, hkv):
     assert_close("out", host(out), ref, OUT_TOL, bf16_output=True)
 
 
+@pytest.mark.parametrize("shape", [(9, 7, 9), (20, 20, 21), (13, 4, 4)])
+def test_compressed_branch_ragged_tile_counts(shape):
+    # 18, 150 and 4 tiles: score rows that are not a multiple of 4 wide, GEMM
+    # tiles cut by the tile count, and a single partial output tile
+    tile = (4, 4, 4)
+    (qt, kt, vt), sizes = _tiled(shape, tile, 1, 4, 2, 128, seed=385)
+    gate = _gate_tiled(shape, tile, 1, 4, 128, 386)
+    base = randn_bf16(qt.shape, 387)
+    announce("compressed branch ragged", shape, sizes.size)
+    out = dev(base)
+    sav.attn_vsa_compressed_add(dev(qt), dev(kt), dev(vt), dev(sizes.astype(np.int32)), dev(gate), 128 ** -0.5, out)
+    torch.cuda.synchronize()
+    ref, _ = oracle.compressed_branch(qt, kt, vt, sizes, 128 ** -0.5, gate, base)
+    assert_close("out", host(out), ref, OUT_TOL, bf16_output=True)
+
+
+@pytest.mark.parametrize("shape,topk", [((9, 7, 9), 5), ((20, 20, 21), 17), ((12, 24, 28), 9), ((32, 28, 36), 40),
+                                        ((32, 32, 36), 64), ((44, 44, 36), 50)])
+def test_block_map_ragged_tile_counts(shape, topk):
+    tile = (4, 4, 4)
+    (qt, kt, vt), sizes = _tiled(shape, tile, 1, 4, 2, 128, seed=388)
+    announce("vsa block map ragged", shape, sizes.size, topk)
+    gmap = sav.attn_vsa_block_map(dev(qt), dev(kt), dev(sizes), 128 ** -0.5, topk)
+    torch.cuda.synchronize()
+    scores = oracle.pooled_scores(oracle.pool_tiles(qt, sizes),
+                                  np.repeat(oracle.pool_tiles(kt, sizes), 2, axis=1), 128 ** -0.5)
+    check_map_is_valid_topk(gmap.cpu().numpy(), scores, topk)
+
+
+def test_block_map_exact_ties_lower_index_wins():
+    # 64 full tiles whose keys are one of three exactly representable rows, and
+    # one query row everywhere: every score is exact and ties are exact, so the
+    # map must equal the oracle's (lower tile index first) bit for bit
+    shape, tile, d = (16, 16, 16), (4, 4, 4), 128
+    part, sizes, non_pad, _ = oracle.tile_metadata(shape, tile, 64)
+    nt = sizes.size
+    rng = np.random.default_rng(392)
+    protos = torch.tensor(rng.integers(-4, 5, (3, d)) * 0.25, dtype=torch.bfloat16)
+    which = rng.integers(0, 3, nt)
+    kt = torch.zeros((1, nt * 64, 1, d), dtype=torch.bfloat16)
+    for c in range(nt):
+        kt[0, c * 64:(c + 1) * 64, 0] = protos[which[c]]
+    qt = torch.zeros_like(kt)
+    qt[0, :, 0] = torch.tensor(rng.integers(-4, 5, d) * 0.25, dtype=torch.bfloat16)
+    scores = oracle.pooled_scores(oracle.pool_tiles(qt, sizes), oracle.pool_tiles(kt, sizes), 0.125)
+    for topk in (1, 7, 21, 22, 40):
+        gmap = sav.attn_vsa_block_map(dev(qt), dev(kt), dev(sizes), 0.125, topk)
+        torch.cuda.synchronize()
+        assert np.array_equal(gmap.cpu().numpy().astype(bool), oracle.topk_block_map(scores, topk)), topk
+
+
 def test_compressed_branch_zero_gate_keeps_output():
     shape, tile = (4, 8, 8), (4, 4, 4)
     (qt, kt, vt), sizes = _tiled(shape, tile, 1, 3, 3, 128, seed=380)
