@@ -53,3 +53,8 @@ from .blockmap import (  # noqa: F401
     map_to_index,
     compressed_branch,
 )
+from .variants import (  # noqa: F401
+    sliding_window_decode_attention,
+    padded_prefix_attention,
+    masked_attention,
+)

@@ -163,3 +163,36 @@ def test_compressed_branch_mutants_are_caught(monkeypatch):
 
     monkeypatch.setattr(BM, "pooled_scores", scores_transposed)
     assert _fails(tc.test_brute_force_tiny)
+
+
+def test_variant_mutants_are_caught(monkeypatch):
+    from tests import test_oracle_variants as tv
+
+    orig_window = tv.oracle.sliding_window_decode_attention
+
+    def window_one_short(q, kv_cache, block_tables, context_lens, scale, window, seqs=None):
+        # plant: the window counts the query itself among its tokens
+        return orig_window(q, kv_cache, block_tables, context_lens, scale, max(window - 1, 0), seqs)
+
+    monkeypatch.setattr(tv.oracle, "sliding_window_decode_attention", window_one_short)
+    assert _fails(tv.test_window_brute_force_tiny)
+    monkeypatch.setattr(tv.oracle, "sliding_window_decode_attention", orig_window)
+
+    orig_padded = tv.oracle.padded_prefix_attention
+
+    def padded_key_lengths_for_queries(q, k, v, q_lens, k_lens, scale, causal):
+        # plant: the query prefix taken from the key lengths
+        return orig_padded(q, k, v, np.minimum(k_lens, q.shape[1]), k_lens, scale, causal)
+
+    monkeypatch.setattr(tv.oracle, "padded_prefix_attention", padded_key_lengths_for_queries)
+    assert _fails(tv.test_padded_prefix_equals_packed_varlen)
+    monkeypatch.setattr(tv.oracle, "padded_prefix_attention", orig_padded)
+
+    orig_masked = tv.oracle.masked_attention
+
+    def masked_keeps_every_query(q, k, v, key_mask, scale, causal, mask_queries):
+        # plant: self-attention keeps the padding tokens' query rows
+        return orig_masked(q, k, v, key_mask, scale, causal, False)
+
+    monkeypatch.setattr(tv.oracle, "masked_attention", masked_keeps_every_query)
+    assert _fails(tv.test_self_mask_with_holes_brute_force_tiny)
