@@ -138,6 +138,97 @@ attn_status_t attn_paged_decode(const void* q, const void* kv_cache,
                                 void* stream);
 
 /*
+ * Single-token decode with a sliding window (vLLM-Ascend attention_v1.py page:
+ * AscendAttentionBackendImpl._forward_fia_slidingwindow, the decode-only route
+ * of a layer with a sliding window, which hands the window to the fused kernel
+ * as pre_tokens). The query of sequence b sits at position L - 1
+ * (L = context_lens[b]) and sees keys t with L - 1 - window <= t <= L - 1:
+ * the window counts the tokens before the query that stay visible.
+ *
+ * Arguments as for attn_paged_decode, plus
+ *   window        (host) >= 0; window >= max_context_len - 1 is plain decode.
+ * The workspace is the one attn_paged_decode_workspace_size() reports for the
+ * same sizes. Errors: window < 0 gives ATTN_ERR_INVALID_ARG; otherwise as for
+ * attn_paged_decode.
+ */
+attn_status_t attn_paged_decode_sliding_window(const void* q, const void* kv_cache,
+                                               const int32_t* block_tables, const int32_t* context_lens,
+                                               int32_t num_seqs, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                               int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t head_dim, int32_t block_size, int32_t window,
+                                               float softmax_scale, void* out, float* lse, void* workspace,
+                                               size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes attn_padded_fwd needs (two int32 arrays of batch + 1).
+ */
+attn_status_t attn_padded_fwd_workspace_size(int32_t batch, size_t* bytes);
+
+/*
+ * Attention over the valid prefix of each entry of a padded batch (vLLM-Omni
+ * fastvideo_vsa.py page: FastVideoVSAImpl._fallback and forward_cuda with
+ * packed_padding: the first q_length query rows and kv_length key rows are
+ * real, attention runs on those prefixes and the output rows past q_length are
+ * zero).
+ *
+ *   q             [batch, seqlen_q, num_heads, head_dim] bf16
+ *   k, v          [batch, seqlen_k, num_kv_heads, head_dim] bf16
+ *   q_lens        [batch] int32 (device), 0 <= q_lens[b] <= seqlen_q (clamped)
+ *   k_lens        [batch] int32 (device), 0 <= k_lens[b] <= seqlen_k (clamped)
+ *   causal        bottom-right on (q_lens[b], k_lens[b]), as attn_varlen_fwd
+ *   out           [batch, seqlen_q, num_heads, head_dim] bf16; rows at or past
+ *                 q_lens[b] are written as zeros
+ *   lse           nullable; [num_heads, batch * seqlen_q] fp32, -inf on pad rows
+ *                 and on rows that see no key
+ *   workspace     >= attn_padded_fwd_workspace_size() bytes
+ * The contents of pad rows of q, k and v are never read into the result.
+ * batch == 0 or seqlen_q == 0 is a no-op. Errors: negative sizes, a bad
+ * scale or null pointers give ATTN_ERR_INVALID_ARG; an unsupported head_dim
+ * or head ratio ATTN_ERR_UNSUPPORTED; a short workspace
+ * ATTN_ERR_WORKSPACE_TOO_SMALL.
+ */
+attn_status_t attn_padded_fwd(const void* q, const void* k, const void* v, const int32_t* q_lens,
+                              const int32_t* k_lens, int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                              int32_t causal, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Workspace bytes attn_masked_fwd needs: packed copies of k and v (and of q and
+ * the output when mask_queries is set) plus the per-entry index arrays.
+ */
+attn_status_t attn_masked_fwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t mask_queries, size_t* bytes);
+
+/*
+ * Attention under a 2-D key-padding mask (vLLM-Omni flash_attn.py page:
+ * FlashAttentionImpl._forward_varlen_masked, which unpads by the mask, runs
+ * varlen attention and pads the result back).
+ *
+ *   q             [batch, seqlen_q, num_heads, head_dim] bf16
+ *   k, v          [batch, seqlen_k, num_kv_heads, head_dim] bf16
+ *   key_mask      [batch, seqlen_k] uint8 (device), nonzero = real token
+ *   mask_queries  nonzero: self-attention, the mask also selects the query rows
+ *                 (needs seqlen_q == seqlen_k); the real tokens of an entry, in
+ *                 order, form one document and padding rows come back as
+ *                 zeros. Zero: cross-attention, the mask covers keys only and
+ *                 every query row attends the real keys of its entry.
+ *   causal        bottom-right on the real-token counts, as attn_varlen_fwd
+ *   out           [batch, seqlen_q, num_heads, head_dim] bf16
+ *   lse           nullable; [num_heads, batch * seqlen_q] fp32, -inf on
+ *                 padding rows and on rows that see no key
+ *   workspace     >= attn_masked_fwd_workspace_size() bytes (same mask_queries)
+ * batch == 0 or seqlen_q == 0 is a no-op. Errors as for attn_padded_fwd, and
+ * mask_queries with seqlen_q != seqlen_k gives ATTN_ERR_INVALID_ARG.
+ */
+attn_status_t attn_masked_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask,
+                              int32_t batch, int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
+                              int32_t mask_queries, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
  * Paged KV cache write (vLLM-Ascend attention_v1.py page:
  * AscendAttentionImpl.reshape_and_cache with AscendMetadata.slot_mapping).
  * New token i's K and V rows are stored at cache slot slot_mapping[i]: block

@@ -26,6 +26,11 @@ __all__ = [
     "attn_varlen_fwd",
     "attn_paged_decode_workspace_size",
     "attn_paged_decode",
+    "attn_paged_decode_sliding_window",
+    "attn_padded_fwd_workspace_size",
+    "attn_padded_fwd",
+    "attn_masked_fwd_workspace_size",
+    "attn_masked_fwd",
     "attn_paged_kv_write",
     "attn_paged_prefill",
     "attn_paged_prefill_workspace_size",
@@ -57,6 +62,15 @@ _SIGS = {
     "attn_paged_decode_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "attn_paged_decode": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _p,
                                          _p, _p, _sz, _p]),
+    "attn_paged_decode_sliding_window": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                        _i32, _i32, _f32, _p, _p, _p, _sz, _p]),
+    "attn_padded_fwd_workspace_size": (ctypes.c_int, [_i32, ctypes.POINTER(_sz)]),
+    "attn_padded_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _p,
+                                       _sz, _p]),
+    "attn_masked_fwd_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                      ctypes.POINTER(_sz)]),
+    "attn_masked_fwd": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _p, _p,
+                                       _p, _sz, _p]),
     "attn_paged_kv_write": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _p, _p]),
     "attn_paged_prefill": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                           _i32, _f32, _p, _p, _p, _sz, _p]),
@@ -188,8 +202,9 @@ def attn_paged_decode_workspace_size(num_seqs: int, num_heads: int, num_kv_heads
 
 
 def attn_paged_decode(q, kv_cache, block_tables, context_lens, max_context_len: int, softmax_scale: float,
-                      out=None, lse=None, return_lse: bool = False, workspace=None, stream=None):
-    """Single-token decode over a paged cache [2, NB, 128, Hkv, D]. q [S, Hq, D]."""
+                      out=None, lse=None, return_lse: bool = False, workspace=None, stream=None, window=None):
+    """Single-token decode over a paged cache [2, NB, 128, Hkv, D]. q [S, Hq, D].
+    With ``window`` (>= 0) the call goes to attn_paged_decode_sliding_window."""
     dev = q.device
     nseq, hq, d = q.shape
     two, nblocks, bs, hkv, dk = kv_cache.shape
@@ -209,13 +224,103 @@ def attn_paged_decode(q, kv_cache, block_tables, context_lens, max_context_len: 
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     lib = load_library()
-    st = lib.attn_paged_decode(
-        _dev(q, "q", torch.bfloat16), _dev(kv_cache, "kv_cache", torch.bfloat16, dev),
-        _dev(block_tables, "block_tables", torch.int32, dev), _dev(context_lens, "context_lens", torch.int32, dev),
-        nseq, nblocks, mbps, int(max_context_len), hq, hkv, d, bs, float(softmax_scale),
-        _dev(out, "out", torch.bfloat16, dev), _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
+    head = (_dev(q, "q", torch.bfloat16), _dev(kv_cache, "kv_cache", torch.bfloat16, dev),
+            _dev(block_tables, "block_tables", torch.int32, dev), _dev(context_lens, "context_lens", torch.int32, dev),
+            nseq, nblocks, mbps, int(max_context_len), hq, hkv, d, bs)
+    tail = (float(softmax_scale), _dev(out, "out", torch.bfloat16, dev),
+            _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
+            _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(), _stream_ptr(q, stream))
+    if window is None:
+        _check("attn_paged_decode", lib.attn_paged_decode(*head, *tail))
+    else:
+        _check("attn_paged_decode_sliding_window", lib.attn_paged_decode_sliding_window(*head, int(window), *tail))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def attn_paged_decode_sliding_window(q, kv_cache, block_tables, context_lens, max_context_len: int, window: int,
+                                     softmax_scale: float, **kw):
+    """Decode where the query at position L - 1 sees keys L - 1 - window .. L - 1."""
+    return attn_paged_decode(q, kv_cache, block_tables, context_lens, max_context_len, softmax_scale,
+                             window=window, **kw)
+
+
+def attn_padded_fwd_workspace_size(batch: int) -> int:
+    n = _sz(0)
+    _check("attn_padded_fwd_workspace_size", load_library().attn_padded_fwd_workspace_size(batch, ctypes.byref(n)))
+    return n.value
+
+
+def attn_padded_fwd(q, k, v, q_lens, k_lens, softmax_scale: float, causal: bool = False, out=None, lse=None,
+                    return_lse: bool = False, workspace=None, stream=None):
+    """Attention over valid prefixes of a padded batch: q [B, Sq, Hq, D],
+    k/v [B, Sk, Hkv, D], q_lens/k_lens [B] int32 on the device. Rows past
+    q_lens[b] come back as zeros; lse is [Hq, B * Sq]."""
+    dev = q.device
+    b, sq, hq, d = q.shape
+    _, sk, hkv, _ = k.shape
+    _shape(k, "k", (b, sk, hkv, d))
+    _shape(v, "v", (b, sk, hkv, d))
+    _shape(q_lens, "q_lens", (b,))
+    _shape(k_lens, "k_lens", (b,))
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, b * sq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _shape(lse, "lse", (hq, b * sq))
+    if workspace is None:
+        workspace = torch.empty(max(attn_padded_fwd_workspace_size(b), 1), dtype=torch.uint8, device=dev)
+    st = load_library().attn_padded_fwd(
+        _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16, dev), _dev(v, "v", torch.bfloat16, dev),
+        _dev(q_lens, "q_lens", torch.int32, dev), _dev(k_lens, "k_lens", torch.int32, dev), b, sq, sk, hq, hkv, d,
+        float(softmax_scale), int(bool(causal)), _dev(out, "out", torch.bfloat16, dev),
+        _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
         _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(), _stream_ptr(q, stream))
-    _check("attn_paged_decode", st)
+    _check("attn_padded_fwd", st)
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def attn_masked_fwd_workspace_size(batch: int, seqlen_q: int, seqlen_k: int, num_heads: int, num_kv_heads: int,
+                                   head_dim: int, mask_queries: bool) -> int:
+    n = _sz(0)
+    _check("attn_masked_fwd_workspace_size",
+           load_library().attn_masked_fwd_workspace_size(batch, seqlen_q, seqlen_k, num_heads, num_kv_heads,
+                                                         head_dim, int(bool(mask_queries)), ctypes.byref(n)))
+    return n.value
+
+
+def attn_masked_fwd(q, k, v, key_mask, softmax_scale: float, causal: bool = False, mask_queries=None, out=None,
+                    lse=None, return_lse: bool = False, workspace=None, stream=None):
+    """Attention under a key-padding mask [B, Sk] (nonzero = real token).
+    mask_queries defaults to self-attention when Sq == Sk (the mask then also
+    selects the query rows; padding rows come back as zeros); pass False for
+    cross-attention. lse is [Hq, B * Sq]."""
+    dev = q.device
+    b, sq, hq, d = q.shape
+    _, sk, hkv, _ = k.shape
+    _shape(k, "k", (b, sk, hkv, d))
+    _shape(v, "v", (b, sk, hkv, d))
+    _shape(key_mask, "key_mask", (b, sk))
+    if mask_queries is None:
+        mask_queries = sq == sk
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, b * sq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _shape(lse, "lse", (hq, b * sq))
+    if workspace is None:
+        need = attn_masked_fwd_workspace_size(b, sq, sk, hq, hkv, d, mask_queries)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = load_library().attn_masked_fwd(
+        _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16, dev), _dev(v, "v", torch.bfloat16, dev),
+        _dev(key_mask, "key_mask", torch.uint8, dev), b, sq, sk, hq, hkv, d, float(softmax_scale),
+        int(bool(causal)), int(bool(mask_queries)), _dev(out, "out", torch.bfloat16, dev),
+        _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
+        _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(), _stream_ptr(q, stream))
+    _check("attn_masked_fwd", st)
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -19,6 +19,20 @@ constexpr long long kMaxRows = 0x7fffffffLL;
 
 attn_status_t from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH; }
 
+// Shape checks shared by the padded-batch and key-padding-mask entry points.
+attn_status_t check_padded_shape(int batch, int seqlen_q, int seqlen_k, int num_heads, int num_kv_heads,
+                                 int head_dim, float scale) {
+  if (batch < 0 || seqlen_q < 0 || seqlen_k < 0 || num_heads <= 0 || num_kv_heads <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(scale)) return ATTN_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
+  if ((long long)batch * seqlen_q * num_heads > kMaxRows || (long long)batch * seqlen_k * num_kv_heads > kMaxRows) {
+    return ATTN_ERR_UNSUPPORTED;
+  }
+  if (attn::varlen_grid_size(batch, seqlen_q, num_heads) > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -73,11 +87,16 @@ attn_status_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_hea
   return ATTN_OK;
 }
 
-attn_status_t attn_paged_decode(const void* q, const void* kv_cache, const int32_t* block_tables,
+}  // extern "C"
+
+namespace {
+
+attn_status_t paged_decode_impl(const void* q, const void* kv_cache, const int32_t* block_tables,
                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_blocks,
                                 int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_heads,
-                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float softmax_scale,
-                                void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t window,
+                                float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                                void* stream) {
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0) return ATTN_ERR_INVALID_ARG;
   if (num_heads <= 0 || num_kv_heads <= 0) return ATTN_ERR_INVALID_ARG;
   if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
@@ -92,13 +111,126 @@ attn_status_t attn_paged_decode(const void* q, const void* kv_cache, const int32
   }
   if ((long long)num_blocks * block_size * num_kv_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
   if ((long long)num_seqs * max_context_len >= (1LL << 30)) return ATTN_ERR_UNSUPPORTED;  // int32 token prefix
-  const attn::DecodePlan plan = attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len);
-  if (workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
-  if (plan.workspace_bytes > 0 && workspace == nullptr) return ATTN_ERR_INVALID_ARG;
+  const attn::DecodePlan need = attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len);
+  if (workspace_bytes < need.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (need.workspace_bytes > 0 && workspace == nullptr) return ATTN_ERR_INVALID_ARG;
+  // a window at least as long as the context is no window; a shorter one
+  // leaves at most window + 32 streamed keys per sequence, which sizes the splits
+  const int win = window >= 0 && window < max_context_len ? window : -1;
+  const attn::DecodePlan plan =
+      win < 0 ? need : attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, win + 32 < max_context_len
+                                                                                                   ? win + 32
+                                                                                                   : max_context_len);
   attn::DecodeArgs a{q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
                      max_context_len, num_heads, num_kv_heads, head_dim, block_size, softmax_scale, out, lse,
                      workspace};
+  a.window = win;
   return from_hip(attn::launch_paged_decode(a, plan, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status_t attn_paged_decode(const void* q, const void* kv_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, int32_t num_seqs, int32_t num_blocks,
+                                int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float softmax_scale,
+                                void* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return paged_decode_impl(q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
+                           max_context_len, num_heads, num_kv_heads, head_dim, block_size, -1, softmax_scale, out,
+                           lse, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_paged_decode_sliding_window(const void* q, const void* kv_cache, const int32_t* block_tables,
+                                               const int32_t* context_lens, int32_t num_seqs, int32_t num_blocks,
+                                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                               int32_t block_size, int32_t window, float softmax_scale, void* out,
+                                               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (window < 0) return ATTN_ERR_INVALID_ARG;
+  return paged_decode_impl(q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
+                           max_context_len, num_heads, num_kv_heads, head_dim, block_size, window, softmax_scale,
+                           out, lse, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_padded_fwd_workspace_size(int32_t batch, size_t* bytes) {
+  if (bytes == nullptr || batch < 0) return ATTN_ERR_INVALID_ARG;
+  *bytes = attn::padded_workspace_bytes(batch);
+  return ATTN_OK;
+}
+
+attn_status_t attn_padded_fwd(const void* q, const void* k, const void* v, const int32_t* q_lens,
+                              const int32_t* k_lens, int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                              int32_t causal, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  const attn_status_t st = check_padded_shape(batch, seqlen_q, seqlen_k, num_heads, num_kv_heads, head_dim,
+                                              softmax_scale);
+  if (st != ATTN_OK) return st;
+  if (batch == 0 || seqlen_q == 0) return ATTN_OK;
+  if (q == nullptr || out == nullptr || q_lens == nullptr || k_lens == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (seqlen_k > 0 && (k == nullptr || v == nullptr)) return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < attn::padded_workspace_bytes(batch)) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return ATTN_ERR_INVALID_ARG;
+  attn::VarlenArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.batch = batch;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale = softmax_scale;
+  a.causal = causal != 0;
+  a.out = out;
+  a.lse = lse;
+  return from_hip(attn::launch_padded_fwd(a, q_lens, k_lens, seqlen_q, seqlen_k, workspace, (hipStream_t)stream));
+}
+
+attn_status_t attn_masked_fwd_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, int32_t mask_queries,
+                                             size_t* bytes) {
+  if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (batch < 0 || seqlen_q < 0 || seqlen_k < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  *bytes = attn::plan_masked(batch, seqlen_q, seqlen_k, num_heads, num_kv_heads, head_dim, mask_queries != 0).bytes;
+  return ATTN_OK;
+}
+
+attn_status_t attn_masked_fwd(const void* q, const void* k, const void* v, const uint8_t* key_mask, int32_t batch,
+                              int32_t seqlen_q, int32_t seqlen_k, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, float softmax_scale, int32_t causal, int32_t mask_queries, void* out,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  const attn_status_t st = check_padded_shape(batch, seqlen_q, seqlen_k, num_heads, num_kv_heads, head_dim,
+                                              softmax_scale);
+  if (st != ATTN_OK) return st;
+  if (mask_queries != 0 && seqlen_q != seqlen_k) return ATTN_ERR_INVALID_ARG;
+  if (batch == 0 || seqlen_q == 0) return ATTN_OK;
+  if (q == nullptr || out == nullptr) return ATTN_ERR_INVALID_ARG;
+  if (seqlen_k > 0 && (k == nullptr || v == nullptr || key_mask == nullptr)) return ATTN_ERR_INVALID_ARG;
+  const attn::MaskedLayout l =
+      attn::plan_masked(batch, seqlen_q, seqlen_k, num_heads, num_kv_heads, head_dim, mask_queries != 0);
+  if (workspace_bytes < l.bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return ATTN_ERR_INVALID_ARG;
+  attn::VarlenArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.batch = batch;
+  a.num_heads = num_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.scale = softmax_scale;
+  a.causal = causal != 0;
+  a.out = out;
+  a.lse = lse;
+  if (seqlen_k == 0) {  // no key anywhere: every row is a padding row of length 0
+    return from_hip(attn::launch_padded_fwd(a, nullptr, nullptr, seqlen_q, 0, workspace, (hipStream_t)stream));
+  }
+  return from_hip(attn::launch_masked_fwd(a, key_mask, seqlen_q, seqlen_k, mask_queries != 0, l, workspace,
+                                          (hipStream_t)stream));
 }
 
 attn_status_t attn_paged_kv_write(const void* k, const void* v, const int32_t* slot_mapping, int32_t num_tokens,

@@ -27,9 +27,31 @@ struct VarlenArgs {
   const int32_t* block_tables = nullptr;
   const int32_t* context_lens = nullptr;
   int max_blocks_per_seq = 0, num_blocks = 0;
+  // padded documents (nullable): document b keeps only the first q_used[b]
+  // query rows and k_used[b] key rows of its cu_q / cu_k range
+  const int32_t* q_used = nullptr;
+  const int32_t* k_used = nullptr;
 };
 
 hipError_t launch_varlen_fwd(const VarlenArgs& a, hipStream_t stream);
+
+// Padded batch (padding.hip): base carries q, k, v, out, lse, batch, heads,
+// head_dim, scale and causal; q_lens / k_lens are the valid prefix lengths
+// (q_lens null: every row is padding). Workspace: the two strided cu arrays.
+size_t padded_workspace_bytes(int batch);
+hipError_t launch_padded_fwd(const VarlenArgs& base, const int32_t* q_lens, const int32_t* k_lens, int seqlen_q,
+                             int seqlen_k, void* workspace, hipStream_t stream);
+
+// Key-padding mask (padding.hip): byte offsets of the workspace pieces.
+struct MaskedLayout {
+  size_t cu_q, cu_k, count, idx, inv, k, v;  // always
+  size_t q, o, lse;                          // mask over the queries too
+  size_t bytes;
+};
+MaskedLayout plan_masked(int batch, int seqlen_q, int seqlen_k, int num_heads, int num_kv_heads, int head_dim,
+                         bool mask_queries);
+hipError_t launch_masked_fwd(const VarlenArgs& base, const uint8_t* key_mask, int seqlen_q, int seqlen_k,
+                             bool mask_queries, const MaskedLayout& l, void* workspace, hipStream_t stream);
 // head_dim 128: pipelined direct-to-LDS prefill (prefill_d128.hip)
 bool prefill_d128_supported(const VarlenArgs& a);
 hipError_t launch_prefill_d128(const VarlenArgs& a, hipStream_t stream);
@@ -64,6 +86,9 @@ struct DecodeArgs {
   // has cu_q[b+1] - cu_q[b] <= max_q new tokens; nullptr = one token each
   const int32_t* cu_q = nullptr;
   int total_q = 0;
+  // sliding window (single-token queries only): the query at position L - 1
+  // sees keys t >= L - 1 - window; -1 = no window
+  int window = -1;
 };
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
@@ -75,6 +100,7 @@ constexpr int kDecodeStreamWaves = 1024;  // 4 waves on each of MI355X's 256 CUs
 struct DecodeStreamPlan {
   int max_q, q_chunks, n_seg;
   size_t prefix_bytes;  // int32 [num_seqs + 1] token prefix sums
+  size_t skip_bytes;    // int32 [num_seqs] first streamed position (sliding window)
   size_t lse_bytes;     // fp32 [n_seg + num_seqs][max_q][num_heads] partial LSE
   size_t o_bytes;       // fp32 [n_seg + num_seqs][max_q][num_heads][128] partial O
   size_t workspace_bytes;

@@ -15,6 +15,9 @@
 // A split writes a normalised fp32 partial (O_s, LSE_s); a second kernel merges
 // the splits of each (sequence, head) in ascending order. A sequence that fits
 // in one split writes its final bf16 output directly.
+//
+// Sliding window: the splits cover the keys from the 32-token chunk holding
+// the window's first key to the end; keys below the window are masked.
 #include "attn_common.hpp"
 #include "launch.hpp"
 
@@ -97,12 +100,20 @@ struct DecodeChunk {
   }
 };
 
+// First key the single query at position ctx - 1 sees under a sliding window
+// of `window` preceding tokens (window < 0: no window).
+__device__ __forceinline__ int window_start(int ctx, int window) {
+  if (window < 0) return 0;
+  const int lo = ctx - 1 - window;
+  return lo > 0 ? lo : 0;
+}
+
 template <int D>
 __global__ __launch_bounds__(64 * kDecodeWaves) void paged_decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int num_seqs, int num_blocks, int max_blocks_per_seq,
     int max_context_len, int hq, int hkv, int split_tokens, int max_splits, int q_chunks, float c, uint16_t* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_lse, int window) {
   constexpr int VS = kDecodeChunk * 2 + 16;
   constexpr int VT_BYTES = D * VS;
   constexpr int OB = D / 16;  // 16-wide d blocks of the PV output
@@ -121,10 +132,14 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void paged_decode_split_kernel(
   // the host bound (<= max_blocks_per_seq * 128, checked on the host) keeps
   // every split index inside the workspace and every table index in the row
   const int ctx = clampi(context_lens[seq], 0, max_context_len);
-  const int t_begin = split * split_tokens;
-  if (t_begin >= ctx) return;
+  // keys [lo, ctx) are visible; the splits start at the 32-token chunk holding lo
+  const int lo = window_start(ctx, window);
+  const int skip = lo & ~(kDecodeChunk - 1);
+  const int n = ctx - skip;
+  if (split * split_tokens >= n) return;
+  const int t_begin = skip + split * split_tokens;
   const int t_end = ctx - t_begin < split_tokens ? ctx : t_begin + split_tokens;
-  const int nsplit = (ctx + split_tokens - 1) / split_tokens;
+  const int nsplit = (n + split_tokens - 1) / split_tokens;
 
   const int group = hq / hkv;
   const int n16 = lane & 15, g = lane >> 4;
@@ -187,12 +202,13 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void paged_decode_split_kernel(
       const int nv = t_end - t1;
       cur.load(base, base + v_plane, tok_stride, nv < kDecodeChunk ? nv : kDecodeChunk, lane);
     }
-    if (nvalid < kDecodeChunk) {
+    if (nvalid < kDecodeChunk || t0 < lo) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          if (kb * 16 + 4 * g + r >= nvalid) s[kb][r] = kNegInf;
+          const int i = kb * 16 + 4 * g + r;
+          if (i >= nvalid || t0 + i < lo) s[kb][r] = kNegInf;
         }
       }
     }
@@ -201,7 +217,7 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void paged_decode_split_kernel(
     mx = wave_xor_max(mx, 16);
     mx = wave_xor_max(mx, 32);
     const float m_new = fmaxf(m, mx);
-    const float alpha = hw_exp2((m - m_new) * c);  // m_new is finite: every chunk has a real token
+    const float alpha = hw_exp2((m - m_new) * c);  // m_new is finite: every chunk has a visible token
     const float ms = m_new * c;
     f32x8 pt;
     float rs = 0.f;
@@ -252,13 +268,14 @@ template <int D>
 __global__ __launch_bounds__(256) void paged_decode_combine_kernel(
     const int32_t* __restrict__ context_lens, int num_seqs, int max_context_len, int hq, int split_tokens,
     int max_splits, const float* __restrict__ part_o, const float* __restrict__ part_lse,
-    uint16_t* __restrict__ out, float* __restrict__ lse) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int window) {
   const int lane = threadIdx.x & 63;
   const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= (long)num_seqs * hq) return;
   const int seq = (int)(pair / hq), h = (int)(pair % hq);
   const int ctx = clampi(context_lens[seq], 0, max_context_len);
-  const int nsplit = (ctx + split_tokens - 1) / split_tokens;
+  const int n = ctx - (window_start(ctx, window) & ~(kDecodeChunk - 1));
+  const int nsplit = (n + split_tokens - 1) / split_tokens;
   uint16_t* orow = out + pair * D;
   if (ctx == 0) {
     for (int d = lane; d < D; d += 64) orow[d] = 0;
@@ -314,13 +331,14 @@ static hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipS
   hipLaunchKernelGGL((paged_decode_split_kernel<D>), dim3((unsigned)grid), dim3(64 * kDecodeWaves), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.kv_cache, a.block_tables, a.context_lens,
                      a.num_seqs, a.num_blocks, a.max_blocks_per_seq, a.max_context_len, a.num_heads, a.num_kv_heads,
-                     p.split_tokens, p.max_splits, p.q_chunks, c, (uint16_t*)a.out, a.lse, part_o, part_lse);
+                     p.split_tokens, p.max_splits, p.q_chunks, c, (uint16_t*)a.out, a.lse, part_o, part_lse,
+                     a.window);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long pairs = (long)a.num_seqs * a.num_heads;
   hipLaunchKernelGGL((paged_decode_combine_kernel<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream,
                      a.context_lens, a.num_seqs, a.max_context_len, a.num_heads, p.split_tokens,
-                     p.max_splits, part_o, part_lse, (uint16_t*)a.out, a.lse);
+                     p.max_splits, part_o, part_lse, (uint16_t*)a.out, a.lse, a.window);
   return hipGetLastError();
 }
 

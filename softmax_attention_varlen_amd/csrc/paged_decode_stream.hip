@@ -28,6 +28,11 @@
 // the last max_q positions, bottom-right causal) share one pass over its K/V;
 // plain decode is max_q = 1.
 //
+// Sliding window ([ASC] AscendAttentionBackendImpl._forward_fia_slidingwindow,
+// decode only): a sequence streams only its last window + 1 keys, from the
+// 32-token chunk that holds the first of them; the keys of that chunk below
+// the window are masked like the causal limit.
+//
 // Math per chunk (16x16x32 bf16 MFMA): S^T = K Q^T with K from LDS (A) and the
 // (token, head) columns (B); online softmax per column; O^T += V^T P^T
 // with V^T from transposing LDS reads (A) and P straight from the S^T
@@ -84,16 +89,36 @@ __device__ __forceinline__ int find_seq(const int32_t* prefix, int n, int pos, i
   return lo;
 }
 
-// Exclusive prefix sums of the clamped context lengths, prefix[num_seqs] = T.
+// Tokens a sequence puts on the stream. With a sliding window (window >= 0)
+// the single query at position L - 1 sees keys t >= L - 1 - window; the stream
+// then starts at that key rounded down to a whole 32-token chunk (*skip), so
+// chunks stay inside one 128-token cache block, and the keys below the window
+// in that first chunk are masked by the kernel.
+constexpr int kNoLowerLimit = -(1 << 30);  // below every key index (windows are at most 2^30)
+
+__device__ __forceinline__ int stream_tokens(int ctx_raw, int max_context_len, int window, int* skip) {
+  const int len = clampi(ctx_raw, 0, max_context_len);
+  int sk = 0;
+  if (window >= 0) {
+    const int lo = len - 1 - window;
+    sk = lo > 0 ? (lo & ~(kSChunk - 1)) : 0;
+  }
+  *skip = sk;
+  return len - sk;
+}
+
+// Exclusive prefix sums of the streamed token counts, prefix[num_seqs] = T;
+// skip[s] (when windowed) is the first streamed position of sequence s.
 __global__ __launch_bounds__(1024) void decode_prefix_kernel(const int32_t* __restrict__ context_lens, int num_seqs,
-                                                             int max_context_len, int32_t* __restrict__ prefix) {
+                                                             int max_context_len, int window,
+                                                             int32_t* __restrict__ prefix, int32_t* __restrict__ skip) {
   __shared__ int part[1024];
   const int t = threadIdx.x;
   const int per = (num_seqs + 1023) / 1024;
   const int b = t * per < num_seqs ? t * per : num_seqs;
   const int e = b + per < num_seqs ? b + per : num_seqs;
-  int sum = 0;
-  for (int i = b; i < e; ++i) sum += clampi(context_lens[i], 0, max_context_len);
+  int sum = 0, sk;
+  for (int i = b; i < e; ++i) sum += stream_tokens(context_lens[i], max_context_len, window, &sk);
   part[t] = sum;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {  // inclusive Hillis-Steele scan
@@ -105,7 +130,8 @@ __global__ __launch_bounds__(1024) void decode_prefix_kernel(const int32_t* __re
   int run = part[t] - sum;
   for (int i = b; i < e; ++i) {
     prefix[i] = run;
-    run += clampi(context_lens[i], 0, max_context_len);
+    run += stream_tokens(context_lens[i], max_context_len, window, &sk);
+    if (skip != nullptr) skip[i] = sk;
   }
   if (t == 1023) prefix[num_seqs] = part[1023];
 }
@@ -120,7 +146,7 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
     const int32_t* __restrict__ prefix, int num_seqs, int num_blocks, int max_blocks_per_seq, int hq, int hkv,
     int q_chunks, int n_seg, float c, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_lse, const int32_t* __restrict__ cu_q, int max_q,
-    int total_q) {
+    int total_q, const int32_t* __restrict__ skip, int window) {
   __shared__ __attribute__((aligned(1024))) char smem[kSWaves * kSWaveLds];
   // every cursor below is wave-uniform (scalar registers, scalar loads): no
   // compiler-visible vector load may sit in the streaming loop, since the
@@ -164,6 +190,7 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
   int ls = s0;
   int lbase = prefix[ls];
   int lctx = prefix[ls + 1] - lbase;
+  int lskip = skip != nullptr ? skip[ls] : 0;  // cache position of stream token 0
   int lc = (seg_begin - lbase) / kSChunk;
   int lc_end = ((seg_end < lbase + lctx ? seg_end : lbase + lctx) - lbase - 1) / kSChunk;
   bool lvalid = true;
@@ -171,7 +198,7 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
   // issue the loader's chunk into `stage` and advance the cursor
   auto issue = [&](int stage) {
     const int t0 = lc * kSChunk;
-    int blk = block_tables[(long)ls * max_blocks_per_seq + (t0 >> 7)];
+    int blk = block_tables[(long)ls * max_blocks_per_seq + ((t0 + lskip) >> 7)];
     blk = clampi(blk, 0, num_blocks - 1);
     const uint16_t* kb = kv + (long)blk * blk_elems + (long)hk * kSD;
     const uint32_t st = ring + stage * kSStage;
@@ -179,7 +206,7 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
     for (int b = 0; b < 8; ++b) {
       int t = t0 + b + 8 * (lane >> 4);
       t = t < lctx ? t : lctx - 1;  // rows past the context re-read the last one (same block)
-      const uint32_t voff = (uint32_t)(t & 127) * row_bytes + (uint32_t)(lane & 15) * 16u;
+      const uint32_t voff = (uint32_t)((t + lskip) & 127) * row_bytes + (uint32_t)(lane & 15) * 16u;
       load_lds16(kb, voff, st + b * kSBlk);
       load_lds16(kb + v_plane, voff, st + kSHalf + b * kSBlk);
     }
@@ -194,6 +221,7 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
       } while (ls < num_seqs && lctx == 0 && lbase < seg_end);
       lvalid = ls < num_seqs && lbase < seg_end;
       if (lvalid) {
+        lskip = skip != nullptr ? skip[ls] : 0;
         lc = 0;
         lc_end = ((seg_end < lbase + lctx ? seg_end : lbase + lctx) - lbase - 1) / kSChunk;
       }
@@ -217,7 +245,7 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
   bf16x8 qb[4];
   f32x4 o[8];
   float m = kNegInf, l = 0.f;
-  int q_row = 0, lim = 0, lim_min = 0;
+  int q_row = 0, lim = 0, lim_min = 0, lo_lim = 0, lo_max = 0;
   bool live = false;
   for (int j = 0;; ++j) {
     if (fresh) {
@@ -234,6 +262,10 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
       q_row = live ? q_first + qi : 0;  // row 0 exists whenever this kernel runs
       lim = qi + cctx - lq;
       lim_min = cctx - lq;
+      // sliding window: keys below lim - window are hidden (the stream's first
+      // chunk may start up to 31 keys early); lo_max is the largest such bound
+      lo_lim = window >= 0 ? lim - window : kNoLowerLimit;
+      lo_max = window >= 0 ? cctx - 1 - window : kNoLowerLimit;
       const uint16_t* qrow = q + ((long)q_row * hq + h) * kSD;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -266,13 +298,13 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
       }
     }
     const int t0 = cc * kSChunk;
-    if (t0 < t_lo || t0 + kSChunk > t_hi || t0 + kSChunk - 1 > lim_min) {
+    if (t0 < t_lo || t0 + kSChunk > t_hi || t0 + kSChunk - 1 > lim_min || t0 < lo_max) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = t0 + kb * 16 + 4 * G + r;
-          if (t < t_lo || t >= t_hi || t > lim) s[kb][r] = kNegInf;
+          if (t < t_lo || t >= t_hi || t > lim || t < lo_lim) s[kb][r] = kNegInf;
         }
       }
     }
@@ -415,20 +447,23 @@ DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_head
   const int lanes = num_kv_heads * p.q_chunks;
   p.n_seg = kDecodeStreamWaves / lanes > 1 ? kDecodeStreamWaves / lanes : 1;
   p.prefix_bytes = ((size_t)(num_seqs + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
+  p.skip_bytes = ((size_t)num_seqs * sizeof(int32_t) + 255) & ~(size_t)255;
   const size_t slots = (size_t)(p.n_seg + num_seqs) * p.max_q * num_heads;
   p.lse_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
   p.o_bytes = slots * kSD * sizeof(float);
-  p.workspace_bytes = p.prefix_bytes + p.lse_bytes + p.o_bytes;
+  p.workspace_bytes = p.prefix_bytes + p.skip_bytes + p.lse_bytes + p.o_bytes;
   return p;
 }
 
 hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, hipStream_t stream) {
+  if (a.window >= 0 && a.cu_q != nullptr) return hipErrorInvalidValue;  // windows: one query token each
   int32_t* prefix = (int32_t*)a.workspace;
-  float* part_lse = (float*)((char*)a.workspace + p.prefix_bytes);
-  float* part_o = (float*)((char*)a.workspace + p.prefix_bytes + p.lse_bytes);
+  int32_t* skip = a.window >= 0 ? (int32_t*)((char*)a.workspace + p.prefix_bytes) : nullptr;
+  float* part_lse = (float*)((char*)a.workspace + p.prefix_bytes + p.skip_bytes);
+  float* part_o = (float*)((char*)a.workspace + p.prefix_bytes + p.skip_bytes + p.lse_bytes);
   const int total_q = a.cu_q != nullptr ? a.total_q : a.num_seqs;
   hipLaunchKernelGGL(decode_prefix_kernel, dim3(1), dim3(1024), 0, stream, a.context_lens, a.num_seqs,
-                     a.max_context_len, prefix);
+                     a.max_context_len, a.window, prefix, skip);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long waves = (long)p.n_seg * a.num_kv_heads * p.q_chunks;
@@ -436,7 +471,7 @@ hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, 
                      dim3(64 * kSWaves), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.kv_cache,
                      a.block_tables, prefix, a.num_seqs, a.num_blocks, a.max_blocks_per_seq, a.num_heads,
                      a.num_kv_heads, p.q_chunks, p.n_seg, a.scale * kLog2e, (uint16_t*)a.out, a.lse, part_o,
-                     part_lse, a.cu_q, p.max_q, total_q);
+                     part_lse, a.cu_q, p.max_q, total_q, skip, a.window);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long pairs = (long)a.num_seqs * p.max_q * a.num_heads;

@@ -34,14 +34,16 @@ struct Ring {
 
 // PAGED: keys come from a paged cache (k, v = its K and V planes) through
 // block_tables, with context_lens[doc] (clamped to max_len_k) keys per
-// document; otherwise from contiguous rows delimited by cu_k.
+// document; otherwise from contiguous rows delimited by cu_k. q_used / k_used
+// (nullable) cut each document to a valid prefix of its rows.
 template <bool CAUSAL, bool PAGED, int NW, int NS>
 __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int total_q, int total_k,
     int tiles_per_doc, int hq, int hkv, int n_items, int per_xcd, float c, uint16_t* __restrict__ out,
     float* __restrict__ lse, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
-    int max_blocks_per_seq, int num_blocks, int max_len_k) {
+    int max_blocks_per_seq, int num_blocks, int max_len_k, const int32_t* __restrict__ q_used,
+    const int32_t* __restrict__ k_used) {
   using R = Ring<NW>;
   constexpr int BM = 32 * NW;
   static_assert(NS == 3 || NS == 4, "the load-count waits below cover 3- and 4-stage rings");
@@ -68,13 +70,15 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
   const int h = hk * group + qh;
 
   const int q0 = clampi(cu_q[doc], 0, total_q);
-  const int q1 = clampi(cu_q[doc + 1], q0, total_q);
+  int q1 = clampi(cu_q[doc + 1], q0, total_q);
+  if (q_used != nullptr) q1 = q0 + clampi(q_used[doc], 0, q1 - q0);  // valid prefix of the slot
   int k0 = 0, len_k;
   if (PAGED) {
     len_k = clampi(context_lens[doc], 0, max_len_k);
   } else {
     k0 = clampi(cu_k[doc], 0, total_k);
     len_k = clampi(cu_k[doc + 1], k0, total_k) - k0;
+    if (k_used != nullptr) len_k = clampi(k_used[doc], 0, len_k);
   }
   const int len_q = q1 - q0;
   const int m0 = tile * BM;
@@ -197,7 +201,8 @@ static void launch_prefill_d128_t(const VarlenArgs& a, int tiles, long n_items, 
                      dim3(64 * kPrefillWaves), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch, a.total_q, a.total_k, tiles, a.num_heads,
                      a.num_kv_heads, (int)n_items, (int)per_xcd, c, (uint16_t*)a.out, a.lse, a.block_tables,
-                     a.context_lens, a.max_blocks_per_seq, a.num_blocks, a.max_seqlen_k);
+                     a.context_lens, a.max_blocks_per_seq, a.num_blocks, a.max_seqlen_k, a.q_used,
+                     PAGED ? nullptr : a.k_used);
 }
 
 hipError_t launch_prefill_d128(const VarlenArgs& a, hipStream_t stream) {

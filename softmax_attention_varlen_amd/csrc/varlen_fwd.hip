@@ -21,14 +21,15 @@ constexpr int kVarlenThreads = 256;
 
 // PAGED: keys come from a paged cache (k, v = its K and V planes) through
 // block_tables, with context_lens[doc] (clamped to max_len_k) keys per
-// document; otherwise from contiguous rows delimited by cu_k.
+// document; otherwise from contiguous rows delimited by cu_k. q_used / k_used
+// (nullable) cut each document to a valid prefix of its rows.
 template <int D, bool CAUSAL, bool PAGED>
 __global__ __launch_bounds__(kVarlenThreads, (D <= 128 ? 2 : 1)) void varlen_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int total_q, int total_k,
     int tiles_per_doc, int hq, int hkv, float c, uint16_t* __restrict__ out, float* __restrict__ lse,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens, int max_blocks_per_seq,
-    int num_blocks, int max_len_k) {
+    int num_blocks, int max_len_k, const int32_t* __restrict__ q_used, const int32_t* __restrict__ k_used) {
   using Tile = KVTile<D, kVarlenBN, kVarlenThreads>;
   __shared__ __attribute__((aligned(16))) char smem[Tile::BYTES];
 
@@ -41,13 +42,15 @@ __global__ __launch_bounds__(kVarlenThreads, (D <= 128 ? 2 : 1)) void varlen_fwd
   const int tile = tiles_per_doc - 1 - y / batch;
 
   const int q0 = clampi(cu_q[doc], 0, total_q);
-  const int q1 = clampi(cu_q[doc + 1], q0, total_q);
+  int q1 = clampi(cu_q[doc + 1], q0, total_q);
+  if (q_used != nullptr) q1 = q0 + clampi(q_used[doc], 0, q1 - q0);  // valid prefix of the slot
   int k0 = 0, len_k;
   if (PAGED) {
     len_k = clampi(context_lens[doc], 0, max_len_k);
   } else {
     k0 = clampi(cu_k[doc], 0, total_k);
     len_k = clampi(cu_k[doc + 1], k0, total_k) - k0;
+    if (k_used != nullptr) len_k = clampi(k_used[doc], 0, len_k);
   }
   const int len_q = q1 - q0;
   const int m0 = tile * kVarlenBM;
@@ -128,12 +131,13 @@ static hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL((varlen_fwd_kernel<D, CAUSAL, true>), dim3((unsigned)grid), dim3(kVarlenThreads), 0, stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch,
                        a.total_q, a.total_k, tiles, a.num_heads, a.num_kv_heads, c, (uint16_t*)a.out, a.lse,
-                       a.block_tables, a.context_lens, a.max_blocks_per_seq, a.num_blocks, a.max_seqlen_k);
+                       a.block_tables, a.context_lens, a.max_blocks_per_seq, a.num_blocks, a.max_seqlen_k, a.q_used,
+                       nullptr);
   } else {
     hipLaunchKernelGGL((varlen_fwd_kernel<D, CAUSAL, false>), dim3((unsigned)grid), dim3(kVarlenThreads), 0,
                        stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.cu_q, a.cu_k,
                        a.batch, a.total_q, a.total_k, tiles, a.num_heads, a.num_kv_heads, c, (uint16_t*)a.out,
-                       a.lse, nullptr, nullptr, 0, 0, 0);
+                       a.lse, nullptr, nullptr, 0, 0, 0, a.q_used, a.k_used);
   }
   return hipGetLastError();
 }

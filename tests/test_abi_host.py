@@ -189,3 +189,84 @@ def test_paged_prefill_workspace_query():
     n1 = sav.attn_paged_prefill_workspace_size(64, 32, 8, 128, 1, 32768)
     assert n4 > n1 > 0
     assert n1 == sav.attn_paged_decode_workspace_size(64, 32, 8, 128, 32768)
+
+
+def _window(**kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, ctx=FAKE, nseq=4, nblocks=10, mbps=4, maxctx=500, hq=8, hkv=2, d=128,
+             bs=128, window=100, scale=0.1, out=FAKE, lse=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib().attn_paged_decode_sliding_window(a["q"], a["kv"], a["bt"], a["ctx"], a["nseq"], a["nblocks"],
+                                                  a["mbps"], a["maxctx"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                                  a["window"], a["scale"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                                  None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(window=-1), INVALID), (dict(bs=64), UNSUPPORTED), (dict(d=100), UNSUPPORTED), (dict(maxctx=513), INVALID),
+    (dict(q=None), INVALID), (dict(out=None), INVALID), (dict(ctx=None), INVALID), (dict(wsb=0), WS_SMALL),
+    (dict(scale=float("nan")), INVALID),
+])
+def test_sliding_window_validation(kw, code):
+    assert _window(**kw) == code
+
+
+def test_sliding_window_empty_is_noop():
+    assert _window(nseq=0, q=None, out=None, ws=None, wsb=0) == OK
+
+
+def _padded(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ql=FAKE, kl=FAKE, b=2, sq=100, sk=80, hq=8, hkv=2, d=128, scale=0.1, causal=0,
+             out=FAKE, lse=None, ws=FAKE, wsb=1 << 20)
+    a.update(kw)
+    return lib().attn_padded_fwd(a["q"], a["k"], a["v"], a["ql"], a["kl"], a["b"], a["sq"], a["sk"], a["hq"],
+                                 a["hkv"], a["d"], a["scale"], a["causal"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=80), UNSUPPORTED), (dict(hq=6, hkv=4), UNSUPPORTED), (dict(b=-1), INVALID), (dict(sq=-1), INVALID),
+    (dict(sk=-2), INVALID), (dict(hq=0), INVALID), (dict(scale=0.0), INVALID), (dict(q=None), INVALID),
+    (dict(out=None), INVALID), (dict(ql=None), INVALID), (dict(kl=None), INVALID), (dict(k=None), INVALID),
+    (dict(wsb=0), WS_SMALL), (dict(ws=None), INVALID), (dict(b=70000, sq=70000), UNSUPPORTED),
+])
+def test_padded_validation(kw, code):
+    assert _padded(**kw) == code
+
+
+@pytest.mark.parametrize("kw", [dict(b=0), dict(sq=0)])
+def test_padded_empty_is_noop(kw):
+    assert _padded(q=None, out=None, ws=None, wsb=0, **kw) == OK
+
+
+def _masked(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, mask=FAKE, b=2, sq=100, sk=100, hq=8, hkv=2, d=128, scale=0.1, causal=0, mq=1,
+             out=FAKE, lse=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return lib().attn_masked_fwd(a["q"], a["k"], a["v"], a["mask"], a["b"], a["sq"], a["sk"], a["hq"], a["hkv"],
+                                 a["d"], a["scale"], a["causal"], a["mq"], a["out"], a["lse"], a["ws"], a["wsb"],
+                                 None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sk=90), INVALID), (dict(d=80), UNSUPPORTED), (dict(hq=6, hkv=4), UNSUPPORTED), (dict(b=-1), INVALID),
+    (dict(scale=-1.0), INVALID), (dict(q=None), INVALID), (dict(mask=None), INVALID), (dict(v=None), INVALID),
+    (dict(out=None), INVALID), (dict(wsb=0), WS_SMALL), (dict(ws=None), INVALID),
+])
+def test_masked_validation(kw, code):
+    assert _masked(**kw) == code
+
+
+def test_masked_empty_is_noop():
+    assert _masked(b=0, q=None, out=None, ws=None, wsb=0) == OK
+    assert _masked(sq=0, sk=0, q=None, out=None, ws=None, wsb=0) == OK
+
+
+def test_padding_workspace_queries():
+    assert sav.attn_padded_fwd_workspace_size(4) >= 2 * 5 * 4
+    cross = sav.attn_masked_fwd_workspace_size(2, 4096, 512, 24, 24, 128, False)
+    self_ = sav.attn_masked_fwd_workspace_size(2, 512, 512, 24, 24, 128, True)
+    # packed k and v at least; self-attention also packs q and the output
+    assert cross >= 2 * (2 * 512 * 24 * 128 * 2)
+    assert self_ >= 4 * (2 * 512 * 24 * 128 * 2)
+    with pytest.raises(sav.AttnError):
+        sav.attn_padded_fwd_workspace_size(-1)

@@ -307,3 +307,78 @@ def config5() -> VideoCase:
     """Video block-sparse: 16x32x32 latent, (4,4,4) tiles (256 tiles of 64), 12 heads, D 128, top-32."""
     return video_case((16, 32, 32), num_heads=12, head_dim=128, topk=32, seed=5,
                       name="video-block-sparse-16x32x32-t444-h12-d128-top32")
+
+
+SLIDING_WINDOW = 4096  # tokens before the query that stay visible
+
+
+def config8() -> PagedCase:
+    """Sliding-window decode: the decode workload (64 contexts of 1k..32k over
+    a shuffled block pool, 32/8 heads, D=128) with a window of 4096 preceding
+    tokens (the window length of common sliding-window decoders)."""
+    c = config4()
+    c.name = "swa-decode-64seq-ctx1k-32k-w4096-h32kv8-d128"
+    return c
+
+
+@dataclass
+class PaddedCase:
+    name: str
+    q: torch.Tensor  # [B, Sq, Hq, D] bf16
+    k: torch.Tensor  # [B, Sk, Hkv, D]
+    v: torch.Tensor  # [B, Sk, Hkv, D]
+    q_lens: np.ndarray  # int32 [B] valid prefix lengths (padded batch)
+    k_lens: np.ndarray
+    key_mask: np.ndarray  # uint8 [B, Sk] (key-padding mask)
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    causal: bool
+    scale: float
+    seed: int
+
+
+def padded_case(batch, seqlen_q, seqlen_k, *, num_heads, num_kv_heads, head_dim, seed, q_lens=None, k_lens=None,
+                key_mask=None, causal=False, name="padded") -> PaddedCase:
+    """A padded batch with N(0, 1) rows everywhere (padding rows included, so a
+    kernel that reads them is caught). Valid lengths default to full; the key
+    mask defaults to the key prefixes."""
+    ql = np.full(batch, seqlen_q) if q_lens is None else np.asarray(q_lens)
+    kl = np.full(batch, seqlen_k) if k_lens is None else np.asarray(k_lens)
+    if key_mask is None:
+        key_mask = (np.arange(seqlen_k)[None, :] < kl[:, None]).astype(np.uint8)
+    return PaddedCase(
+        name=name,
+        q=randn_bf16((batch, seqlen_q, num_heads, head_dim), 1000 * seed + 0),
+        k=randn_bf16((batch, seqlen_k, num_kv_heads, head_dim), 1000 * seed + 1),
+        v=randn_bf16((batch, seqlen_k, num_kv_heads, head_dim), 1000 * seed + 2),
+        q_lens=ql.astype(np.int32),
+        k_lens=kl.astype(np.int32),
+        key_mask=np.asarray(key_mask, dtype=np.uint8),
+        num_heads=num_heads,
+        num_kv_heads=num_kv_heads,
+        head_dim=head_dim,
+        causal=causal,
+        scale=1.0 / math.sqrt(head_dim),
+        seed=seed,
+    )
+
+
+def config9() -> PaddedCase:
+    """Cross-attention under a text padding mask (DiT text conditioning): 2
+    latent sequences of 4096 query tokens attend 512 text tokens whose real
+    count is uniform in [64, 512] (the rest are padding), 24 heads, D=128."""
+    rng = np.random.default_rng(9)
+    kl = rng.integers(64, 513, 2)
+    return padded_case(2, 4096, 512, num_heads=24, num_kv_heads=24, head_dim=128, seed=9, k_lens=kl,
+                       name="masked-cross-b2-q4096-k512-h24-d128")
+
+
+def config10() -> PaddedCase:
+    """Padded batch (packed padding): 4 sequences padded to 4096 tokens with
+    valid lengths uniform in [1024, 4096], non-causal self-attention, 24 heads,
+    D=128."""
+    rng = np.random.default_rng(10)
+    ln = rng.integers(1024, 4097, 4)
+    return padded_case(4, 4096, 4096, num_heads=24, num_kv_heads=24, head_dim=128, seed=10, q_lens=ln, k_lens=ln,
+                       name="padded-b4-s4096-valid1k-4k-h24-d128")
