@@ -55,6 +55,9 @@ TRAFFIC = {
                       "write_kib": 87201.8, "sources": _PREFILL_SRC, "sha256": "7b72c5eccb5c4b2b"},
     "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445745.0, "write_kib": 12148.7,
              "sources": ["paged_decode_stream.hip", "attn_common.hpp"], "sha256": "e954fcbfba207e55"},
+    "swa": {"kernel": "paged_decode_stream_kernel"},
+    "masked": {"kernel": "prefill_d128_kernel<false,false,8,3>"},
+    "padded": {"kernel": "prefill_d128_kernel<false,false,8,3>"},
 }
 
 
@@ -111,6 +114,22 @@ def paged_bytes(case) -> float:
     kv = float(case.context_lens.astype(np.int64).sum()) * case.num_kv_heads * case.head_dim * 2 * 2
     qo = 2.0 * case.num_seqs * case.num_heads * case.head_dim * 2
     return kv + qo + case.block_tables.nbytes + case.context_lens.nbytes
+
+
+def window_bytes(case, window: int) -> float:
+    """K and V bytes of the keys inside each sequence's window, plus Q, O,
+    block tables and lengths."""
+    keys = np.minimum(case.context_lens.astype(np.int64), window + 1).sum()
+    kv = float(keys) * case.num_kv_heads * case.head_dim * 2 * 2
+    qo = 2.0 * case.num_seqs * case.num_heads * case.head_dim * 2
+    return kv + qo + case.block_tables.nbytes + case.context_lens.nbytes
+
+
+def padded_flops(case, q_rows, k_rows) -> float:
+    """4 * D flops per visible (query, key) pair and query head: q_rows[b]
+    real query rows attend k_rows[b] real keys (non-causal)."""
+    pairs = float((np.asarray(q_rows, dtype=np.int64) * np.asarray(k_rows, dtype=np.int64)).sum())
+    return 4.0 * case.head_dim * case.num_heads * pairs
 
 
 def paged_prefill_flops(case) -> float:
@@ -174,7 +193,7 @@ def bench_varlen(case, steps, warmup, with_lse=True):
     return ms, varlen_flops(case)
 
 
-def bench_paged(case, steps, warmup):
+def bench_paged(case, steps, warmup, window=None):
     dev = torch.device("cuda")
     q, kv = case.q.to(dev), case.kv_cache.to(dev)
     bt = torch.from_numpy(case.block_tables).to(dev)
@@ -186,11 +205,42 @@ def bench_paged(case, steps, warmup):
                      dtype=torch.uint8, device=dev)
 
     def step():
-        sav.attn_paged_decode(q, kv, bt, cl, case.max_context_len, case.scale, out=out, lse=lse, workspace=ws)
+        sav.attn_paged_decode(q, kv, bt, cl, case.max_context_len, case.scale, out=out, lse=lse, workspace=ws,
+                              window=window)
 
     ms = time_steps(step, steps, warmup)
     del kv
-    return ms, paged_bytes(case)
+    return ms, (paged_bytes(case) if window is None else window_bytes(case, window))
+
+
+def bench_padded(case, steps, warmup, masked: bool):
+    """attn_masked_fwd (key mask, cross-attention) or attn_padded_fwd (valid
+    prefixes): the whole entry call, its gathers and fills included."""
+    dev = torch.device("cuda")
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((case.num_heads, q.shape[0] * q.shape[1]), dtype=torch.float32, device=dev)
+    if masked:
+        mask = torch.from_numpy(case.key_mask).to(dev)
+        ws = torch.empty(sav.attn_masked_fwd_workspace_size(q.shape[0], q.shape[1], k.shape[1], case.num_heads,
+                                                            case.num_kv_heads, case.head_dim, False),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            sav.attn_masked_fwd(q, k, v, mask, case.scale, case.causal, mask_queries=False, out=out, lse=lse,
+                                workspace=ws)
+
+        flops = padded_flops(case, np.full(q.shape[0], q.shape[1]), case.key_mask.sum(1))
+    else:
+        ql = torch.from_numpy(case.q_lens).to(dev)
+        kl = torch.from_numpy(case.k_lens).to(dev)
+        ws = torch.empty(sav.attn_padded_fwd_workspace_size(q.shape[0]), dtype=torch.uint8, device=dev)
+
+        def step():
+            sav.attn_padded_fwd(q, k, v, ql, kl, case.scale, case.causal, out=out, lse=lse, workspace=ws)
+
+        flops = padded_flops(case, case.q_lens, case.k_lens)
+    return time_steps(step, steps, warmup), flops
 
 
 def bench_paged_prefill(case, steps, warmup):
@@ -293,7 +343,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse", "paged_prefill", "spec", "copy"],
+    ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse", "paged_prefill", "spec", "swa", "masked",
+                                       "padded", "copy"],
                     default=None,
                     help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
                          "copy, the reference that scales the HBM byte counters")
@@ -378,6 +429,26 @@ def main():
                           "roofline": roofline("spec", "hbm", gbs, nbytes)})
         del case
         torch.cuda.empty_cache()
+
+    if args.only in (None, "swa") and not (args.only is None and args.no_secondary):
+        case = workloads.config8()
+        ms, nbytes = bench_paged(case, args.steps, args.warmup, window=workloads.SLIDING_WINDOW)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"{case.name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+        secondary.append({"workload": case.name, "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
+                          "roofline": roofline("swa", "hbm", gbs, nbytes)})
+        del case
+        torch.cuda.empty_cache()
+    for name, cfg, masked in (("masked", workloads.config9, True), ("padded", workloads.config10, False)):
+        if args.only in (None, name) and not (args.only is None and args.no_secondary):
+            case = cfg()
+            ms, flops = bench_padded(case, args.steps, args.warmup, masked)
+            tf = flops / (ms * 1e-3) / 1e12
+            log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s")
+            secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+                              "roofline": roofline(name, "mfma", tf, flops)})
+            del case
+            torch.cuda.empty_cache()
 
     if head is None:  # a single secondary workload was asked for
         print(json.dumps({"metric": "attention throughput", "secondary": secondary}))

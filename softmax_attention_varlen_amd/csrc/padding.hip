@@ -22,13 +22,15 @@
 namespace attn {
 namespace {
 
-// cu_q[b] = b * seqlen_q, cu_k[b] = b * seqlen_k for b = 0..batch.
-__global__ __launch_bounds__(256) void strided_cu_kernel(int32_t* __restrict__ cu_q, int32_t* __restrict__ cu_k,
-                                                         int batch, int seqlen_q, int seqlen_k) {
-  const int b = (int)(blockIdx.x * blockDim.x + threadIdx.x);
-  if (b > batch) return;
-  cu_q[b] = b * seqlen_q;
-  cu_k[b] = b * seqlen_k;
+// The strided document bounds of a padded batch: cu_q[b] = b * seqlen_q,
+// cu_k[b] = b * seqlen_k for b = 0..batch (written by the first threads of the
+// kernels below, ahead of the attention launch on the same stream).
+__device__ __forceinline__ void write_strided_cu(long t, int32_t* cu_q, int32_t* cu_k, int batch, int seqlen_q,
+                                                 int seqlen_k) {
+  if (t <= batch) {
+    cu_q[t] = (int32_t)(t * seqlen_q);
+    cu_k[t] = (int32_t)(t * seqlen_k);
+  }
 }
 
 __device__ __forceinline__ void zero_row(uint16_t* row, int elems, int lane) {
@@ -43,7 +45,9 @@ __device__ __forceinline__ void copy_row(const uint16_t* src, uint16_t* dst, int
 // is null): zero output and LSE = -inf (LSE layout [Hq][batch * seqlen]).
 __global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict__ used, int batch, int seqlen,
                                                        int hq, int head_dim, uint16_t* __restrict__ out,
-                                                       float* __restrict__ lse) {
+                                                       float* __restrict__ lse, int32_t* __restrict__ cu_q,
+                                                       int32_t* __restrict__ cu_k, int seqlen_k) {
+  write_strided_cu((long)blockIdx.x * 256 + threadIdx.x, cu_q, cu_k, batch, seqlen, seqlen_k);
   const int lane = threadIdx.x & 63;
   const long rows = (long)batch * seqlen;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -61,9 +65,12 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(const int32_t* __restrict
 // tokens or -1.
 __global__ __launch_bounds__(256) void mask_compact_kernel(const uint8_t* __restrict__ mask, int s,
                                                            int32_t* __restrict__ idx, int32_t* __restrict__ inv,
-                                                           int32_t* __restrict__ count) {
+                                                           int32_t* __restrict__ count, int32_t* __restrict__ cu_q,
+                                                           int32_t* __restrict__ cu_k, int batch, int seqlen_q) {
   __shared__ int wave_count[4];
   const long b = blockIdx.x;
+  if (threadIdx.x == 0) write_strided_cu(b, cu_q, cu_k, batch, seqlen_q, s);
+  if (threadIdx.x == 1 && b + 1 == batch) write_strided_cu(batch, cu_q, cu_k, batch, seqlen_q, s);
   const uint8_t* m = mask + b * s;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   int carry = 0;  // real tokens before this pass (the same in every thread)
@@ -86,11 +93,16 @@ __global__ __launch_bounds__(256) void mask_compact_kernel(const uint8_t* __rest
   if (tid == 0) count[b] = carry;
 }
 
-// dst row b*s + j = src row b*s + idx[b*s + j] for j < count[b].
-__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ src,
+// dst row b*s + j = src row b*s + idx[b*s + j] for j < count[b]; blockIdx.y
+// picks the (src, dst) pair, so k and v move in one launch.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ src0,
+                                                          const uint16_t* __restrict__ src1,
                                                           const int32_t* __restrict__ idx,
                                                           const int32_t* __restrict__ count, int batch, int s,
-                                                          int row_elems, uint16_t* __restrict__ dst) {
+                                                          int row_elems, uint16_t* __restrict__ dst0,
+                                                          uint16_t* __restrict__ dst1) {
+  const uint16_t* src = blockIdx.y == 0 ? src0 : src1;
+  uint16_t* dst = blockIdx.y == 0 ? dst0 : dst1;
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= (long)batch * s) return;
@@ -136,13 +148,10 @@ hipError_t launch_padded_fwd(const VarlenArgs& base, const int32_t* q_lens, cons
                              int seqlen_k, void* workspace, hipStream_t stream) {
   int32_t* cu_q = (int32_t*)workspace;
   int32_t* cu_k = (int32_t*)((char*)workspace + align256((size_t)(base.batch + 1) * sizeof(int32_t)));
-  hipLaunchKernelGGL(strided_cu_kernel, dim3((unsigned)((base.batch + 1 + 255) / 256)), dim3(256), 0, stream, cu_q,
-                     cu_k, base.batch, seqlen_q, seqlen_k);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(pad_rows_kernel, dim3(row_grid((long)base.batch * seqlen_q)), dim3(256), 0, stream, q_lens,
-                     base.batch, seqlen_q, base.num_heads, base.head_dim, (uint16_t*)base.out, base.lse);
-  e = hipGetLastError();
+                     base.batch, seqlen_q, base.num_heads, base.head_dim, (uint16_t*)base.out, base.lse, cu_q, cu_k,
+                     seqlen_k);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || q_lens == nullptr) return e;  // no valid prefix: padding rows only
   VarlenArgs a = base;
   a.cu_q = cu_q;
@@ -194,15 +203,10 @@ hipError_t launch_masked_fwd(const VarlenArgs& base, const uint8_t* key_mask, in
   uint16_t* vc = (uint16_t*)(ws + l.v);
   const int batch = base.batch;
   const int kv_elems = base.num_kv_heads * base.head_dim, q_elems = base.num_heads * base.head_dim;
-  hipLaunchKernelGGL(strided_cu_kernel, dim3((unsigned)((batch + 1 + 255) / 256)), dim3(256), 0, stream, cu_q, cu_k,
-                     batch, seqlen_q, seqlen_k);
   hipLaunchKernelGGL(mask_compact_kernel, dim3((unsigned)batch), dim3(256), 0, stream, key_mask, seqlen_k, idx, inv,
-                     count);
-  const unsigned gk = row_grid((long)batch * seqlen_k);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(gk), dim3(256), 0, stream, (const uint16_t*)base.k, idx, count, batch,
-                     seqlen_k, kv_elems, kc);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(gk), dim3(256), 0, stream, (const uint16_t*)base.v, idx, count, batch,
-                     seqlen_k, kv_elems, vc);
+                     count, cu_q, cu_k, batch, seqlen_q);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(row_grid((long)batch * seqlen_k), 2), dim3(256), 0, stream,
+                     (const uint16_t*)base.k, (const uint16_t*)base.v, idx, count, batch, seqlen_k, kv_elems, kc, vc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   VarlenArgs a = base;
@@ -219,8 +223,8 @@ hipError_t launch_masked_fwd(const VarlenArgs& base, const uint8_t* key_mask, in
   uint16_t* qc = (uint16_t*)(ws + l.q);
   uint16_t* oc = (uint16_t*)(ws + l.o);
   float* lc = (float*)(ws + l.lse);
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(row_grid((long)batch * seqlen_q)), dim3(256), 0, stream,
-                     (const uint16_t*)base.q, idx, count, batch, seqlen_q, q_elems, qc);
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(row_grid((long)batch * seqlen_q), 1), dim3(256), 0, stream,
+                     (const uint16_t*)base.q, (const uint16_t*)base.q, idx, count, batch, seqlen_q, q_elems, qc, qc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   a.q = qc;
