@@ -45,11 +45,15 @@ from .tiles import (  # noqa: F401
     tile_metadata,
     to_tile_order,
     from_tile_order,
+    h3_tile_metadata,
+    h3_to_tile_order,
+    h3_from_tile_order,
 )
 from .blockmap import (  # noqa: F401
     pool_tiles,
     pooled_scores,
     topk_block_map,
+    h3_block_map,
     map_to_index,
     compressed_branch,
 )

@@ -54,6 +54,28 @@ def topk_block_map(scores, topk: int) -> np.ndarray:
     return out
 
 
+def h3_block_map(scores, n_prefix: int, n_video: int, topk: int) -> np.ndarray:
+    """[VSA] _build_h3_block_map: prefix key tiles are kept for every query
+    tile and prefix query tiles keep every key tile; a video query tile keeps
+    the min(topk, n_video) best-scoring video key tiles (ties: lower index), on
+    top of the prefix columns. When that is every video tile the map is all
+    ones. scores [B, H, nT, nT] with nT = n_prefix + n_video.
+
+    Pinned: no prefix = topk_block_map, hand example, forced rows and columns.
+    """
+    s = np.asarray(scores)
+    if s.shape[-1] != n_prefix + n_video or s.shape[-2] != n_prefix + n_video:
+        raise ValueError("scores must cover the prefix and video tiles")
+    keep = min(int(topk), int(n_video))
+    if keep == n_video:
+        return np.ones(s.shape, dtype=bool)
+    out = np.zeros(s.shape, dtype=bool)
+    out[..., n_prefix:] = topk_block_map(s[..., n_prefix:], keep)
+    out[..., :n_prefix] = True
+    out[..., :n_prefix, :] = True
+    return out
+
+
 def map_to_index(block_map):
     """Ascending kept key-tile indices per row, int32 [..., nK] padded with -1,
     and the kept count per row, int32 [...] (any number of leading dims)."""

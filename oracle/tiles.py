@@ -86,3 +86,43 @@ def from_tile_order(y, shape, tile, block: int = 64) -> np.ndarray:
     """Padded tile order [B, n_tiles*block, ...] -> raster [B, N, ...]."""
     _, _, _, untile = tile_metadata(shape, tile, block)
     return np.asarray(y)[:, untile]
+
+
+def h3_tile_metadata(prefix_segments, video_shape, tile=(4, 4, 4), block: int = 64):
+    """[VSA] _get_h3_tile_metadata: the prefix rows (the segments before the
+    target video, e.g. text and reference frames) come first, in their own
+    order, each segment cut into chunks of ``block`` rows with its remainder as
+    a last, partial chunk; the target video's boxes follow, with their raster
+    token indices shifted past the prefix.
+
+    Returns (partition, sizes, non_pad, untile, n_prefix_tiles, n_video_tiles).
+
+    Pinned: a hand-computed geometry, no prefix = tile_metadata, permutation and
+    round trip.
+    """
+    prefix_len = int(sum(int(s) for s in prefix_segments))
+    prefix_sizes = []
+    for seg in prefix_segments:
+        full, rem = divmod(int(seg), block)
+        prefix_sizes += [block] * full + ([rem] if rem else [])
+    video_part = tile_partition_indices(video_shape, tile) + prefix_len
+    video_sizes = variable_block_sizes(video_shape, tile)
+    partition = np.concatenate([np.arange(prefix_len, dtype=np.int64), video_part])
+    sizes = np.concatenate([np.asarray(prefix_sizes, dtype=np.int32), video_sizes])
+    non_pad = non_pad_index(sizes, block)
+    return partition, sizes, non_pad, untile_index(partition, non_pad), len(prefix_sizes), int(video_sizes.size)
+
+
+def h3_to_tile_order(x, prefix_segments, video_shape, tile=(4, 4, 4), block: int = 64) -> np.ndarray:
+    """Raster [B, prefix + T*H*W, ...] -> padded H3 tile order (pad rows 0)."""
+    xf = np.asarray(x)
+    partition, sizes, non_pad, _, _, _ = h3_tile_metadata(prefix_segments, video_shape, tile, block)
+    out = np.zeros((xf.shape[0], sizes.size * block) + xf.shape[2:], dtype=xf.dtype)
+    out[:, non_pad] = xf[:, partition]
+    return out
+
+
+def h3_from_tile_order(y, prefix_segments, video_shape, tile=(4, 4, 4), block: int = 64) -> np.ndarray:
+    """Padded H3 tile order -> raster [B, prefix + T*H*W, ...]."""
+    untile = h3_tile_metadata(prefix_segments, video_shape, tile, block)[3]
+    return np.asarray(y)[:, untile]

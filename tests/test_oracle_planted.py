@@ -196,3 +196,28 @@ def test_variant_mutants_are_caught(monkeypatch):
 
     monkeypatch.setattr(tv.oracle, "masked_attention", masked_keeps_every_query)
     assert _fails(tv.test_self_mask_with_holes_brute_force_tiny)
+
+
+def test_h3_mutants_are_caught(monkeypatch):
+    from tests import test_oracle_h3 as th
+
+    orig_meta = th.oracle.h3_tile_metadata
+
+    def segments_merged(prefix_segments, video_shape, tile=(4, 4, 4), block=64):
+        # plant: the prefix chunked as one run instead of segment by segment
+        return orig_meta((sum(prefix_segments),), video_shape, tile, block)
+
+    monkeypatch.setattr(th.oracle, "h3_tile_metadata", segments_merged)
+    assert _fails(th.test_hand_derived_geometry)
+    monkeypatch.setattr(th.oracle, "h3_tile_metadata", orig_meta)
+
+    orig_map = th.oracle.h3_block_map
+
+    def prefix_columns_ranked(scores, n_prefix, n_video, topk):
+        # plant: the prefix columns compete in the top-k instead of being kept
+        out = BM.topk_block_map(scores, min(topk, n_video))
+        out[..., :n_prefix, :] = True
+        return out
+
+    monkeypatch.setattr(th.oracle, "h3_block_map", prefix_columns_ranked)
+    assert _fails(th.test_block_map_hand_scored)
