@@ -380,6 +380,51 @@ attn_status_t attn_vsa_block_map(const void* q_tiled, const void* k_tiled, const
                                  int32_t head_dim, float softmax_scale, int32_t topk, uint8_t* block_map,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * H3 layout (vLLM-Omni fastvideo_vsa.py page: _get_h3_tile_metadata): prefix
+ * rows (the segments before the target video, e.g. text and reference frames)
+ * come first, each segment cut into 64-row tiles with its remainder as a last,
+ * partial tile; the video's (tile_t, tile_h, tile_w) boxes follow (the page
+ * uses (4, 4, 4)). The raster input holds the prefix rows, then the video in
+ * (t, h, w) raster order.
+ *
+ *   prefix_segments  (host) int32 [num_segments] row counts >= 0 (empty segments
+ *                    add no tile); num_segments <= 16
+ *   num_prefix_tiles, num_tiles (host outputs of attn_vsa_h3_num_tiles)
+ * Tile gather / untile: as attn_vsa_tile_gather / attn_vsa_untile with
+ *   x  [batch, prefix rows + t*h*w, row_elems] bf16 raster
+ *   x_tiled [batch, num_tiles * 64, row_elems], tile_sizes [num_tiles] int32
+ *   (nullable), prefix tiles first.
+ * Errors: more than 16 segments gives ATTN_ERR_UNSUPPORTED; a negative segment
+ * or a null prefix_segments with num_segments > 0 ATTN_ERR_INVALID_ARG;
+ * otherwise as for the video-only calls.
+ */
+attn_status_t attn_vsa_h3_num_tiles(const int32_t* prefix_segments, int32_t num_segments, int32_t t, int32_t h,
+                                    int32_t w, int32_t tile_t, int32_t tile_h, int32_t tile_w,
+                                    int32_t* num_prefix_tiles, int32_t* num_tiles);
+attn_status_t attn_vsa_h3_tile_gather(const void* x, const int32_t* prefix_segments, int32_t num_segments,
+                                      int32_t batch, int32_t t, int32_t h, int32_t w, int32_t tile_t,
+                                      int32_t tile_h, int32_t tile_w, int32_t row_elems, void* x_tiled,
+                                      int32_t* tile_sizes, void* stream);
+attn_status_t attn_vsa_h3_untile(const void* x_tiled, const int32_t* prefix_segments, int32_t num_segments,
+                                 int32_t batch, int32_t t, int32_t h, int32_t w, int32_t tile_t, int32_t tile_h,
+                                 int32_t tile_w, int32_t row_elems, void* x, void* stream);
+
+/*
+ * H3 block map (vLLM-Omni fastvideo_vsa.py page: _build_h3_block_map): as
+ * attn_vsa_block_map, except that the first num_prefix_tiles tiles are prefix
+ * tiles: prefix query tiles keep every key tile, every query tile keeps the
+ * prefix key tiles, and a video query tile keeps min(topk, video tiles) video
+ * key tiles by pooled score (ties: lower tile index). When that is every video
+ * tile the map is all ones. Workspace: attn_vsa_block_map_workspace_size().
+ * Errors: num_prefix_tiles outside [0, num_tiles] gives ATTN_ERR_INVALID_ARG;
+ * otherwise as attn_vsa_block_map.
+ */
+attn_status_t attn_vsa_h3_block_map(const void* q_tiled, const void* k_tiled, const int32_t* tile_sizes,
+                                    int32_t batch, int32_t num_tiles, int32_t num_prefix_tiles, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t topk,
+                                    uint8_t* block_map, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes for attn_vsa_compressed_add (fp32 tile means of q, k, v and
  * the per-tile compressed rows). Written to *bytes (host pointer). */
 attn_status_t attn_vsa_compressed_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,

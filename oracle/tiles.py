@@ -36,7 +36,7 @@ def tile_partition_indices(shape, tile) -> np.ndarray:
     """Raster token index of each position in tile order, int64 [T*H*W]."""
     t_len, h_len, w_len = shape
     raster = np.arange(t_len * h_len * w_len, dtype=np.int64).reshape(t_len, h_len, w_len)
-    parts = []
+    parts = [np.zeros(0, dtype=np.int64)]  # an empty video has no box
     for (t0, t1), (h0, h1), (w0, w1) in _boxes(shape, tile):
         parts.append(raster[t0:t1, h0:h1, w0:w1].reshape(-1))
     return np.concatenate(parts)
@@ -55,7 +55,8 @@ def non_pad_index(sizes, block: int = 64) -> np.ndarray:
     sizes = np.asarray(sizes, dtype=np.int64)
     if np.any(sizes > block) or np.any(sizes < 0):
         raise ValueError("tile sizes must lie in [0, block]")
-    return np.concatenate([c * block + np.arange(s) for c, s in enumerate(sizes)]).astype(np.int64)
+    return np.concatenate([np.zeros(0, dtype=np.int64)]
+                          + [c * block + np.arange(s) for c, s in enumerate(sizes)]).astype(np.int64)
 
 
 def untile_index(partition, non_pad) -> np.ndarray:

@@ -15,6 +15,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import torch
 
 __all__ = [
@@ -38,6 +39,11 @@ __all__ = [
     "attn_block_sparse_workspace_size",
     "attn_block_sparse_fwd",
     "attn_vsa_tile_gather",
+    "attn_vsa_h3_num_tiles",
+    "attn_vsa_h3_tile_gather",
+    "attn_vsa_h3_untile",
+    "attn_vsa_h3_block_map",
+    "vsa_h3_prepare",
     "attn_vsa_untile",
     "attn_vsa_block_map_workspace_size",
     "attn_vsa_block_map",
@@ -83,6 +89,13 @@ _SIGS = {
     "attn_vsa_untile": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]),
     "attn_vsa_block_map_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "attn_vsa_block_map": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _sz, _p]),
+    "attn_vsa_h3_num_tiles": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                             ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "attn_vsa_h3_tile_gather": (ctypes.c_int, [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p,
+                                               _p]),
+    "attn_vsa_h3_untile": (ctypes.c_int, [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]),
+    "attn_vsa_h3_block_map": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _sz,
+                                             _p]),
     "attn_vsa_compressed_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "attn_vsa_compressed_add": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _sz,
                                                _p]),
@@ -567,6 +580,105 @@ def attn_vsa_compressed_add(q_tiled, k_tiled, v_tiled, tile_sizes, gate_tiled, s
         _stream_ptr(q_tiled, stream))
     _check("attn_vsa_compressed_add", st)
     return out
+
+
+def _segments(prefix_segments):
+    segs = (ctypes.c_int32 * max(len(prefix_segments), 1))(*[int(x) for x in prefix_segments])
+    return segs, len(prefix_segments)
+
+
+def attn_vsa_h3_num_tiles(prefix_segments, video_shape, tile_shape=(4, 4, 4)):
+    """(prefix tiles, all tiles) of the H3 layout: prefix segments cut into 64-row
+    tiles, then the video's boxes."""
+    segs, n = _segments(prefix_segments)
+    a, b = _i32(0), _i32(0)
+    _check("attn_vsa_h3_num_tiles",
+           load_library().attn_vsa_h3_num_tiles(segs, n, *(int(x) for x in video_shape),
+                                                *(int(x) for x in tile_shape), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def attn_vsa_h3_tile_gather(x, prefix_segments, video_shape, tile_shape=(4, 4, 4), x_tiled=None, tile_sizes=None,
+                            stream=None):
+    """Raster [B, prefix + t*h*w, H, D] -> H3 tile order [B, n_tiles*64, H, D] (+ int32 tile sizes)."""
+    b, n = x.shape[:2]
+    row = 1
+    for v_ in x.shape[2:]:
+        row *= int(v_)
+    _, nt = attn_vsa_h3_num_tiles(prefix_segments, video_shape, tile_shape)
+    if n != sum(int(v) for v in prefix_segments) + int(np.prod([int(v) for v in video_shape])):
+        raise ValueError("x's sequence length must equal the prefix rows plus t*h*w")
+    dev = x.device
+    if x_tiled is None:
+        x_tiled = torch.empty((b, nt * 64) + tuple(x.shape[2:]), dtype=x.dtype, device=dev)
+    _shape(x_tiled, "x_tiled", (b, nt * 64) + tuple(x.shape[2:]))
+    if tile_sizes is None:
+        tile_sizes = torch.empty(nt, dtype=torch.int32, device=dev)
+    _shape(tile_sizes, "tile_sizes", (nt,))
+    segs, ns = _segments(prefix_segments)
+    st = load_library().attn_vsa_h3_tile_gather(
+        _dev(x, "x", torch.bfloat16), segs, ns, b, *(int(v) for v in video_shape), *(int(v) for v in tile_shape), row,
+        _dev(x_tiled, "x_tiled", torch.bfloat16, dev), _dev(tile_sizes, "tile_sizes", torch.int32, dev),
+        _stream_ptr(x, stream))
+    _check("attn_vsa_h3_tile_gather", st)
+    return x_tiled, tile_sizes
+
+
+def attn_vsa_h3_untile(x_tiled, prefix_segments, video_shape, tile_shape=(4, 4, 4), out=None, stream=None):
+    """H3 tile order [B, n_tiles*64, H, D] -> raster [B, prefix + t*h*w, H, D]."""
+    b = x_tiled.shape[0]
+    _, nt = attn_vsa_h3_num_tiles(prefix_segments, video_shape, tile_shape)
+    _shape(x_tiled, "x_tiled", (b, nt * 64) + tuple(x_tiled.shape[2:]))
+    row = 1
+    for v_ in x_tiled.shape[2:]:
+        row *= int(v_)
+    n = sum(int(v) for v in prefix_segments) + int(np.prod([int(v) for v in video_shape]))
+    dev = x_tiled.device
+    if out is None:
+        out = torch.empty((b, n) + tuple(x_tiled.shape[2:]), dtype=x_tiled.dtype, device=dev)
+    _shape(out, "out", (b, n) + tuple(x_tiled.shape[2:]))
+    segs, ns = _segments(prefix_segments)
+    st = load_library().attn_vsa_h3_untile(
+        _dev(x_tiled, "x_tiled", torch.bfloat16), segs, ns, b, *(int(v) for v in video_shape),
+        *(int(v) for v in tile_shape), row, _dev(out, "out", torch.bfloat16, dev), _stream_ptr(x_tiled, stream))
+    _check("attn_vsa_h3_untile", st)
+    return out
+
+
+def attn_vsa_h3_block_map(q_tiled, k_tiled, tile_sizes, num_prefix_tiles: int, softmax_scale: float, topk: int,
+                          block_map=None, workspace=None, stream=None):
+    """H3 map: prefix rows and columns kept, top-k over the video columns -> uint8 [B, H, nT, nT]."""
+    b, s_, hq, d = q_tiled.shape
+    hkv = k_tiled.shape[2]
+    nt = s_ // 64
+    _shape(k_tiled, "k_tiled", (b, s_, hkv, d))
+    _shape(tile_sizes, "tile_sizes", (nt,))
+    dev = q_tiled.device
+    if block_map is None:
+        block_map = torch.empty((b, hq, nt, nt), dtype=torch.uint8, device=dev)
+    _shape(block_map, "block_map", (b, hq, nt, nt))
+    if workspace is None:
+        workspace = torch.empty(max(attn_vsa_block_map_workspace_size(b, hq, hkv, nt, d), 1), dtype=torch.uint8,
+                                device=dev)
+    st = load_library().attn_vsa_h3_block_map(
+        _dev(q_tiled, "q_tiled", torch.bfloat16), _dev(k_tiled, "k_tiled", torch.bfloat16, dev),
+        _dev(tile_sizes, "tile_sizes", torch.int32, dev), b, nt, int(num_prefix_tiles), hq, hkv, d,
+        float(softmax_scale), int(topk), _dev(block_map, "block_map", torch.uint8, dev),
+        _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(), _stream_ptr(q_tiled, stream))
+    _check("attn_vsa_h3_block_map", st)
+    return block_map
+
+
+def vsa_h3_prepare(q, k, v, prefix_segments, video_shape, topk: int, softmax_scale: float, tile_shape=(4, 4, 4),
+                   stream=None):
+    """Raster [prefix + video] q/k/v -> H3 tile order plus the H3 block map, all in
+    the library's kernels. Returns a dict like vsa_prepare's plus num_prefix_tiles."""
+    qt, sizes = attn_vsa_h3_tile_gather(q, prefix_segments, video_shape, tile_shape, stream=stream)
+    kt, _ = attn_vsa_h3_tile_gather(k, prefix_segments, video_shape, tile_shape, stream=stream)
+    vt, _ = attn_vsa_h3_tile_gather(v, prefix_segments, video_shape, tile_shape, stream=stream)
+    n_pre, _ = attn_vsa_h3_num_tiles(prefix_segments, video_shape, tile_shape)
+    bmap = attn_vsa_h3_block_map(qt, kt, sizes, n_pre, softmax_scale, topk, stream=stream)
+    return {"q": qt, "k": kt, "v": vt, "block_map": bmap, "tile_sizes": sizes, "num_prefix_tiles": n_pre}
 
 
 def vsa_prepare(q, k, v, video_shape, tile_shape, topk: int, softmax_scale: float, stream=None):

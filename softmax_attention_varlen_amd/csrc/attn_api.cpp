@@ -400,6 +400,76 @@ attn_status_t attn_vsa_untile(const void* x_tiled, int32_t batch, int32_t t, int
   return from_hip(attn::launch_untile(x_tiled, g, batch, row_elems, x, (hipStream_t)stream));
 }
 
+static attn_status_t check_prefix(const int32_t* prefix_segments, int32_t num_segments, long long* rows) {
+  if (num_segments < 0 || num_segments > attn::kMaxPrefixSegments) return ATTN_ERR_UNSUPPORTED;
+  if (num_segments > 0 && prefix_segments == nullptr) return ATTN_ERR_INVALID_ARG;
+  long long n = 0;
+  for (int i = 0; i < num_segments; ++i) {
+    if (prefix_segments[i] < 0) return ATTN_ERR_INVALID_ARG;
+    n += prefix_segments[i];
+  }
+  *rows = n;
+  return ATTN_OK;
+}
+
+// H3 layout checks: the prefix rows and their 64-row tiles added to the video's.
+static attn_status_t check_h3_geometry(const int32_t* prefix_segments, int32_t num_segments, int32_t batch,
+                                       int32_t t, int32_t h, int32_t w, int32_t tile_t, int32_t tile_h,
+                                       int32_t tile_w, int32_t row_elems) {
+  attn_status_t st = check_vsa_geometry(batch, t, h, w, tile_t, tile_h, tile_w, row_elems);
+  if (st != ATTN_OK) return st;
+  long long prefix = 0;
+  st = check_prefix(prefix_segments, num_segments, &prefix);
+  if (st != ATTN_OK) return st;
+  const long long tiles = (long long)((t + tile_t - 1) / tile_t) * ((h + tile_h - 1) / tile_h) *
+                              ((w + tile_w - 1) / tile_w) + prefix / 64 + num_segments;
+  if ((long long)batch * (prefix + (long long)t * h * w + tiles * 64) > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+attn_status_t attn_vsa_h3_num_tiles(const int32_t* prefix_segments, int32_t num_segments, int32_t t, int32_t h,
+                                    int32_t w, int32_t tile_t, int32_t tile_h, int32_t tile_w,
+                                    int32_t* num_prefix_tiles, int32_t* num_tiles) {
+  if (num_prefix_tiles == nullptr || num_tiles == nullptr) return ATTN_ERR_INVALID_ARG;
+  const attn_status_t st = check_h3_geometry(prefix_segments, num_segments, 1, t, h, w, tile_t, tile_h, tile_w, 8);
+  if (st != ATTN_OK) return st;
+  attn::VsaGeometry g{t, h, w, tile_t, tile_h, tile_w};
+  g.prefix_segments = prefix_segments;
+  g.num_segments = num_segments;
+  *num_prefix_tiles = attn::vsa_prefix_tiles(g);
+  *num_tiles = attn::vsa_num_tiles(g);
+  return ATTN_OK;
+}
+
+attn_status_t attn_vsa_h3_tile_gather(const void* x, const int32_t* prefix_segments, int32_t num_segments,
+                                      int32_t batch, int32_t t, int32_t h, int32_t w, int32_t tile_t, int32_t tile_h,
+                                      int32_t tile_w, int32_t row_elems, void* x_tiled, int32_t* tile_sizes,
+                                      void* stream) {
+  const attn_status_t st =
+      check_h3_geometry(prefix_segments, num_segments, batch, t, h, w, tile_t, tile_h, tile_w, row_elems);
+  if (st != ATTN_OK) return st;
+  attn::VsaGeometry g{t, h, w, tile_t, tile_h, tile_w};
+  g.prefix_segments = prefix_segments;
+  g.num_segments = num_segments;
+  if (batch == 0 || attn::vsa_num_tiles(g) == 0) return ATTN_OK;
+  if (x == nullptr || x_tiled == nullptr) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_tile_gather(x, g, batch, row_elems, x_tiled, tile_sizes, (hipStream_t)stream));
+}
+
+attn_status_t attn_vsa_h3_untile(const void* x_tiled, const int32_t* prefix_segments, int32_t num_segments,
+                                 int32_t batch, int32_t t, int32_t h, int32_t w, int32_t tile_t, int32_t tile_h,
+                                 int32_t tile_w, int32_t row_elems, void* x, void* stream) {
+  const attn_status_t st =
+      check_h3_geometry(prefix_segments, num_segments, batch, t, h, w, tile_t, tile_h, tile_w, row_elems);
+  if (st != ATTN_OK) return st;
+  attn::VsaGeometry g{t, h, w, tile_t, tile_h, tile_w};
+  g.prefix_segments = prefix_segments;
+  g.num_segments = num_segments;
+  if (batch == 0 || attn::vsa_num_tiles(g) == 0) return ATTN_OK;
+  if (x == nullptr || x_tiled == nullptr) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_untile(x_tiled, g, batch, row_elems, x, (hipStream_t)stream));
+}
+
 attn_status_t attn_vsa_block_map_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                                                 int32_t num_tiles, int32_t head_dim, size_t* bytes) {
   if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;
@@ -410,11 +480,13 @@ attn_status_t attn_vsa_block_map_workspace_size(int32_t batch, int32_t num_heads
   return ATTN_OK;
 }
 
-attn_status_t attn_vsa_block_map(const void* q_tiled, const void* k_tiled, const int32_t* tile_sizes,
-                                 int32_t batch, int32_t num_tiles, int32_t num_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, float softmax_scale, int32_t topk, uint8_t* block_map,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+static attn_status_t vsa_block_map_impl(const void* q_tiled, const void* k_tiled, const int32_t* tile_sizes,
+                                        int32_t batch, int32_t num_tiles, int32_t num_prefix_tiles,
+                                        int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        float softmax_scale, int32_t topk, uint8_t* block_map, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
   if (batch < 0 || num_tiles < 0 || num_heads <= 0 || num_kv_heads <= 0 || topk < 1) return ATTN_ERR_INVALID_ARG;
+  if (num_prefix_tiles < 0 || num_prefix_tiles > num_tiles) return ATTN_ERR_INVALID_ARG;
   if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
   if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
@@ -428,8 +500,25 @@ attn_status_t attn_vsa_block_map(const void* q_tiled, const void* k_tiled, const
   if (workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (workspace == nullptr) return ATTN_ERR_INVALID_ARG;
   return from_hip(attn::launch_vsa_block_map(q_tiled, k_tiled, tile_sizes, batch, num_tiles, num_heads, num_kv_heads,
-                                             head_dim, softmax_scale, topk, block_map, workspace,
-                                             (hipStream_t)stream));
+                                             head_dim, softmax_scale, topk, block_map, workspace, (hipStream_t)stream,
+                                             num_prefix_tiles));
+}
+
+attn_status_t attn_vsa_block_map(const void* q_tiled, const void* k_tiled, const int32_t* tile_sizes,
+                                 int32_t batch, int32_t num_tiles, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float softmax_scale, int32_t topk, uint8_t* block_map,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return vsa_block_map_impl(q_tiled, k_tiled, tile_sizes, batch, num_tiles, 0, num_heads, num_kv_heads, head_dim,
+                            softmax_scale, topk, block_map, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_vsa_h3_block_map(const void* q_tiled, const void* k_tiled, const int32_t* tile_sizes,
+                                    int32_t batch, int32_t num_tiles, int32_t num_prefix_tiles, int32_t num_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t topk,
+                                    uint8_t* block_map, void* workspace, size_t workspace_bytes, void* stream) {
+  return vsa_block_map_impl(q_tiled, k_tiled, tile_sizes, batch, num_tiles, num_prefix_tiles, num_heads,
+                            num_kv_heads, head_dim, softmax_scale, topk, block_map, workspace, workspace_bytes,
+                            stream);
 }
 
 attn_status_t attn_vsa_compressed_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,

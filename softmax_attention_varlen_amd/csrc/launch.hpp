@@ -143,19 +143,28 @@ hipError_t launch_block_sparse_fwd(const SparseArgs& a, hipStream_t stream);
 constexpr int kSparseD128MaxTiles = 3072;
 hipError_t launch_block_sparse_d128(const SparseArgs& a, hipStream_t stream);
 
-// Video tile geometry (raster (t, h, w) cut into (tile_t, tile_h, tile_w) boxes).
+// Video tile geometry (raster (t, h, w) cut into (tile_t, tile_h, tile_w) boxes),
+// optionally behind prefix segments (host array of num_segments lengths >= 0):
+// the H3 layout, whose prefix rows come first and are cut into 64-row tiles
+// segment by segment.
+constexpr int kMaxPrefixSegments = 16;
 struct VsaGeometry {
   int t, h, w, tile_t, tile_h, tile_w;
+  const int32_t* prefix_segments = nullptr;
+  int num_segments = 0;
 };
 
-int vsa_num_tiles(const VsaGeometry& g);
+int vsa_num_tiles(const VsaGeometry& g);  // prefix tiles included
+int vsa_prefix_tiles(const VsaGeometry& g);
 hipError_t launch_tile_gather(const void* x, const VsaGeometry& g, int batch, int row_elems, void* y,
                               int32_t* sizes, hipStream_t stream);
 hipError_t launch_untile(const void* y, const VsaGeometry& g, int batch, int row_elems, void* x, hipStream_t stream);
 size_t vsa_map_workspace_bytes(int batch, int heads, int kv_heads, int n_tiles, int head_dim);
+// n_prefix > 0: the first n_prefix tiles are H3 prefix tiles (their rows and
+// columns of the map are kept; top-k ranks the video columns only)
 hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const int32_t* sizes, int batch,
                                 int n_tiles, int heads, int kv_heads, int head_dim, float scale, int topk,
-                                uint8_t* map, void* workspace, hipStream_t stream);
+                                uint8_t* map, void* workspace, hipStream_t stream, int n_prefix = 0);
 
 // VSA compressed branch: out (tile order, bf16) += broadcast_rows(softmax(pooled
 // scores) @ value tile means) * gate. Workspace: fp32 means of q, k, v and c.

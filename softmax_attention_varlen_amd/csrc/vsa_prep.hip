@@ -37,10 +37,39 @@ struct BoxGeom {
   }
 };
 
+// H3 prefix rows ([VSA] _get_h3_tile_metadata): segment s covers raster rows
+// [start[s], start[s + 1]) (start[n_seg] = len) and tiles [tile0[s],
+// tile0[s + 1]), 64 rows each, its last tile holding the remainder. Segments
+// are non-empty; n_seg = 0 is the plain video layout.
+struct PrefixLayout {
+  int n_seg, n_tiles, len;
+  int start[kMaxPrefixSegments + 1];
+  int tile0[kMaxPrefixSegments + 1];
+};
+
+// Raster row (batch-local) that fills padded row r of tile c, or -1 for a
+// padding row; *size = the tile's real row count.
+__device__ __forceinline__ int tile_source(const BoxGeom& gm, const PrefixLayout& pl, int c, int r, int* size) {
+  if (c < pl.n_tiles) {
+    int s = 0;
+    while (s + 1 < pl.n_seg && pl.tile0[s + 1] <= c) ++s;
+    const int first = pl.start[s] + (c - pl.tile0[s]) * 64;
+    const int sz = min(64, pl.start[s + 1] - first);
+    *size = sz;
+    return r < sz ? first + r : -1;
+  }
+  int bt, bh, bw, et, eh, ew;
+  gm.box_extent(c - pl.n_tiles, bt, bh, bw, et, eh, ew);
+  *size = et * eh * ew;
+  if (r >= *size) return -1;
+  const int it = r / (eh * ew), ih = (r / ew) % eh, iw = r % ew;
+  return pl.len + ((bt * gm.tt + it) * gm.H + (bh * gm.th + ih)) * gm.W + (bw * gm.tw + iw);
+}
+
 // One wave per tile-order destination row.
 __global__ __launch_bounds__(256) void tile_gather_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-                                                          int32_t* __restrict__ sizes, BoxGeom gm, int n_tiles,
-                                                          int batch, int row_elems) {
+                                                          int32_t* __restrict__ sizes, BoxGeom gm, PrefixLayout pl,
+                                                          int n_tiles, int batch, int row_elems) {
   const int lane = threadIdx.x & 63;
   const long dst = (long)blockIdx.x * 4 + (threadIdx.x >> 6);  // over batch * n_tiles * 64
   const long rows_per_batch = (long)n_tiles * 64;
@@ -48,36 +77,46 @@ __global__ __launch_bounds__(256) void tile_gather_kernel(const uint16_t* __rest
   const int b = (int)(dst / rows_per_batch);
   const int p = (int)(dst % rows_per_batch);
   const int c = p >> 6, r = p & 63;
-  int bt, bh, bw, et, eh, ew;
-  gm.box_extent(c, bt, bh, bw, et, eh, ew);
-  const int size = et * eh * ew;
+  int size;
+  const int src = tile_source(gm, pl, c, r, &size);
   if (sizes != nullptr && b == 0 && r == 0 && lane == 0) sizes[c] = size;
   uint16_t* yrow = y + dst * row_elems;
   const int chunks = row_elems / 8;
-  if (r >= size) {
+  if (src < 0) {
     for (int j = lane; j < chunks; j += 64) *reinterpret_cast<u32x4*>(yrow + j * 8) = u32x4{0u, 0u, 0u, 0u};
     return;
   }
-  const int it = r / (eh * ew), ih = (r / ew) % eh, iw = r % ew;
-  const long tok = ((long)(bt * gm.tt + it) * gm.H + (bh * gm.th + ih)) * gm.W + (bw * gm.tw + iw);
-  const uint16_t* xrow = x + ((long)b * gm.T * gm.H * gm.W + tok) * row_elems;
+  const long n_rows = (long)pl.len + (long)gm.T * gm.H * gm.W;
+  const uint16_t* xrow = x + ((long)b * n_rows + src) * row_elems;
   for (int j = lane; j < chunks; j += 64) *reinterpret_cast<u32x4*>(yrow + j * 8) = ld_global16(xrow + j * 8);
 }
 
 // One wave per raster destination row.
 __global__ __launch_bounds__(256) void untile_kernel(const uint16_t* __restrict__ y, uint16_t* __restrict__ x,
-                                                     BoxGeom gm, int n_tiles, int batch, int row_elems) {
+                                                     BoxGeom gm, PrefixLayout pl, int n_tiles, int batch,
+                                                     int row_elems) {
   const int lane = threadIdx.x & 63;
-  const long n_tok = (long)gm.T * gm.H * gm.W;
+  const long n_rows = (long)pl.len + (long)gm.T * gm.H * gm.W;
   const long dst = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (dst >= batch * n_tok) return;
-  const int b = (int)(dst / n_tok);
-  const long tok = dst % n_tok;
-  const int w = (int)(tok % gm.W), h = (int)((tok / gm.W) % gm.H), t = (int)(tok / ((long)gm.W * gm.H));
-  const int c = ((t / gm.tt) * gm.nbh + h / gm.th) * gm.nbw + w / gm.tw;
-  int bt, bh, bw, et, eh, ew;
-  gm.box_extent(c, bt, bh, bw, et, eh, ew);
-  const int r = ((t - bt * gm.tt) * eh + (h - bh * gm.th)) * ew + (w - bw * gm.tw);
+  if (dst >= batch * n_rows) return;
+  const int b = (int)(dst / n_rows);
+  const long n = dst % n_rows;
+  int c, r;
+  if (n < pl.len) {
+    int s = 0;
+    while (s + 1 < pl.n_seg && pl.start[s + 1] <= n) ++s;
+    const int off = (int)n - pl.start[s];
+    c = pl.tile0[s] + off / 64;
+    r = off % 64;
+  } else {
+    const long tok = n - pl.len;
+    const int w = (int)(tok % gm.W), h = (int)((tok / gm.W) % gm.H), t = (int)(tok / ((long)gm.W * gm.H));
+    const int cv = ((t / gm.tt) * gm.nbh + h / gm.th) * gm.nbw + w / gm.tw;
+    int bt, bh, bw, et, eh, ew;
+    gm.box_extent(cv, bt, bh, bw, et, eh, ew);
+    r = ((t - bt * gm.tt) * eh + (h - bh * gm.th)) * ew + (w - bw * gm.tw);
+    c = pl.n_tiles + cv;
+  }
   const uint16_t* yrow = y + ((long)b * n_tiles * 64 + (long)c * 64 + r) * row_elems;
   uint16_t* xrow = x + dst * row_elems;
   const int chunks = row_elems / 8;
@@ -314,19 +353,23 @@ __device__ __forceinline__ float block_sum(float x, float* red) {
 
 // One map row per workgroup: the row's scores go to LDS, then tile c is kept
 // when fewer than k tiles beat it (a higher score, or an equal score at a
-// lower index), or when k reaches the tile count.
+// lower index), or when k reaches the tile count. With an H3 prefix
+// (n_prefix tiles), prefix rows and prefix columns are kept and only the video
+// columns are ranked.
 __global__ __launch_bounds__(256) void topk_map_kernel(const float* __restrict__ scores, uint8_t* __restrict__ map,
-                                                       int n_tiles, int ld, int keep) {
+                                                       int n_tiles, int ld, int keep, int n_prefix) {
   extern __shared__ float srow[];  // [stride]
   const int stride = (n_tiles + 3) & ~3;
   const long row = blockIdx.x;
+  const bool dense_row = keep >= n_tiles - n_prefix || (int)(row % n_tiles) < n_prefix;
   const float* in = scores + row * ld;
-  for (int c = threadIdx.x; c < stride; c += blockDim.x) srow[c] = c < n_tiles ? in[c] : kNegInf;
+  // prefix columns sit out the ranking (kept anyway): below every score
+  for (int c = threadIdx.x; c < stride; c += blockDim.x) srow[c] = c < n_tiles && c >= n_prefix ? in[c] : kNegInf;
   __syncthreads();
   uint8_t* mrow = map + row * n_tiles;
   for (int c = threadIdx.x; c < n_tiles; c += blockDim.x) {
     uint8_t kept = 1;
-    if (keep < n_tiles) {
+    if (!dense_row && c >= n_prefix) {
       const float v = srow[c];
       int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
       for (int j = 0; j < stride; j += 4) {
@@ -353,19 +396,28 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 // l, l + 64, ...). The keep-th largest key T is found bit by bit from the top
 // (the largest T with at least keep keys >= T, counted with wave ballots);
 // then every key above T is kept, and of the keys equal to T the lowest-index
-// ones until keep is reached.
+// ones until keep is reached. With an H3 prefix, prefix rows keep everything
+// and prefix columns are kept outside the ranking (keep < video tiles here).
 template <int R>
 __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ scores, uint8_t* __restrict__ map,
-                                                        int n_tiles, int ld, int keep, long rows) {
+                                                        int n_tiles, int ld, int keep, long rows, int n_prefix) {
   const int lane = threadIdx.x & 63;
   const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
+  uint8_t* mrow = map + row * n_tiles;
+  if ((int)(row % n_tiles) < n_prefix) {  // a prefix query tile keeps every key tile
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (r * 64 + lane < n_tiles) mrow[r * 64 + lane] = 1;
+    }
+    return;
+  }
   const float* in = scores + row * ld;
-  uint32_t key[R];
+  uint32_t key[R];  // prefix columns get key 0: below every score, never counted
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int idx = r * 64 + lane;
-    key[r] = idx < n_tiles ? order_key(in[idx]) : 0u;
+    key[r] = idx < n_tiles && idx >= n_prefix ? order_key(in[idx]) : 0u;
   }
   uint32_t t = 0;
   for (int bit = 31; bit >= 0; --bit) {
@@ -380,15 +432,16 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
   for (int r = 0; r < R; ++r) above += __popcll(__ballot(key[r] > t));
   const int quota = keep - above;
   int eq_before = 0;
-  uint8_t* mrow = map + row * n_tiles;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int idx = r * 64 + lane;
-    const unsigned long long eq = __ballot(idx < n_tiles && key[r] == t);
+    const unsigned long long eq = __ballot(idx < n_tiles && idx >= n_prefix && key[r] == t);
     const int rank = eq_before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
     eq_before += __popcll(eq);
-    if (idx < n_tiles) mrow[idx] = (uint8_t)(key[r] > t || (key[r] == t && rank < quota));
+    if (idx < n_tiles) {
+      mrow[idx] = (uint8_t)(idx < n_prefix || key[r] > t || (key[r] == t && idx >= n_prefix && rank < quota));
+    }
   }
 }
 
@@ -493,53 +546,75 @@ static BoxGeom make_geom(const VsaGeometry& g) {
   return b;
 }
 
+// Non-empty segments only; the host has checked num_segments <= kMaxPrefixSegments.
+static PrefixLayout make_prefix(const VsaGeometry& g) {
+  PrefixLayout p{};
+  for (int i = 0; i < g.num_segments; ++i) {
+    const int len = g.prefix_segments[i];
+    if (len <= 0) continue;
+    p.start[p.n_seg] = p.len;
+    p.tile0[p.n_seg] = p.n_tiles;
+    p.len += len;
+    p.n_tiles += (len + 63) / 64;
+    ++p.n_seg;
+  }
+  p.start[p.n_seg] = p.len;
+  p.tile0[p.n_seg] = p.n_tiles;
+  return p;
+}
+
+int vsa_prefix_tiles(const VsaGeometry& g) { return make_prefix(g).n_tiles; }
+
 int vsa_num_tiles(const VsaGeometry& g) {
   const BoxGeom b = make_geom(g);
-  return b.nbt * b.nbh * b.nbw;
+  return vsa_prefix_tiles(g) + b.nbt * b.nbh * b.nbw;
 }
 
 hipError_t launch_tile_gather(const void* x, const VsaGeometry& g, int batch, int row_elems, void* y,
                               int32_t* sizes, hipStream_t stream) {
   const BoxGeom gm = make_geom(g);
-  const int nt = gm.nbt * gm.nbh * gm.nbw;
+  const PrefixLayout pl = make_prefix(g);
+  const int nt = pl.n_tiles + gm.nbt * gm.nbh * gm.nbw;
   const long rows = (long)batch * nt * 64;
   hipLaunchKernelGGL(tile_gather_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream,
-                     (const uint16_t*)x, (uint16_t*)y, sizes, gm, nt, batch, row_elems);
+                     (const uint16_t*)x, (uint16_t*)y, sizes, gm, pl, nt, batch, row_elems);
   return hipGetLastError();
 }
 
 hipError_t launch_untile(const void* y, const VsaGeometry& g, int batch, int row_elems, void* x, hipStream_t stream) {
   const BoxGeom gm = make_geom(g);
-  const int nt = gm.nbt * gm.nbh * gm.nbw;
-  const long rows = (long)batch * g.t * g.h * g.w;
+  const PrefixLayout pl = make_prefix(g);
+  const int nt = pl.n_tiles + gm.nbt * gm.nbh * gm.nbw;
+  const long rows = (long)batch * (pl.len + (long)g.t * g.h * g.w);
   hipLaunchKernelGGL(untile_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, (const uint16_t*)y,
-                     (uint16_t*)x, gm, nt, batch, row_elems);
+                     (uint16_t*)x, gm, pl, nt, batch, row_elems);
   return hipGetLastError();
 }
 
 template <int R>
 static void launch_topk_wave(const float* scores, uint8_t* map, int n_tiles, int ld, int keep, long rows,
-                             hipStream_t stream) {
+                             int n_prefix, hipStream_t stream) {
   hipLaunchKernelGGL(topk_wave_kernel<R>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, scores, map,
-                     n_tiles, ld, keep, rows);
+                     n_tiles, ld, keep, rows, n_prefix);
 }
 
 // Rows of up to 1024 tiles take the one-wave radix select; longer rows (and
-// k >= the tile count) the workgroup-per-row ranking.
+// k covering every video tile) the workgroup-per-row ranking.
 static hipError_t launch_topk(const float* scores, uint8_t* map, int n_tiles, int ld, int keep, long rows, size_t lds,
-                              hipStream_t stream) {
-  if (keep >= n_tiles || n_tiles > 1024) {
-    hipLaunchKernelGGL(topk_map_kernel, dim3((unsigned)rows), dim3(256), lds, stream, scores, map, n_tiles, ld, keep);
+                              int n_prefix, hipStream_t stream) {
+  if (keep >= n_tiles - n_prefix || n_tiles > 1024) {
+    hipLaunchKernelGGL(topk_map_kernel, dim3((unsigned)rows), dim3(256), lds, stream, scores, map, n_tiles, ld, keep,
+                       n_prefix);
   } else if (n_tiles <= 64) {
-    launch_topk_wave<1>(scores, map, n_tiles, ld, keep, rows, stream);
+    launch_topk_wave<1>(scores, map, n_tiles, ld, keep, rows, n_prefix, stream);
   } else if (n_tiles <= 128) {
-    launch_topk_wave<2>(scores, map, n_tiles, ld, keep, rows, stream);
+    launch_topk_wave<2>(scores, map, n_tiles, ld, keep, rows, n_prefix, stream);
   } else if (n_tiles <= 256) {
-    launch_topk_wave<4>(scores, map, n_tiles, ld, keep, rows, stream);
+    launch_topk_wave<4>(scores, map, n_tiles, ld, keep, rows, n_prefix, stream);
   } else if (n_tiles <= 512) {
-    launch_topk_wave<8>(scores, map, n_tiles, ld, keep, rows, stream);
+    launch_topk_wave<8>(scores, map, n_tiles, ld, keep, rows, n_prefix, stream);
   } else {
-    launch_topk_wave<16>(scores, map, n_tiles, ld, keep, rows, stream);
+    launch_topk_wave<16>(scores, map, n_tiles, ld, keep, rows, n_prefix, stream);
   }
   return hipGetLastError();
 }
@@ -551,7 +626,7 @@ size_t vsa_map_workspace_bytes(int batch, int heads, int kv_heads, int n_tiles, 
 
 hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const int32_t* sizes, int batch,
                                 int n_tiles, int heads, int kv_heads, int head_dim, float scale, int topk,
-                                uint8_t* map, void* workspace, hipStream_t stream) {
+                                uint8_t* map, void* workspace, hipStream_t stream, int n_prefix) {
   float* qpool = (float*)workspace;
   float* kpool = qpool + (size_t)batch * heads * n_tiles * head_dim;
   float* scores = kpool + (size_t)batch * kv_heads * n_tiles * head_dim;
@@ -560,7 +635,8 @@ hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const 
   pa.s[1] = PoolSrc{(const uint16_t*)k_tiled, kpool, kv_heads};
   hipError_t e = launch_pool(pa, 2, sizes, batch, n_tiles, head_dim, stream);
   if (e != hipSuccess) return e;
-  const int keep = topk < n_tiles ? topk : n_tiles;
+  const int n_video = n_tiles - n_prefix;
+  const int keep = topk < n_video ? topk : n_video;
   const int total = batch * heads, chunk = score_chunk(batch, heads, n_tiles), ld = score_ld(n_tiles);
   const size_t lds = (size_t)((n_tiles + 3) & ~3) * sizeof(float);
   const size_t mat = (size_t)n_tiles * head_dim;
@@ -570,7 +646,7 @@ hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const 
                            nz, heads, kv_heads, scale, stream);
     if (e != hipSuccess) return e;
     e = launch_topk(scores, map + (size_t)z0 * n_tiles * n_tiles, n_tiles, ld, keep, (long)nz * n_tiles, lds,
-                    stream);
+                    n_prefix, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

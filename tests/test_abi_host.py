@@ -270,3 +270,26 @@ def test_padding_workspace_queries():
     assert self_ >= 4 * (2 * 512 * 24 * 128 * 2)
     with pytest.raises(sav.AttnError):
         sav.attn_padded_fwd_workspace_size(-1)
+
+
+def test_h3_geometry_validation():
+    segs = (ctypes.c_int32 * 17)(*([10] * 17))
+    a, b = ctypes.c_int32(0), ctypes.c_int32(0)
+    f = lib().attn_vsa_h3_num_tiles
+    assert f(segs, 17, 4, 4, 4, 4, 4, 4, ctypes.byref(a), ctypes.byref(b)) == UNSUPPORTED
+    neg = (ctypes.c_int32 * 2)(10, -1)
+    assert f(neg, 2, 4, 4, 4, 4, 4, 4, ctypes.byref(a), ctypes.byref(b)) == INVALID
+    assert f(None, 2, 4, 4, 4, 4, 4, 4, ctypes.byref(a), ctypes.byref(b)) == INVALID
+    assert f(segs, 3, 4, 4, 4, 4, 4, 4, None, ctypes.byref(b)) == INVALID
+    assert sav.attn_vsa_h3_num_tiles((70, 5), (2, 5, 4)) == (3, 5)
+    assert sav.attn_vsa_h3_num_tiles((0, 130), (5, 9, 7)) == (3, 15)
+    assert lib().attn_vsa_h3_tile_gather(FAKE, segs, 17, 1, 4, 4, 4, 4, 4, 4, 64, FAKE, None, None) == UNSUPPORTED
+    assert lib().attn_vsa_h3_untile(FAKE, neg, 2, 1, 4, 4, 4, 4, 4, 4, 64, FAKE, None) == INVALID
+
+
+def test_h3_block_map_validation():
+    f = lib().attn_vsa_h3_block_map
+    assert f(FAKE, FAKE, FAKE, 1, 10, 11, 4, 4, 128, 0.1, 4, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 1, 10, -1, 4, 4, 128, 0.1, 4, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 1, 10, 2, 4, 4, 128, 0.1, 0, FAKE, FAKE, 1 << 30, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 1, 10, 2, 4, 4, 128, 0.1, 4, FAKE, FAKE, 0, None) == WS_SMALL

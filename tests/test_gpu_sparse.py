@@ -375,3 +375,74 @@ def test_compressed_branch_config5():
     ref, _ = oracle.compressed_branch(qt.cpu(), kt.cpu(), vt.cpu(), sizes.cpu().numpy(), case.scale, gate.cpu(),
                                       base.cpu())
     assert_close("out", host(out), ref, OUT_TOL, bf16_output=True)
+
+
+H3_CASES = [((70, 5), (2, 5, 4)), ((130, 64, 1), (5, 9, 7)), ((), (5, 7, 9)), ((300,), (0, 0, 0)),
+            ((0, 512), (16, 32, 32))]
+
+
+@pytest.mark.parametrize("segs,shape", H3_CASES)
+def test_h3_tile_gather_untile_bit_exact(segs, shape):
+    n = sum(segs) + int(np.prod(shape))
+    x = randn_bf16((2, n, 3, 64), 395)
+    announce("h3 tile gather", segs, shape)
+    xt, sizes = sav.attn_vsa_h3_tile_gather(dev(x), segs, shape)
+    back = sav.attn_vsa_h3_untile(xt, segs, shape)
+    torch.cuda.synchronize()
+    _, ref_sizes, _, _, n_pre, _ = oracle.h3_tile_metadata(segs, shape)
+    ref_t = oracle.h3_to_tile_order(x.view(torch.int16).numpy(), segs, shape)
+    assert np.array_equal(sizes.cpu().numpy(), ref_sizes)
+    assert np.array_equal(xt.cpu().view(torch.int16).numpy(), ref_t)
+    assert torch.equal(back.cpu().view(torch.int16), x.view(torch.int16))
+    assert sav.attn_vsa_h3_num_tiles(segs, shape)[0] == n_pre
+
+
+def _h3_scores(qt, kt, sizes, group, scale):
+    return oracle.pooled_scores(oracle.pool_tiles(qt, sizes), np.repeat(oracle.pool_tiles(kt, sizes), group, axis=1),
+                                scale)
+
+
+def check_h3_map(gmap, scores, n_pre, topk):
+    g = np.asarray(gmap).astype(bool)
+    n_vid = g.shape[-1] - n_pre
+    if min(topk, n_vid) == n_vid:
+        assert g.all()
+        return
+    assert g[..., :n_pre, :].all() and g[..., :n_pre].all()  # prefix rows and columns kept
+    check_map_is_valid_topk(g[..., n_pre:, n_pre:], np.asarray(scores)[..., n_pre:, n_pre:], topk)
+
+
+@pytest.mark.parametrize("segs,shape,topk", [((70, 5), (8, 9, 10), 5), ((130, 64, 1), (5, 9, 7), 4),
+                                             ((512,), (16, 16, 16), 20), ((70,), (4, 4, 8), 40),
+                                             ((2000, 100), (20, 32, 32), 32)])
+def test_h3_block_map(segs, shape, topk):
+    n = sum(segs) + int(np.prod(shape))
+    q, k = randn_bf16((1, n, 4, 128), 396), randn_bf16((1, n, 2, 128), 397)
+    announce("h3 block map", segs, shape, topk)
+    qt, sizes = sav.attn_vsa_h3_tile_gather(dev(q), segs, shape)
+    kt, _ = sav.attn_vsa_h3_tile_gather(dev(k), segs, shape)
+    n_pre, nt = sav.attn_vsa_h3_num_tiles(segs, shape)
+    gmap = sav.attn_vsa_h3_block_map(qt, kt, sizes, n_pre, 128 ** -0.5, topk)
+    torch.cuda.synchronize()
+    scores = _h3_scores(qt.cpu(), kt.cpu(), sizes.cpu().numpy(), 2, 128 ** -0.5)
+    check_h3_map(gmap.cpu().numpy(), scores, n_pre, topk)
+
+
+def test_h3_raster_pipeline_end_to_end():
+    """raster [prefix + video] q/k/v -> H3 tiles -> GPU H3 map -> block-sparse ->
+    untile, against the oracle on the same (validated) map."""
+    segs, shape, hq, d, topk = (90, 40), (5, 7, 9), 2, 128, 6
+    n = sum(segs) + int(np.prod(shape))
+    q, k, v = (randn_bf16((1, n, hq, d), 398 + j) for j in range(3))
+    announce("h3 pipeline")
+    prep = sav.vsa_h3_prepare(dev(q), dev(k), dev(v), segs, shape, topk, d ** -0.5)
+    out_t = sav.attn_block_sparse_fwd(prep["q"], prep["k"], prep["v"], prep["block_map"], prep["tile_sizes"],
+                                      d ** -0.5)
+    out = sav.attn_vsa_h3_untile(out_t, segs, shape)
+    torch.cuda.synchronize()
+    bmap = prep["block_map"].cpu().numpy().astype(bool)
+    _, sizes, _, _, n_pre, _ = oracle.h3_tile_metadata(segs, shape)
+    qt, kt, vt = (oracle.h3_to_tile_order(x.double().numpy(), segs, shape) for x in (q, k, v))
+    check_h3_map(bmap, _h3_scores(qt, kt, sizes, 1, d ** -0.5), n_pre, topk)
+    ref_t, _ = oracle.block_sparse_attention(qt, kt, vt, bmap, sizes, d ** -0.5)
+    assert_close("out", host(out), oracle.h3_from_tile_order(ref_t, segs, shape), OUT_TOL, bf16_output=True)
