@@ -56,6 +56,7 @@ TRAFFIC = {
                       "write_kib": 87201.7, "sources": _PREFILL_SRC, "sha256": "58bb7222d2318ced"},
     "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445751.0, "write_kib": 12150.3,
              "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
+    "h3": {"kernel": "block_sparse_d128_kernel"},
     "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531393.3, "write_kib": 3081.2,
             "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
     "masked": {"kernel": "prefill_d128_kernel<false,false,8,3>", "fetch_kib": 28908.6, "write_kib": 49926.4,
@@ -282,6 +283,29 @@ def bench_kv_write(case, steps, warmup):
     return ms, 2.0 * 2 * n * case.num_kv_heads * case.head_dim + 4 * n  # read + write of K and V, slots
 
 
+def bench_h3(case, steps, warmup):
+    """H3 layout: prefix + video tiles and the H3 map built in the library's
+    kernels; the block-sparse call is the timed step, the map build is reported."""
+    dev = torch.device("cuda")
+    q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    segs = case.extra["prefix_segments"]
+    prep = sav.vsa_h3_prepare(q, k, v, segs, case.video_shape, case.topk, case.scale)
+    qt, kt, vt, bmap, sizes = prep["q"], prep["k"], prep["v"], prep["block_map"], prep["tile_sizes"]
+    out = torch.empty_like(qt)
+    lse = torch.empty((qt.shape[0], case.num_heads, qt.shape[1]), dtype=torch.float32, device=dev)
+    ws = torch.empty(sav.attn_block_sparse_workspace_size(qt.shape[0], case.num_heads, sizes.numel()),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        sav.attn_block_sparse_fwd(qt, kt, vt, bmap, sizes, case.scale, out=out, lse=lse, workspace=ws)
+
+    ms = time_steps(step, steps, warmup)
+    flops = sparse_flops(bmap.cpu().numpy(), sizes.cpu().numpy(), case.head_dim)
+    prep_ms = time_steps(lambda: sav.vsa_h3_prepare(q, k, v, segs, case.video_shape, case.topk, case.scale), steps,
+                         warmup)
+    return ms, flops, prep_ms
+
+
 def bench_sparse(case, steps, warmup):
     """Tile order, pooled-score top-k map and the block-sparse call all run in the
     library's kernels; only the block-sparse call is in the timed step."""
@@ -347,8 +371,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse", "paged_prefill", "spec", "swa", "masked",
-                                       "padded", "copy"],
+    ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse", "h3", "paged_prefill", "spec", "swa",
+                                       "masked", "padded", "copy"],
                     default=None,
                     help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
                          "copy, the reference that scales the HBM byte counters")
@@ -409,6 +433,14 @@ def main():
         secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
                           "roofline": roofline("sparse", "mfma", tf, flops),
                           "tile_prep_and_map_ms": round(prep_ms, 4), "compressed_branch_ms": round(comp_ms, 4)})
+
+    if args.only in (None, "h3") and not (args.only is None and args.no_secondary):
+        case = workloads.config11()
+        ms, flops, prep_ms = bench_h3(case, args.steps, args.warmup)
+        tf = flops / (ms * 1e-3) / 1e12
+        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s (H3 map build {prep_ms * 1e3:.0f} us)")
+        secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+                          "roofline": roofline("h3", "mfma", tf, flops), "tile_prep_and_map_ms": round(prep_ms, 4)})
 
     if args.only in (None, "paged_prefill") and not (args.only is None and args.no_secondary):
         case = workloads.config6()

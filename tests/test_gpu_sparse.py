@@ -446,3 +446,31 @@ def test_h3_raster_pipeline_end_to_end():
     check_h3_map(bmap, _h3_scores(qt, kt, sizes, 1, d ** -0.5), n_pre, topk)
     ref_t, _ = oracle.block_sparse_attention(qt, kt, vt, bmap, sizes, d ** -0.5)
     assert_close("out", host(out), oracle.h3_from_tile_order(ref_t, segs, shape), OUT_TOL, bf16_output=True)
+
+
+def test_h3_full_size_sampled_tiles():
+    # workload 11: 512 prefix rows (8 dense tiles) ahead of the 16x32x32 video;
+    # the GPU-built H3 map is checked against fp64 scores, then sampled prefix
+    # and video query tiles against the oracle on that map
+    from workloads import config11
+
+    case = config11()
+    segs = case.extra["prefix_segments"]
+    announce("h3 full size")
+    prep = sav.vsa_h3_prepare(dev(case.q), dev(case.k), dev(case.v), segs, case.video_shape, case.topk, case.scale)
+    torch.cuda.synchronize()
+    qt, kt, vt = prep["q"].cpu(), prep["k"].cpu(), prep["v"].cpu()
+    sizes = prep["tile_sizes"].cpu().numpy()
+    n_pre = prep["num_prefix_tiles"]
+    bmap = prep["block_map"].cpu().numpy().astype(bool)
+    assert n_pre == 8 and np.array_equal(sizes, oracle.h3_tile_metadata(segs, case.video_shape)[1])
+    check_h3_map(bmap, _h3_scores(qt, kt, sizes, 1, case.scale), n_pre, case.topk)
+    out, lse = run(qt, kt, vt, bmap.astype(np.uint8), sizes, case.scale)
+    tiles = [0, 7, 8, 9, 100, 263]
+    heads = [0, 11]
+    ref_o, ref_l = oracle.block_sparse_attention(qt, kt, vt, bmap, sizes, case.scale, heads=heads, q_tiles=tiles)
+    rows = np.concatenate([np.arange(a * 64, a * 64 + 64) for a in tiles])
+    rt = torch.from_numpy(rows).cuda()
+    assert_close("out", host(out.index_select(1, rt))[:, :, heads], ref_o[:, rows][:, :, heads], OUT_TOL,
+                 bf16_output=True)
+    assert_close("lse", host(lse.index_select(2, rt))[:, heads], ref_l[:, heads][:, :, rows], LSE_TOL)

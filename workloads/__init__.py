@@ -382,3 +382,21 @@ def config10() -> PaddedCase:
     ln = rng.integers(1024, 4097, 4)
     return padded_case(4, 4096, 4096, num_heads=24, num_kv_heads=24, head_dim=128, seed=10, q_lens=ln, k_lens=ln,
                        name="padded-b4-s4096-valid1k-4k-h24-d128")
+
+
+def config11() -> VideoCase:
+    """H3 layout: workload 5's 16x32x32 video behind a 512-row text prefix (one
+    segment: 8 dense prefix tiles ahead of 256 video tiles), 12 heads, D=128,
+    top-32 among the video tiles."""
+    segs = (512,)
+    n = sum(segs) + 16 * 32 * 32
+    seed = 11
+    return VideoCase(
+        name="h3-prefix512-video-16x32x32-t444-h12-d128-top32",
+        q=randn_bf16((1, n, 12, 128), 1000 * seed + 0),
+        k=randn_bf16((1, n, 12, 128), 1000 * seed + 1),
+        v=randn_bf16((1, n, 12, 128), 1000 * seed + 2),
+        topk=32,
+        seed=seed,
+        extra={"prefix_segments": segs},
+    )
