@@ -312,13 +312,15 @@ def config5() -> VideoCase:
 SLIDING_WINDOW = 4096  # tokens before the query that stay visible
 
 
-def config8() -> PagedCase:
+def config8(decode_case: PagedCase | None = None) -> PagedCase:
     """Sliding-window decode: the decode workload (64 contexts of 1k..32k over
     a shuffled block pool, 32/8 heads, D=128) with a window of 4096 preceding
-    tokens (the window length of common sliding-window decoders)."""
-    c = config4()
-    c.name = "swa-decode-64seq-ctx1k-32k-w4096-h32kv8-d128"
-    return c
+    tokens (the window length of common sliding-window decoders). An already
+    built workload 4 may be passed in to share its cache."""
+    import dataclasses
+
+    base = config4() if decode_case is None else decode_case
+    return dataclasses.replace(base, name="swa-decode-64seq-ctx1k-32k-w4096-h32kv8-d128")
 
 
 @dataclass
