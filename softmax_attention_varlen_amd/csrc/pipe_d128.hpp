@@ -240,6 +240,111 @@ __device__ __forceinline__ void tile_step(f32x16 (&s)[KB], f32x16 (&sn)[KB], con
   pv<KB>(vt, L, p, o);
 }
 
+// V^T operand of PV MFMA (chunk c, d-block b) for the transposing reads of pv().
+__device__ __forceinline__ bf16x8 read_vt(const lds_bf16x4* base, int c, int b) {
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 32 * c + 8 * b));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 260 + 32 * c + 8 * b));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Software-pipelined step for tile j of 64 keys (two 32-key halves per wave):
+// the softmax of tile j (s) runs under 32 MFMAs, the S^T of tile j+1 (sn, K from
+// nk) on even slots and, when PV, the O^T += V^T P^T of tile j-1 (P in p_prev,
+// V^T from vt_prev) on odd slots, so every MFMA has VALU work beside it. Slots
+// 0-5 carry the row maximum, slot 6 the reference update, slots 7-31 the 32
+// exp2. P of tile j goes to p_cur. O and the row sum are rescaled at the end
+// (after the PV of tile j-1, which still belongs to the old reference).
+template <bool PV>
+__device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], const char* nk, uint32_t vt_prev,
+                                             const Lane& L, const bf16x8 (&q)[8], const bf16x8 (&p_prev)[4],
+                                             bf16x8 (&p_cur)[4], f32x16 (&o)[4], Softmax& st, float c, bool mask,
+                                             int key0, int len_k, int lim) {
+  if (mask) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * L.g + (r & 3);
+        if (key >= len_k || key > lim) s[kb][r] = kNegInf;
+      }
+    }
+  }
+  const char* kbase = nk + L.k_base;
+  const lds_bf16x4* vbase = (const lds_bf16x4*)(vt_prev + L.v_base);
+  bf16x8 kr[2];  // K operand two S^T steps (four slots) ahead
+#pragma unroll
+  for (int i = 0; i < 2; ++i) kr[i] = ld_lds16(kbase, (i % 2) * kHalfBytes + (i / 2) * 32);
+  bf16x8 va[2];
+  if (PV) {
+    va[0] = read_vt(vbase, 0, 0);
+    va[1] = read_vt(vbase, 0, 1);
+  }
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sn[kb][r] = 0.f;
+  }
+  float mx4[4];
+  float alpha = 1.f, ms = 0.f, m_ref = st.m;
+  bool need = false;
+  f32x8 e;
+  float rs0 = 0.f, rs1 = 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int slot = 0; slot < 32; ++slot) {
+    const int t = slot >> 1;
+    if ((slot & 1) == 0) {  // S^T of tile j+1: step t = (d-block t/2, key half t%2)
+      sn[t & 1] = mfma32x32x16(kr[t & 1], q[t >> 1], sn[t & 1]);
+      if (t + 2 < 16) kr[t & 1] = ld_lds16(kbase, ((t + 2) % 2) * kHalfBytes + ((t + 2) / 2) * 32);
+    } else if (PV) {  // PV of tile j-1: chunk t/4, d-block t%4
+      const bf16x8 a = va[t & 1];
+      if (t + 2 < 16) va[t & 1] = read_vt(vbase, (t + 2) >> 2, (t + 2) & 3);
+      o[t & 3] = mfma32x32x16(a, p_prev[t >> 2], o[t & 3]);
+    }
+    if (slot < 4) {  // row maximum: chain slot over 8 keys (2 slots per chain pair)
+#pragma unroll
+      for (int u = 0; u < 1; ++u) {
+        const int ch = slot;  // chain ch: half ch/2, elements 8(ch%2) .. +7
+        float m = fmaxf(s[ch >> 1][8 * (ch & 1)], s[ch >> 1][8 * (ch & 1) + 1]);
+#pragma unroll
+        for (int i = 2; i < 8; ++i) m = fmaxf(m, s[ch >> 1][8 * (ch & 1) + i]);
+        mx4[ch] = m;
+      }
+    } else if (slot == 5) {
+      const float mx = pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
+      const float m_new = fmaxf(st.m, mx);
+      need = (m_new - st.m) * c > kRescaleThreshold;  // true on the first finite maximum
+      alpha = need ? hw_exp2((st.m - m_new) * c) : 1.f;
+      m_ref = need ? m_new : st.m;
+      ms = (m_ref == kNegInf ? 0.f : m_ref) * c;
+    } else if (slot >= 7) {  // elements x with 7 + (3x)/4 == slot: 32 exp2 over slots 7..31
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        if (7 + (3 * x) / 4 == slot) {
+          const int ch = x >> 3, u = x & 7;
+          e[u] = hw_exp2(__builtin_fmaf(s[ch >> 1][8 * (ch & 1) + u], c, -ms));
+          if (u & 1) {
+            rs1 += e[u];
+          } else {
+            rs0 += e[u];
+          }
+          if (u == 7) p_cur[ch] = to_bf16x8(e);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float rs = rs0 + rs1;
+  st.l = st.l * alpha + rs;
+  st.m = m_ref;
+  // Rare rescale of O, after the PV of tile j-1 (old reference). The row sum
+  // takes part in the condition so that the exp2 stay in their slots.
+  if (__builtin_amdgcn_ballot_w64(need || rs != rs) != 0ull) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) o[b] *= alpha;
+  }
+}
+
 // Write the wave's 32 normalised output rows (bf16) and their LSE. o holds
 // O^T (d = 32b + 8*grp + 4g + i for element 4*grp + i of block b); st.l is
 // lane-partial.

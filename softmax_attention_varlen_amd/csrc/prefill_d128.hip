@@ -7,6 +7,8 @@
 // pipe_d128.hpp. Per tile a wave issues the S^T MFMAs of the next tile
 // interleaved with the softmax of the current one, then the PV MFMAs of the
 // current tile. One barrier per tile guards the ring.
+#include <type_traits>
+
 #include "key_rows.hpp"
 #include "launch.hpp"
 #include "pipe_d128.hpp"
@@ -36,7 +38,7 @@ struct Ring {
 // block_tables, with context_lens[doc] (clamped to max_len_k) keys per
 // document; otherwise from contiguous rows delimited by cu_k. q_used / k_used
 // (nullable) cut each document to a valid prefix of its rows.
-template <bool CAUSAL, bool PAGED, int NW, int NS>
+template <bool CAUSAL, bool PAGED, int NW, int NS, bool PP>
 __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int total_q, int total_k,
@@ -47,6 +49,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
   using R = Ring<NW>;
   constexpr int BM = 32 * NW;
   static_assert(NS == 3 || NS == 4, "the load-count waits below cover 3- and 4-stage rings");
+  static_assert(!PP || NS == 4, "the pipelined loop keeps tile j-1's V while tile j+2 loads: 4 stages");
   __shared__ __attribute__((aligned(1024))) char smem[NS * kStageBytes];
 
   // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs, so
@@ -124,9 +127,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
 #pragma unroll
     for (int b = 0; b < 8; ++b) qr[b] = as_bf16x8(ld_global16(qp + b * 16));
   }
-  // prologue: the first NS-1 tiles in flight
+  // prologue: the first NS-1 tiles in flight (the pipelined loop: 2)
+  constexpr int PRE = PP ? 2 : NS - 1;
 #pragma unroll
-  for (int s = 0; s < NS - 1; ++s) {
+  for (int s = 0; s < PRE; ++s) {
     if (s < ntiles) {
       const long off = rows.row(s * kBN);
       R::issue(kb0 + off, vb0 + off, stride_bytes, len_k - s * kBN, ring + s * kStageBytes, w, lane);
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
 
   if (ntiles > 0) {
     // tile 0 has landed once at most the later prologue tiles are in flight
-    const int later = (ntiles < NS - 1 ? ntiles : NS - 1) - 1;
+    const int later = (ntiles < PRE ? ntiles : PRE) - 1;
     if (later >= 2) {
       wait_loads_barrier<2 * R::LOADS>();
     } else if (later == 1) {
@@ -154,6 +158,55 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
     if (ntiles_w > 0) qk<2>(smem, L, qr, sa);
   }
   settle_q(qr);
+
+  if constexpr (PP) {
+    // Pipelined loop: step j runs the softmax of tile j under the S^T MFMAs of
+    // tile j+1 and the PV MFMAs of tile j-1. Tile j+2 is issued at step j into
+    // the stage of tile j-2, whose PV every wave finished in step j-1 (the
+    // barrier); tile j-1's V stays resident through step j.
+    bf16x8 pa[4], pb[4];
+    auto step = [&](int j, auto pv_tag, f32x16 (&s)[2], f32x16 (&sn)[2], bf16x8 (&pp)[4], bf16x8 (&pc)[4]) {
+      constexpr bool HAS_PV = decltype(pv_tag)::value;
+      if (j + 1 < ntiles) {
+        wait_loads_barrier<0>();  // tile j+1 (issued at step j-1) has landed everywhere
+        const int jn = j + 2;
+        if (jn < ntiles) {
+          const long off = rows.row(jn * kBN);
+          R::issue(kb0 + off, vb0 + off, stride_bytes, len_k - jn * kBN, ring + (jn % 4) * kStageBytes, w, lane);
+        }
+      }
+      const uint32_t vt_prev = ring + ((j + 3) % 4) * kStageBytes + kTileBytes;  // V of tile j-1
+      if (j < ntiles_w) {
+        const char* nk = smem + ((j + 1 < ntiles ? j + 1 : j) % 4) * kStageBytes;
+        const int key0 = j * kBN;
+        const bool mask = !(j < nomask_w && key0 + kBN <= len_k);
+        tile_step_pp<HAS_PV>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, mask, key0, len_k,
+                             CAUSAL ? row + diag : 0x7fffffff);
+      } else if (HAS_PV && j == ntiles_w) {
+        pv<2>(vt_prev, L, pp, o);  // this wave's last tile
+      }
+    };
+    using yes = std::integral_constant<bool, true>;
+    using no = std::integral_constant<bool, false>;
+    if (ntiles > 0) {
+      step(0, no{}, sa, sb, pb, pa);
+      for (int j = 1; j < ntiles; j += 2) {
+        step(j, yes{}, sb, sa, pa, pb);
+        if (j + 1 < ntiles) step(j + 1, yes{}, sa, sb, pb, pa);
+      }
+      if (ntiles_w == ntiles) {  // the last tile's PV (its stage is never refilled)
+        const uint32_t vt = ring + ((ntiles - 1) % 4) * kStageBytes + kTileBytes;
+        if ((ntiles - 1) & 1) {
+          pv<2>(vt, L, pb, o);
+        } else {
+          pv<2>(vt, L, pa, o);
+        }
+      }
+    }
+    store_rows(o, st, L, c, row < len_q, out + ((long)(q0 + row_c) * hq + h) * kD,
+               lse != nullptr ? lse + (long)h * total_q + q0 + row_c : nullptr);
+    return;
+  }
 
   // one iteration of the ring: refill, then this wave's compute for tile j
   auto iteration = [&](int j, f32x16 (&s)[2], f32x16 (&sn)[2]) {
@@ -191,13 +244,18 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
 
 constexpr int kPrefillWaves = 8;
 constexpr int kPrefillStages = 3;
+#ifndef PREFILL_PIPELINED
+#define PREFILL_PIPELINED 1
+#endif
+constexpr bool kPrefillPipelined = PREFILL_PIPELINED;
 
 bool prefill_d128_supported(const VarlenArgs& a) { return a.head_dim == 128; }
 
 template <bool CAUSAL, bool PAGED>
 static void launch_prefill_d128_t(const VarlenArgs& a, int tiles, long n_items, long per_xcd, hipStream_t stream) {
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((prefill_d128_kernel<CAUSAL, PAGED, kPrefillWaves, kPrefillStages>), dim3((unsigned)(per_xcd * 8)),
+  constexpr int NS = kPrefillPipelined ? 4 : kPrefillStages;
+  hipLaunchKernelGGL((prefill_d128_kernel<CAUSAL, PAGED, kPrefillWaves, NS, kPrefillPipelined>), dim3((unsigned)(per_xcd * 8)),
                      dim3(64 * kPrefillWaves), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch, a.total_q, a.total_k, tiles, a.num_heads,
                      a.num_kv_heads, (int)n_items, (int)per_xcd, c, (uint16_t*)a.out, a.lse, a.block_tables,
