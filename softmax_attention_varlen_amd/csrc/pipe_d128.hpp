@@ -317,18 +317,27 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
       alpha = need ? hw_exp2((st.m - m_new) * c) : 1.f;
       m_ref = need ? m_new : st.m;
       ms = (m_ref == kNegInf ? 0.f : m_ref) * c;
-    } else if (slot >= 7) {  // elements x with 7 + (3x)/4 == slot: 32 exp2 over slots 7..31
+    } else if (slot >= 7) {
+      // element x's exp2 runs in slot 7 + 3x/4 (slots 7..30); its row-sum add,
+      // and the bf16 packing of a finished chunk, one slot later, so that no
+      // VALU op waits on the exp2 issued just before it
 #pragma unroll
       for (int x = 0; x < 32; ++x) {
-        if (7 + (3 * x) / 4 == slot) {
-          const int ch = x >> 3, u = x & 7;
-          e[u] = hw_exp2(__builtin_fmaf(s[ch >> 1][8 * (ch & 1) + u], c, -ms));
+        if (8 + (3 * x) / 4 == slot) {
+          const int u = x & 7;
           if (u & 1) {
             rs1 += e[u];
           } else {
             rs0 += e[u];
           }
-          if (u == 7) p_cur[ch] = to_bf16x8(e);
+          if (u == 7) p_cur[x >> 3] = to_bf16x8(e);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 32; ++x) {
+        if (7 + (3 * x) / 4 == slot) {
+          const int ch = x >> 3, u = x & 7;
+          e[u] = hw_exp2(__builtin_fmaf(s[ch >> 1][8 * (ch & 1) + u], c, -ms));
         }
       }
     }
