@@ -43,26 +43,28 @@ WRITE_SCALE = 1.0
 CSRC = os.path.join(ROOT, "softmax_attention_varlen_amd", "csrc")
 _PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "key_rows.hpp"]
 _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
+_SPARSE_SRC = ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"]
 TRAFFIC = {
-    "dense": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 73840.5, "write_kib": 49944.6,
-              "sources": _PREFILL_SRC, "sha256": "8506cc1a2e07b95a"},
-    "causal": {"kernel": "prefill_d128_kernel<true,false,8,4,true>", "fetch_kib": 109916.6, "write_kib": 142434.3,
-               "sources": _PREFILL_SRC, "sha256": "8506cc1a2e07b95a"},
+    "dense": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 73841.0, "write_kib": 49944.1,
+              "sources": _PREFILL_SRC, "sha256": "198dafcc65ab3f7c"},
+    "causal": {"kernel": "prefill_d128_kernel<true,false,8,4,true>", "fetch_kib": 109773.1, "write_kib": 142435.2,
+               "sources": _PREFILL_SRC, "sha256": "198dafcc65ab3f7c"},
     "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443512.9, "write_kib": 3040.5,
               "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
-    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 428675.5, "write_kib": 49920.1,
-               "sources": ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"], "sha256": "0189fa2bd092cb4f"},
-    "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true>", "fetch_kib": 711151.3,
-                      "write_kib": 87200.1, "sources": _PREFILL_SRC, "sha256": "8506cc1a2e07b95a"},
+    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 428221.4, "write_kib": 49920.1,
+               "sources": _SPARSE_SRC, "sha256": "0ddcd913037e3a26"},
+    "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true>", "fetch_kib": 707643.5,
+                      "write_kib": 87202.4, "sources": _PREFILL_SRC, "sha256": "198dafcc65ab3f7c"},
     "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445751.0, "write_kib": 12150.3,
              "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
-    "h3": {"kernel": "block_sparse_d128_kernel"},
+    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 580915.4, "write_kib": 51480.3,
+           "sources": _SPARSE_SRC, "sha256": "0ddcd913037e3a26"},
     "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531393.3, "write_kib": 3081.2,
             "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
-    "masked": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 28935.0, "write_kib": 49923.3,
-               "sources": _PREFILL_SRC, "sha256": "8506cc1a2e07b95a"},
-    "padded": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 103344.3, "write_kib": 66229.3,
-               "sources": _PREFILL_SRC, "sha256": "8506cc1a2e07b95a"},
+    "masked": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 28935.0, "write_kib": 49922.6,
+               "sources": _PREFILL_SRC, "sha256": "198dafcc65ab3f7c"},
+    "padded": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 103608.4, "write_kib": 66229.1,
+               "sources": _PREFILL_SRC, "sha256": "198dafcc65ab3f7c"},
 }
 
 
