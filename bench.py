@@ -296,7 +296,8 @@ def bench_kv_write(case, steps, warmup):
     sl = torch.from_numpy(slots.astype(np.int32)).to(dev)
     ms = time_steps(lambda: sav.attn_paged_kv_write(k_new, v_new, sl, kv), steps, warmup)
     del kv
-    return ms, 2.0 * 2 * n * case.num_kv_heads * case.head_dim + 4 * n  # read + write of K and V, slots
+    # bf16 K and V rows read once and written once, plus the int32 slot of each token
+    return ms, 2 * 2 * 2.0 * n * case.num_kv_heads * case.head_dim + 4 * n
 
 
 def bench_h3(case, steps, warmup):
