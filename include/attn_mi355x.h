@@ -304,7 +304,8 @@ attn_status_t attn_paged_prefill_workspace_size(int32_t batch, int32_t num_heads
 attn_status_t attn_block_map_to_index(const uint8_t* block_map, int32_t rows, int32_t n_cols,
                                       int32_t* idx, int32_t* num, void* stream);
 
-/* Workspace bytes for attn_block_sparse_fwd (the index lists it builds). */
+/* Workspace bytes for attn_block_sparse_fwd: the kept-tile index lists it
+ * builds, their lengths, and the order in which it runs the query tiles. */
 attn_status_t attn_block_sparse_workspace_size(int32_t batch, int32_t num_heads, int32_t num_tiles,
                                                size_t* bytes);
 

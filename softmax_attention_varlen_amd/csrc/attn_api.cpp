@@ -361,8 +361,9 @@ attn_status_t attn_block_sparse_fwd(const void* q, const void* k, const void* v,
   const size_t rows = (size_t)batch * num_heads * num_tiles;
   int32_t* idx = (int32_t*)workspace;
   int32_t* num = idx + rows * (size_t)num_tiles;
+  int32_t* order = num + rows;
   attn::SparseArgs a{q, k, v, block_map, tile_sizes, batch, num_tiles, num_heads, num_kv_heads, head_dim,
-                     softmax_scale, out, lse, idx, num};
+                     softmax_scale, out, lse, idx, num, order};
   return from_hip(attn::launch_block_sparse_fwd(a, (hipStream_t)stream));
 }
 

@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kSparseThreads, (D <= 128 ? 2 : 1)) void block_spar
 
 size_t sparse_workspace_bytes(int batch, int num_heads, int num_tiles) {
   const size_t rows = (size_t)batch * num_heads * num_tiles;
-  return rows * (size_t)num_tiles * sizeof(int32_t) + rows * sizeof(int32_t);
+  return rows * (size_t)num_tiles * sizeof(int32_t) + 2 * rows * sizeof(int32_t);
 }
 
 template <int D>

@@ -18,6 +18,15 @@
 // Padding keys (at or past a tile's size) are masked; padding query rows are
 // written as zeros with LSE = -inf; a query tile with no kept key gets zeros
 // and -inf as well.
+//
+// Item order: workgroup slot s of XCD x runs item order[x*per_xcd + s]. A small
+// kernel fills order per XCD chunk (the items that XCD runs, so its L2 keeps
+// serving the same heads) with the longest items first: a map can keep every
+// key tile for a few query tiles (the dense prefix rows of the H3 layout) and
+// far fewer for the rest, and a long item dispatched late in its chunk would
+// set the end of the launch. Items fall into 16 classes by kept-tile count;
+// the order is stable within a class, so a map with equal counts keeps the
+// plain order. The order changes when an item runs, never what it computes.
 #include "launch.hpp"
 #include "pipe_d128.hpp"
 
@@ -33,6 +42,85 @@ constexpr int kMergeOBytes = 32 * 128 * 4;   // one wave's fp32 O^T block
 constexpr int kListCap = kSparseD128MaxTiles;  // the whole kept-tile list is staged in LDS
 static_assert(2 * kMergeOBytes + 2 * 512 <= kSparseLds, "merge area must fit in the ring");
 
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderWaves = kOrderThreads / 64;
+constexpr int kOrderBins = 16;
+
+// One workgroup per XCD chunk [x*per_xcd, min((x+1)*per_xcd, n_items)):
+// writes a permutation of the chunk's item ids into the same range of order,
+// class by class (class 0 holds the longest items), in item order within a
+// class.
+__global__ __launch_bounds__(kOrderThreads) void order_items_kernel(const int32_t* __restrict__ num, int n_items,
+                                                                    int per_xcd, int32_t* __restrict__ order) {
+  __shared__ int wave_max[kOrderWaves];
+  __shared__ int wave_cnt[kOrderWaves][kOrderBins];
+  __shared__ int next[kOrderBins];  // bin sizes, then the next free position of each class
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int base = blockIdx.x * per_xcd;
+  const int len = clampi(n_items - base, 0, per_xcd);
+  const unsigned long long below = (1ull << lane) - 1ull;
+
+  int m = 0;
+  for (int i = tid; i < len; i += kOrderThreads) m = max(m, num[base + i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+  if (lane == 0) wave_max[w] = m;
+  if (tid < kOrderBins) next[tid] = 0;
+  __syncthreads();
+  int mx = 0;
+#pragma unroll
+  for (int j = 0; j < kOrderWaves; ++j) mx = max(mx, wave_max[j]);
+  // class of item i of the chunk (-1 past the end): non-increasing in the count
+  auto cls = [&](int i) -> int {
+    if (i >= len) return -1;
+    const int c = clampi(num[base + i], 0, mx);
+    return (kOrderBins - 1) - (int)(((long)c * kOrderBins) / ((long)mx + 1));
+  };
+
+  for (int i0 = 0; i0 < len; i0 += kOrderThreads) {
+    const int k = cls(i0 + tid);
+#pragma unroll
+    for (int b = 0; b < kOrderBins; ++b) {
+      const unsigned long long bits = __ballot(k == b);
+      if (lane == 0 && bits != 0ull) atomicAdd(&next[b], __popcll(bits));
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int sum = 0;
+    for (int b = 0; b < kOrderBins; ++b) {
+      const int t = next[b];
+      next[b] = sum;
+      sum += t;
+    }
+  }
+  __syncthreads();
+
+  for (int i0 = 0; i0 < len; i0 += kOrderThreads) {
+    const int k = cls(i0 + tid);
+    int rank = 0;
+#pragma unroll
+    for (int b = 0; b < kOrderBins; ++b) {
+      const unsigned long long bits = __ballot(k == b);
+      if (k == b) rank = __popcll(bits & below);
+      if (lane == 0) wave_cnt[w][b] = __popcll(bits);
+    }
+    __syncthreads();
+    if (k >= 0) {
+      int pos = next[k] + rank;
+      for (int j = 0; j < w; ++j) pos += wave_cnt[j][k];
+      order[base + pos] = base + i0 + tid;
+    }
+    __syncthreads();
+    if (tid < kOrderBins) {
+      int add = 0;
+      for (int j = 0; j < kOrderWaves; ++j) add += wave_cnt[j][tid];
+      next[tid] += add;
+    }
+    __syncthreads();
+  }
+}
+
 struct Entry {
   int tile, size;
 };
@@ -47,16 +135,17 @@ __device__ __forceinline__ Entry unpack(int32_t v, int num_tiles) {
 __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ tile_sizes, const int32_t* __restrict__ kidx, const int32_t* __restrict__ knum,
-    int num_tiles, int hq, int hkv, int n_items, int per_xcd, float c, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ order, int num_tiles, int hq, int hkv, int n_items, int per_xcd, float c,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) char smem[kSparseLds];
   __shared__ int32_t lst[kListCap];
 
-  // XCD-aware order: XCD x runs logical items [x*per_xcd, (x+1)*per_xcd); query
-  // tiles run fastest, so one XCD's L2 serves the K/V of few heads.
+  // XCD-aware order: XCD x runs the items of [x*per_xcd, (x+1)*per_xcd) (query
+  // tiles fastest, so one XCD's L2 serves the K/V of few heads), longest first.
   const int hw = blockIdx.x;
-  const int item = (hw & 7) * per_xcd + (hw >> 3);
-  if (item >= n_items) return;
+  const int slot = (hw & 7) * per_xcd + (hw >> 3);
+  if (slot >= n_items) return;
+  const int item = clampi(order[slot], 0, n_items - 1);
   const int a = item % num_tiles;
   const int bh = item / num_tiles;
   const int h = bh % hq;
@@ -201,9 +290,11 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
 hipError_t launch_block_sparse_d128(const SparseArgs& a, hipStream_t stream) {
   const long n_items = (long)a.batch * a.num_heads * a.num_tiles;
   const long per_xcd = (n_items + 7) / 8;
+  hipLaunchKernelGGL(order_items_kernel, dim3(8), dim3(kOrderThreads), 0, stream, a.num, (int)n_items, (int)per_xcd,
+                     a.order);
   hipLaunchKernelGGL(block_sparse_d128_kernel, dim3((unsigned)(per_xcd * 8)), dim3(64 * kSW), 0, stream,
                      (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.tile_sizes, a.idx, a.num,
-                     a.num_tiles, a.num_heads, a.num_kv_heads, (int)n_items, (int)per_xcd, a.scale * kLog2e,
+                     a.order, a.num_tiles, a.num_heads, a.num_kv_heads, (int)n_items, (int)per_xcd, a.scale * kLog2e,
                      (uint16_t*)a.out, a.lse);
   return hipGetLastError();
 }

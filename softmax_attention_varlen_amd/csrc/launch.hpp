@@ -134,6 +134,7 @@ struct SparseArgs {
   float* lse;
   int32_t* idx;  // workspace: [batch*num_heads*num_tiles][num_tiles]
   int32_t* num;  // workspace: [batch*num_heads*num_tiles]
+  int32_t* order;  // workspace: [batch*num_heads*num_tiles], the order the head_dim-128 kernel runs items in
 };
 
 size_t sparse_workspace_bytes(int batch, int num_heads, int num_tiles);

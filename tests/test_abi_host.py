@@ -115,7 +115,7 @@ def test_sparse_validation(kw, code):
 
 
 def test_sparse_workspace_query():
-    assert sav.attn_block_sparse_workspace_size(1, 12, 256) == 12 * 256 * 256 * 4 + 12 * 256 * 4
+    assert sav.attn_block_sparse_workspace_size(1, 12, 256) == 12 * 256 * 256 * 4 + 2 * 12 * 256 * 4
 
 
 def test_map_to_index_validation():

@@ -106,6 +106,45 @@ def test_full_map_matches_dense_oracle_and_is_deterministic():
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+def test_item_order_longest_first_is_a_permutation():
+    # The head_dim-128 kernel runs the query tiles of each XCD chunk (8 equal
+    # chunks of the (batch, head, tile) items) longest first. The order it
+    # leaves in the workspace (after the index lists and their lengths) must
+    # be a permutation of each chunk, non-increasing in the 16 count classes
+    # and in item order within a class; the result must not depend on it.
+    b, nt, h, d = 1, 40, 3, 128
+    q, k, v = (randn_bf16((b, nt * 64, h, d), 350 + j) for j in range(3))
+    rng = np.random.default_rng(35)
+    bmap = rng.random((b, h, nt, nt)) < 0.1
+    bmap[0, :, :4] = True      # dense rows at the start of every head
+    bmap[0, 1, 20:23] = True   # and in the middle of one
+    bmap[0, 2, 30] = False     # an empty row
+    sizes = np.full(nt, 64, dtype=np.int32)
+    ws = torch.empty(sav.attn_block_sparse_workspace_size(b, h, nt), dtype=torch.uint8, device="cuda")
+    announce("sparse item order")
+    out, lse = sav.attn_block_sparse_fwd(dev(q), dev(k), dev(v), dev(bmap.astype(np.uint8)), dev(sizes), d ** -0.5,
+                                         return_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.block_sparse_attention(q, k, v, bmap, sizes, d ** -0.5)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("lse", host(lse), ref_l, LSE_TOL)
+    rows = b * h * nt
+    words = ws.view(torch.int32).cpu().numpy()
+    counts = bmap.reshape(rows, nt).sum(1)
+    assert np.array_equal(words[rows * nt:rows * nt + rows], counts)
+    order = words[rows * nt + rows:rows * nt + 2 * rows]
+    per = (rows + 7) // 8
+    for x in range(8):
+        lo, hi = x * per, min((x + 1) * per, rows)
+        chunk = order[lo:hi]
+        assert sorted(chunk.tolist()) == list(range(lo, hi))
+        cls = 15 - (counts[chunk] * 16) // (counts[lo:hi].max() + 1)
+        assert np.all(np.diff(cls) >= 0)
+        for c in np.unique(cls):
+            assert np.all(np.diff(chunk[cls == c]) > 0)
+    assert order[0] < 4 and counts[order[0]] == nt
+
+
 def test_guards_and_pad_rows_zero():
     shape, tile = (3, 5, 6), (2, 2, 3)
     (qt, kt, vt), sizes = _tiled(shape, tile, 1, 2, 2, 64, seed=330)
