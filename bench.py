@@ -51,14 +51,14 @@ TRAFFIC = {
                "sources": _PREFILL_SRC, "sha256": "198dafcc65ab3f7c"},
     "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443512.9, "write_kib": 3040.5,
               "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
-    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 428221.4, "write_kib": 49920.1,
-               "sources": _SPARSE_SRC, "sha256": "0ddcd913037e3a26"},
+    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 419446.2, "write_kib": 49920.1,
+               "sources": _SPARSE_SRC, "sha256": "e02a201a96d0d3bd"},
     "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true>", "fetch_kib": 707643.5,
                       "write_kib": 87202.4, "sources": _PREFILL_SRC, "sha256": "198dafcc65ab3f7c"},
     "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445751.0, "write_kib": 12150.3,
              "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
-    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 580915.4, "write_kib": 51480.3,
-           "sources": _SPARSE_SRC, "sha256": "0ddcd913037e3a26"},
+    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 610403.7, "write_kib": 51480.2,
+           "sources": _SPARSE_SRC, "sha256": "e02a201a96d0d3bd"},
     "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531393.3, "write_kib": 3081.2,
             "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
     "masked": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 28935.0, "write_kib": 49922.6,

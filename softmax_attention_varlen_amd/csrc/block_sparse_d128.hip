@@ -45,6 +45,7 @@ static_assert(2 * kMergeOBytes + 2 * 512 <= kSparseLds, "merge area must fit in 
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderWaves = kOrderThreads / 64;
 constexpr int kOrderBins = 16;
+constexpr int kOrderStaged = 4 * kOrderThreads;  // counts held in LDS; the rest of a chunk is re-read
 
 // One workgroup per XCD chunk [x*per_xcd, min((x+1)*per_xcd, n_items)):
 // writes a permutation of the chunk's item ids into the same range of order,
@@ -55,13 +56,20 @@ __global__ __launch_bounds__(kOrderThreads) void order_items_kernel(const int32_
   __shared__ int wave_max[kOrderWaves];
   __shared__ int wave_cnt[kOrderWaves][kOrderBins];
   __shared__ int next[kOrderBins];  // bin sizes, then the next free position of each class
+  __shared__ int staged[kOrderStaged];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int base = blockIdx.x * per_xcd;
   const int len = clampi(n_items - base, 0, per_xcd);
   const unsigned long long below = (1ull << lane) - 1ull;
 
+  // one pass over the counts (all loads in flight together), the first
+  // kOrderStaged of them kept in LDS
   int m = 0;
-  for (int i = tid; i < len; i += kOrderThreads) m = max(m, num[base + i]);
+  for (int i = tid; i < len; i += kOrderThreads) {
+    const int c = num[base + i];
+    if (i < kOrderStaged) staged[i] = c;
+    m = max(m, c);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
   if (lane == 0) wave_max[w] = m;
@@ -73,7 +81,7 @@ __global__ __launch_bounds__(kOrderThreads) void order_items_kernel(const int32_
   // class of item i of the chunk (-1 past the end): non-increasing in the count
   auto cls = [&](int i) -> int {
     if (i >= len) return -1;
-    const int c = clampi(num[base + i], 0, mx);
+    const int c = clampi(i < kOrderStaged ? staged[i] : num[base + i], 0, mx);
     return (kOrderBins - 1) - (int)(((long)c * kOrderBins) / ((long)mx + 1));
   };
 
