@@ -10,9 +10,10 @@
 // The kept key tiles come from the block map as ascending lists with empty
 // tiles dropped, each entry packed as (size << 24) | tile. K and V stream
 // through separate two-stage LDS rings (direct-to-LDS loads, the
-// conflict-free layout of pipe_d128.hpp): step j reads K of tile j+1 (the S^T
-// MFMAs of the next tile run under this tile's softmax) and V of tile j, while
-// K of tile j+2 and V of tile j+1 are in flight. With two workgroups per CU
+// conflict-free layout of pipe_d128.hpp): step j runs the softmax of tile j
+// under the S^T MFMAs of tile j+1 and the PV MFMAs of tile j-1, reading K of
+// tile j+1 and V of tile j-1, while K of tile j+2 and V of tile j are in
+// flight. With two workgroups per CU
 // (66.5 KB of LDS each) a SIMD holds two waves.
 //
 // Padding keys (at or past a tile's size) are masked; padding query rows are
@@ -27,6 +28,8 @@
 // set the end of the launch. Items fall into 16 classes by kept-tile count;
 // the order is stable within a class, so a map with equal counts keeps the
 // plain order. The order changes when an item runs, never what it computes.
+#include <type_traits>
+
 #include "launch.hpp"
 #include "pipe_d128.hpp"
 
@@ -211,47 +214,66 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   auto entry = [&](int j) -> int32_t { return lst[j]; };
   // entry of tile j (unpacked) and raw entries of tiles j+1, j+2: each list
   // word is read one step before its first use
-  Entry e0{0, 1};
+  Entry cur{0, 1};
   int32_t n1 = 0, n2 = 0;
-  if (count > 0) e0 = unpack(entry(0), num_tiles);
+  if (count > 0) cur = unpack(entry(0), num_tiles);
   if (count > 1) n1 = entry(1);
   if (count > 2) n2 = entry(2);
 
   if (count > 0) {
-    issue_k(e0, 0);
-    issue_v(e0, 0);
+    issue_k(cur, 0);
     if (count > 1) {
       issue_k(unpack(n1, num_tiles), 1);
-      wait_loads_barrier<2 * kSIPW>();  // K of tile 0 has landed
+      wait_loads_barrier<kSIPW>();  // K of tile 0 has landed
     } else {
-      wait_loads_barrier<kSIPW>();
+      wait_loads_barrier<0>();
     }
     if (wave_live) qk<1>(smem, L, qr, sa);
   }
   settle_q(qr);
 
-  // step j: K of tile j+1 and V of tile j must have landed (everything issued
-  // so far); all waves are done with K of tile j and V of tile j-1, whose
-  // stages receive K of tile j+2 and V of tile j+1.
-  auto iteration = [&](int j, f32x16 (&s)[1], f32x16 (&sn)[1]) {
+  // Pipelined step j: the softmax of tile j runs under the S^T MFMAs of tile
+  // j+1 and the PV MFMAs of tile j-1. On entry K of tile j+1 and V of tile j-1
+  // (issued one step earlier) must have landed, and every wave is done with K
+  // of tile j (its S^T ran one step earlier) and V of tile j-2 (its PV ran one
+  // step earlier): their stages (j & 1) receive K of tile j+2 and V of tile j.
+  bf16x8 pa[2], pb[2];
+  auto step = [&](int j, auto pv_tag, f32x16 (&s)[1], f32x16 (&sn)[1], bf16x8 (&pp)[2], bf16x8 (&pc)[2]) {
+    constexpr bool HAS_PV = decltype(pv_tag)::value;
     wait_loads_barrier<0>();
     if (j + 2 < count) issue_k(unpack(n2, num_tiles), j & 1);
-    const Entry e1 = unpack(n1, num_tiles);
-    if (j + 1 < count) issue_v(e1, (j + 1) & 1);
-    const int size = e0.size;
-    e0 = e1;
+    issue_v(cur, j & 1);
+    const int size = cur.size;
+    cur = unpack(n1, num_tiles);
     n1 = n2;
     if (j + 3 < count) n2 = entry(j + 3);
     if (wave_live) {
       // after the last tile the "next" K stage holds stale data; its S^T is unused
       const char* nk = smem + ((j + 1) & 1) * kTileBytes;
-      const uint32_t vt = ring + (2 + (j & 1)) * kTileBytes;
-      tile_step<1>(s, sn, nk, vt, L, qr, o, st, c, size < 32 * kh + 32, 32 * kh, size, 0x7fffffff);
+      const uint32_t vt_prev = ring + (2 + ((j + 1) & 1)) * kTileBytes;  // V of tile j-1
+      tile_step_pp1<HAS_PV>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, size < 32 * kh + 32, 32 * kh, size,
+                            0x7fffffff);
     }
   };
-  for (int j = 0; j < count; j += 2) {
-    iteration(j, sa, sb);
-    if (j + 1 < count) iteration(j + 1, sb, sa);
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  if (count > 0) {
+    step(0, no{}, sa, sb, pb, pa);
+    for (int j = 1; j < count; j += 2) {
+      step(j, yes{}, sb, sa, pa, pb);
+      if (j + 1 < count) step(j + 1, yes{}, sa, sb, pb, pa);
+    }
+    // PV of the last tile (P of tile j sits in pa for even j, pb for odd j);
+    // its V was issued in the last step
+    wait_loads_barrier<0>();
+    if (wave_live) {
+      const uint32_t vt = ring + (2 + ((count - 1) & 1)) * kTileBytes;
+      if ((count - 1) & 1) {
+        pv<1>(vt, L, pb, o);
+      } else {
+        pv<1>(vt, L, pa, o);
+      }
+    }
   }
 
   // merge the two key halves of each row: wave (rh, 1) hands its O^T block,

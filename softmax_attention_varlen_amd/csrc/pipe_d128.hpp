@@ -354,6 +354,95 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   }
 }
 
+// The same pipeline for a 32-key share per wave (KB = 1): 16 MFMA slots, the
+// S^T of tile j+1 (8 MFMAs, K from nk) on even slots and, when PV, the PV of
+// tile j-1 (8 MFMAs, P in p_prev, V^T from vt_prev) on odd slots. Slots 0-1
+// carry the two row-maximum chains, slot 2 the reference update, slots 3-14
+// the 16 exp2 (each row-sum add and bf16 packing one slot after its exp2).
+template <bool PV>
+__device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], const char* nk, uint32_t vt_prev,
+                                              const Lane& L, const bf16x8 (&q)[8], const bf16x8 (&p_prev)[2],
+                                              bf16x8 (&p_cur)[2], f32x16 (&o)[4], Softmax& st, float c, bool mask,
+                                              int key0, int len_k, int lim) {
+  if (mask) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = key0 + 8 * (r >> 2) + 4 * L.g + (r & 3);
+      if (key >= len_k || key > lim) s[0][r] = kNegInf;
+    }
+  }
+  const char* kbase = nk + L.k_base;
+  const lds_bf16x4* vbase = (const lds_bf16x4*)(vt_prev + L.v_base);
+  bf16x8 kr[2];  // K operand two S^T steps ahead
+  kr[0] = ld_lds16(kbase, 0);
+  kr[1] = ld_lds16(kbase, 32);
+  bf16x8 va[2];
+  if (PV) {
+    va[0] = read_vt(vbase, 0, 0);
+    va[1] = read_vt(vbase, 0, 1);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sn[0][r] = 0.f;
+  float mx2[2];
+  float alpha = 1.f, ms = 0.f, m_ref = st.m;
+  bool need = false;
+  f32x8 e;
+  float rs0 = 0.f, rs1 = 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int slot = 0; slot < 16; ++slot) {
+    const int t = slot >> 1;
+    if ((slot & 1) == 0) {  // S^T of tile j+1, d-block t
+      sn[0] = mfma32x32x16(kr[t & 1], q[t], sn[0]);
+      if (t + 2 < 8) kr[t & 1] = ld_lds16(kbase, (t + 2) * 32);
+    } else if (PV) {  // PV of tile j-1: chunk t/4, d-block t%4
+      const bf16x8 a = va[t & 1];
+      if (t + 2 < 8) va[t & 1] = read_vt(vbase, (t + 2) >> 2, (t + 2) & 3);
+      o[t & 3] = mfma32x32x16(a, p_prev[t >> 2], o[t & 3]);
+    }
+    if (slot < 2) {  // row maximum: chain slot over elements 8*slot .. +7
+      float m = fmaxf(s[0][8 * slot], s[0][8 * slot + 1]);
+#pragma unroll
+      for (int i = 2; i < 8; ++i) m = fmaxf(m, s[0][8 * slot + i]);
+      mx2[slot] = m;
+    } else if (slot == 2) {
+      const float mx = pair_max(fmaxf(mx2[0], mx2[1]));
+      const float m_new = fmaxf(st.m, mx);
+      need = (m_new - st.m) * c > kRescaleThreshold;  // true on the first finite maximum
+      alpha = need ? hw_exp2((st.m - m_new) * c) : 1.f;
+      m_ref = need ? m_new : st.m;
+      ms = (m_ref == kNegInf ? 0.f : m_ref) * c;
+    } else {
+      // element x's exp2 runs in slot 3 + 3x/4 (slots 3..14); its row-sum add,
+      // and the packing of a finished chunk, one slot later
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        if (4 + (3 * x) / 4 == slot) {
+          const int u = x & 7;
+          if (u & 1) {
+            rs1 += e[u];
+          } else {
+            rs0 += e[u];
+          }
+          if (u == 7) p_cur[x >> 3] = to_bf16x8(e);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        if (3 + (3 * x) / 4 == slot) e[x & 7] = hw_exp2(__builtin_fmaf(s[0][x], c, -ms));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const float rs = rs0 + rs1;
+  st.l = st.l * alpha + rs;
+  st.m = m_ref;
+  if (__builtin_amdgcn_ballot_w64(need || rs != rs) != 0ull) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) o[b] *= alpha;
+  }
+}
+
 // Write the wave's 32 normalised output rows (bf16) and their LSE. o holds
 // O^T (d = 32b + 8*grp + 4g + i for element 4*grp + i of block b); st.l is
 // lane-partial.
