@@ -8,7 +8,7 @@ import torch
 import oracle
 import softmax_attention_varlen_amd as sav
 from tests._gpu_helpers import LSE_TOL, OUT_TOL, announce, assert_close, dev, guard_intact, guarded_empty, host
-from workloads import config5, randn_bf16
+from workloads import config5, randn_bf16, randn_bf16_on
 
 pytestmark = pytest.mark.gpu
 
@@ -143,6 +143,55 @@ def test_item_order_longest_first_is_a_permutation():
         for c in np.unique(cls):
             assert np.all(np.diff(chunk[cls == c]) > 0)
     assert order[0] < 4 and counts[order[0]] == nt
+
+
+def test_item_order_beyond_staged_counts():
+    # 33600 items, 4200 per XCD chunk: the order kernel keeps the first 4096
+    # counts of a chunk in LDS and re-reads the rest from memory. Every row
+    # keeps one key tile; rows a % 97 == 0 keep 40 more (long items in every
+    # chunk, also past position 4096 of a chunk).
+    b, nt, hq, hkv, d = 1, 2800, 12, 1, 128
+    rows = b * hq * nt
+    q = randn_bf16_on((b, nt * 64, hq, d), 360, "cuda")
+    k, v = (dev(randn_bf16((b, nt * 64, hkv, d), 361 + j)) for j in range(2))
+    bmap = np.zeros((b, hq, nt, nt), dtype=np.uint8)
+    a_idx, h_idx = np.arange(nt)[None, :], np.arange(hq)[:, None]
+    bmap[0, h_idx, a_idx, (7 * a_idx + 13 * h_idx) % nt] = 1
+    long_rows = np.arange(0, nt, 97)
+    for j in range(40):
+        bmap[0, :, long_rows, (3 * long_rows + 61 * j + 1) % nt] = 1
+    sizes = np.full(nt, 64, dtype=np.int32)
+    scale = d ** -0.5
+    ws = torch.empty(sav.attn_block_sparse_workspace_size(b, hq, nt), dtype=torch.uint8, device="cuda")
+    announce("sparse item order beyond staged counts", rows)
+    out, lse = sav.attn_block_sparse_fwd(q, k, v, dev(bmap), dev(sizes), scale, return_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    words = ws.view(torch.int32)[rows * nt:rows * nt + 2 * rows].cpu().numpy()
+    counts = bmap.reshape(rows, nt).sum(1, dtype=np.int64)
+    assert np.array_equal(words[:rows], counts)
+    order = words[rows:]
+    per = (rows + 7) // 8
+    assert per > 4096
+    for x in range(8):
+        lo, hi = x * per, min((x + 1) * per, rows)
+        chunk = order[lo:hi]
+        assert np.array_equal(np.sort(chunk), np.arange(lo, hi))
+        cls = 15 - (counts[chunk] * 16) // (counts[lo:hi].max() + 1)
+        assert np.all(np.diff(cls) >= 0)
+        for c in np.unique(cls):
+            assert np.all(np.diff(chunk[cls == c]) > 0)
+    # sampled items (long and short, early and past position 4096 of a chunk)
+    # against dense attention over their kept tiles
+    kh, vh = k.cpu(), v.cpu()
+    for item in [0, 97, 4200 * 3 + 4150, 4200 * 3 + 4151, 4200 * 7 + 4199 - 41, rows - 1,
+                 2 * nt + 97 * 5, 5 * nt + 97 * 28]:
+        h, a = divmod(item, nt)
+        kept = np.nonzero(bmap[0, h, a])[0]
+        sel = torch.from_numpy(np.concatenate([np.arange(c * 64, c * 64 + 64) for c in kept]))
+        ref_o, ref_l = oracle.dense_attention(q[:, a * 64:a * 64 + 64, h:h + 1].cpu(), kh[:, sel], vh[:, sel], scale,
+                                              False)
+        assert_close("out", host(out[:, a * 64:a * 64 + 64, h:h + 1]), ref_o, OUT_TOL, bf16_output=True)
+        assert_close("lse", host(lse[:, h:h + 1, a * 64:a * 64 + 64]), ref_l, LSE_TOL)
 
 
 def test_guards_and_pad_rows_zero():

@@ -30,6 +30,14 @@ def randn_bf16(shape, seed: int) -> torch.Tensor:
     return torch.randn(tuple(shape), dtype=torch.float32, generator=g).to(BF16)
 
 
+def randn_bf16_on(shape, seed: int, device) -> torch.Tensor:
+    """N(0, 1) bf16 drawn on ``device`` by a seeded generator of that device,
+    for inputs too large to draw on the host (the oracle reads slices of the
+    same tensor)."""
+    g = torch.Generator(device).manual_seed(int(seed))
+    return torch.randn(tuple(shape), dtype=torch.float32, generator=g, device=device).to(BF16)
+
+
 def cumulative(lengths) -> np.ndarray:
     """[0, l0, l0+l1, ...] as int32 (the cu_seqlens layout)."""
     out = np.zeros(len(lengths) + 1, dtype=np.int64)
