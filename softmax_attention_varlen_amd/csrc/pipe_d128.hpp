@@ -330,7 +330,13 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
           } else {
             rs0 += e[u];
           }
-          if (u == 7) p_cur[x >> 3] = to_bf16x8(e);
+          if (u == 7) {
+            p_cur[x >> 3] = to_bf16x8(e);
+            // keep the packing in this slot: otherwise it is sunk past the
+            // rescale branch below, off the MFMAs and with all 32 exp2
+            // results held until the end of the step
+            asm volatile("" : : "v"(p_cur[x >> 3]));
+          }
         }
       }
 #pragma unroll
@@ -424,7 +430,10 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
           } else {
             rs0 += e[u];
           }
-          if (u == 7) p_cur[x >> 3] = to_bf16x8(e);
+          if (u == 7) {
+            p_cur[x >> 3] = to_bf16x8(e);
+            asm volatile("" : : "v"(p_cur[x >> 3]));  // keep the packing in this slot
+          }
         }
       }
 #pragma unroll
