@@ -60,6 +60,19 @@ def test_empty_documents():
     check_full(case)
 
 
+@pytest.mark.parametrize("batch", [511, 512, 700])
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_documents(batch, causal):
+    # hundreds of documents, most shorter than one 256-row query tile (many
+    # empty workgroup slots), a few spanning several tiles, some empty
+    rng = np.random.default_rng(batch + causal)
+    lens = rng.integers(0, 96, batch)
+    lens[rng.choice(batch, 5, replace=False)] = [257, 300, 513, 700, 1]
+    lens[rng.choice(batch, 20, replace=False)] = 0
+    case = varlen_case(lens.tolist(), num_heads=4, num_kv_heads=2, head_dim=128, causal=causal, seed=44 + batch)
+    check_full(case)
+
+
 def test_no_lse_and_determinism():
     case = varlen_case([300, 77], num_heads=4, num_kv_heads=2, head_dim=128, causal=True, seed=43)
     announce("varlen determinism")
