@@ -271,6 +271,9 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   }
   const char* kbase = nk + L.k_base;
   const lds_bf16x4* vbase = (const lds_bf16x4*)(vt_prev + L.v_base);
+  // no LDS read is outstanding here (the step's barrier waited for them all);
+  // saying so lets the compiler's first MFMA wait for its own K operand only
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
   bf16x8 kr[2];  // K operand two S^T steps (four slots) ahead
 #pragma unroll
   for (int i = 0; i < 2; ++i) kr[i] = ld_lds16(kbase, (i % 2) * kHalfBytes + (i / 2) * 32);
@@ -379,6 +382,7 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
   }
   const char* kbase = nk + L.k_base;
   const lds_bf16x4* vbase = (const lds_bf16x4*)(vt_prev + L.v_base);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): as in tile_step_pp
   bf16x8 kr[2];  // K operand two S^T steps ahead
   kr[0] = ld_lds16(kbase, 0);
   kr[1] = ld_lds16(kbase, 32);

@@ -145,6 +145,23 @@ def test_item_order_longest_first_is_a_permutation():
     assert order[0] < 4 and counts[order[0]] == nt
 
 
+@pytest.mark.parametrize("b,nt,h", [(1, 1, 1), (1, 2, 1), (1, 3, 2), (1, 7, 1)])
+def test_fewer_items_than_xcd_chunks(b, nt, h):
+    # 1 to 7 (batch, head, tile) items: some XCD chunks of the item order are
+    # empty or hold a single item
+    q, k, v = (randn_bf16((b, nt * 64, h, 128), 370 + 10 * nt + j) for j in range(3))
+    rng = np.random.default_rng(37 + nt)
+    bmap = rng.random((b, h, nt, nt)) < 0.6
+    bmap[..., 0, 0] = True
+    sizes = np.full(nt, 64, dtype=np.int32)
+    sizes[-1] = 41
+    announce("sparse few items", b, nt, h)
+    out, lse = run(q, k, v, bmap, sizes, 128 ** -0.5)
+    ref_o, ref_l = oracle.block_sparse_attention(q, k, v, bmap, sizes, 128 ** -0.5)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("lse", host(lse), ref_l, LSE_TOL)
+
+
 def test_item_order_beyond_staged_counts():
     # 33600 items, 4200 per XCD chunk: the order kernel keeps the first 4096
     # counts of a chunk in LDS and re-reads the rest from memory. Every row
