@@ -45,26 +45,26 @@ _PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "key_row
 _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
 _SPARSE_SRC = ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"]
 TRAFFIC = {
-    "dense": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 73841.0, "write_kib": 49932.5,
-              "sources": _PREFILL_SRC, "sha256": "c8f85268e8f48576"},
-    "causal": {"kernel": "prefill_d128_kernel<true,false,8,4,true>", "fetch_kib": 109814.9, "write_kib": 142434.7,
-               "sources": _PREFILL_SRC, "sha256": "c8f85268e8f48576"},
+    "dense": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 73841.0, "write_kib": 49932.9,
+              "sources": _PREFILL_SRC, "sha256": "965cd528a6254137"},
+    "causal": {"kernel": "prefill_d128_kernel<true,false,8,4,true>", "fetch_kib": 109807.0, "write_kib": 142434.7,
+               "sources": _PREFILL_SRC, "sha256": "965cd528a6254137"},
     "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443512.9, "write_kib": 3040.5,
               "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
-    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 427761.3, "write_kib": 49920.1,
-               "sources": _SPARSE_SRC, "sha256": "fbd7f605bf7577c3"},
-    "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true>", "fetch_kib": 705516.5,
-                      "write_kib": 87200.3, "sources": _PREFILL_SRC, "sha256": "c8f85268e8f48576"},
+    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 426642.7, "write_kib": 49920.1,
+               "sources": _SPARSE_SRC, "sha256": "e1bb0d0d0e24ea25"},
+    "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true>", "fetch_kib": 705242.0,
+                      "write_kib": 87200.8, "sources": _PREFILL_SRC, "sha256": "965cd528a6254137"},
     "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445751.0, "write_kib": 12150.3,
              "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
-    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 634519.2, "write_kib": 51480.7,
-           "sources": _SPARSE_SRC, "sha256": "fbd7f605bf7577c3"},
+    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 636156.0, "write_kib": 51480.8,
+           "sources": _SPARSE_SRC, "sha256": "e1bb0d0d0e24ea25"},
     "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531393.3, "write_kib": 3081.2,
             "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
-    "masked": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 28935.0, "write_kib": 49924.3,
-               "sources": _PREFILL_SRC, "sha256": "c8f85268e8f48576"},
-    "padded": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 103629.6, "write_kib": 66229.2,
-               "sources": _PREFILL_SRC, "sha256": "c8f85268e8f48576"},
+    "masked": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 28935.0, "write_kib": 49923.2,
+               "sources": _PREFILL_SRC, "sha256": "965cd528a6254137"},
+    "padded": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 103672.3, "write_kib": 66229.3,
+               "sources": _PREFILL_SRC, "sha256": "965cd528a6254137"},
 }
 
 
