@@ -37,7 +37,8 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 # the same counters read for a plain 1 GiB device copy (bench.py --only copy):
 # FETCH_SIZE reports half the bytes read, WRITE_SIZE all the bytes written.
 # A record holds only while the kernel sources it was taken from are unchanged:
-# their sha256 is stored with it and a mismatch reports null.
+# the sha256 of their code (comments and blank lines stripped) is stored with
+# it and a mismatch reports null.
 FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 CSRC = os.path.join(ROOT, "softmax_attention_varlen_amd", "csrc")
@@ -46,34 +47,66 @@ _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
 _SPARSE_SRC = ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"]
 TRAFFIC = {
     "dense": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 73841.0, "write_kib": 49932.9,
-              "sources": _PREFILL_SRC, "sha256": "965cd528a6254137"},
+              "sources": _PREFILL_SRC, "sha256": "bc7b9435684b9fb1"},
     "causal": {"kernel": "prefill_d128_kernel<true,false,8,4,true>", "fetch_kib": 109807.0, "write_kib": 142434.7,
-               "sources": _PREFILL_SRC, "sha256": "965cd528a6254137"},
+               "sources": _PREFILL_SRC, "sha256": "bc7b9435684b9fb1"},
     "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443512.9, "write_kib": 3040.5,
-              "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
+              "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
     "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 426642.7, "write_kib": 49920.1,
-               "sources": _SPARSE_SRC, "sha256": "e1bb0d0d0e24ea25"},
+               "sources": _SPARSE_SRC, "sha256": "d0bd2a851cac2170"},
     "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true>", "fetch_kib": 705242.0,
-                      "write_kib": 87200.8, "sources": _PREFILL_SRC, "sha256": "965cd528a6254137"},
+                      "write_kib": 87200.8, "sources": _PREFILL_SRC, "sha256": "bc7b9435684b9fb1"},
     "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445751.0, "write_kib": 12150.3,
-             "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
+             "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
     "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 636156.0, "write_kib": 51480.8,
-           "sources": _SPARSE_SRC, "sha256": "e1bb0d0d0e24ea25"},
+           "sources": _SPARSE_SRC, "sha256": "d0bd2a851cac2170"},
     "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531393.3, "write_kib": 3081.2,
-            "sources": _DECODE_SRC, "sha256": "84f6a122f4c86072"},
+            "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
     "masked": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 28935.0, "write_kib": 49923.2,
-               "sources": _PREFILL_SRC, "sha256": "965cd528a6254137"},
+               "sources": _PREFILL_SRC, "sha256": "bc7b9435684b9fb1"},
     "padded": {"kernel": "prefill_d128_kernel<false,false,8,4,true>", "fetch_kib": 103672.3, "write_kib": 66229.3,
-               "sources": _PREFILL_SRC, "sha256": "965cd528a6254137"},
+               "sources": _PREFILL_SRC, "sha256": "bc7b9435684b9fb1"},
 }
+
+
+def code_only(text: str) -> str:
+    """C/C++ source without comments and blank lines (string literals kept), so
+    that editing a comment does not void a measurement of the code."""
+    out, i, n, in_str = [], 0, len(text), False
+    while i < n:
+        ch = text[i]
+        if in_str:
+            out.append(ch)
+            if ch == "\\" and i + 1 < n:
+                out.append(text[i + 1])
+                i += 2
+                continue
+            if ch == '"':
+                in_str = False
+            i += 1
+        elif ch == '"':
+            in_str = True
+            out.append(ch)
+            i += 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(ch)
+            i += 1
+    lines = (ln.rstrip() for ln in "".join(out).split("\n"))
+    return "\n".join(ln for ln in lines if ln)
 
 
 def sources_sha256(files) -> str:
     import hashlib
     m = hashlib.sha256()
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            m.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            m.update(code_only(fh.read()).encode())
     return m.hexdigest()[:16]
 
 

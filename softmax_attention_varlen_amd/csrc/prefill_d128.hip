@@ -4,9 +4,11 @@
 // and one query head; wave w owns rows [32w, 32w+32). K/V tiles of 64 keys
 // stream through an NS-stage LDS ring filled by direct-to-LDS loads (no VGPR
 // staging, no transpose on the way in), in the bank-conflict-free layout of
-// pipe_d128.hpp. Per tile a wave issues the S^T MFMAs of the next tile
-// interleaved with the softmax of the current one, then the PV MFMAs of the
-// current tile. One barrier per tile guards the ring.
+// pipe_d128.hpp. The default pipelined loop (PP, 4 stages) runs the softmax of
+// tile j under the S^T MFMAs of tile j+1 and the PV MFMAs of tile j-1; the
+// plain loop (PP = false, 3 or 4 stages) interleaves the S^T MFMAs of tile
+// j+1 with the softmax of tile j and then runs the PV of tile j. One barrier
+// per tile guards the ring.
 #include <type_traits>
 
 #include "key_rows.hpp"
