@@ -8,7 +8,10 @@
 // tile j under the S^T MFMAs of tile j+1 and the PV MFMAs of tile j-1; the
 // plain loop (PP = false, 3 or 4 stages) interleaves the S^T MFMAs of tile
 // j+1 with the softmax of tile j and then runs the PV of tile j. One barrier
-// per tile guards the ring.
+// per tile guards the ring. SPLIT replaces the ring by separate two-stage K
+// and V rings (at step j, K of tile j+2 and V of tile j are in flight while K
+// of tile j+1 and V of tile j-1 are read), which fit two 4-wave workgroups
+// per CU.
 #include <type_traits>
 
 #include "key_rows.hpp"
@@ -40,8 +43,8 @@ struct Ring {
 // block_tables, with context_lens[doc] (clamped to max_len_k) keys per
 // document; otherwise from contiguous rows delimited by cu_k. q_used / k_used
 // (nullable) cut each document to a valid prefix of its rows.
-template <bool CAUSAL, bool PAGED, int NW, int NS, bool PP>
-__global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
+template <bool CAUSAL, bool PAGED, int NW, int NS, bool PP, bool SPLIT = false>
+__global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int total_q, int total_k,
     int tiles_per_doc, int hq, int hkv, int n_items, int per_xcd, float c, uint16_t* __restrict__ out,
@@ -52,7 +55,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
   constexpr int BM = 32 * NW;
   static_assert(NS == 3 || NS == 4, "the load-count waits below cover 3- and 4-stage rings");
   static_assert(!PP || NS == 4, "the pipelined loop keeps tile j-1's V while tile j+2 loads: 4 stages");
-  __shared__ __attribute__((aligned(1024))) char smem[NS * kStageBytes];
+  static_assert(!SPLIT || PP, "split rings serve the pipelined loop");
+  // SPLIT: separate two-stage K and V rings (K stages 0, 1, then V stages 0, 1)
+  __shared__ __attribute__((aligned(1024))) char smem[SPLIT ? 4 * kTileBytes : NS * kStageBytes];
 
   // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs, so
   // XCD x receives logical items [x*per_xcd, (x+1)*per_xcd), laid out
@@ -133,7 +138,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
   constexpr int PRE = PP ? 2 : NS - 1;
 #pragma unroll
   for (int s = 0; s < PRE; ++s) {
-    if (s < ntiles) {
+    if (SPLIT) {
+      if (s < ntiles) {
+        const long off = rows.row(s * kBN);
+        issue_tile<R::IPW>(kb0 + off, stride_bytes, len_k - s * kBN, ring + s * kTileBytes, w * R::IPW, lane);
+      }
+    } else if (s < ntiles) {
       const long off = rows.row(s * kBN);
       R::issue(kb0 + off, vb0 + off, stride_bytes, len_k - s * kBN, ring + s * kStageBytes, w, lane);
     }
@@ -150,7 +160,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
   if (ntiles > 0) {
     // tile 0 has landed once at most the later prologue tiles are in flight
     const int later = (ntiles < PRE ? ntiles : PRE) - 1;
-    if (later >= 2) {
+    if (SPLIT) {
+      if (later >= 1) {
+        wait_loads_barrier<R::IPW>();
+      } else {
+        wait_loads_barrier<0>();
+      }
+    } else if (later >= 2) {
       wait_loads_barrier<2 * R::LOADS>();
     } else if (later == 1) {
       wait_loads_barrier<R::LOADS>();
@@ -169,17 +185,37 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
     bf16x8 pa[4], pb[4];
     auto step = [&](int j, auto pv_tag, f32x16 (&s)[2], f32x16 (&sn)[2], bf16x8 (&pp)[4], bf16x8 (&pc)[4]) {
       constexpr bool HAS_PV = decltype(pv_tag)::value;
-      if (j + 1 < ntiles) {
-        wait_loads_barrier<0>();  // tile j+1 (issued at step j-1) has landed everywhere
-        const int jn = j + 2;
-        if (jn < ntiles) {
-          const long off = rows.row(jn * kBN);
-          R::issue(kb0 + off, vb0 + off, stride_bytes, len_k - jn * kBN, ring + (jn % 4) * kStageBytes, w, lane);
+      uint32_t vt_prev;
+      const char* nk;
+      if (SPLIT) {
+        // K of tile j+2 into the K stage of tile j (its S^T ran in step j-1),
+        // V of tile j into the V stage of tile j-2 (its PV ran in step j-1)
+        wait_loads_barrier<0>();
+        if (j + 2 < ntiles) {
+          const long off = rows.row((j + 2) * kBN);
+          issue_tile<R::IPW>(kb0 + off, stride_bytes, len_k - (j + 2) * kBN, ring + (j & 1) * kTileBytes,
+                             w * R::IPW, lane);
         }
+        {
+          const long off = rows.row(j * kBN);
+          issue_tile<R::IPW>(vb0 + off, stride_bytes, len_k - j * kBN, ring + (2 + (j & 1)) * kTileBytes,
+                             w * R::IPW, lane);
+        }
+        vt_prev = ring + (2 + ((j + 1) & 1)) * kTileBytes;
+        nk = smem + ((j + 1) & 1) * kTileBytes;
+      } else {
+        if (j + 1 < ntiles) {
+          wait_loads_barrier<0>();  // tile j+1 (issued at step j-1) has landed everywhere
+          const int jn = j + 2;
+          if (jn < ntiles) {
+            const long off = rows.row(jn * kBN);
+            R::issue(kb0 + off, vb0 + off, stride_bytes, len_k - jn * kBN, ring + (jn % 4) * kStageBytes, w, lane);
+          }
+        }
+        vt_prev = ring + ((j + 3) % 4) * kStageBytes + kTileBytes;  // V of tile j-1
+        nk = smem + ((j + 1 < ntiles ? j + 1 : j) % 4) * kStageBytes;
       }
-      const uint32_t vt_prev = ring + ((j + 3) % 4) * kStageBytes + kTileBytes;  // V of tile j-1
       if (j < ntiles_w) {
-        const char* nk = smem + ((j + 1 < ntiles ? j + 1 : j) % 4) * kStageBytes;
         const int key0 = j * kBN;
         const bool mask = !(j < nomask_w && key0 + kBN <= len_k);
         tile_step_pp<HAS_PV>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, mask, key0, len_k,
@@ -196,8 +232,10 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
         step(j, yes{}, sb, sa, pa, pb);
         if (j + 1 < ntiles) step(j + 1, yes{}, sa, sb, pb, pa);
       }
+      if (SPLIT) wait_loads_barrier<0>();  // V of the last tile was issued in the last step
       if (ntiles_w == ntiles) {  // the last tile's PV (its stage is never refilled)
-        const uint32_t vt = ring + ((ntiles - 1) % 4) * kStageBytes + kTileBytes;
+        const uint32_t vt = SPLIT ? ring + (2 + ((ntiles - 1) & 1)) * kTileBytes
+                                  : ring + ((ntiles - 1) % 4) * kStageBytes + kTileBytes;
         if ((ntiles - 1) & 1) {
           pv<2>(vt, L, pb, o);
         } else {
@@ -244,7 +282,6 @@ __global__ __launch_bounds__(64 * NW) void prefill_d128_kernel(
 
 }  // namespace
 
-constexpr int kPrefillWaves = 8;
 constexpr int kPrefillStages = 3;
 #ifndef PREFILL_PIPELINED
 #define PREFILL_PIPELINED 1
@@ -253,33 +290,40 @@ constexpr bool kPrefillPipelined = PREFILL_PIPELINED;
 
 bool prefill_d128_supported(const VarlenArgs& a) { return a.head_dim == 128; }
 
+// Contiguous causal prefill runs 4-wave workgroups (128 query rows) on split
+// two-stage K and V rings (66.5 KB), two workgroups per CU: its many short
+// items then overlap one workgroup's prologue and store with the other's
+// loop. Everything else runs 8-wave workgroups (256 rows) on the 4-stage
+// ring, one per CU, which copies each K/V tile into LDS for twice as many rows.
 template <bool CAUSAL, bool PAGED>
-static void launch_prefill_d128_t(const VarlenArgs& a, int tiles, long n_items, long per_xcd, hipStream_t stream) {
-  const float c = a.scale * kLog2e;
+static void launch_prefill_d128_t(const VarlenArgs& a, hipStream_t stream) {
+  constexpr bool SPLIT = kPrefillPipelined && CAUSAL && !PAGED;
+  constexpr int NW = SPLIT ? 4 : 8;
   constexpr int NS = kPrefillPipelined ? 4 : kPrefillStages;
-  hipLaunchKernelGGL((prefill_d128_kernel<CAUSAL, PAGED, kPrefillWaves, NS, kPrefillPipelined>), dim3((unsigned)(per_xcd * 8)),
-                     dim3(64 * kPrefillWaves), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch, a.total_q, a.total_k, tiles, a.num_heads,
-                     a.num_kv_heads, (int)n_items, (int)per_xcd, c, (uint16_t*)a.out, a.lse, a.block_tables,
-                     a.context_lens, a.max_blocks_per_seq, a.num_blocks, a.max_seqlen_k, a.q_used,
+  constexpr int BM = 32 * NW;
+  const int tiles = (a.max_seqlen_q + BM - 1) / BM;
+  const long n_items = (long)tiles * a.batch * a.num_heads;
+  const long per_xcd = (n_items + 7) / 8;
+  const float c = a.scale * kLog2e;
+  hipLaunchKernelGGL((prefill_d128_kernel<CAUSAL, PAGED, NW, NS, kPrefillPipelined, SPLIT>),
+                     dim3((unsigned)(per_xcd * 8)), dim3(64 * NW), 0, stream, (const uint16_t*)a.q,
+                     (const uint16_t*)a.k, (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch, a.total_q, a.total_k, tiles,
+                     a.num_heads, a.num_kv_heads, (int)n_items, (int)per_xcd, c, (uint16_t*)a.out, a.lse,
+                     a.block_tables, a.context_lens, a.max_blocks_per_seq, a.num_blocks, a.max_seqlen_k, a.q_used,
                      PAGED ? nullptr : a.k_used);
 }
 
 hipError_t launch_prefill_d128(const VarlenArgs& a, hipStream_t stream) {
-  constexpr int BM = 32 * kPrefillWaves;
-  const int tiles = (a.max_seqlen_q + BM - 1) / BM;
-  const long n_items = (long)tiles * a.batch * a.num_heads;
-  const long per_xcd = (n_items + 7) / 8;
   if (a.paged) {
     if (a.causal) {
-      launch_prefill_d128_t<true, true>(a, tiles, n_items, per_xcd, stream);
+      launch_prefill_d128_t<true, true>(a, stream);
     } else {
-      launch_prefill_d128_t<false, true>(a, tiles, n_items, per_xcd, stream);
+      launch_prefill_d128_t<false, true>(a, stream);
     }
   } else if (a.causal) {
-    launch_prefill_d128_t<true, false>(a, tiles, n_items, per_xcd, stream);
+    launch_prefill_d128_t<true, false>(a, stream);
   } else {
-    launch_prefill_d128_t<false, false>(a, tiles, n_items, per_xcd, stream);
+    launch_prefill_d128_t<false, false>(a, stream);
   }
   return hipGetLastError();
 }
