@@ -46,26 +46,26 @@ _PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "key_row
 _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
 _SPARSE_SRC = ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"]
 TRAFFIC = {
-    "dense": {"kernel": "prefill_d128_kernel<false,false,8,4,true,false>", "fetch_kib": 73849.5, "write_kib": 50090.8,
-              "sources": _PREFILL_SRC, "sha256": "83a5924434893af2"},
-    "causal": {"kernel": "prefill_d128_kernel<true,false,4,4,true,true>", "fetch_kib": 112202.1, "write_kib": 142475.8,
-               "sources": _PREFILL_SRC, "sha256": "83a5924434893af2"},
+    "dense": {"kernel": "prefill_d128_kernel<false,false,8,4,true,false>", "fetch_kib": 73849.5, "write_kib": 49931.7,
+              "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
+    "causal": {"kernel": "prefill_d128_kernel<true,false,4,4,true,true>", "fetch_kib": 113054.2, "write_kib": 142478.4,
+               "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
     "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443512.9, "write_kib": 3040.5,
               "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
-    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 426642.7, "write_kib": 49920.1,
-               "sources": _SPARSE_SRC, "sha256": "d0bd2a851cac2170"},
-    "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true,false>", "fetch_kib": 703548.1,
-                      "write_kib": 87201.8, "sources": _PREFILL_SRC, "sha256": "83a5924434893af2"},
+    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 301121.7, "write_kib": 49920.1,
+               "sources": _SPARSE_SRC, "sha256": "cba39a50b68e4a80"},
+    "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true,false>", "fetch_kib": 703201.0,
+                      "write_kib": 87200.8, "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
     "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445751.0, "write_kib": 12150.3,
              "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
-    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 636156.0, "write_kib": 51480.8,
-           "sources": _SPARSE_SRC, "sha256": "d0bd2a851cac2170"},
+    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 488968.7, "write_kib": 51480.3,
+           "sources": _SPARSE_SRC, "sha256": "cba39a50b68e4a80"},
     "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531393.3, "write_kib": 3081.2,
             "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
-    "masked": {"kernel": "prefill_d128_kernel<false,false,8,4,true,false>", "fetch_kib": 28940.0, "write_kib": 49923.0,
-               "sources": _PREFILL_SRC, "sha256": "83a5924434893af2"},
-    "padded": {"kernel": "prefill_d128_kernel<false,false,8,4,true,false>", "fetch_kib": 103632.3, "write_kib": 66228.8,
-               "sources": _PREFILL_SRC, "sha256": "83a5924434893af2"},
+    "masked": {"kernel": "prefill_d128_kernel<false,false,8,4,true,false>", "fetch_kib": 28940.0, "write_kib": 49923.1,
+               "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
+    "padded": {"kernel": "prefill_d128_kernel<false,false,8,4,true,false>", "fetch_kib": 103589.0, "write_kib": 66229.2,
+               "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
 }
 
 
