@@ -52,14 +52,14 @@ TRAFFIC = {
                "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
     "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443512.9, "write_kib": 3040.5,
               "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
-    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 301121.7, "write_kib": 49920.1,
-               "sources": _SPARSE_SRC, "sha256": "cba39a50b68e4a80"},
+    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 262925.8, "write_kib": 49921.5,
+               "sources": _SPARSE_SRC, "sha256": "53af8ba5ca710d51"},
     "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true,false>", "fetch_kib": 703201.0,
                       "write_kib": 87200.8, "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
     "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445751.0, "write_kib": 12150.3,
              "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
-    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 488968.7, "write_kib": 51480.3,
-           "sources": _SPARSE_SRC, "sha256": "cba39a50b68e4a80"},
+    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 462370.9, "write_kib": 51484.1,
+           "sources": _SPARSE_SRC, "sha256": "53af8ba5ca710d51"},
     "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531393.3, "write_kib": 3081.2,
             "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
     "masked": {"kernel": "prefill_d128_kernel<false,false,8,4,true,false>", "fetch_kib": 28940.0, "write_kib": 49923.1,

@@ -258,6 +258,9 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   using yes = std::integral_constant<bool, true>;
   using no = std::integral_constant<bool, false>;
   if (count > 0) {
+    // the loop runs at issue priority 1, its MFMA slots at 2 (tile_step_pp1);
+    // prologue, merge and store stay at 0
+    __builtin_amdgcn_s_setprio(1);
     step(0, no{}, sa, sb, pb, pa);
     for (int j = 1; j < count; j += 2) {
       step(j, yes{}, sb, sa, pa, pb);
@@ -276,6 +279,7 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // merge the two key halves of each row: wave (rh, 1) hands its O^T block,
   // reference maximum and lane-partial sum to wave (rh, 0) through LDS
   wait_loads_barrier<0>();

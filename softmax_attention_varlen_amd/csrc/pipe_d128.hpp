@@ -398,10 +398,11 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
   bool need = false;
   f32x8 e;
   float rs0 = 0.f, rs1 = 0.f;
-  // Raised issue priority for the MFMA slots: the block-sparse kernel runs two
-  // workgroups per CU out of phase, and the other workgroup's prologue, merge
-  // and ring refills then yield the issue slot to these steps.
-  __builtin_amdgcn_s_setprio(1);
+  // Issue priority 2 for the MFMA slots, back to 1 (the caller's loop level)
+  // after them: the block-sparse kernel runs two workgroups per CU out of
+  // phase, and the other workgroup's ring refills (1) and prologue, merge and
+  // store (0) then yield the issue slot to these steps.
+  __builtin_amdgcn_s_setprio(2);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int slot = 0; slot < 16; ++slot) {
@@ -451,7 +452,7 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_s_setprio(1);
   const float rs = rs0 + rs1;
   st.l = st.l * alpha + rs;
   st.m = m_ref;
