@@ -46,26 +46,26 @@ _PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "key_row
 _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
 _SPARSE_SRC = ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"]
 TRAFFIC = {
-    "dense": {"kernel": "prefill_d128_kernel<false,false,8,4,true,false>", "fetch_kib": 73849.5, "write_kib": 49931.7,
-              "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
-    "causal": {"kernel": "prefill_d128_kernel<true,false,4,4,true,true>", "fetch_kib": 113054.2, "write_kib": 142478.4,
-               "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
+    "dense": {"kernel": "prefill_d128_kernel<false,false,4,4,true,true>", "fetch_kib": 73853.1, "write_kib": 49952.6,
+              "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
+    "causal": {"kernel": "prefill_d128_kernel<true,false,4,4,true,true>", "fetch_kib": 111923.0, "write_kib": 142491.4,
+               "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
     "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443512.9, "write_kib": 3040.5,
               "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
-    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 262925.8, "write_kib": 49921.5,
-               "sources": _SPARSE_SRC, "sha256": "53af8ba5ca710d51"},
-    "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true,false>", "fetch_kib": 703201.0,
-                      "write_kib": 87200.8, "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
+    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 262648.9, "write_kib": 49921.3,
+               "sources": _SPARSE_SRC, "sha256": "1fb8b151b776db88"},
+    "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true,false>", "fetch_kib": 701680.5,
+                      "write_kib": 87201.8, "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
     "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445751.0, "write_kib": 12150.3,
              "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
-    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 462370.9, "write_kib": 51484.1,
-           "sources": _SPARSE_SRC, "sha256": "53af8ba5ca710d51"},
+    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 460280.1, "write_kib": 51483.5,
+           "sources": _SPARSE_SRC, "sha256": "1fb8b151b776db88"},
     "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531393.3, "write_kib": 3081.2,
             "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
-    "masked": {"kernel": "prefill_d128_kernel<false,false,8,4,true,false>", "fetch_kib": 28940.0, "write_kib": 49923.1,
-               "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
-    "padded": {"kernel": "prefill_d128_kernel<false,false,8,4,true,false>", "fetch_kib": 103589.0, "write_kib": 66229.2,
-               "sources": _PREFILL_SRC, "sha256": "c9e429ab30399c33"},
+    "masked": {"kernel": "prefill_d128_kernel<false,false,4,4,true,true>", "fetch_kib": 28943.5, "write_kib": 50005.0,
+               "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
+    "padded": {"kernel": "prefill_d128_kernel<false,false,4,4,true,true>", "fetch_kib": 108036.1, "write_kib": 66235.8,
+               "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
 }
 
 

@@ -254,7 +254,7 @@ __device__ __forceinline__ bf16x8 read_vt(const lds_bf16x4* base, int c, int b) 
 // 0-5 carry the row maximum, slot 6 the reference update, slots 7-31 the 32
 // exp2. P of tile j goes to p_cur. O and the row sum are rescaled at the end
 // (after the PV of tile j-1, which still belongs to the old reference).
-template <bool PV>
+template <bool PV, bool PRIO = false>
 __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], const char* nk, uint32_t vt_prev,
                                              const Lane& L, const bf16x8 (&q)[8], const bf16x8 (&p_prev)[4],
                                              bf16x8 (&p_cur)[4], f32x16 (&o)[4], Softmax& st, float c, bool mask,
@@ -292,6 +292,9 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   bool need = false;
   f32x8 e;
   float rs0 = 0.f, rs1 = 0.f;
+  // PRIO: issue priority 2 for the MFMA slots, back to the caller's loop
+  // level 1 after them (kernels that run two workgroups per CU out of phase)
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(2);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int slot = 0; slot < 32; ++slot) {
@@ -352,6 +355,7 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
   const float rs = rs0 + rs1;
   st.l = st.l * alpha + rs;
   st.m = m_ref;

@@ -11,7 +11,8 @@
 // per tile guards the ring. SPLIT replaces the ring by separate two-stage K
 // and V rings (at step j, K of tile j+2 and V of tile j are in flight while K
 // of tile j+1 and V of tile j-1 are read), which fit two 4-wave workgroups
-// per CU.
+// per CU, and raises the issue priority of the loop (1) and of its MFMA slots
+// (2) above the prologue and store (0).
 #include <type_traits>
 
 #include "key_rows.hpp"
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
       if (j < ntiles_w) {
         const int key0 = j * kBN;
         const bool mask = !(j < nomask_w && key0 + kBN <= len_k);
-        tile_step_pp<HAS_PV>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, mask, key0, len_k,
+        tile_step_pp<HAS_PV, SPLIT>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, mask, key0, len_k,
                              CAUSAL ? row + diag : 0x7fffffff);
       } else if (HAS_PV && j == ntiles_w) {
         pv<2>(vt_prev, L, pp, o);  // this wave's last tile
@@ -227,6 +228,9 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
     using yes = std::integral_constant<bool, true>;
     using no = std::integral_constant<bool, false>;
     if (ntiles > 0) {
+      // SPLIT: the loop runs at issue priority 1 and its MFMA slots at 2, so
+      // the other workgroup's prologue and store (at 0) yield to them
+      if constexpr (SPLIT) __builtin_amdgcn_s_setprio(1);
       step(0, no{}, sa, sb, pb, pa);
       for (int j = 1; j < ntiles; j += 2) {
         step(j, yes{}, sb, sa, pa, pb);
@@ -243,6 +247,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
         }
       }
     }
+    if constexpr (SPLIT) __builtin_amdgcn_s_setprio(0);
     store_rows(o, st, L, c, row < len_q, out + ((long)(q0 + row_c) * hq + h) * kD,
                lse != nullptr ? lse + (long)h * total_q + q0 + row_c : nullptr);
     return;
@@ -290,14 +295,15 @@ constexpr bool kPrefillPipelined = PREFILL_PIPELINED;
 
 bool prefill_d128_supported(const VarlenArgs& a) { return a.head_dim == 128; }
 
-// Contiguous causal prefill runs 4-wave workgroups (128 query rows) on split
-// two-stage K and V rings (66.5 KB), two workgroups per CU: its many short
-// items then overlap one workgroup's prologue and store with the other's
-// loop. Everything else runs 8-wave workgroups (256 rows) on the 4-stage
-// ring, one per CU, which copies each K/V tile into LDS for twice as many rows.
+// Keys from contiguous rows: 4-wave workgroups (128 query rows) on split
+// two-stage K and V rings (66.5 KB), two workgroups per CU out of phase, so
+// one workgroup's prologue and store run under the other's loop, with the
+// loop at raised issue priority. Keys from the paged cache: 8-wave workgroups
+// (256 rows) on the 4-stage ring, one per CU, which copies each K/V tile into
+// LDS for twice as many rows.
 template <bool CAUSAL, bool PAGED>
 static void launch_prefill_d128_t(const VarlenArgs& a, hipStream_t stream) {
-  constexpr bool SPLIT = kPrefillPipelined && CAUSAL && !PAGED;
+  constexpr bool SPLIT = kPrefillPipelined && !PAGED;
   constexpr int NW = SPLIT ? 4 : 8;
   constexpr int NS = kPrefillPipelined ? 4 : kPrefillStages;
   constexpr int BM = 32 * NW;
