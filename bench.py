@@ -52,14 +52,14 @@ TRAFFIC = {
                "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
     "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443512.9, "write_kib": 3040.5,
               "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
-    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 262648.9, "write_kib": 49921.3,
-               "sources": _SPARSE_SRC, "sha256": "1fb8b151b776db88"},
+    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 249179.4, "write_kib": 49920.8,
+               "sources": _SPARSE_SRC, "sha256": "b87edb9f712a3369"},
     "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true,false>", "fetch_kib": 701680.5,
                       "write_kib": 87201.8, "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
     "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445751.0, "write_kib": 12150.3,
              "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
-    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 460280.1, "write_kib": 51483.5,
-           "sources": _SPARSE_SRC, "sha256": "1fb8b151b776db88"},
+    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 444200.8, "write_kib": 51483.4,
+           "sources": _SPARSE_SRC, "sha256": "b87edb9f712a3369"},
     "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531393.3, "write_kib": 3081.2,
             "sources": _DECODE_SRC, "sha256": "61eec092b9b2f046"},
     "masked": {"kernel": "prefill_d128_kernel<false,false,4,4,true,true>", "fetch_kib": 28943.5, "write_kib": 50005.0,

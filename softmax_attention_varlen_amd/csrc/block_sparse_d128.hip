@@ -211,7 +211,20 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   // sends tile counts up to kListCap here.)
   for (int i = tid; i < count; i += 64 * kSW) lst[i] = list[i];
   __syncthreads();
-  auto entry = [&](int j) -> int32_t { return lst[j]; };
+  // A 64-entry window of the list sits in one VGPR (lane i holds entry
+  // win_base + i) and entries are taken with v_readlane: one LDS read per 64
+  // kept tiles instead of one per step, whose wait would otherwise sit in
+  // every step right before the MFMA slots. Entries are asked for in
+  // increasing order, so the window only moves forward.
+  int win_base = 0;
+  int32_t win = lst[lane];
+  auto entry = [&](int j) -> int32_t {
+    if (j >= win_base + 64) {
+      win_base += 64;
+      win = lst[win_base + lane];  // win_base + 63 < kListCap since j < count <= kListCap
+    }
+    return __builtin_amdgcn_readlane(win, j - win_base);
+  };
   // entry of tile j (unpacked) and raw entries of tiles j+1, j+2: each list
   // word is read one step before its first use
   Entry cur{0, 1};
