@@ -417,23 +417,45 @@ __global__ __launch_bounds__(256) void paged_decode_stream_combine_kernel(
   const int first = b0 / L, last = (b1 - 1) / L;
   if (first == last) return;
   auto slot = [&](int gg) { return ((long)(gg + s) * max_q + qi) * hq + h; };
+  // The pieces' LSEs are read lane-parallel (lane i holds piece c0 + i of a
+  // 64-piece chunk) and reduced across the wave; the weighted sum of the
+  // partial O then takes each piece's weight from its lane with v_readlane, in
+  // ascending piece order (the same order on every run).
   float mx = kNegInf;
-  for (int gg = first; gg <= last; ++gg) mx = fmaxf(mx, part_lse[slot(gg)]);
+  for (int c0 = first; c0 <= last; c0 += 64) {
+    const int gg = c0 + lane;
+    if (gg <= last) mx = fmaxf(mx, part_lse[slot(gg)]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = wave_xor_max(mx, o);
   if (mx == kNegInf) {  // no key visible to this query in any piece
     for (int d = lane; d < kSD; d += 64) orow[d] = 0;
     if (lse != nullptr && lane == 0) lse[(long)h * total_q + row] = kNegInf;
     return;
   }
   float tot = 0.f;
-  for (int gg = first; gg <= last; ++gg) tot += hw_exp2((part_lse[slot(gg)] - mx) * kLog2e);
-  const float lse_all = mx + hw_log2(tot) * kLn2;
-  for (int d = lane; d < kSD; d += 64) {
-    float acc = 0.f;
-    for (int gg = first; gg <= last; ++gg) {
-      acc += hw_exp2((part_lse[slot(gg)] - lse_all) * kLog2e) * part_o[slot(gg) * kSD + d];
-    }
-    orow[d] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+  for (int c0 = first; c0 <= last; c0 += 64) {
+    const int gg = c0 + lane;
+    if (gg <= last) tot += hw_exp2((part_lse[slot(gg)] - mx) * kLog2e);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tot = wave_xor_sum(tot, o);
+  const float lse_all = mx + hw_log2(tot) * kLn2;
+  float acc0 = 0.f, acc1 = 0.f;  // columns lane and lane + 64
+  for (int c0 = first; c0 <= last; c0 += 64) {
+    const int gg = c0 + lane;
+    const float wl = gg <= last ? hw_exp2((part_lse[slot(gg)] - lse_all) * kLog2e) : 0.f;
+    const int n = last - c0 + 1 < 64 ? last - c0 + 1 : 64;
+#pragma unroll 4
+    for (int i = 0; i < n; ++i) {
+      const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+      const float* po = part_o + slot(c0 + i) * kSD;
+      acc0 += wi * po[lane];
+      acc1 += wi * po[lane + 64];
+    }
+  }
+  orow[lane] = __builtin_bit_cast(uint16_t, (__bf16)acc0);
+  orow[lane + 64] = __builtin_bit_cast(uint16_t, (__bf16)acc1);
   if (lse != nullptr && lane == 0) lse[(long)h * total_q + row] = lse_all;
 }
 
