@@ -426,6 +426,33 @@ attn_status_t attn_vsa_h3_block_map(const void* q_tiled, const void* k_tiled, co
                                     int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t topk,
                                     uint8_t* block_map, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Tile gather and block map in one call (vLLM-Omni fastvideo_vsa.py page:
+ * _get_tile_partition_indices and the tile gather, then _pool_h3_tiles, the
+ * pooled score matmul and _build_h3_block_map). Raster q and k go to tile
+ * order exactly as attn_vsa_h3_tile_gather writes them, and the map equals
+ * attn_vsa_h3_block_map's on those copies, bit for bit: the tile means are
+ * summed in the same fp32 order while the rows are copied, so the copies are
+ * not read back. num_segments == 0 is the plain video layout
+ * (attn_vsa_tile_gather + attn_vsa_block_map).
+ *   q           [batch, prefix rows + t*h*w, num_heads, head_dim] bf16 raster
+ *   k           [batch, prefix rows + t*h*w, num_kv_heads, head_dim] bf16 raster
+ *   q_tiled     [batch, num_tiles * 64, num_heads, head_dim] bf16, written
+ *   k_tiled     [batch, num_tiles * 64, num_kv_heads, head_dim] bf16, written
+ *   tile_sizes  [num_tiles] int32, written (nullable)
+ *   block_map   [batch, num_heads, num_tiles, num_tiles] uint8, written
+ *   workspace   >= attn_vsa_block_map_workspace_size() bytes for num_tiles
+ *               (attn_vsa_h3_num_tiles gives num_tiles)
+ * batch == 0 or num_tiles == 0 is a no-op. Errors: as attn_vsa_h3_tile_gather
+ * (with row_elems = num_heads * head_dim) and attn_vsa_h3_block_map.
+ */
+attn_status_t attn_vsa_h3_gather_block_map(const void* q, const void* k, const int32_t* prefix_segments,
+                                           int32_t num_segments, int32_t batch, int32_t t, int32_t h, int32_t w,
+                                           int32_t tile_t, int32_t tile_h, int32_t tile_w, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t topk,
+                                           void* q_tiled, void* k_tiled, int32_t* tile_sizes, uint8_t* block_map,
+                                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes for attn_vsa_compressed_add (fp32 tile means of q, k, v and
  * the per-tile compressed rows). Written to *bytes (host pointer). */
 attn_status_t attn_vsa_compressed_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,

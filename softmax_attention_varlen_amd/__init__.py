@@ -43,6 +43,7 @@ __all__ = [
     "attn_vsa_h3_tile_gather",
     "attn_vsa_h3_untile",
     "attn_vsa_h3_block_map",
+    "attn_vsa_h3_gather_block_map",
     "vsa_h3_prepare",
     "attn_vsa_untile",
     "attn_vsa_block_map_workspace_size",
@@ -96,6 +97,8 @@ _SIGS = {
     "attn_vsa_h3_untile": (ctypes.c_int, [_p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _p, _p]),
     "attn_vsa_h3_block_map": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _sz,
                                              _p]),
+    "attn_vsa_h3_gather_block_map": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                    _i32, _i32, _i32, _f32, _i32, _p, _p, _p, _p, _p, _sz, _p]),
     "attn_vsa_compressed_workspace_size": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "attn_vsa_compressed_add": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _f32, _p, _p, _sz,
                                                _p]),
@@ -669,23 +672,60 @@ def attn_vsa_h3_block_map(q_tiled, k_tiled, tile_sizes, num_prefix_tiles: int, s
     return block_map
 
 
+def attn_vsa_h3_gather_block_map(q, k, prefix_segments, video_shape, softmax_scale: float, topk: int,
+                                 tile_shape=(4, 4, 4), q_tiled=None, k_tiled=None, tile_sizes=None, block_map=None,
+                                 workspace=None, stream=None):
+    """Raster [B, prefix + t*h*w, H, D] q and k -> their (H3) tile order and the block
+    map in one call (empty prefix_segments: the plain video layout). Returns
+    (q_tiled, k_tiled, tile_sizes, block_map)."""
+    b, n, hq, d = q.shape
+    hkv = k.shape[2]
+    _shape(k, "k", (b, n, hkv, d))
+    _, nt = attn_vsa_h3_num_tiles(prefix_segments, video_shape, tile_shape)
+    if n != sum(int(v) for v in prefix_segments) + int(np.prod([int(v) for v in video_shape])):
+        raise ValueError("q's sequence length must equal the prefix rows plus t*h*w")
+    dev = q.device
+    if q_tiled is None:
+        q_tiled = torch.empty((b, nt * 64, hq, d), dtype=q.dtype, device=dev)
+    if k_tiled is None:
+        k_tiled = torch.empty((b, nt * 64, hkv, d), dtype=k.dtype, device=dev)
+    if tile_sizes is None:
+        tile_sizes = torch.empty(nt, dtype=torch.int32, device=dev)
+    if block_map is None:
+        block_map = torch.empty((b, hq, nt, nt), dtype=torch.uint8, device=dev)
+    _shape(q_tiled, "q_tiled", (b, nt * 64, hq, d))
+    _shape(k_tiled, "k_tiled", (b, nt * 64, hkv, d))
+    _shape(tile_sizes, "tile_sizes", (nt,))
+    _shape(block_map, "block_map", (b, hq, nt, nt))
+    if workspace is None:
+        workspace = torch.empty(max(attn_vsa_block_map_workspace_size(b, hq, hkv, nt, d), 1), dtype=torch.uint8,
+                                device=dev)
+    segs, ns = _segments(prefix_segments)
+    st = load_library().attn_vsa_h3_gather_block_map(
+        _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16, dev), segs, ns, b,
+        *(int(v) for v in video_shape), *(int(v) for v in tile_shape), hq, hkv, d, float(softmax_scale), int(topk),
+        _dev(q_tiled, "q_tiled", torch.bfloat16, dev), _dev(k_tiled, "k_tiled", torch.bfloat16, dev),
+        _dev(tile_sizes, "tile_sizes", torch.int32, dev), _dev(block_map, "block_map", torch.uint8, dev),
+        _dev(workspace, "workspace", torch.uint8, dev), workspace.numel(), _stream_ptr(q, stream))
+    _check("attn_vsa_h3_gather_block_map", st)
+    return q_tiled, k_tiled, tile_sizes, block_map
+
+
 def vsa_h3_prepare(q, k, v, prefix_segments, video_shape, topk: int, softmax_scale: float, tile_shape=(4, 4, 4),
                    stream=None):
     """Raster [prefix + video] q/k/v -> H3 tile order plus the H3 block map, all in
     the library's kernels. Returns a dict like vsa_prepare's plus num_prefix_tiles."""
-    qt, sizes = attn_vsa_h3_tile_gather(q, prefix_segments, video_shape, tile_shape, stream=stream)
-    kt, _ = attn_vsa_h3_tile_gather(k, prefix_segments, video_shape, tile_shape, stream=stream)
+    qt, kt, sizes, bmap = attn_vsa_h3_gather_block_map(q, k, prefix_segments, video_shape, softmax_scale, topk,
+                                                       tile_shape, stream=stream)
     vt, _ = attn_vsa_h3_tile_gather(v, prefix_segments, video_shape, tile_shape, stream=stream)
     n_pre, _ = attn_vsa_h3_num_tiles(prefix_segments, video_shape, tile_shape)
-    bmap = attn_vsa_h3_block_map(qt, kt, sizes, n_pre, softmax_scale, topk, stream=stream)
     return {"q": qt, "k": kt, "v": vt, "block_map": bmap, "tile_sizes": sizes, "num_prefix_tiles": n_pre}
 
 
 def vsa_prepare(q, k, v, video_shape, tile_shape, topk: int, softmax_scale: float, stream=None):
     """Raster q/k/v -> tile order plus the top-k block map, all in the library's
     kernels. Returns a dict with q, k, v (tile order), block_map and tile_sizes."""
-    qt, sizes = attn_vsa_tile_gather(q, video_shape, tile_shape, stream=stream)
-    kt, _ = attn_vsa_tile_gather(k, video_shape, tile_shape, stream=stream)
+    qt, kt, sizes, bmap = attn_vsa_h3_gather_block_map(q, k, [], video_shape, softmax_scale, topk, tile_shape,
+                                                       stream=stream)
     vt, _ = attn_vsa_tile_gather(v, video_shape, tile_shape, stream=stream)
-    bmap = attn_vsa_block_map(qt, kt, sizes, softmax_scale, topk, stream=stream)
     return {"q": qt, "k": kt, "v": vt, "block_map": bmap, "tile_sizes": sizes}

@@ -522,6 +522,37 @@ attn_status_t attn_vsa_h3_block_map(const void* q_tiled, const void* k_tiled, co
                             stream);
 }
 
+attn_status_t attn_vsa_h3_gather_block_map(const void* q, const void* k, const int32_t* prefix_segments,
+                                           int32_t num_segments, int32_t batch, int32_t t, int32_t h, int32_t w,
+                                           int32_t tile_t, int32_t tile_h, int32_t tile_w, int32_t num_heads,
+                                           int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t topk,
+                                           void* q_tiled, void* k_tiled, int32_t* tile_sizes, uint8_t* block_map,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_heads <= 0 || num_kv_heads <= 0 || topk < 1) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
+  if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
+  const attn_status_t st = check_h3_geometry(prefix_segments, num_segments, batch, t, h, w, tile_t, tile_h, tile_w,
+                                             num_heads * head_dim);
+  if (st != ATTN_OK) return st;
+  attn::VsaGeometry g{t, h, w, tile_t, tile_h, tile_w};
+  g.prefix_segments = prefix_segments;
+  g.num_segments = num_segments;
+  const int num_tiles = attn::vsa_num_tiles(g);
+  if (num_tiles > 16384) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0 || num_tiles == 0) return ATTN_OK;
+  if (q == nullptr || k == nullptr || q_tiled == nullptr || k_tiled == nullptr || block_map == nullptr) {
+    return ATTN_ERR_INVALID_ARG;
+  }
+  if ((long long)batch * num_heads * num_tiles * num_tiles > kMaxRows) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn::vsa_map_workspace_bytes(batch, num_heads, num_kv_heads, num_tiles, head_dim);
+  if (workspace_bytes < need) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (workspace == nullptr) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_vsa_gather_block_map(q, k, g, batch, num_heads, num_kv_heads, head_dim, softmax_scale,
+                                                    topk, q_tiled, k_tiled, tile_sizes, block_map, workspace,
+                                                    (hipStream_t)stream));
+}
+
 attn_status_t attn_vsa_compressed_workspace_size(int32_t batch, int32_t num_heads, int32_t num_kv_heads,
                                                  int32_t num_tiles, int32_t head_dim, size_t* bytes) {
   if (bytes == nullptr) return ATTN_ERR_INVALID_ARG;

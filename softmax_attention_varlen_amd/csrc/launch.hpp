@@ -166,6 +166,13 @@ size_t vsa_map_workspace_bytes(int batch, int heads, int kv_heads, int n_tiles, 
 hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const int32_t* sizes, int batch,
                                 int n_tiles, int heads, int kv_heads, int head_dim, float scale, int topk,
                                 uint8_t* map, void* workspace, hipStream_t stream, int n_prefix = 0);
+// Tile gather of raster q and k and the block map from their tile means in
+// one pass over the raster rows (the tile-order copies are written, not read
+// back); same workspace layout and map as launch_vsa_block_map.
+hipError_t launch_vsa_gather_block_map(const void* q, const void* k, const VsaGeometry& g, int batch, int heads,
+                                       int kv_heads, int head_dim, float scale, int topk, void* q_tiled,
+                                       void* k_tiled, int32_t* sizes, uint8_t* map, void* workspace,
+                                       hipStream_t stream);
 
 // VSA compressed branch: out (tile order, bf16) += broadcast_rows(softmax(pooled
 // scores) @ value tile means) * gate. Workspace: fp32 means of q, k, v and c.

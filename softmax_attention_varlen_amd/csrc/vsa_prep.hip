@@ -188,6 +188,86 @@ __global__ __launch_bounds__(256) void tile_pool_kernel(PoolArgs pa, const int32
   }
 }
 
+// Tile gather and tile means in one pass (q and k of the block map): one
+// workgroup per (batch, tile, tensor, group of 64 16-byte column chunks)
+// copies those columns of the tile's 64 rows from raster to tile order, as
+// tile_gather_kernel does (padding rows written as zeros), and sums them
+// exactly as tile_pool_kernel does (wave g adds rows 16g .. 16g + 15 in order,
+// the four wave partials are added in ascending wave order), so the means, and
+// the map built from them, are bit-identical to the two-pass form while the
+// tile-order copies are not read back.
+struct GatherPoolSrc {
+  const uint16_t* x;  // raster [batch][n_rows][heads * head_dim]
+  uint16_t* y;        // tile order [batch][n_tiles * 64][heads * head_dim]
+  float* pooled;      // [batch][heads][n_tiles][head_dim]
+  int heads;
+};
+struct GatherPoolArgs {
+  GatherPoolSrc s[2];
+};
+
+__global__ __launch_bounds__(256) void tile_gather_pool_kernel(GatherPoolArgs pa, BoxGeom gm, PrefixLayout pl,
+                                                               int n_tiles, long n_rows, int head_dim,
+                                                               int32_t* __restrict__ sizes) {
+  __shared__ f32x4 part[4][64][2];
+  const GatherPoolSrc src = pa.s[blockIdx.y];
+  const int c = (int)(blockIdx.x % n_tiles);
+  const long b = blockIdx.x / n_tiles;
+  const int tid = threadIdx.x, g = tid >> 6, jl = tid & 63;
+  int size = 0;
+  int srow[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) srow[i] = tile_source(gm, pl, c, 16 * g + i, &size);
+  if (sizes != nullptr && b == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) sizes[c] = size;
+  const float inv = 1.f / (float)(size > 1 ? size : 1);
+  const long row_elems = (long)src.heads * head_dim;
+  const uint16_t* xb = src.x + b * n_rows * row_elems;
+  uint16_t* yb = src.y + (b * n_tiles + c) * 64 * row_elems;
+  const int chunks = (int)(row_elems / 8);
+  const int j0 = (int)blockIdx.z * 64;  // this workgroup's 64 chunk columns
+  if (j0 >= chunks) return;             // whole workgroup (k may have fewer heads than q)
+  {
+    const int j = j0 + jl;
+    f32x4 lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+    if (j < chunks) {
+      u32x4 v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        v[i] = srow[i] >= 0 ? ld_global16(xb + (long)srow[i] * row_elems + j * 8) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) *reinterpret_cast<u32x4*>(yb + (long)(16 * g + i) * row_elems + j * 8) = v[i];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (16 * g + i < size) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            lo[2 * e] += __uint_as_float(v[i][e] << 16);
+            lo[2 * e + 1] += __uint_as_float(v[i][e] & 0xffff0000u);
+            hi[2 * e] += __uint_as_float(v[i][2 + e] << 16);
+            hi[2 * e + 1] += __uint_as_float(v[i][2 + e] & 0xffff0000u);
+          }
+        }
+      }
+    }
+    part[g][jl][0] = lo;
+    part[g][jl][1] = hi;
+    __syncthreads();
+    if (tid < 128) {
+      const int jj = j0 + (tid >> 1), half = tid & 1;
+      if (jj < chunks) {
+        f32x4 t = part[0][tid >> 1][half];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) t += part[w][tid >> 1][half];
+        const int h = (jj * 8) / head_dim, d = (jj * 8) % head_dim + 4 * half;
+        float* prow = src.pooled + ((b * src.heads + h) * n_tiles + c) * (long)head_dim + d;
+        *reinterpret_cast<f32x4*>(prow) = t * inv;
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Batched fp32 GEMM for the pooled scores and the compressed rows:
 // C[z] = alpha * A[z] B'[z], A [M][K] (row stride lda); B' = B^T with B stored
 // [N][K] (TRANS_B), else B' = B stored [K][N]; C row stride ldc. The launch
@@ -624,6 +704,10 @@ size_t vsa_map_workspace_bytes(int batch, int heads, int kv_heads, int n_tiles, 
          score_bytes(batch, heads, n_tiles);
 }
 
+static hipError_t map_from_means(const float* qpool, const float* kpool, float* scores, int batch, int n_tiles,
+                                 int heads, int kv_heads, int head_dim, float scale, int topk, uint8_t* map,
+                                 hipStream_t stream, int n_prefix);
+
 hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const int32_t* sizes, int batch,
                                 int n_tiles, int heads, int kv_heads, int head_dim, float scale, int topk,
                                 uint8_t* map, void* workspace, hipStream_t stream, int n_prefix) {
@@ -633,8 +717,41 @@ hipError_t launch_vsa_block_map(const void* q_tiled, const void* k_tiled, const 
   PoolArgs pa{};
   pa.s[0] = PoolSrc{(const uint16_t*)q_tiled, qpool, heads};
   pa.s[1] = PoolSrc{(const uint16_t*)k_tiled, kpool, kv_heads};
-  hipError_t e = launch_pool(pa, 2, sizes, batch, n_tiles, head_dim, stream);
+  const hipError_t e = launch_pool(pa, 2, sizes, batch, n_tiles, head_dim, stream);
   if (e != hipSuccess) return e;
+  return map_from_means(qpool, kpool, scores, batch, n_tiles, heads, kv_heads, head_dim, scale, topk, map, stream,
+                        n_prefix);
+}
+
+hipError_t launch_vsa_gather_block_map(const void* q, const void* k, const VsaGeometry& g, int batch, int heads,
+                                       int kv_heads, int head_dim, float scale, int topk, void* q_tiled,
+                                       void* k_tiled, int32_t* sizes, uint8_t* map, void* workspace,
+                                       hipStream_t stream) {
+  const BoxGeom gm = make_geom(g);
+  const PrefixLayout pl = make_prefix(g);
+  const int n_tiles = pl.n_tiles + gm.nbt * gm.nbh * gm.nbw;
+  const long n_rows = (long)pl.len + (long)gm.T * gm.H * gm.W;
+  float* qpool = (float*)workspace;
+  float* kpool = qpool + (size_t)batch * heads * n_tiles * head_dim;
+  float* scores = kpool + (size_t)batch * kv_heads * n_tiles * head_dim;
+  GatherPoolArgs pa{};
+  pa.s[0] = GatherPoolSrc{(const uint16_t*)q, (uint16_t*)q_tiled, qpool, heads};
+  pa.s[1] = GatherPoolSrc{(const uint16_t*)k, (uint16_t*)k_tiled, kpool, kv_heads};
+  const int col_groups = (heads * head_dim / 8 + 63) / 64;  // q has at least as many heads as k
+  hipLaunchKernelGGL(tile_gather_pool_kernel, dim3((unsigned)((long)batch * n_tiles), 2u, (unsigned)col_groups),
+                     dim3(256), 0, stream, pa, gm, pl, n_tiles, n_rows, head_dim, sizes);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return map_from_means(qpool, kpool, scores, batch, n_tiles, heads, kv_heads, head_dim, scale, topk, map, stream,
+                        pl.n_tiles);
+}
+
+// Pooled scores (batched fp32 GEMM of the tile means) and the per-row top-k,
+// in chunks of (batch, head) pairs sized to the score buffer.
+static hipError_t map_from_means(const float* qpool, const float* kpool, float* scores, int batch, int n_tiles,
+                                 int heads, int kv_heads, int head_dim, float scale, int topk, uint8_t* map,
+                                 hipStream_t stream, int n_prefix) {
+  hipError_t e = hipSuccess;
   const int n_video = n_tiles - n_prefix;
   const int keep = topk < n_video ? topk : n_video;
   const int total = batch * heads, chunk = score_chunk(batch, heads, n_tiles), ld = score_ld(n_tiles);

@@ -293,3 +293,32 @@ def test_h3_block_map_validation():
     assert f(FAKE, FAKE, FAKE, 1, 10, -1, 4, 4, 128, 0.1, 4, FAKE, FAKE, 1 << 30, None) == INVALID
     assert f(FAKE, FAKE, FAKE, 1, 10, 2, 4, 4, 128, 0.1, 0, FAKE, FAKE, 1 << 30, None) == INVALID
     assert f(FAKE, FAKE, FAKE, 1, 10, 2, 4, 4, 128, 0.1, 4, FAKE, FAKE, 0, None) == WS_SMALL
+
+
+def test_h3_gather_block_map_validation():
+    f = lib().attn_vsa_h3_gather_block_map
+    segs = (ctypes.c_int32 * 2)(70, 5)
+    many = (ctypes.c_int32 * 17)(*([10] * 17))
+    neg = (ctypes.c_int32 * 2)(10, -1)
+
+    def call(segments=segs, nseg=2, batch=1, shape=(2, 5, 4), tiles=(4, 4, 4), hq=4, hkv=2, d=128, scale=0.1,
+             topk=4, q=FAKE, k=FAKE, qt=FAKE, kt=FAKE, sizes=None, bmap=FAKE, ws=FAKE, ws_bytes=1 << 30):
+        return f(q, k, segments, nseg, batch, *shape, *tiles, hq, hkv, d, scale, topk, qt, kt, sizes, bmap, ws,
+                 ws_bytes, None)
+
+    assert call(topk=0) == INVALID
+    assert call(hq=0) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(d=80) == UNSUPPORTED
+    assert call(hq=6, hkv=4) == UNSUPPORTED
+    assert call(segments=many, nseg=17) == UNSUPPORTED
+    assert call(segments=neg) == INVALID
+    assert call(segments=None) == INVALID
+    assert call(tiles=(4, 4, 8)) == UNSUPPORTED  # a tile of more than 64 rows
+    assert call(batch=-1) == INVALID
+    assert call(q=None) == INVALID
+    assert call(bmap=None) == INVALID
+    assert call(ws_bytes=0) == WS_SMALL
+    assert call(ws=None) == INVALID
+    assert call(batch=0) == OK  # no-op
+    assert call(segments=None, nseg=0, shape=(0, 0, 0)) == OK  # no tiles: no-op

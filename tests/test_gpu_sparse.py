@@ -579,3 +579,33 @@ def test_h3_full_size_sampled_tiles():
     assert_close("out", host(out.index_select(1, rt))[:, :, heads], ref_o[:, rows][:, :, heads], OUT_TOL,
                  bf16_output=True)
     assert_close("lse", host(lse.index_select(2, rt))[:, heads], ref_l[:, heads][:, :, rows], LSE_TOL)
+
+
+@pytest.mark.parametrize("segs,shape,d,hq,hkv,topk", [((70, 5), (2, 5, 4), 64, 4, 2, 3),
+                                                    ((130, 64, 1), (5, 9, 7), 128, 2, 2, 4),
+                                                    ((), (5, 7, 9), 256, 3, 1, 5),
+                                                    ((300,), (0, 0, 0), 128, 2, 1, 2),
+                                                    ((), (16, 32, 32), 128, 12, 12, 32)])
+def test_gather_block_map_equals_separate_calls(segs, shape, d, hq, hkv, topk):
+    """The one-call gather + map gives the tile-order copies, sizes and map of the
+    separate gather and map calls bit for bit (the tile means are summed in the
+    same order), and its copies are the oracle's tile order."""
+    n = sum(segs) + int(np.prod(shape))
+    q, k = randn_bf16((2, n, hq, d), 399), randn_bf16((2, n, hkv, d), 400)
+    announce("gather block map", segs, shape, d, hq, hkv, topk)
+    scale = d ** -0.5
+    qt, kt, sizes, gmap = sav.attn_vsa_h3_gather_block_map(dev(q), dev(k), segs, shape, scale, topk)
+    rq, rsizes = sav.attn_vsa_h3_tile_gather(dev(q), segs, shape)
+    rk, _ = sav.attn_vsa_h3_tile_gather(dev(k), segs, shape)
+    n_pre, _ = sav.attn_vsa_h3_num_tiles(segs, shape)
+    rmap = sav.attn_vsa_h3_block_map(rq, rk, rsizes, n_pre, scale, topk)
+    torch.cuda.synchronize()
+    assert torch.equal(qt.view(torch.int16), rq.view(torch.int16))
+    assert torch.equal(kt.view(torch.int16), rk.view(torch.int16))
+    assert torch.equal(sizes, rsizes)
+    assert torch.equal(gmap, rmap)
+    assert np.array_equal(qt.cpu().view(torch.int16).numpy(), oracle.h3_to_tile_order(q.view(torch.int16).numpy(),
+                                                                                       segs, shape))
+    if sizes.numel() <= 64:
+        scores = _h3_scores(qt.cpu(), kt.cpu(), sizes.cpu().numpy(), hq // hkv, scale)
+        check_h3_map(gmap.cpu().numpy(), scores, n_pre, topk)
