@@ -138,6 +138,24 @@ def test_indexing_probe_bit_exact(causal, d):
     assert checked > 500
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_random_varlen_head_dim_128(seed):
+    """Seeded random packings for the pipelined head_dim-128 kernels: 1-6
+    documents of 1-700 query rows, key lengths equal or drawn separately
+    (bottom-right causal then covers rows that see no key), grouped heads, causal
+    or not, so ring wrap-around, partial tiles and diagonal positions vary."""
+    rng = np.random.default_rng(7000 + seed)
+    batch = int(rng.integers(1, 7))
+    lq = rng.integers(1, 701, batch).tolist()
+    lk = lq if rng.random() < 0.5 else rng.integers(1, 701, batch).tolist()
+    group = int(rng.choice([1, 2, 4]))
+    hkv = int(rng.integers(1, 3))
+    causal = bool(rng.random() < 0.6)
+    case = varlen_case(lq, lk, num_heads=hkv * group, num_kv_heads=hkv, head_dim=128, causal=causal,
+                       seed=7000 + seed, name=f"random-{seed}")
+    check_full(case)
+
+
 def _sample_rows(case, rng, extra=24):
     rows = []
     cu = case.cu_seqlens_q
