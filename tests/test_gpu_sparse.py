@@ -92,6 +92,34 @@ def test_head_dim_128_beyond_staged_list_capacity():
     assert_close("lse", host(lse)[:, :, rows], ref_l[:, :, rows], LSE_TOL)
 
 
+@pytest.mark.parametrize("density", [0.45, 0.9])
+def test_head_dim_128_long_kept_lists(density):
+    """Kept lists longer than 64 tiles (the D=128 kernel reads its list through a
+    64-entry window that moves forward), with partial and empty tiles that are
+    dropped from the lists, a row with every tile, one with none and one with 65."""
+    b, nt, hq, hkv, d = 1, 150, 4, 2, 128
+    q = randn_bf16((b, nt * 64, hq, d), 350)
+    k, v = (randn_bf16((b, nt * 64, hkv, d), 351 + j) for j in range(2))
+    rng = np.random.default_rng(35 + int(density * 100))
+    sizes = np.full(nt, 64, dtype=np.int32)
+    sizes[rng.choice(nt, 30, replace=False)] = rng.integers(0, 64, 30)  # some empty tiles
+    bmap = rng.random((b, hq, nt, nt)) < density
+    bmap[0, 0, 7] = True
+    bmap[0, 1, 8] = False
+    bmap[0, 2, 9] = False
+    bmap[0, 2, 9, rng.choice(nt, 65, replace=False)] = True
+    scale = d ** -0.5
+    announce("sparse long kept lists", density, int(bmap.sum(-1).max()))
+    out, lse = run(q, k, v, bmap, sizes, scale)
+    sample = sorted({0, 7, 8, 9, nt - 1} | set(rng.choice(nt, 12, replace=False).tolist()))
+    ref_o, ref_l = oracle.block_sparse_attention(q, k, v, bmap, sizes, scale, q_tiles=sample)
+    rows = np.concatenate([np.arange(a * 64, a * 64 + 64) for a in sample])
+    assert_close("out", host(out)[:, rows], ref_o[:, rows], OUT_TOL, bf16_output=True)
+    fin = np.isfinite(ref_l[:, :, rows])
+    assert np.array_equal(fin, np.isfinite(host(lse)[:, :, rows]))
+    assert_close("lse", host(lse)[:, :, rows][fin], ref_l[:, :, rows][fin], LSE_TOL)
+
+
 def test_full_map_matches_dense_oracle_and_is_deterministic():
     b, nt, h, d = 1, 5, 3, 128
     q, k, v = (randn_bf16((b, nt * 64, h, d), 320 + j) for j in range(3))
