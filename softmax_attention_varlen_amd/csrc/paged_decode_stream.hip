@@ -16,9 +16,10 @@
 //
 // Streaming. Each wave keeps a two-stage LDS ring of 32-token chunks (K and V
 // of its kv head, 8 KB each) filled by direct-to-LDS loads, and issues chunk
-// j+2 as soon as chunk j is consumed: one chunk is always in flight, which is
-// what keeps HBM busy (a wave that waits for its whole chunk before issuing
-// the next leaves gaps). Load block b of a chunk holds tokens b, b+8, b+16,
+// j+2 as soon as chunk j is consumed (its K half right after chunk j's S^T,
+// its V half after the PV): one chunk is always in flight, which is what
+// keeps HBM busy (a wave that waits for its whole chunk before issuing the
+// next leaves gaps). Load block b of a chunk holds tokens b, b+8, b+16,
 // b+24 (4 rows x 256 B); blocks sit 1056 bytes apart, which makes the
 // transposing V reads conflict-free and the K reads at most 2-way.
 //
@@ -195,21 +196,27 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
   int lc_end = ((seg_end < lbase + lctx ? seg_end : lbase + lctx) - lbase - 1) / kSChunk;
   bool lvalid = true;
 
-  // issue the loader's chunk into `stage` and advance the cursor
-  auto issue = [&](int stage) {
+  // issue the loader's chunk into `stage` in two halves: K as soon as the
+  // stage's K has been read (after this chunk's S^T), then V and the cursor
+  // advance once its V has been read (after the PV)
+  const uint16_t* lkb = kv;  // K base of the block being issued, kept between the halves
+  auto issue_half = [&](int stage, bool v_half) {
     const int t0 = lc * kSChunk;
-    int blk = block_tables[(long)ls * max_blocks_per_seq + ((t0 + lskip) >> 7)];
-    blk = clampi(blk, 0, num_blocks - 1);
-    const uint16_t* kb = kv + (long)blk * blk_elems + (long)hk * kSD;
-    const uint32_t st = ring + stage * kSStage;
+    if (!v_half) {
+      int blk = block_tables[(long)ls * max_blocks_per_seq + ((t0 + lskip) >> 7)];
+      blk = clampi(blk, 0, num_blocks - 1);
+      lkb = kv + (long)blk * blk_elems + (long)hk * kSD;
+    }
+    const uint16_t* src = v_half ? lkb + v_plane : lkb;
+    const uint32_t st = ring + stage * kSStage + (v_half ? kSHalf : 0);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
       int t = t0 + b + 8 * (lane >> 4);
       t = t < lctx ? t : lctx - 1;  // rows past the context re-read the last one (same block)
       const uint32_t voff = (uint32_t)((t + lskip) & 127) * row_bytes + (uint32_t)(lane & 15) * 16u;
-      load_lds16(kb, voff, st + b * kSBlk);
-      load_lds16(kb + v_plane, voff, st + kSHalf + b * kSBlk);
+      load_lds16(src, voff, st + b * kSBlk);
     }
+    if (!v_half) return;
     if (lc < lc_end) {
       ++lc;
     } else {
@@ -226,6 +233,10 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
         lc_end = ((seg_end < lbase + lctx ? seg_end : lbase + lctx) - lbase - 1) / kSChunk;
       }
     }
+  };
+  auto issue = [&](int stage) {
+    issue_half(stage, false);
+    issue_half(stage, true);
   };
 
   issue(0);
@@ -296,6 +307,10 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
         const bf16x8 a = ld_lds16(kt, (int)(k_lane + (uint32_t)kb * 512u + (uint32_t)b * 64u));
         s[kb] = mfma16x16x32(a, qb[b], s[kb]);
       }
+    }
+    if (lvalid) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");  // this chunk's K reads are done
+      issue_half(stage, false);
     }
     const int t0 = cc * kSChunk;
     if (t0 < t_lo || t0 + kSChunk > t_hi || t0 + kSChunk - 1 > lim_min || t0 < lo_max) {
@@ -376,10 +391,10 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
     } else {
       ++cc;
     }
-    // this chunk's LDS reads are done before its stage is refilled
+    // this chunk's V reads are done before the V half of its stage is refilled
     asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
     second = lvalid;
-    if (lvalid) issue(stage);
+    if (lvalid) issue_half(stage, true);
   }
 }
 
