@@ -26,7 +26,12 @@ namespace attn {
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeChunk = 32;       // tokens per inner step
 constexpr int kDecodeBlock = 128;      // cache block size
-constexpr int kDecodeTargetItems = 4096;
+// Work items the split plan aims for (at most 64 splits per sequence): each
+// wave keeps one 32-token chunk in flight, so the grid needs many waves to
+// cover HBM latency. On 64 sequences of 1k-32k tokens, 4096 items (4096-token
+// splits) streamed 3.4 TB/s at D=64 and 4.5 at D=256; 32768 items (512-token
+// splits) 4.7 and 5.3.
+constexpr int kDecodeTargetItems = 32768;
 
 // LDS slot of token t (0..31) in a transposed V row: t = 16a + 4g + r sits at
 // 8g + 4a + r, so the 8 tokens one lane feeds into a PV MFMA (4g+{0..3} and
