@@ -50,18 +50,18 @@ TRAFFIC = {
               "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
     "causal": {"kernel": "prefill_d128_kernel<true,false,4,4,true,true>", "fetch_kib": 111923.0, "write_kib": 142491.4,
                "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
-    "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443493.6, "write_kib": 3043.0,
-              "sources": _DECODE_SRC, "sha256": "a64aebbcf2948e64"},
+    "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443493.1, "write_kib": 3043.0,
+              "sources": _DECODE_SRC, "sha256": "84ce7c15c1448e8c"},
     "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 235877.9, "write_kib": 49920.5,
                "sources": _SPARSE_SRC, "sha256": "b87edb9f712a3369"},
     "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,4,true,false>", "fetch_kib": 701680.5,
                       "write_kib": 87201.8, "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
-    "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445731.0, "write_kib": 12163.8,
-             "sources": _DECODE_SRC, "sha256": "a64aebbcf2948e64"},
+    "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445730.6, "write_kib": 12163.8,
+             "sources": _DECODE_SRC, "sha256": "84ce7c15c1448e8c"},
     "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 432763.5, "write_kib": 51482.8,
            "sources": _SPARSE_SRC, "sha256": "b87edb9f712a3369"},
-    "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531366.9, "write_kib": 3081.3,
-            "sources": _DECODE_SRC, "sha256": "a64aebbcf2948e64"},
+    "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531366.6, "write_kib": 3081.4,
+            "sources": _DECODE_SRC, "sha256": "84ce7c15c1448e8c"},
     "masked": {"kernel": "prefill_d128_kernel<false,false,4,4,true,true>", "fetch_kib": 28943.5, "write_kib": 50005.0,
                "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
     "padded": {"kernel": "prefill_d128_kernel<false,false,4,4,true,true>", "fetch_kib": 108036.1, "write_kib": 66235.8,

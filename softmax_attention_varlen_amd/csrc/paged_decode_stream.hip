@@ -461,7 +461,6 @@ __global__ __launch_bounds__(256) void paged_decode_stream_combine_kernel(
     const int gg = c0 + lane;
     const float wl = gg <= last ? hw_exp2((part_lse[slot(gg)] - lse_all) * kLog2e) : 0.f;
     const int n = last - c0 + 1 < 64 ? last - c0 + 1 : 64;
-#pragma unroll 4
     for (int i = 0; i < n; ++i) {
       const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
       const float* po = part_o + slot(c0 + i) * kSD;
