@@ -386,6 +386,52 @@ def bench_sparse(case, steps, warmup):
     return ms, flops, prep_ms, comp_ms
 
 
+def bench_head_dims(steps, warmup):
+    """Head dims other than 128 (the first-generation kernels), opt-in with
+    --only head_dims and not part of the default line: dense non-causal prefill
+    of 2 x 4096 rows with 24 heads, and decode over workload 4's 64 contexts
+    (32 query / 8 kv heads, a random permutation of cache blocks), inputs drawn
+    on the device."""
+    dev = torch.device("cuda")
+    rows = []
+    for d in (64, 96, 192, 256):
+        n, h = 2 * 4096, 24
+        q, k, v = (workloads.randn_bf16_on((n, h, d), 7700 + 10 * d + j, dev) for j in range(3))
+        cu = torch.tensor([0, 4096, 8192], dtype=torch.int32, device=dev)
+        out = torch.empty_like(q)
+        lse = torch.empty((h, n), dtype=torch.float32, device=dev)
+        ms = time_steps(lambda: sav.attn_varlen_fwd(q, k, v, cu, cu, 4096, 4096, d ** -0.5, False, out=out, lse=lse),
+                        steps, warmup)
+        flops = 4.0 * 2 * h * d * 4096 * 4096
+        rows.append({"workload": f"dense-b2-s4096-h24-d{d}", "value": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "unit": "TFLOP/s", "ms": round(ms, 4)})
+        del q, k, v, out
+    ctx = workloads.config4_lengths()
+    nblk = [(int(c) + 127) // 128 for c in ctx]
+    perm = np.random.default_rng(4).permutation(sum(nblk))
+    tables = np.full((len(ctx), max(nblk)), -1, dtype=np.int32)
+    o = 0
+    for i, nb in enumerate(nblk):
+        tables[i, :nb] = perm[o:o + nb]
+        o += nb
+    bt = torch.from_numpy(tables).to(dev)
+    cl = torch.from_numpy(np.asarray(ctx, dtype=np.int32)).to(dev)
+    for d in (64, 256):
+        cache = workloads.randn_bf16_on((2, sum(nblk), 128, 8, d), 7800 + d, dev)
+        q = workloads.randn_bf16_on((len(ctx), 32, d), 7801 + d, dev)
+        out = torch.empty_like(q)
+        ws = torch.empty(max(sav.attn_paged_decode_workspace_size(len(ctx), 32, 8, d, int(max(ctx))), 1),
+                         dtype=torch.uint8, device=dev)
+        ms = time_steps(lambda: sav.attn_paged_decode(q, cache, bt, cl, int(max(ctx)), d ** -0.5, out=out,
+                                                      workspace=ws), steps, warmup)
+        nbytes = float(sum(int(c) for c in ctx)) * 8 * d * 2 * 2
+        rows.append({"workload": f"paged-decode-64seq-ctx1k-32k-h32kv8-d{d}",
+                     "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms": round(ms, 4)})
+        del cache, q, out, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
 # ----------------------------------------------------------------------------
 # CPU baseline: the fp64 oracle on a bounded sample of the headline workload
 # ----------------------------------------------------------------------------
@@ -423,10 +469,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse", "h3", "paged_prefill", "spec", "swa",
-                                       "masked", "padded", "copy"],
+                                       "masked", "padded", "copy", "head_dims"],
                     default=None,
                     help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
-                         "copy, the reference that scales the HBM byte counters")
+                         "copy, the reference that scales the HBM byte counters; 'head_dims' times the head "
+                         "dims other than 128 (not part of the default line)")
     ap.add_argument("--clock-warmup-ms", type=float, default=CLOCK_WARMUP_MS,
                     help="repeat each workload's step for this long before its warm-up steps (0: off)")
     ap.add_argument("--no-secondary", action="store_true")
@@ -452,6 +499,13 @@ def main():
         ms = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
         print(json.dumps({"metric": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
                           "ms": round(ms, 5), "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
+        return
+
+    if args.only == "head_dims":
+        rows = bench_head_dims(args.steps, args.warmup)
+        for r in rows:
+            log(f"{r['workload']}: {r['ms'] * 1e3:.1f} us/step, {r['value']} {r['unit']}")
+        print(json.dumps({"metric": "head dims other than 128", "workloads": rows}))
         return
 
     secondary = []

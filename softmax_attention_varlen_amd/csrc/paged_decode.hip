@@ -289,18 +289,43 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(
   }
   if (nsplit == 1) return;  // written by the split kernel
   const long base = (long)seq * max_splits * hq + h;
+  auto slot = [&](int sp) { return base + (long)sp * hq; };
+  // The splits' LSEs are read lane-parallel (lane i holds split c0 + i of a
+  // 64-split chunk) and reduced across the wave; the weighted sum of the
+  // partial O takes each split's weight from its lane with v_readlane, in
+  // ascending split order.
   float mx = kNegInf;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, part_lse[base + (long)s * hq]);
+  for (int c0 = 0; c0 < nsplit; c0 += 64) {
+    if (c0 + lane < nsplit) mx = fmaxf(mx, part_lse[slot(c0 + lane)]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = wave_xor_max(mx, o);
   float tot = 0.f;
-  for (int s = 0; s < nsplit; ++s) tot += hw_exp2((part_lse[base + (long)s * hq] - mx) * kLog2e);
+  for (int c0 = 0; c0 < nsplit; c0 += 64) {
+    if (c0 + lane < nsplit) tot += hw_exp2((part_lse[slot(c0 + lane)] - mx) * kLog2e);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tot = wave_xor_sum(tot, o);
   const float lse_all = mx + hw_log2(tot) * kLn2;
-  for (int d = lane; d < D; d += 64) {
-    float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const long slot = base + (long)s * hq;
-      acc += hw_exp2((part_lse[slot] - lse_all) * kLog2e) * part_o[slot * D + d];
+  constexpr int NC = (D + 63) / 64;  // columns lane + 64k of the output row
+  float acc[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) acc[k] = 0.f;
+  for (int c0 = 0; c0 < nsplit; c0 += 64) {
+    const float wl = c0 + lane < nsplit ? hw_exp2((part_lse[slot(c0 + lane)] - lse_all) * kLog2e) : 0.f;
+    const int cnt = nsplit - c0 < 64 ? nsplit - c0 : 64;
+    for (int i = 0; i < cnt; ++i) {
+      const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
+      const float* po = part_o + slot(c0 + i) * D;
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        if (lane + 64 * k < D) acc[k] += wi * po[lane + 64 * k];
+      }
     }
-    orow[d] = __builtin_bit_cast(uint16_t, (__bf16)acc);
+  }
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    if (lane + 64 * k < D) orow[lane + 64 * k] = __builtin_bit_cast(uint16_t, (__bf16)acc[k]);
   }
   if (lse != nullptr && lane == 0) lse[(long)h * num_seqs + seq] = lse_all;
 }
