@@ -115,12 +115,13 @@ attn_status_t paged_decode_impl(const void* q, const void* kv_cache, const int32
   if (workspace_bytes < need.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (need.workspace_bytes > 0 && workspace == nullptr) return ATTN_ERR_INVALID_ARG;
   // a window at least as long as the context is no window; a shorter one
-  // leaves at most window + 32 streamed keys per sequence, which sizes the splits
+  // streams fewer keys per sequence, which sizes the splits (never beyond the
+  // workspace checked above)
   const int win = window >= 0 && window < max_context_len ? window : -1;
   const attn::DecodePlan plan =
-      win < 0 ? need : attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, win + 32 < max_context_len
-                                                                                                   ? win + 32
-                                                                                                   : max_context_len);
+      win < 0 ? need
+              : attn::plan_paged_decode_window(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, win);
+  if (plan.o_bytes + plan.lse_bytes > workspace_bytes && head_dim != 128) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   attn::DecodeArgs a{q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
                      max_context_len, num_heads, num_kv_heads, head_dim, block_size, softmax_scale, out, lse,
                      workspace};

@@ -70,6 +70,12 @@ struct DecodePlan {
 };
 
 DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len);
+// The plan a sliding-window call runs (window >= 0 and < max_context_len;
+// otherwise the full plan): sized for the keys a sequence streams, with never
+// more splits, partial bytes or workspace than plan_paged_decode's for the
+// full max_context_len, so the workspace that plan reports always suffices.
+DecodePlan plan_paged_decode_window(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
+                                    int window);
 
 struct DecodeArgs {
   const void* q;

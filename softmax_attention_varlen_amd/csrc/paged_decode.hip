@@ -351,6 +351,30 @@ DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int 
   return p;
 }
 
+DecodePlan plan_paged_decode_window(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
+                                    int window) {
+  const DecodePlan full = plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len);
+  if (window < 0 || window >= max_context_len) return full;
+  // the splits start at the 32-token chunk holding the window's first key, so
+  // a sequence streams at most window + 32 keys
+  const long streamed_l = (long)window + kDecodeChunk < max_context_len ? (long)window + kDecodeChunk : max_context_len;
+  const int streamed = (int)streamed_l;
+  DecodePlan p = plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, streamed);
+  if (p.max_splits > full.max_splits) {
+    // Splits round up to whole blocks, so the shorter stream can plan more
+    // splits than the full context did; cap them at the full plan's count so
+    // the partials fit the workspace that plan sized.
+    long split = (streamed + full.max_splits - 1) / full.max_splits;
+    split = ((split + kDecodeBlock - 1) / kDecodeBlock) * kDecodeBlock;
+    p.split_tokens = (int)split;
+    p.max_splits = (int)((streamed + split - 1) / split);
+    p.o_bytes = (size_t)num_seqs * p.max_splits * num_heads * head_dim * sizeof(float);
+    p.lse_bytes = (size_t)num_seqs * p.max_splits * num_heads * sizeof(float);
+  }
+  p.workspace_bytes = full.workspace_bytes;
+  return p;
+}
+
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
   const float c = a.scale * kLog2e;

@@ -1,5 +1,6 @@
 """Shared helpers for the GPU parity tests (not collected by pytest)."""
 
+import os
 import sys
 
 import numpy as np
@@ -27,6 +28,18 @@ def host(x):
     return x.detach().to("cpu", torch.float64).numpy()
 
 
+# Above this magnitude half a bf16 ulp (2**-6) exceeds OUT_TOL by itself, so a
+# bf16 output cannot hold the flat bound there whatever the kernel does; below
+# it the rounding of the stored result takes at most 2**-7 and the flat bound
+# stands.
+BF16_FLAT_LIMIT = 4.0
+
+# Every assert_close result of the session: the plain max-abs error, the same
+# over the elements the flat bound covers, and the test that produced it. The
+# session writes them out as JSON lines when ATTN_PARITY_RECORD names a file.
+RECORDS = []
+
+
 def bf16_half_ulp(x):
     """Half a bf16 unit in the last place at |x| (8 significant bits): the
     rounding error that storing an exact result as bf16 may add by itself."""
@@ -35,10 +48,18 @@ def bf16_half_ulp(x):
     return np.where(ax > 0, 2.0 ** (e - 8), 0.0)
 
 
-def assert_close(name, got, ref, tol, bf16_output=False):
-    """max |got - ref| <= tol elementwise (fp64 oracle as ref). For a bf16
-    output tensor the bound is tol plus the output's own storage rounding
-    (half a bf16 ulp of the exact value), which no bf16-output kernel avoids."""
+def assert_close(name, got, ref, tol, bf16_output=False, few_keys=False):
+    """max |got - ref| <= tol elementwise against the fp64 oracle (ref). For a
+    bf16 output the bound stays flat wherever |ref| < BF16_FLAT_LIMIT; only
+    elements of larger magnitude, where the output's own storage rounding (half
+    a bf16 ulp of the exact value) passes tol by itself, get that rounding added.
+
+    few_keys: edge cases whose rows see only a handful of keys (documents of a
+    few tokens, the first rows under a causal mask, contexts of 1-33 tokens).
+    Their outputs reach 2.5-4.5 (a weighted mean of a few N(0, 1) values), where
+    storing the result as bf16 takes up to 2**-7 and rounding each probability
+    to bf16 for the P V product adds up to 2**-9 of sum_j w_j |v_j| on top, so
+    such tests add half a bf16 ulp of the exact value at every magnitude."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
@@ -51,15 +72,24 @@ def assert_close(name, got, ref, tol, bf16_output=False):
     diff = np.zeros_like(ref)
     diff[fin_r] = np.abs(got[fin_r] - ref[fin_r])
     err = float(diff.max())
-    allowed = tol + (bf16_half_ulp(np.where(fin_r, ref, 0.0)) if bf16_output else 0.0)
+    aref = np.abs(np.where(fin_r, ref, 0.0))
+    flat = aref < (0.0 if few_keys else BF16_FLAT_LIMIT) if bf16_output else np.ones(ref.shape, dtype=bool)
+    err_flat = float(diff[flat].max()) if flat.any() else 0.0
+    allowed = tol + (np.where(flat, 0.0, bf16_half_ulp(aref)) if bf16_output else 0.0)
     bad = diff > allowed
+    RECORDS.append({"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0], "name": name,
+                    "max_abs": err, "max_abs_flat_region": err_flat, "tol": tol, "elements": int(ref.size),
+                    "over_tol": int(bad.sum()), "max_abs_ref": float(aref.max()), "few_keys": bool(few_keys),
+                    "max_abs_below_flat_limit": float(diff[aref < BF16_FLAT_LIMIT].max()) if (aref < BF16_FLAT_LIMIT).any() else 0.0})
     if bad.any():
         i = tuple(np.argwhere(bad)[0])
         raise AssertionError(f"{name}: error {diff[i]:.3e} > allowed {allowed[i] if np.ndim(allowed) else allowed:.3e} "
                              f"at {i} (got {got[i]!r}, ref {ref[i]!r}); max-abs {err:.3e}, "
                              f"{int(bad.sum())} of {bad.size} elements over")
-    print(f"[parity] {name}: max-abs {err:.3e} (tol {tol:.0e}{' + bf16 half-ulp' if bf16_output else ''})",
-          flush=True)
+    rule = ""
+    if bf16_output:
+        rule = ", + bf16 half-ulp" + ("" if few_keys else f" where |ref| >= {BF16_FLAT_LIMIT:g}")
+    print(f"[parity] {name}: max-abs {err:.3e} (tol {tol:.0e}{rule})", flush=True)
     return err
 
 

@@ -27,3 +27,19 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # parity records of the GPU tests (tests/_gpu_helpers.py), one JSON object a line
+    path = os.environ.get("ATTN_PARITY_RECORD")
+    if not path:
+        return
+    mod = sys.modules.get("tests._gpu_helpers")
+    if mod is None or not mod.RECORDS:
+        return
+    import json
+
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        for r in mod.RECORDS:
+            f.write(json.dumps(r) + "\n")

@@ -20,7 +20,7 @@ def run_case(case, with_lse=True, max_context_len=None):
     return res
 
 
-def check(case, seqs=None):
+def check(case, seqs=None, few_keys=False):
     announce("paged", case.name, case.context_lens.tolist()[:10], case.num_heads, case.num_kv_heads, case.head_dim)
     out, lse = run_case(case)
     ref_o, ref_l = oracle.paged_decode_attention(case.q, case.kv_cache, case.block_tables, case.context_lens,
@@ -28,7 +28,7 @@ def check(case, seqs=None):
     if seqs is not None:
         s = torch.from_numpy(np.asarray(seqs)).cuda()
         out, lse = out.index_select(0, s), lse.index_select(1, s)
-    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True, few_keys=few_keys)
     assert_close("lse", host(lse), ref_l, LSE_TOL)
 
 
@@ -40,20 +40,20 @@ CTX_EDGE = [1, 2, 31, 32, 33, 127, 128, 129, 255, 256, 1000, 4097]
 def test_sweep_edges(d, hq, hkv):
     case = paged_case(CTX_EDGE, num_heads=hq, num_kv_heads=hkv, head_dim=d, seed=200 + d + hq, spare_blocks=5,
                       max_blocks_per_seq=40, name=f"edges-d{d}-h{hq}kv{hkv}")
-    check(case)
+    check(case, few_keys=True)
 
 
 def test_long_contexts_many_splits():
     ctx = [20000, 1, 32768, 9000, 128 * 70 + 5, 3]
     case = paged_case(ctx, num_heads=32, num_kv_heads=8, head_dim=128, seed=210, spare_blocks=2,
                       name="long-contexts")
-    check(case)
+    check(case, few_keys=True)
 
 
 def test_zero_context_gives_zero_and_neg_inf():
     case = paged_case([0, 5, 0], num_heads=4, num_kv_heads=2, head_dim=64, seed=211, spare_blocks=1,
                       max_blocks_per_seq=2, name="zero-ctx")
-    check(case)
+    check(case, few_keys=True)
 
 
 # head_dim 128 streams equal segments of the concatenated token stream (at
@@ -75,7 +75,7 @@ def test_stream_segments_d128(name, hq, hkv):
     ctx = STREAM_CASES[name]
     case = paged_case(ctx, num_heads=hq, num_kv_heads=hkv, head_dim=128, seed=230 + len(ctx) + hq, spare_blocks=3,
                       name=f"stream-{name}-h{hq}kv{hkv}")
-    check(case)
+    check(case, few_keys=True)
 
 
 def test_host_max_context_len_larger_than_needed():
@@ -86,7 +86,7 @@ def test_host_max_context_len_larger_than_needed():
     o2, l2 = run_case(case, max_context_len=64 * 128)
     ref_o, ref_l = oracle.paged_decode_attention(case.q, case.kv_cache, case.block_tables, case.context_lens,
                                                  case.scale)
-    assert_close("out", host(o2), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("out", host(o2), ref_o, OUT_TOL, bf16_output=True, few_keys=True)
     assert_close("lse", host(l2), ref_l, LSE_TOL)
     assert_close("out-vs-tight", host(o1), host(o2), OUT_TOL)
 
@@ -147,8 +147,5 @@ def test_block_table_probe_bit_exact():
             assert torch.equal(out[b, h], expect), (b, h, t)
 
 
-def test_config4_full_size_sampled_sequences():
-    case = config4()
-    ctx = case.context_lens
-    seqs = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 1, 17, 31, 32, 47, 62, 63})
-    check(case, seqs=seqs)
+def test_config4_full_size_every_sequence():
+    check(config4())

@@ -66,7 +66,7 @@ def test_partial_tiles_random_map(d, hq, hkv):
     announce("sparse", d, hq, hkv, sizes.tolist())
     out, lse = run(qt, kt, vt, bmap, sizes, scale)
     ref_o, ref_l = oracle.block_sparse_attention(qt, kt, vt, bmap, sizes, scale)
-    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True, few_keys=True)
     assert_close("lse", host(lse), ref_l, LSE_TOL)
 
 
@@ -88,7 +88,7 @@ def test_head_dim_128_beyond_staged_list_capacity():
     sample = sorted({0, 1, 1500, 3071, 3072, 3073, nt - 2, nt - 1} | set(rng.choice(nt, 8, replace=False).tolist()))
     ref_o, ref_l = oracle.block_sparse_attention(q, k, v, bmap, sizes, scale, q_tiles=sample)
     rows = np.concatenate([np.arange(a * 64, a * 64 + 64) for a in sample])
-    assert_close("out", host(out)[:, rows], ref_o[:, rows], OUT_TOL, bf16_output=True)
+    assert_close("out", host(out)[:, rows], ref_o[:, rows], OUT_TOL, bf16_output=True, few_keys=True)
     assert_close("lse", host(lse)[:, :, rows], ref_l[:, :, rows], LSE_TOL)
 
 
@@ -114,7 +114,7 @@ def test_head_dim_128_long_kept_lists(density):
     sample = sorted({0, 7, 8, 9, nt - 1} | set(rng.choice(nt, 12, replace=False).tolist()))
     ref_o, ref_l = oracle.block_sparse_attention(q, k, v, bmap, sizes, scale, q_tiles=sample)
     rows = np.concatenate([np.arange(a * 64, a * 64 + 64) for a in sample])
-    assert_close("out", host(out)[:, rows], ref_o[:, rows], OUT_TOL, bf16_output=True)
+    assert_close("out", host(out)[:, rows], ref_o[:, rows], OUT_TOL, bf16_output=True, few_keys=True)
     fin = np.isfinite(ref_l[:, :, rows])
     assert np.array_equal(fin, np.isfinite(host(lse)[:, :, rows]))
     assert_close("lse", host(lse)[:, :, rows][fin], ref_l[:, :, rows][fin], LSE_TOL)
@@ -154,7 +154,7 @@ def test_item_order_longest_first_is_a_permutation():
                                          return_lse=True, workspace=ws)
     torch.cuda.synchronize()
     ref_o, ref_l = oracle.block_sparse_attention(q, k, v, bmap, sizes, d ** -0.5)
-    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True, few_keys=True)
     assert_close("lse", host(lse), ref_l, LSE_TOL)
     rows = b * h * nt
     words = ws.view(torch.int32).cpu().numpy()
@@ -186,7 +186,7 @@ def test_fewer_items_than_xcd_chunks(b, nt, h):
     announce("sparse few items", b, nt, h)
     out, lse = run(q, k, v, bmap, sizes, 128 ** -0.5)
     ref_o, ref_l = oracle.block_sparse_attention(q, k, v, bmap, sizes, 128 ** -0.5)
-    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True, few_keys=True)
     assert_close("lse", host(lse), ref_l, LSE_TOL)
 
 
@@ -235,7 +235,8 @@ def test_item_order_beyond_staged_counts():
         sel = torch.from_numpy(np.concatenate([np.arange(c * 64, c * 64 + 64) for c in kept]))
         ref_o, ref_l = oracle.dense_attention(q[:, a * 64:a * 64 + 64, h:h + 1].cpu(), kh[:, sel], vh[:, sel], scale,
                                               False)
-        assert_close("out", host(out[:, a * 64:a * 64 + 64, h:h + 1]), ref_o, OUT_TOL, bf16_output=True)
+        assert_close("out", host(out[:, a * 64:a * 64 + 64, h:h + 1]), ref_o, OUT_TOL, bf16_output=True,
+                     few_keys=True)
         assert_close("lse", host(lse[:, h:h + 1, a * 64:a * 64 + 64]), ref_l, LSE_TOL)
 
 
@@ -283,7 +284,7 @@ def test_kept_tile_probe_bit_exact():
     assert hits >= 6
 
 
-def test_config5_full_size_with_oracle_map_sampled_tiles():
+def test_config5_full_size_with_oracle_map_every_tile():
     case = config5()
     part, sizes, non_pad, untile = oracle.tile_metadata(case.video_shape, case.tile_shape, 64)
     nt = sizes.size
@@ -299,16 +300,9 @@ def test_config5_full_size_with_oracle_map_sampled_tiles():
     assert np.all(bmap.sum(-1) == 32)
     announce("sparse config5")
     out, lse = run(qt, kt, vt, bmap, sizes, case.scale)
-    tiles = [0, 1, 63, 64, 127, 128, 200, 255]
-    heads = [0, 5, 11]
-    ref_o, ref_l = oracle.block_sparse_attention(qt, kt, vt, bmap, sizes, case.scale, heads=heads, q_tiles=tiles)
-    rows = np.concatenate([np.arange(a * 64, a * 64 + 64) for a in tiles])
-    rt = torch.from_numpy(rows).cuda()
-    got_o = host(out.index_select(1, rt))[:, :, heads]
-    got_l = host(lse.index_select(2, rt))[:, heads]
-    assert_close("out", got_o, ref_o[:, rows][:, :, heads], OUT_TOL, bf16_output=True)
-    assert_close("lse", got_l, ref_l[:, heads][:, :, rows], LSE_TOL)
-    assert torch.isfinite(lse).all()
+    ref_o, ref_l = oracle.block_sparse_attention(qt, kt, vt, bmap, sizes, case.scale)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("lse", host(lse), ref_l, LSE_TOL)
 
 
 # --------------------------------------------------------------------------
@@ -385,7 +379,8 @@ def test_raster_pipeline_end_to_end():
     scores = oracle.pooled_scores(oracle.pool_tiles(qt, sizes), oracle.pool_tiles(kt, sizes), d ** -0.5)
     check_map_is_valid_topk(bmap, scores, topk)
     ref_t, _ = oracle.block_sparse_attention(qt, kt, vt, bmap, sizes, d ** -0.5)
-    assert_close("out", host(out), oracle.from_tile_order(ref_t, shape, tile), OUT_TOL, bf16_output=True)
+    assert_close("out", host(out), oracle.from_tile_order(ref_t, shape, tile), OUT_TOL, bf16_output=True,
+                 few_keys=True)
 
 
 def test_config5_gpu_map_matches_oracle_map():

@@ -21,13 +21,13 @@ def run_case(case, with_lse=True):
     return res
 
 
-def check_full(case):
+def check_full(case, few_keys=False):
     announce("varlen", case.name, case.cu_seqlens_q.tolist()[:8], case.num_heads, case.num_kv_heads,
              case.head_dim, case.causal)
     out, lse = run_case(case)
     ref_o, ref_l = oracle.varlen_attention(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k, case.scale,
                                            case.causal)
-    e_o = assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    e_o = assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True, few_keys=few_keys)
     e_l = assert_close("lse", host(lse), ref_l, LSE_TOL)
     return e_o, e_l
 
@@ -43,7 +43,7 @@ def test_sweep_ragged(d, causal, hq, hkv):
     # several 128-row query tiles and 64-key tiles, ragged tails, a 1-row doc
     lens = [1, 129, 300, 64, 190]
     case = varlen_case(lens, num_heads=hq, num_kv_heads=hkv, head_dim=d, causal=causal, seed=100 + d + hq + causal)
-    check_full(case)
+    check_full(case, few_keys=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -51,13 +51,13 @@ def test_cross_lengths_bottom_right(causal):
     # Lq != Lk per document, including Lq > Lk (rows with no key under causal)
     case = varlen_case([5, 200, 130, 70], [77, 150, 130, 1], num_heads=4, num_kv_heads=2, head_dim=128,
                        causal=causal, seed=41)
-    check_full(case)
+    check_full(case, few_keys=True)
 
 
 def test_empty_documents():
     case = varlen_case([0, 70, 0, 33], [0, 70, 5, 0], num_heads=2, num_kv_heads=2, head_dim=64, causal=False,
                        seed=42)
-    check_full(case)
+    check_full(case, few_keys=True)
 
 
 @pytest.mark.parametrize("batch", [511, 512, 700])
@@ -70,7 +70,7 @@ def test_many_documents(batch, causal):
     lens[rng.choice(batch, 5, replace=False)] = [257, 300, 513, 700, 1]
     lens[rng.choice(batch, 20, replace=False)] = 0
     case = varlen_case(lens.tolist(), num_heads=4, num_kv_heads=2, head_dim=128, causal=causal, seed=44 + batch)
-    check_full(case)
+    check_full(case, few_keys=True)
 
 
 def test_no_lse_and_determinism():
@@ -153,33 +153,16 @@ def test_random_varlen_head_dim_128(seed):
     causal = bool(rng.random() < 0.6)
     case = varlen_case(lq, lk, num_heads=hkv * group, num_kv_heads=hkv, head_dim=128, causal=causal,
                        seed=7000 + seed, name=f"random-{seed}")
-    check_full(case)
-
-
-def _sample_rows(case, rng, extra=24):
-    rows = []
-    cu = case.cu_seqlens_q
-    for b in range(case.batch):
-        L = int(cu[b + 1] - cu[b])
-        cand = {0, 1, 31, 32, 63, 64, 127, 128, 129, L // 2, L - 129, L - 128, L - 2, L - 1}
-        cand |= set(rng.integers(0, L, extra).tolist())
-        rows += [int(cu[b]) + r for r in sorted(cand) if 0 <= r < L]
-    return np.array(rows)
+    check_full(case, few_keys=True)
 
 
 @pytest.mark.parametrize("make", [config2, config3])
-def test_full_size_config_sampled_rows(make):
+def test_full_size_config_every_row(make):
+    """Configs 2 and 3 at full size, every row and head against the oracle."""
     case = make()
     announce("varlen full-size", case.name)
     out, lse = run_case(case)
-    rng = np.random.default_rng(7)
-    rows = _sample_rows(case, rng)
     ref_o, ref_l = oracle.varlen_attention(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k, case.scale,
-                                           case.causal, rows=rows)
-    rows_t = torch.from_numpy(rows).cuda()
-    assert_close("out", host(out.index_select(0, rows_t)), ref_o, OUT_TOL, bf16_output=True)
-    assert_close("lse", host(lse.index_select(1, rows_t)), ref_l, LSE_TOL)
-    # properties over every row: finite, inside the value range of V
-    assert torch.isfinite(lse).all()
-    vmax = case.v.float().abs().max().item()
-    assert out.float().abs().max().item() <= vmax + 1e-2
+                                           case.causal)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("lse", host(lse), ref_l, LSE_TOL)
