@@ -20,7 +20,8 @@
  *   - Output buffers belong to the caller (the pages' backends all declare
  *     accept_output_buffer and the Ascend forward requires an output tensor).
  *     The library allocates nothing, never synchronises the host, keeps no
- *     state besides cached launch parameters, and enqueues its kernels on
+ *     state besides cached launch parameters (and the fixed device array of
+ *     attn_paged_decode_scratch, part of the loaded code), and enqueues its kernels on
  *     `stream` (a hipStream_t; NULL = the default stream). Every call is
  *     therefore capturable in a HIP graph.
  *   - Host-side sizes (batch, totals, max lengths) plan the launch; device-side
@@ -158,6 +159,42 @@ attn_status_t attn_paged_decode_sliding_window(const void* q, const void* kv_cac
                                                int32_t head_dim, int32_t block_size, int32_t window,
                                                float softmax_scale, void* out, float* lse, void* workspace,
                                                size_t workspace_bytes, void* stream);
+
+/* Bytes of the device scratch array behind attn_paged_decode_scratch (per GPU). */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * attn_paged_decode without a workspace, for callers that cannot allocate
+ * device memory or pass one in: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. Arguments, layouts and results are
+ * those of attn_paged_decode minus workspace / workspace_bytes; the call
+ * allocates nothing.
+ *
+ * The split partials live in the library's own device array of
+ * ATTN_DECODE_SCRATCH_BYTES, one per GPU, which stays allocated from the first
+ * use until the process ends. Head dims other than 128 plan no more KV splits
+ * than fit there (at most 64 per sequence, at least 1). A call whose partials
+ * still do not fit returns ATTN_ERR_WORKSPACE_TOO_SMALL before any HIP call:
+ * for head_dim 128 that is 4 * num_heads * 129 * (num_seqs + 1024 /
+ * (num_kv_heads * ceil(num_heads / num_kv_heads / 16))) bytes plus two int32
+ * arrays of num_seqs + 1 above the limit (about 1900 sequences at 32/8 heads);
+ * for other head dims one split of num_seqs * num_heads * (head_dim + 1) * 4
+ * bytes above it. Nothing in the array needs clearing: every call writes each
+ * partial before it reads it.
+ * Every call on one GPU shares that GPU's array and leaves its partials there,
+ * so calls that overlap on one GPU (other streams, other host threads) race:
+ * issue them in order on one stream. The first call on each device looks the
+ * array's device address up in the HIP runtime (no allocation) and caches it;
+ * a failed lookup returns ATTN_ERR_LAUNCH. For head_dim 128 the result equals
+ * attn_paged_decode's bit for bit; for other head dims it can differ in the
+ * last bits where the split plan is capped.
+ */
+attn_status_t attn_paged_decode_scratch(const void* q, const void* kv_cache,
+                                        const int32_t* block_tables, const int32_t* context_lens,
+                                        int32_t num_seqs, int32_t num_blocks, int32_t max_blocks_per_seq,
+                                        int32_t max_context_len, int32_t num_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, float softmax_scale,
+                                        void* out, float* lse, void* stream);
 
 /*
  * Workspace bytes attn_padded_fwd needs (two int32 arrays of batch + 1).

@@ -28,6 +28,7 @@ __all__ = [
     "attn_paged_decode_workspace_size",
     "attn_paged_decode",
     "attn_paged_decode_sliding_window",
+    "attn_paged_decode_scratch",
     "attn_padded_fwd_workspace_size",
     "attn_padded_fwd",
     "attn_masked_fwd_workspace_size",
@@ -71,6 +72,8 @@ _SIGS = {
                                          _p, _p, _sz, _p]),
     "attn_paged_decode_sliding_window": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                                         _i32, _i32, _f32, _p, _p, _p, _sz, _p]),
+    "attn_paged_decode_scratch": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                 _f32, _p, _p, _p]),
     "attn_padded_fwd_workspace_size": (ctypes.c_int, [_i32, ctypes.POINTER(_sz)]),
     "attn_padded_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _p, _p, _p,
                                        _sz, _p]),
@@ -250,6 +253,36 @@ def attn_paged_decode(q, kv_cache, block_tables, context_lens, max_context_len: 
         _check("attn_paged_decode", lib.attn_paged_decode(*head, *tail))
     else:
         _check("attn_paged_decode_sliding_window", lib.attn_paged_decode_sliding_window(*head, int(window), *tail))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def attn_paged_decode_scratch(q, kv_cache, block_tables, context_lens, max_context_len: int, softmax_scale: float,
+                              out=None, lse=None, return_lse: bool = False, stream=None):
+    """attn_paged_decode without a workspace: the split partials go to the
+    library's fixed per-GPU device array (ATTN_DECODE_SCRATCH_BYTES); nothing is
+    allocated by the library. Calls that overlap on one GPU race."""
+    dev = q.device
+    nseq, hq, d = q.shape
+    two, nblocks, bs, hkv, dk = kv_cache.shape
+    if two != 2 or dk != d:
+        raise ValueError("kv_cache must be [2, num_blocks, block_size, num_kv_heads, head_dim]")
+    mbps = block_tables.shape[1] if block_tables.dim() == 2 else 0
+    _shape(block_tables, "block_tables", (nseq, mbps))
+    _shape(context_lens, "context_lens", (nseq,))
+    if out is None:
+        out = torch.empty_like(q)
+    _shape(out, "out", q.shape)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, nseq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _shape(lse, "lse", (hq, nseq))
+    st = load_library().attn_paged_decode_scratch(
+        _dev(q, "q", torch.bfloat16), _dev(kv_cache, "kv_cache", torch.bfloat16, dev),
+        _dev(block_tables, "block_tables", torch.int32, dev), _dev(context_lens, "context_lens", torch.int32, dev),
+        nseq, nblocks, mbps, int(max_context_len), hq, hkv, d, bs, float(softmax_scale),
+        _dev(out, "out", torch.bfloat16, dev), _dev(lse, "lse", torch.float32, dev) if lse is not None else None,
+        _stream_ptr(q, stream))
+    _check("attn_paged_decode_scratch", st)
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -96,7 +96,7 @@ attn_status_t paged_decode_impl(const void* q, const void* kv_cache, const int32
                                 int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_heads,
                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t window,
                                 float softmax_scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+                                void* stream, bool use_scratch = false) {
   if (num_seqs < 0 || num_blocks < 0 || max_blocks_per_seq < 0 || max_context_len < 0) return ATTN_ERR_INVALID_ARG;
   if (num_heads <= 0 || num_kv_heads <= 0) return ATTN_ERR_INVALID_ARG;
   if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
@@ -111,6 +111,18 @@ attn_status_t paged_decode_impl(const void* q, const void* kv_cache, const int32
   }
   if ((long long)num_blocks * block_size * num_kv_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
   if ((long long)num_seqs * max_context_len >= (1LL << 30)) return ATTN_ERR_UNSUPPORTED;  // int32 token prefix
+  if (use_scratch) {
+    // the library's fixed scratch: plan no more partials than it holds, refuse
+    // what still does not fit, then resolve its address on this device
+    const attn::DecodePlan plan = attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                          max_context_len, attn::kDecodeScratchBytes);
+    if (plan.workspace_bytes > attn::kDecodeScratchBytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+    void* ws = nullptr;
+    if (attn::decode_scratch_address(&ws) != hipSuccess) return ATTN_ERR_LAUNCH;
+    attn::DecodeArgs a{q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
+                       max_context_len, num_heads, num_kv_heads, head_dim, block_size, softmax_scale, out, lse, ws};
+    return from_hip(attn::launch_paged_decode(a, plan, (hipStream_t)stream));
+  }
   const attn::DecodePlan need = attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len);
   if (workspace_bytes < need.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
   if (need.workspace_bytes > 0 && workspace == nullptr) return ATTN_ERR_INVALID_ARG;
@@ -141,6 +153,16 @@ attn_status_t attn_paged_decode(const void* q, const void* kv_cache, const int32
   return paged_decode_impl(q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
                            max_context_len, num_heads, num_kv_heads, head_dim, block_size, -1, softmax_scale, out,
                            lse, workspace, workspace_bytes, stream);
+}
+
+attn_status_t attn_paged_decode_scratch(const void* q, const void* kv_cache, const int32_t* block_tables,
+                                        const int32_t* context_lens, int32_t num_seqs, int32_t num_blocks,
+                                        int32_t max_blocks_per_seq, int32_t max_context_len, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        float softmax_scale, void* out, float* lse, void* stream) {
+  return paged_decode_impl(q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
+                           max_context_len, num_heads, num_kv_heads, head_dim, block_size, -1, softmax_scale, out,
+                           lse, nullptr, 0, stream, true);
 }
 
 attn_status_t attn_paged_decode_sliding_window(const void* q, const void* kv_cache, const int32_t* block_tables,

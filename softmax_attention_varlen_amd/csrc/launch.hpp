@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/attn_mi355x.h"
+
 namespace attn {
 
 struct VarlenArgs {
@@ -69,7 +71,11 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 
-DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len);
+// max_partial_bytes (head dims other than 128): plan no more splits than fit
+// their fp32 partials in that many bytes (at least one split per sequence, so
+// workspace_bytes can still exceed it).
+DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
+                             size_t max_partial_bytes = SIZE_MAX);
 // The plan a sliding-window call runs (window >= 0 and < max_context_len;
 // otherwise the full plan): sized for the keys a sequence streams, with never
 // more splits, partial bytes or workspace than plan_paged_decode's for the
@@ -98,6 +104,13 @@ struct DecodeArgs {
 };
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+// The library's own decode scratch (decode_scratch.hip): a fixed device array
+// of kDecodeScratchBytes per GPU, held until the process ends, for the
+// allocation-free decode entry point. Its device address on the current
+// device is looked up once per device and cached.
+constexpr size_t kDecodeScratchBytes = ATTN_DECODE_SCRATCH_BYTES;
+hipError_t decode_scratch_address(void** ptr);
 
 // head_dim 128: balanced streaming decode (paged_decode_stream.hip). The
 // token stream of all sequences is cut into n_seg equal segments per kv head

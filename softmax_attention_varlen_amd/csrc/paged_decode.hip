@@ -330,7 +330,8 @@ __global__ __launch_bounds__(256) void paged_decode_combine_kernel(
   if (lse != nullptr && lane == 0) lse[(long)h * num_seqs + seq] = lse_all;
 }
 
-DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len) {
+DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
+                             size_t max_partial_bytes) {
   DecodePlan p{};
   const int group = num_heads / num_kv_heads;
   p.q_chunks = (group + 15) / 16;
@@ -338,6 +339,13 @@ DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int 
   long want = pairs > 0 ? (kDecodeTargetItems + pairs - 1) / pairs : 1;
   if (want < 1) want = 1;
   if (want > 64) want = 64;
+  // fewer splits when their partials (O and LSE of every sequence and head)
+  // must fit a fixed buffer; one split per sequence at the least
+  const size_t per_split = (size_t)num_seqs * num_heads * (head_dim + 1) * sizeof(float);
+  if (head_dim != 128 && per_split > 0 && (size_t)want * per_split > max_partial_bytes) {
+    const size_t cap = max_partial_bytes / per_split;
+    want = cap > 0 ? (long)cap : 1;
+  }
   const int ctx = max_context_len > 0 ? max_context_len : 1;
   long split = (ctx + want - 1) / want;
   split = ((split + kDecodeBlock - 1) / kDecodeBlock) * kDecodeBlock;

@@ -322,3 +322,29 @@ def test_h3_gather_block_map_validation():
     assert call(ws=None) == INVALID
     assert call(batch=0) == OK  # no-op
     assert call(segments=None, nseg=0, shape=(0, 0, 0)) == OK  # no tiles: no-op
+
+
+def _decode_scratch(**kw):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, ctx=FAKE, nseq=4, nblocks=10, mbps=4, maxctx=500, hq=8, hkv=2, d=128,
+             bs=128, scale=0.1, out=FAKE, lse=None)
+    a.update(kw)
+    return lib().attn_paged_decode_scratch(a["q"], a["kv"], a["bt"], a["ctx"], a["nseq"], a["nblocks"], a["mbps"],
+                                           a["maxctx"], a["hq"], a["hkv"], a["d"], a["bs"], a["scale"], a["out"],
+                                           a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(bs=64), UNSUPPORTED), (dict(d=100), UNSUPPORTED), (dict(hq=6, hkv=4), UNSUPPORTED),
+    (dict(maxctx=513), INVALID), (dict(nseq=-1), INVALID), (dict(q=None), INVALID), (dict(out=None), INVALID),
+    (dict(scale=0.0), INVALID),
+    # partials that do not fit the 32 MiB array: (128 + 4096) * 32 * 129 * 4 B at head_dim 128, and one split
+    # of 4096 * 32 * 65 * 4 B at head_dim 64
+    (dict(nseq=4096, hq=32, hkv=8, d=128), WS_SMALL), (dict(nseq=4096, hq=32, hkv=8, d=64), WS_SMALL),
+])
+def test_decode_scratch_validation(kw, code):
+    # every case is refused before the call looks up its device array
+    assert _decode_scratch(**kw) == code
+
+
+def test_decode_scratch_empty_is_noop():
+    assert _decode_scratch(nseq=0, q=None, out=None) == OK
