@@ -46,6 +46,7 @@ _PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "key_row
 _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
 _SPARSE_SRC = ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"]
 TRAFFIC = {
+    "tiny": {"kernel": "varlen_fwd_kernel<64,false,false>"},
     "dense": {"kernel": "prefill_d128_kernel<false,false,4,4,true,true>", "fetch_kib": 73853.1, "write_kib": 49952.6,
               "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
     "causal": {"kernel": "prefill_d128_kernel<true,false,4,4,true,true>", "fetch_kib": 111923.0, "write_kib": 142491.4,
@@ -204,8 +205,22 @@ def sparse_flops(bmap: np.ndarray, sizes: np.ndarray, head_dim: int) -> float:
 CLOCK_WARMUP_MS = 200.0  # set from --clock-warmup-ms
 
 
-def time_steps(step, steps: int, warmup: int) -> float:
-    """Average milliseconds per step over `steps` timed steps (HIP events).
+class StepTime:
+    """Milliseconds per step: the mean over the timed window and the median and
+    minimum of the individual steps (one HIP event between consecutive steps)."""
+
+    def __init__(self, per_step, mean):
+        self.mean = mean
+        self.median = float(np.median(per_step))
+        self.min = float(np.min(per_step))
+
+    def stats(self):
+        return {"ms_median": round(self.median, 5), "ms_min": round(self.min, 5)}
+
+
+def time_steps(step, steps: int, warmup: int) -> StepTime:
+    """Milliseconds per step over `steps` timed steps (HIP events on the stream
+    the kernels run on).
 
     Before the `warmup` untimed steps, the step is repeated for CLOCK_WARMUP_MS
     of wall time: under sustained load the GPU's clocks ramp for tens of
@@ -221,14 +236,14 @@ def time_steps(step, steps: int, warmup: int) -> float:
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
         step()
-    end.record(stream)
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return StepTime(per_step, ev[0].elapsed_time(ev[-1]) / steps)
 
 
 def bench_varlen(case, steps, warmup, with_lse=True):
@@ -327,7 +342,7 @@ def bench_kv_write(case, steps, warmup):
                             for b in range(case.batch)
                             for t in [np.arange(case.context_lens[b] - lq[b], case.context_lens[b])]])
     sl = torch.from_numpy(slots.astype(np.int32)).to(dev)
-    ms = time_steps(lambda: sav.attn_paged_kv_write(k_new, v_new, sl, kv), steps, warmup)
+    ms = time_steps(lambda: sav.attn_paged_kv_write(k_new, v_new, sl, kv), steps, warmup).mean
     del kv
     # bf16 K and V rows read once and written once, plus the int32 slot of each token
     return ms, 2 * 2 * 2.0 * n * case.num_kv_heads * case.head_dim + 4 * n
@@ -352,7 +367,7 @@ def bench_h3(case, steps, warmup):
     ms = time_steps(step, steps, warmup)
     flops = sparse_flops(bmap.cpu().numpy(), sizes.cpu().numpy(), case.head_dim)
     prep_ms = time_steps(lambda: sav.vsa_h3_prepare(q, k, v, segs, case.video_shape, case.topk, case.scale), steps,
-                         warmup)
+                         warmup).mean
     return ms, flops, prep_ms
 
 
@@ -374,7 +389,7 @@ def bench_sparse(case, steps, warmup):
     ms = time_steps(step, steps, warmup)
     flops = sparse_flops(bmap.cpu().numpy(), sizes.cpu().numpy(), case.head_dim)
     prep_ms = time_steps(lambda: sav.vsa_prepare(q, k, v, case.video_shape, case.tile_shape, case.topk, case.scale),
-                         steps, warmup)
+                         steps, warmup).mean
     # the gate branch on the same tiles, with a synthetic gate (a trained one
     # comes from a checkpoint's projection)
     gate = workloads.randn_bf16(tuple(qt.shape), 1000 * case.seed + 6).to(dev)
@@ -382,8 +397,10 @@ def bench_sparse(case, steps, warmup):
                                                              sizes.numel(), case.head_dim), dtype=torch.uint8,
                       device=dev)
     comp_ms = time_steps(lambda: sav.attn_vsa_compressed_add(qt, kt, vt, sizes, gate, case.scale, out, workspace=cws),
-                         steps, warmup)
-    return ms, flops, prep_ms, comp_ms
+                         steps, warmup).mean
+    host = {"q": qt.cpu(), "k": kt.cpu(), "v": vt.cpu(), "block_map": bmap.cpu().numpy(),
+            "tile_sizes": sizes.cpu().numpy()}
+    return ms, flops, prep_ms, comp_ms, host
 
 
 def bench_head_dims(steps, warmup):
@@ -401,7 +418,7 @@ def bench_head_dims(steps, warmup):
         out = torch.empty_like(q)
         lse = torch.empty((h, n), dtype=torch.float32, device=dev)
         ms = time_steps(lambda: sav.attn_varlen_fwd(q, k, v, cu, cu, 4096, 4096, d ** -0.5, False, out=out, lse=lse),
-                        steps, warmup)
+                        steps, warmup).mean
         flops = 4.0 * 2 * h * d * 4096 * 4096
         rows.append({"workload": f"dense-b2-s4096-h24-d{d}", "value": round(flops / (ms * 1e-3) / 1e12, 2),
                      "unit": "TFLOP/s", "ms": round(ms, 4)})
@@ -423,7 +440,7 @@ def bench_head_dims(steps, warmup):
         ws = torch.empty(max(sav.attn_paged_decode_workspace_size(len(ctx), 32, 8, d, int(max(ctx))), 1),
                          dtype=torch.uint8, device=dev)
         ms = time_steps(lambda: sav.attn_paged_decode(q, cache, bt, cl, int(max(ctx)), d ** -0.5, out=out,
-                                                      workspace=ws), steps, warmup)
+                                                      workspace=ws), steps, warmup).mean
         nbytes = float(sum(int(c) for c in ctx)) * 8 * d * 2 * 2
         rows.append({"workload": f"paged-decode-64seq-ctx1k-32k-h32kv8-d{d}",
                      "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms": round(ms, 4)})
@@ -433,32 +450,109 @@ def bench_head_dims(steps, warmup):
 
 
 # ----------------------------------------------------------------------------
-# CPU baseline: the fp64 oracle on a bounded sample of the headline workload
+# CPU baseline: the fp64 oracle timed on a bounded sample of each workload
 # ----------------------------------------------------------------------------
 
-def cpu_baseline(case, budget_s=10.0):
-    import oracle  # test infrastructure: used only for this reported baseline
+def _oracle_threads():
     from threadpoolctl import threadpool_info
 
-    cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    rows_per_doc = 128
-    lq = np.diff(case.cu_seqlens_q)
+    return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+
+
+def _growing_sample(run, start, limit, budget_s):
+    """Double the sample size n (from start, at most limit) until run(n) takes
+    budget_s; returns (n, seconds of the last run)."""
+    n = start
     while True:
-        rows = np.concatenate([case.cu_seqlens_q[b] + np.arange(min(rows_per_doc, lq[b]))
-                               for b in range(case.batch)])
         t0 = time.perf_counter()
+        run(n)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s or n >= limit:
+            return n, dt
+        n = min(2 * n, limit)
+
+
+def cpu_baseline_varlen(case, budget_s):
+    """The first n query rows of every document (all heads), n doubling until the
+    oracle takes budget_s; rate in the GPU line's unit (algorithmic flops of the
+    sampled rows: under the causal mask only their visible keys count)."""
+    import oracle  # test infrastructure: used only for this reported baseline
+
+    lq = np.diff(case.cu_seqlens_q).astype(np.int64)
+    lk = np.diff(case.cu_seqlens_k).astype(np.int64)
+
+    def local_rows(n, b):
+        # n rows spread evenly over the document, so that under the causal
+        # mask the sample sees the workload's mix of short and long rows
+        return np.unique(np.linspace(0, lq[b] - 1, min(n, lq[b])).round().astype(np.int64)) if lq[b] else \
+            np.zeros(0, dtype=np.int64)
+
+    def run(n):
+        rows = np.concatenate([case.cu_seqlens_q[b] + local_rows(n, b) for b in range(case.batch)])
         oracle.varlen_attention(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k, case.scale,
                                 case.causal, rows=rows)
-        dt = time.perf_counter() - t0
-        if dt >= budget_s or rows_per_doc >= int(lq.max()):
-            break
-        rows_per_doc *= 2
-    lk = np.diff(case.cu_seqlens_k)
-    flops = 4.0 * case.head_dim * case.num_heads * float(sum(min(rows_per_doc, lq[b]) * lk[b]
-                                                             for b in range(case.batch)))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {rows_per_doc} query rows of each of the {case.batch} documents, all {case.num_heads} "
-                      f"heads, fp64 numpy ({dt:.1f} s)",
+
+    n, dt = _growing_sample(run, 64, int(lq.max()), budget_s)
+    whole = n >= int(lq.max())
+    reps = 1
+    if whole and dt < 0.25 * budget_s:  # a small workload: repeat it for a measurable time
+        reps = max(1, int(0.25 * budget_s / max(dt, 1e-3)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            run(n)
+        dt = (time.perf_counter() - t0) / reps
+    pairs = 0
+    for b in range(case.batch):
+        i = local_rows(n, b)
+        pairs += int(np.clip(i + (lk[b] - lq[b]) + 1, 0, lk[b]).sum()) if case.causal else int(i.size * lk[b])
+    flops = 4.0 * case.head_dim * case.num_heads * pairs
+    sample = ("the whole workload" + (f" (mean of {reps} runs)" if reps > 1 else "") if whole
+              else f"{n} query rows spread over each of the {case.batch} documents") + \
+        f", all {case.num_heads} heads, fp64 numpy ({dt:.2f} s)"
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": sample, "seconds": round(dt, 2)}
+
+
+def cpu_baseline_paged(case, budget_s):
+    """Whole sequences, one at a time in order, until the oracle takes budget_s;
+    rate in GB/s of the same algorithmic bytes the GPU line counts."""
+    import oracle  # test infrastructure: used only for this reported baseline
+
+    t0 = time.perf_counter()
+    done = 0
+    while done < case.num_seqs and time.perf_counter() - t0 < budget_s:
+        oracle.paged_decode_attention(case.q, case.kv_cache, case.block_tables, case.context_lens, case.scale,
+                                      seqs=[done])
+        done += 1
+    dt = time.perf_counter() - t0
+    ctx = case.context_lens[:done].astype(np.int64)
+    nbytes = float(ctx.sum()) * case.num_kv_heads * case.head_dim * 2 * 2 + \
+        2.0 * done * case.num_heads * case.head_dim * 2 + 4.0 * done * (case.block_tables.shape[1] + 1)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"the first {done} of {case.num_seqs} sequences ({int(ctx.sum())} context tokens), one at a "
+                      f"time, all {case.num_heads} heads, fp64 numpy ({dt:.1f} s)",
+            "seconds": round(dt, 2)}
+
+
+def cpu_baseline_sparse(case, host, budget_s):
+    """The first n query tiles of every head (the GPU's own tile-order inputs
+    and map), n doubling until the oracle takes budget_s; rate in TFLOP/s of
+    the kept tile pairs of those tiles."""
+    import oracle  # test infrastructure: used only for this reported baseline
+
+    sizes, bmap = host["tile_sizes"], host["block_map"]
+    nt = sizes.size
+
+    def run(n):
+        oracle.block_sparse_attention(host["q"], host["k"], host["v"], bmap, sizes, case.scale,
+                                      q_tiles=list(range(n)))
+
+    n, dt = _growing_sample(run, 4, nt, budget_s)
+    sz = sizes.astype(np.float64)
+    flops = 4.0 * case.head_dim * float((bmap[:, :, :n].astype(np.float64) * np.outer(sz[:n], sz)[None, None]).sum())
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"the first {n} of {nt} query tiles of all {case.num_heads} heads with their kept key tiles, "
+                      f"fp64 numpy ({dt:.1f} s)",
             "seconds": round(dt, 2)}
 
 
@@ -468,7 +562,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--only", choices=["dense", "causal", "paged", "sparse", "h3", "paged_prefill", "spec", "swa",
+    ap.add_argument("--only", choices=["dense", "tiny", "causal", "paged", "sparse", "h3", "paged_prefill", "spec", "swa",
                                        "masked", "padded", "copy", "head_dims"],
                     default=None,
                     help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
@@ -478,6 +572,8 @@ def main():
                     help="repeat each workload's step for this long before its warm-up steps (0: off)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=4.0,
+                    help="seconds of fp64 oracle work per workload for the cpu baselines (workloads 1-5)")
     args = ap.parse_args()
     CLOCK_WARMUP_MS = max(0.0, args.clock_warmup_ms)
     if args.gpus != 1:
@@ -496,7 +592,7 @@ def main():
         n = 1 << 30
         src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
-        ms = time_steps(lambda: dst.copy_(src), args.steps, args.warmup)
+        ms = time_steps(lambda: dst.copy_(src), args.steps, args.warmup).mean
         print(json.dumps({"metric": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
                           "ms": round(ms, 5), "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
         return
@@ -510,95 +606,108 @@ def main():
 
     secondary = []
     head = None
+    want = lambda name: args.only == name or (args.only is None and not args.no_secondary)  # noqa: E731
+    cpu = not args.no_cpu_baseline
+    budget = args.cpu_budget_s
+
+    def line_for(name, t, work, bound, extra=None):
+        """One secondary line: throughput over the mean step, median and min step."""
+        rate = work / (t.mean * 1e-3) / (1e12 if bound == "mfma" else 1e9)
+        unit = "TFLOP/s" if bound == "mfma" else "GB/s"
+        rec = {"workload": name, "value": round(rate, 2), "unit": unit, "ms": round(t.mean, 5), **t.stats(),
+               "roofline": roofline(KIND[name], bound, rate, work)}
+        rec.update(extra or {})
+        secondary.append(rec)
+        log(f"{name}: {t.mean * 1e3:.1f} us/step (median {t.median * 1e3:.1f}, min {t.min * 1e3:.1f}), "
+            f"{rate:.1f} {unit}")
+        return rec
+
+    KIND = {}
     if args.only in (None, "dense"):
         case = workloads.config2()
-        ms, flops = bench_varlen(case, args.steps, args.warmup)
-        tf = flops / (ms * 1e-3) / 1e12
-        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s")
-        head = (case, ms, flops, tf)
-    if args.only in (None, "causal") and not (args.only is None and args.no_secondary):
+        t, flops = bench_varlen(case, args.steps, args.warmup)
+        tf = flops / (t.mean * 1e-3) / 1e12
+        log(f"{case.name}: {t.mean * 1e3:.1f} us/step (median {t.median * 1e3:.1f}, min {t.min * 1e3:.1f}), "
+            f"{tf:.1f} TFLOP/s")
+        head = (case, t, flops, tf)
+    if want("tiny"):
+        case = workloads.config1()
+        KIND[case.name] = "tiny"
+        t, flops = bench_varlen(case, args.steps, args.warmup)
+        rec = line_for(case.name, t, flops, "mfma", {"note": "latency-bound: 35 MFLOP in one launch of 8 workgroups"})
+        if cpu:
+            rec["cpu_baseline"] = cpu_baseline_varlen(case, budget)
+    if want("causal"):
         case = workloads.config3()
-        ms, flops = bench_varlen(case, args.steps, args.warmup)
-        tf = flops / (ms * 1e-3) / 1e12
-        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s")
-        secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
-                          "roofline": roofline("causal", "mfma", tf, flops)})
+        KIND[case.name] = "causal"
+        t, flops = bench_varlen(case, args.steps, args.warmup)
+        rec = line_for(case.name, t, flops, "mfma")
+        if cpu:
+            rec["cpu_baseline"] = cpu_baseline_varlen(case, budget)
     decode_case = None  # workload 4's cache (10 GB of bf16) serves the windowed decode line too
-    if args.only in (None, "paged") and not (args.only is None and args.no_secondary):
+    if want("paged"):
         decode_case = workloads.config4()
-        ms, nbytes = bench_paged(decode_case, args.steps, args.warmup)
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        log(f"{decode_case.name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
-        secondary.append({"workload": decode_case.name, "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
-                          "roofline": roofline("paged", "hbm", gbs, nbytes)})
+        KIND[decode_case.name] = "paged"
+        t, nbytes = bench_paged(decode_case, args.steps, args.warmup)
+        rec = line_for(decode_case.name, t, nbytes, "hbm")
+        if cpu:
+            rec["cpu_baseline"] = cpu_baseline_paged(decode_case, budget)
         torch.cuda.empty_cache()
-    if args.only in (None, "sparse") and not (args.only is None and args.no_secondary):
+    if want("sparse"):
         case = workloads.config5()
-        ms, flops, prep_ms, comp_ms = bench_sparse(case, args.steps, args.warmup)
-        tf = flops / (ms * 1e-3) / 1e12
-        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s (map build {prep_ms * 1e3:.0f} us, "
-            f"compressed branch {comp_ms * 1e3:.0f} us)")
-        secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
-                          "roofline": roofline("sparse", "mfma", tf, flops),
-                          "tile_prep_and_map_ms": round(prep_ms, 4), "compressed_branch_ms": round(comp_ms, 4)})
-
-    if args.only in (None, "h3") and not (args.only is None and args.no_secondary):
+        KIND[case.name] = "sparse"
+        t, flops, prep_ms, comp_ms, host = bench_sparse(case, args.steps, args.warmup)
+        rec = line_for(case.name, t, flops, "mfma", {"tile_prep_and_map_ms": round(prep_ms, 4),
+                                                    "compressed_branch_ms": round(comp_ms, 4)})
+        log(f"  map build {prep_ms * 1e3:.0f} us, compressed branch {comp_ms * 1e3:.0f} us")
+        if cpu:
+            rec["cpu_baseline"] = cpu_baseline_sparse(case, host, budget)
+        del host
+    if want("h3"):
         case = workloads.config11()
-        ms, flops, prep_ms = bench_h3(case, args.steps, args.warmup)
-        tf = flops / (ms * 1e-3) / 1e12
-        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s (H3 map build {prep_ms * 1e3:.0f} us)")
-        secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
-                          "roofline": roofline("h3", "mfma", tf, flops), "tile_prep_and_map_ms": round(prep_ms, 4)})
-
-    if args.only in (None, "paged_prefill") and not (args.only is None and args.no_secondary):
+        KIND[case.name] = "h3"
+        t, flops, prep_ms = bench_h3(case, args.steps, args.warmup)
+        line_for(case.name, t, flops, "mfma", {"tile_prep_and_map_ms": round(prep_ms, 4)})
+        log(f"  H3 map build {prep_ms * 1e3:.0f} us")
+    if want("paged_prefill"):
         case = workloads.config6()
-        ms = bench_paged_prefill(case, args.steps, args.warmup)
-        flops = paged_prefill_flops(case)
-        tf = flops / (ms * 1e-3) / 1e12
+        KIND[case.name] = "paged_prefill"
+        t = bench_paged_prefill(case, args.steps, args.warmup)
         wms, wbytes = bench_kv_write(case, args.steps, args.warmup)
-        log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s (kv write {wms * 1e3:.1f} us)")
-        secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
-                          "roofline": roofline("paged_prefill", "mfma", tf, flops),
-                          "kv_write": {"ms": round(wms, 5), "GB/s": round(wbytes / (wms * 1e-3) / 1e9, 1),
-                                       "tokens": int(case.q.shape[0])}})
+        line_for(case.name, t, paged_prefill_flops(case), "mfma",
+                 {"kv_write": {"ms": round(wms, 5), "GB/s": round(wbytes / (wms * 1e-3) / 1e9, 1),
+                               "tokens": int(case.q.shape[0])}})
+        log(f"  kv write {wms * 1e3:.1f} us")
         del case
         torch.cuda.empty_cache()
-    if args.only in (None, "spec") and not (args.only is None and args.no_secondary):
+    if want("spec"):
         case = workloads.config7()
-        ms = bench_paged_prefill(case, args.steps, args.warmup)
-        nbytes = paged_prefill_bytes(case)
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        log(f"{case.name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
-        secondary.append({"workload": case.name, "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
-                          "roofline": roofline("spec", "hbm", gbs, nbytes)})
+        KIND[case.name] = "spec"
+        t = bench_paged_prefill(case, args.steps, args.warmup)
+        line_for(case.name, t, paged_prefill_bytes(case), "hbm")
         del case
         torch.cuda.empty_cache()
-
-    if args.only in (None, "swa") and not (args.only is None and args.no_secondary):
+    if want("swa"):
         case = workloads.config8(decode_case)  # the same cache, tables and queries as workload 4
-        ms, nbytes = bench_paged(case, args.steps, args.warmup, window=workloads.SLIDING_WINDOW)
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        log(f"{case.name}: {ms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
-        secondary.append({"workload": case.name, "value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
-                          "roofline": roofline("swa", "hbm", gbs, nbytes)})
+        KIND[case.name] = "swa"
+        t, nbytes = bench_paged(case, args.steps, args.warmup, window=workloads.SLIDING_WINDOW)
+        line_for(case.name, t, nbytes, "hbm")
         del case
     del decode_case
     torch.cuda.empty_cache()
     for name, cfg, masked in (("masked", workloads.config9, True), ("padded", workloads.config10, False)):
-        if args.only in (None, name) and not (args.only is None and args.no_secondary):
+        if want(name):
             case = cfg()
-            ms, flops = bench_padded(case, args.steps, args.warmup, masked)
-            tf = flops / (ms * 1e-3) / 1e12
-            log(f"{case.name}: {ms * 1e3:.1f} us/step, {tf:.1f} TFLOP/s")
-            secondary.append({"workload": case.name, "value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
-                              "roofline": roofline(name, "mfma", tf, flops)})
+            KIND[case.name] = name
+            t, flops = bench_padded(case, args.steps, args.warmup, masked)
+            line_for(case.name, t, flops, "mfma")
             del case
             torch.cuda.empty_cache()
 
     if head is None:  # a single secondary workload was asked for
         print(json.dumps({"metric": "attention throughput", "secondary": secondary}))
         return
-    case, ms, flops, tf = head
+    case, t, flops, tf = head
     line = {
         "metric": "attention TFLOP/s (prefill, sparse) and HBM GB/s (paged decode), 1 MI355X",
         "value": round(tf, 2),
@@ -606,7 +715,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
+        "ms_per_step": round(t.mean, 5),
+        **t.stats(),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -619,9 +729,9 @@ def main():
         "roofline": roofline("dense", "mfma", tf, flops),
         "secondary": secondary,
     }
-    if not args.no_cpu_baseline:
+    if cpu:
         log("timing the fp64 oracle on a sample (cpu baseline)")
-        line["cpu_baseline"] = cpu_baseline(case)
+        line["cpu_baseline"] = cpu_baseline_varlen(case, budget)
     print(json.dumps(line), flush=True)
 
 

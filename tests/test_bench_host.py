@@ -32,6 +32,10 @@ def test_traffic_records_are_well_formed():
     # bench line then carries "traffic": null until the counters are taken again)
     b = _bench()
     for name, rec in b.TRAFFIC.items():
+        assert rec["kernel"], name
+        if "fetch_kib" not in rec:  # no counters taken for this workload: traffic is null
+            assert b.traffic_bytes(name) is None
+            continue
         assert rec["fetch_kib"] > 0 and rec["write_kib"] > 0, name
         assert len(rec["sha256"]) == 16 and int(rec["sha256"], 16) >= 0, name
         for f in rec["sources"]:
