@@ -156,90 +156,6 @@ struct Softmax {
   float l;  // lane-partial sum of the unrounded probabilities
 };
 
-// One tile of 32*KB keys per wave: masking of `s` when some key is hidden from
-// some row of the wave (a wave-uniform branch; key k of the share is visible to
-// the lane's row when k < len_k and k <= lim), the row maximum, then 8*KB steps
-// that each issue one S^T MFMA of the next tile (K operand prefetched four
-// steps ahead; after the last tile the result is not used) next to two exp2
-// of this tile, so the transcendental/VALU work runs under the matrix unit; a
-// scheduling fence between steps keeps that order. Then O += V^T P^T. The
-// output accumulator is only rescaled when some row maximum grows by more than
-// 2^8 (in exp2 units); until then the stale maximum keeps every exp2 argument
-// <= 8, exact up to rounding.
-template <int KB>
-__device__ __forceinline__ void tile_step(f32x16 (&s)[KB], f32x16 (&sn)[KB], const char* nk, uint32_t vt,
-                                          const Lane& L, const bf16x8 (&q)[8], f32x16 (&o)[4], Softmax& st,
-                                          float c, bool mask, int key0, int len_k, int lim) {
-  constexpr int NSTEP = 8 * KB;
-  if (mask) {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + kb * 32 + 8 * (r >> 2) + 4 * L.g + (r & 3);
-        if (key >= len_k || key > lim) s[kb][r] = kNegInf;
-      }
-    }
-  }
-  // row maximum over the lane's 16*KB keys, 2*KB independent chains
-  float mx4[2 * KB];
-#pragma unroll
-  for (int t = 0; t < 2 * KB; ++t) mx4[t] = fmaxf(s[t >> 1][8 * (t & 1)], s[t >> 1][8 * (t & 1) + 1]);
-#pragma unroll
-  for (int i = 2; i < 8; ++i) {
-#pragma unroll
-    for (int t = 0; t < 2 * KB; ++t) mx4[t] = fmaxf(mx4[t], s[t >> 1][8 * (t & 1) + i]);
-  }
-  float mloc = fmaxf(mx4[0], mx4[1]);
-  if constexpr (KB == 2) mloc = fmaxf(mloc, fmaxf(mx4[2], mx4[3]));
-  const float mx = pair_max(mloc);
-  const float m_new = fmaxf(st.m, mx);
-  const bool need = (m_new - st.m) * c > kRescaleThreshold;  // true on the first finite maximum
-  const float alpha = need ? hw_exp2((st.m - m_new) * c) : 1.f;
-  const float m_ref = need ? m_new : st.m;
-  const float ms = (m_ref == kNegInf ? 0.f : m_ref) * c;
-
-  // step i: MFMA (db = i/KB, kb = i%KB) of the next tile, and elements 2i, 2i+1
-  // of this tile (P chunk t = i/4 collects 8 of them)
-  const char* kbase = nk + L.k_base;
-  bf16x8 kr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) kr[i] = ld_lds16(kbase, (i % KB) * kHalfBytes + (i / KB) * 32);
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sn[kb][r] = 0.f;
-  }
-  bf16x8 p[2 * KB];
-  f32x8 e;
-  float rs0 = 0.f, rs1 = 0.f;
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < NSTEP; ++i) {
-    const int db = i / KB, kb = i % KB;
-    sn[kb] = mfma32x32x16(kr[i & 3], q[db], sn[kb]);
-    if (i + 4 < NSTEP) kr[i & 3] = ld_lds16(kbase, ((i + 4) % KB) * kHalfBytes + ((i + 4) / KB) * 32);
-    const int t = i >> 2, u = 2 * (i & 3);
-    e[u] = hw_exp2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + u], c, -ms));
-    e[u + 1] = hw_exp2(__builtin_fmaf(s[t >> 1][8 * (t & 1) + u + 1], c, -ms));
-    rs0 += e[u];
-    rs1 += e[u + 1];
-    if ((i & 3) == 3) p[t] = to_bf16x8(e);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const float rs = rs0 + rs1;
-  st.l = st.l * alpha + rs;
-  st.m = m_ref;
-  // Rare rescale of O. The row sum takes part in the condition (it is never
-  // NaN for finite inputs) so that the exp2 above stay interleaved with the
-  // MFMAs instead of being sunk past the branch.
-  if (__builtin_amdgcn_ballot_w64(need || rs != rs) != 0ull) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) o[b] *= alpha;
-  }
-  pv<KB>(vt, L, p, o);
-}
-
 // V^T operand of PV MFMA (chunk c, d-block b) for the transposing reads of pv().
 __device__ __forceinline__ bf16x8 read_vt(const lds_bf16x4* base, int c, int b) {
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 32 * c + 8 * b));

@@ -2,12 +2,10 @@
 //
 // Work unit: one workgroup of NW waves owns NW*32 query rows of one document
 // and one query head; wave w owns rows [32w, 32w+32). K/V tiles of 64 keys
-// stream through an NS-stage LDS ring filled by direct-to-LDS loads (no VGPR
+// stream through a 4-stage LDS ring filled by direct-to-LDS loads (no VGPR
 // staging, no transpose on the way in), in the bank-conflict-free layout of
-// pipe_d128.hpp. The default pipelined loop (PP, 4 stages) runs the softmax of
-// tile j under the S^T MFMAs of tile j+1 and the PV MFMAs of tile j-1; the
-// plain loop (PP = false, 3 or 4 stages) interleaves the S^T MFMAs of tile
-// j+1 with the softmax of tile j and then runs the PV of tile j. One barrier
+// pipe_d128.hpp. The loop is software-pipelined: it runs the softmax of tile j
+// under the S^T MFMAs of tile j+1 and the PV MFMAs of tile j-1. One barrier
 // per tile guards the ring. SPLIT replaces the ring by separate two-stage K
 // and V rings (at step j, K of tile j+2 and V of tile j are in flight while K
 // of tile j+1 and V of tile j-1 are read), which fit two 4-wave workgroups
@@ -44,7 +42,7 @@ struct Ring {
 // block_tables, with context_lens[doc] (clamped to max_len_k) keys per
 // document; otherwise from contiguous rows delimited by cu_k. q_used / k_used
 // (nullable) cut each document to a valid prefix of its rows.
-template <bool CAUSAL, bool PAGED, int NW, int NS, bool PP, bool SPLIT = false>
+template <bool CAUSAL, bool PAGED, int NW, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int total_q, int total_k,
@@ -54,11 +52,10 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
     const int32_t* __restrict__ k_used) {
   using R = Ring<NW>;
   constexpr int BM = 32 * NW;
-  static_assert(NS == 3 || NS == 4, "the load-count waits below cover 3- and 4-stage rings");
-  static_assert(!PP || NS == 4, "the pipelined loop keeps tile j-1's V while tile j+2 loads: 4 stages");
-  static_assert(!SPLIT || PP, "split rings serve the pipelined loop");
-  // SPLIT: separate two-stage K and V rings (K stages 0, 1, then V stages 0, 1)
-  __shared__ __attribute__((aligned(1024))) char smem[SPLIT ? 4 * kTileBytes : NS * kStageBytes];
+  // the pipelined loop keeps tile j-1's V while tile j+2 loads: 4 stages of K
+  // and V; SPLIT: separate two-stage K and V rings (K stages 0, 1, then V
+  // stages 0, 1)
+  __shared__ __attribute__((aligned(1024))) char smem[SPLIT ? 4 * kTileBytes : 4 * kStageBytes];
 
   // XCD-aware order: the hardware deals workgroups round-robin over 8 XCDs, so
   // XCD x receives logical items [x*per_xcd, (x+1)*per_xcd), laid out
@@ -135,8 +132,8 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
 #pragma unroll
     for (int b = 0; b < 8; ++b) qr[b] = as_bf16x8(ld_global16(qp + b * 16));
   }
-  // prologue: the first NS-1 tiles in flight (the pipelined loop: 2)
-  constexpr int PRE = PP ? 2 : NS - 1;
+  // prologue: the first two tiles in flight
+  constexpr int PRE = 2;
 #pragma unroll
   for (int s = 0; s < PRE; ++s) {
     if (SPLIT) {
@@ -167,8 +164,6 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
       } else {
         wait_loads_barrier<0>();
       }
-    } else if (later >= 2) {
-      wait_loads_barrier<2 * R::LOADS>();
     } else if (later == 1) {
       wait_loads_barrier<R::LOADS>();
     } else {
@@ -178,7 +173,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
   }
   settle_q(qr);
 
-  if constexpr (PP) {
+  {
     // Pipelined loop: step j runs the softmax of tile j under the S^T MFMAs of
     // tile j+1 and the PV MFMAs of tile j-1. Tile j+2 is issued at step j into
     // the stage of tile j-2, whose PV every wave finished in step j-1 (the
@@ -250,48 +245,10 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
     if constexpr (SPLIT) __builtin_amdgcn_s_setprio(0);
     store_rows(o, st, L, c, row < len_q, out + ((long)(q0 + row_c) * hq + h) * kD,
                lse != nullptr ? lse + (long)h * total_q + q0 + row_c : nullptr);
-    return;
   }
-
-  // one iteration of the ring: refill, then this wave's compute for tile j
-  auto iteration = [&](int j, f32x16 (&s)[2], f32x16 (&sn)[2]) {
-    if (j + 1 < ntiles) {
-      if (NS >= 4 && j + 2 < ntiles) {
-        wait_loads_barrier<(NS - 3) * R::LOADS>();
-      } else {
-        wait_loads_barrier<0>();
-      }
-      const int jn = j + NS - 1;
-      if (jn < ntiles) {
-        const long off = rows.row(jn * kBN);
-        R::issue(kb0 + off, vb0 + off, stride_bytes, len_k - jn * kBN, ring + (jn % NS) * kStageBytes, w, lane);
-      }
-    }
-    if (j >= ntiles_w) return;
-    // the next tile's K (after this wave's last tile: any resident stage; the
-    // result is not used)
-    const char* nk = smem + ((j + 1 < ntiles ? j + 1 : j) % NS) * kStageBytes;
-    const uint32_t vt = ring + (j % NS) * kStageBytes + kTileBytes;
-    const int key0 = j * kBN;
-    const bool mask = !(j < nomask_w && key0 + kBN <= len_k);
-    tile_step<2>(s, sn, nk, vt, L, qr, o, st, c, mask, key0, len_k, CAUSAL ? row + diag : 0x7fffffff);
-  };
-  for (int j = 0; j < ntiles; j += 2) {
-    iteration(j, sa, sb);
-    if (j + 1 < ntiles) iteration(j + 1, sb, sa);
-  }
-
-  store_rows(o, st, L, c, row < len_q, out + ((long)(q0 + row_c) * hq + h) * kD,
-             lse != nullptr ? lse + (long)h * total_q + q0 + row_c : nullptr);
 }
 
 }  // namespace
-
-constexpr int kPrefillStages = 3;
-#ifndef PREFILL_PIPELINED
-#define PREFILL_PIPELINED 1
-#endif
-constexpr bool kPrefillPipelined = PREFILL_PIPELINED;
 
 bool prefill_d128_supported(const VarlenArgs& a) { return a.head_dim == 128; }
 
@@ -303,15 +260,14 @@ bool prefill_d128_supported(const VarlenArgs& a) { return a.head_dim == 128; }
 // LDS for twice as many rows.
 template <bool CAUSAL, bool PAGED>
 static void launch_prefill_d128_t(const VarlenArgs& a, hipStream_t stream) {
-  constexpr bool SPLIT = kPrefillPipelined && !PAGED;
+  constexpr bool SPLIT = !PAGED;
   constexpr int NW = SPLIT ? 4 : 8;
-  constexpr int NS = kPrefillPipelined ? 4 : kPrefillStages;
   constexpr int BM = 32 * NW;
   const int tiles = (a.max_seqlen_q + BM - 1) / BM;
   const long n_items = (long)tiles * a.batch * a.num_heads;
   const long per_xcd = (n_items + 7) / 8;
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((prefill_d128_kernel<CAUSAL, PAGED, NW, NS, kPrefillPipelined, SPLIT>),
+  hipLaunchKernelGGL((prefill_d128_kernel<CAUSAL, PAGED, NW, SPLIT>),
                      dim3((unsigned)(per_xcd * 8)), dim3(64 * NW), 0, stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch, a.total_q, a.total_k, tiles,
                      a.num_heads, a.num_kv_heads, (int)n_items, (int)per_xcd, c, (uint16_t*)a.out, a.lse,
