@@ -41,7 +41,6 @@ from .tiles import (  # noqa: F401
     tile_partition_indices,
     variable_block_sizes,
     non_pad_index,
-    untile_index,
     tile_metadata,
     to_tile_order,
     from_tile_order,

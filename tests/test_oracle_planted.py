@@ -77,14 +77,28 @@ def test_paged_wrong_offset_is_caught(monkeypatch):
 
 
 def test_tile_order_mutant_is_caught(monkeypatch):
-    orig_boxes = T._boxes
+    orig_map = T._video_map
 
-    def boxes_w_slowest(shape, tile):
-        boxes = list(orig_boxes(shape, tile))
-        return reversed(boxes)
+    def boxes_reversed(shape, tile, block):
+        box, row, sizes = orig_map(shape, tile, block)
+        return sizes.size - 1 - box, row, sizes[::-1].copy()
 
-    monkeypatch.setattr(T, "_boxes", boxes_w_slowest)
+    monkeypatch.setattr(T, "_video_map", boxes_reversed)
     assert _fails(ts.test_geometry_hand_example)
+
+
+def test_unclipped_box_rows_mutant_is_caught(monkeypatch):
+    # rows numbered as if every box had its full (tt, th, tw) extent
+    def rows_unclipped(shape, tile, block):
+        box, _, sizes = orig_map(shape, tile, block)
+        t, h, w = np.meshgrid(*(np.arange(int(s)) for s in shape), indexing="ij")
+        tt, th, tw = tile
+        row = (t % tt) * th * tw + (h % th) * tw + (w % tw)
+        return box, row.reshape(-1).astype(np.int64), sizes
+
+    orig_map = T._video_map
+    monkeypatch.setattr(T, "_video_map", rows_unclipped)
+    assert _fails(lambda: ts.test_geometry_properties((5, 7, 9), (4, 4, 4)))
 
 
 def test_topk_smallest_mutant_is_caught(monkeypatch):

@@ -34,6 +34,9 @@ def test_geometry_properties(shape, tile):
     assert np.array_equal(np.sort(part), np.arange(n))  # a permutation
     assert sizes.sum() == n and np.all(sizes >= 1) and np.all(sizes <= 64)
     assert non_pad.size == n and np.all(np.diff(non_pad) > 0)
+    # each box's tokens fill its first sizes[c] rows, padding after them
+    assert np.array_equal(non_pad, oracle.non_pad_index(sizes, 64))
+    assert np.array_equal(np.sort(untile), non_pad)
     x = RNG.standard_normal((2, n, 3, 4))
     xt = oracle.to_tile_order(x, shape, tile)
     assert xt.shape == (2, sizes.size * 64, 3, 4)
