@@ -164,7 +164,8 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   const int hk = h / (hq / hkv);
   const long seq = (long)num_tiles * kBN;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // the same in every lane of a wave
   const int rh = w & 1, kh = w >> 1;
   const Lane L = make_lane(lane, 32 * kh);
   const int qsize = clampi(tile_sizes[a], 0, kBN);
@@ -196,19 +197,35 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   Softmax st{kNegInf, 0.f};
   f32x16 sa[1], sb[1];
 
-  auto issue_k = [&](const Entry& t, int stage) {
-    issue_tile<kSIPW>(kbatch + (long)t.tile * kBN * kv_stride, stride_bytes, t.size, ring + stage * kTileBytes,
-                      w * kSIPW, lane);
+  // This wave's share of a K or V tile: load blocks w*kSIPW .. +kSIPW-1. For a
+  // full tile (size 64: every key real, wave-uniform) each lane's byte offset
+  // within the tile is fixed, so it is computed once here and those loads take
+  // no per-tile vector arithmetic; a partial tile clamps its rows to the last
+  // real key.
+  uint32_t boff[kSIPW];
+#pragma unroll
+  for (int t = 0; t < kSIPW; ++t) {
+    boff[t] = (block_key((uint32_t)(w * kSIPW + t)) + 16u * (uint32_t)(lane >> 4)) * stride_bytes +
+              (uint32_t)(lane & 15) * 16u;
+  }
+  auto issue = [&](const uint16_t* plane, const Entry& t, uint32_t stage_lds) {
+    const uint16_t* tb = plane + (long)t.tile * kBN * kv_stride;
+    if (t.size >= kBN) {
+#pragma unroll
+      for (int i = 0; i < kSIPW; ++i) load_lds16(tb, boff[i], stage_lds + (w * kSIPW + i) * kBlockBytes);
+    } else {
+      issue_tile<kSIPW>(tb, stride_bytes, t.size, stage_lds, w * kSIPW, lane);
+    }
   };
-  auto issue_v = [&](const Entry& t, int stage) {
-    issue_tile<kSIPW>(vbatch + (long)t.tile * kBN * kv_stride, stride_bytes, t.size,
-                      ring + (2 + stage) * kTileBytes, w * kSIPW, lane);
-  };
+  auto issue_k = [&](const Entry& t, int stage) { issue(kbatch, t, ring + stage * kTileBytes); };
+  auto issue_v = [&](const Entry& t, int stage) { issue(vbatch, t, ring + (2 + stage) * kTileBytes); };
 
   // The kept-tile list goes to LDS first: a list word read from memory inside
-  // the loop would be a scalar load, and on this architecture every later wait
-  // for LDS data also waits for outstanding scalar loads. (The launcher only
-  // sends tile counts up to kListCap here.)
+  // the loop would need a wait for its load there, and that wait also holds
+  // for the ring loads issued earlier in the step (a vector load: vmcnt; a
+  // scalar one: lgkmcnt, which every LDS wait also drains). Staged in LDS, a
+  // refill waits only for LDS. (The launcher only sends tile counts up to
+  // kListCap here.)
   for (int i = tid; i < count; i += 64 * kSW) lst[i] = list[i];
   __syncthreads();
   // A 64-entry window of the list sits in one VGPR (lane i holds entry
