@@ -190,13 +190,17 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   // no LDS read is outstanding here (the step's barrier waited for them all);
   // saying so lets the compiler's first MFMA wait for its own K operand only
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt untouched
-  bf16x8 kr[2];  // K operand two S^T steps (four slots) ahead
+  // K and V operands are read PF MFMA steps of their kind (2*PF slots) ahead;
+  // 3 and 4 measured level with 2 on dense, causal and padded prefill (same
+  // box, three alternating rounds), so LDS latency does not hold the loop back
+  constexpr int PF = 2;
+  bf16x8 kr[PF];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) kr[i] = ld_lds16(kbase, (i % 2) * kHalfBytes + (i / 2) * 32);
-  bf16x8 va[2];
+  for (int i = 0; i < PF; ++i) kr[i] = ld_lds16(kbase, (i % 2) * kHalfBytes + (i / 2) * 32);
+  bf16x8 va[PF];
   if (PV) {
-    va[0] = read_vt(vbase, 0, 0);
-    va[1] = read_vt(vbase, 0, 1);
+#pragma unroll
+    for (int i = 0; i < PF; ++i) va[i] = read_vt(vbase, i >> 2, i & 3);
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -216,11 +220,11 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   for (int slot = 0; slot < 32; ++slot) {
     const int t = slot >> 1;
     if ((slot & 1) == 0) {  // S^T of tile j+1: step t = (d-block t/2, key half t%2)
-      sn[t & 1] = mfma32x32x16(kr[t & 1], q[t >> 1], sn[t & 1]);
-      if (t + 2 < 16) kr[t & 1] = ld_lds16(kbase, ((t + 2) % 2) * kHalfBytes + ((t + 2) / 2) * 32);
+      sn[t & 1] = mfma32x32x16(kr[t % PF], q[t >> 1], sn[t & 1]);
+      if (t + PF < 16) kr[t % PF] = ld_lds16(kbase, ((t + PF) % 2) * kHalfBytes + ((t + PF) / 2) * 32);
     } else if (PV) {  // PV of tile j-1: chunk t/4, d-block t%4
-      const bf16x8 a = va[t & 1];
-      if (t + 2 < 16) va[t & 1] = read_vt(vbase, (t + 2) >> 2, (t + 2) & 3);
+      const bf16x8 a = va[t % PF];
+      if (t + PF < 16) va[t % PF] = read_vt(vbase, (t + PF) >> 2, (t + PF) & 3);
       o[t & 3] = mfma32x32x16(a, p_prev[t >> 2], o[t & 3]);
     }
     if (slot < 4) {  // row maximum: chain slot over 8 keys (2 slots per chain pair)
