@@ -172,22 +172,22 @@ attn_status_t attn_paged_decode_sliding_window(const void* q, const void* kv_cac
  *
  * The split partials live in the library's own device array of
  * ATTN_DECODE_SCRATCH_BYTES, one per GPU, which stays allocated from the first
- * use until the process ends. Head dims other than 128 plan no more KV splits
+ * use until the process ends. Head dims 96 and 192 plan no more KV splits
  * than fit there (at most 64 per sequence, at least 1). A call whose partials
  * still do not fit returns ATTN_ERR_WORKSPACE_TOO_SMALL before any HIP call:
- * for head_dim 128 that is 4 * num_heads * 129 * (num_seqs + 1024 /
- * (num_kv_heads * ceil(num_heads / num_kv_heads / 16))) bytes plus two int32
- * arrays of num_seqs + 1 above the limit (about 1900 sequences at 32/8 heads);
- * for other head dims one split of num_seqs * num_heads * (head_dim + 1) * 4
- * bytes above it. Nothing in the array needs clearing: every call writes each
+ * for head_dim 64, 128 and 256 that is 4 * num_heads * (head_dim + 1) *
+ * (num_seqs + 1024 * 128 / head_dim / (num_kv_heads * ceil(num_heads /
+ * num_kv_heads / 16))) bytes plus two int32 arrays of num_seqs + 1 above the
+ * limit (about 1900 sequences at 32/8 heads and head_dim 128); for 96 and 192
+ * one split of num_seqs * num_heads * (head_dim + 1) * 4 bytes above it. Nothing in the array needs clearing: every call writes each
  * partial before it reads it.
  * Every call on one GPU shares that GPU's array and leaves its partials there,
  * so calls that overlap on one GPU (other streams, other host threads) race:
  * issue them in order on one stream. The first call on each device looks the
  * array's device address up in the HIP runtime (no allocation) and caches it;
- * a failed lookup returns ATTN_ERR_LAUNCH. For head_dim 128 the result equals
- * attn_paged_decode's bit for bit; for other head dims it can differ in the
- * last bits where the split plan is capped.
+ * a failed lookup returns ATTN_ERR_LAUNCH. For head_dim 64, 128 and 256 the
+ * result equals attn_paged_decode's bit for bit; for 96 and 192 it can differ
+ * in the last bits where the split plan is capped.
  */
 attn_status_t attn_paged_decode_scratch(const void* q, const void* kv_cache,
                                         const int32_t* block_tables, const int32_t* context_lens,
@@ -308,9 +308,10 @@ attn_status_t attn_paged_kv_write(const void* k, const void* v, const int32_t* s
  *   lse           nullable; [num_heads, total_q] fp32
  *   workspace     device buffer of at least attn_paged_prefill_workspace_size()
  *                 bytes (nullable when that is 0). Short query runs (speculative
- *                 decoding: head_dim 128 and max_seqlen_q * num_heads/num_kv_heads
- *                 <= 64) stream the cache once per kv head like decode and keep
- *                 fp32 partials there; longer ones need none.
+ *                 decoding: head_dim 64, 128 or 256 and max_seqlen_q *
+ *                 num_heads/num_kv_heads <= 64) stream the cache once per kv
+ *                 head like decode and keep fp32 partials there; longer ones
+ *                 need none.
  * batch == 0 or total_q == 0 is a no-op.
  */
 attn_status_t attn_paged_prefill(const void* q, const void* kv_cache, const int32_t* block_tables,

@@ -133,7 +133,9 @@ attn_status_t paged_decode_impl(const void* q, const void* kv_cache, const int32
   const attn::DecodePlan plan =
       win < 0 ? need
               : attn::plan_paged_decode_window(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, win);
-  if (plan.o_bytes + plan.lse_bytes > workspace_bytes && head_dim != 128) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  if (plan.o_bytes + plan.lse_bytes > workspace_bytes && !attn::decode_stream_supported(head_dim)) {
+    return ATTN_ERR_WORKSPACE_TOO_SMALL;
+  }
   attn::DecodeArgs a{q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
                      max_context_len, num_heads, num_kv_heads, head_dim, block_size, softmax_scale, out, lse,
                      workspace};
@@ -278,7 +280,8 @@ namespace {
 // decode, with (query token, head) columns; longer ones run the prefill kernels.
 bool paged_prefill_streams(int batch, int num_heads, int num_kv_heads, int head_dim, int max_seqlen_q,
                            int max_context_len) {
-  return head_dim == 128 && (long long)max_seqlen_q * (num_heads / num_kv_heads) <= attn::kSpecMaxCols &&
+  return attn::decode_stream_supported(head_dim) &&
+         (long long)max_seqlen_q * (num_heads / num_kv_heads) <= attn::kSpecMaxCols &&
          (long long)batch * max_context_len < (1LL << 30);
 }
 }  // namespace
@@ -295,7 +298,7 @@ attn_status_t attn_paged_prefill_workspace_size(int32_t batch, int32_t num_heads
   if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
   if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
   *bytes = paged_prefill_streams(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q, max_context_len)
-               ? attn::plan_decode_stream(batch, num_heads, num_kv_heads, max_seqlen_q).workspace_bytes
+               ? attn::plan_decode_stream(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q).workspace_bytes
                : 0;
   return ATTN_OK;
 }
@@ -326,7 +329,8 @@ attn_status_t attn_paged_prefill(const void* q, const void* kv_cache, const int3
   if ((long long)num_blocks * block_size * num_kv_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
   if (attn::varlen_grid_size(batch, max_seqlen_q, num_heads) > kMaxRows) return ATTN_ERR_UNSUPPORTED;
   if (paged_prefill_streams(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q, max_context_len)) {
-    const attn::DecodeStreamPlan plan = attn::plan_decode_stream(batch, num_heads, num_kv_heads, max_seqlen_q);
+    const attn::DecodeStreamPlan plan =
+        attn::plan_decode_stream(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q);
     if (workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
     if (workspace == nullptr) return ATTN_ERR_INVALID_ARG;
     attn::DecodeArgs d{q, kv_cache, block_tables, context_lens, batch, num_blocks, max_blocks_per_seq,

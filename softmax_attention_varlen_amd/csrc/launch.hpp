@@ -59,7 +59,8 @@ bool prefill_d128_supported(const VarlenArgs& a);
 hipError_t launch_prefill_d128(const VarlenArgs& a, hipStream_t stream);
 long varlen_grid_size(int batch, int max_seqlen_q, int num_heads);
 
-// Paged decode: the context of each sequence is cut into splits of
+// Paged decode at head dims 96 and 192 (the others stream, below): the
+// context of each sequence is cut into splits of
 // split_tokens (a multiple of the 128-token block); split s of a sequence
 // writes a normalised fp32 partial (O_s, LSE_s) that a second kernel merges.
 struct DecodePlan {
@@ -71,7 +72,7 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 
-// max_partial_bytes (head dims other than 128): plan no more splits than fit
+// max_partial_bytes (head dims 96 and 192): plan no more splits than fit
 // their fp32 partials in that many bytes (at least one split per sequence, so
 // workspace_bytes can still exceed it).
 DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
@@ -112,20 +113,21 @@ hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipS
 constexpr size_t kDecodeScratchBytes = ATTN_DECODE_SCRATCH_BYTES;
 hipError_t decode_scratch_address(void** ptr);
 
-// head_dim 128: balanced streaming decode (paged_decode_stream.hip). The
-// token stream of all sequences is cut into n_seg equal segments per kv head
-// (and query-head chunk); one wave streams one segment.
-constexpr int kDecodeStreamWaves = 1024;  // 4 waves on each of MI355X's 256 CUs
+// head_dim 64, 128 and 256: balanced streaming decode (paged_decode_stream.hip).
+// The token stream of all sequences is cut into n_seg equal segments per kv
+// head (and query-head chunk); one wave streams one segment.
+constexpr int kDecodeStreamWaves = 1024;  // at head_dim 128: 4 waves on each of MI355X's 256 CUs
+bool decode_stream_supported(int head_dim);
 struct DecodeStreamPlan {
   int max_q, q_chunks, n_seg;
   size_t prefix_bytes;  // int32 [num_seqs + 1] token prefix sums
   size_t skip_bytes;    // int32 [num_seqs] first streamed position (sliding window)
   size_t lse_bytes;     // fp32 [n_seg + num_seqs][max_q][num_heads] partial LSE
-  size_t o_bytes;       // fp32 [n_seg + num_seqs][max_q][num_heads][128] partial O
+  size_t o_bytes;       // fp32 [n_seg + num_seqs][max_q][num_heads][head_dim] partial O
   size_t workspace_bytes;
 };
 // max_q: new query tokens per sequence at most (1 for decode)
-DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads, int max_q = 1);
+DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_q = 1);
 // multi-token queries take the streaming path when their (token, head)
 // columns per kv head fit in kSpecMaxCols (at most that many / 16 passes over K/V)
 constexpr int kSpecMaxCols = 64;

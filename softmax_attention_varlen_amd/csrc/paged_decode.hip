@@ -1,6 +1,6 @@
 // Single-token decode over a paged KV cache, split over the context (split-KV),
-// for head dims other than 128 (head_dim 128 streams balanced segments
-// instead: paged_decode_stream.hip).
+// for head dims 96 and 192 (head dims 64, 128 and 256 stream balanced
+// segments instead: paged_decode_stream.hip).
 //
 // Cache layout [2][num_blocks][128][num_kv_heads][D] (K plane, then V plane).
 // Work item (one wave): (sequence, split, kv head, chunk of <=16 query heads of
@@ -342,7 +342,7 @@ DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int 
   // fewer splits when their partials (O and LSE of every sequence and head)
   // must fit a fixed buffer; one split per sequence at the least
   const size_t per_split = (size_t)num_seqs * num_heads * (head_dim + 1) * sizeof(float);
-  if (head_dim != 128 && per_split > 0 && (size_t)want * per_split > max_partial_bytes) {
+  if (!decode_stream_supported(head_dim) && per_split > 0 && (size_t)want * per_split > max_partial_bytes) {
     const size_t cap = max_partial_bytes / per_split;
     want = cap > 0 ? (long)cap : 1;
   }
@@ -355,7 +355,9 @@ DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int 
   p.o_bytes = (size_t)num_seqs * p.max_splits * num_heads * head_dim * sizeof(float);
   p.lse_bytes = (size_t)num_seqs * p.max_splits * num_heads * sizeof(float);
   p.workspace_bytes = p.o_bytes + p.lse_bytes;
-  if (head_dim == 128) p.workspace_bytes = plan_decode_stream(num_seqs, num_heads, num_kv_heads).workspace_bytes;
+  if (decode_stream_supported(head_dim)) {
+    p.workspace_bytes = plan_decode_stream(num_seqs, num_heads, num_kv_heads, head_dim).workspace_bytes;
+  }
   return p;
 }
 
@@ -406,11 +408,12 @@ static hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipS
 
 hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t stream) {
   switch (a.head_dim) {
-    case 64: return launch_decode_d<64>(a, p, stream);
+    case 64:
+    case 128:
+    case 256:
+      return launch_decode_stream(a, plan_decode_stream(a.num_seqs, a.num_heads, a.num_kv_heads, a.head_dim), stream);
     case 96: return launch_decode_d<96>(a, p, stream);
-    case 128: return launch_decode_stream(a, plan_decode_stream(a.num_seqs, a.num_heads, a.num_kv_heads), stream);
     case 192: return launch_decode_d<192>(a, p, stream);
-    case 256: return launch_decode_d<256>(a, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

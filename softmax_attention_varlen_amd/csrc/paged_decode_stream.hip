@@ -1,4 +1,5 @@
-// Streaming single-token decode over a paged KV cache, head_dim 128, gfx950.
+// Streaming single-token decode over a paged KV cache, head_dim 64, 128 or
+// 256, gfx950.
 //
 // Work balance. The contexts of all sequences, laid end to end, form one token
 // stream of T = sum(context_lens) positions. For each kv head (and chunk of
@@ -15,13 +16,16 @@
 // scan kernel, so the host never reads the lengths.
 //
 // Streaming. Each wave keeps a two-stage LDS ring of 32-token chunks (K and V
-// of its kv head, 8 KB each) filled by direct-to-LDS loads, and issues chunk
-// j+2 as soon as chunk j is consumed (its K half right after chunk j's S^T,
-// its V half after the PV): one chunk is always in flight, which is what
-// keeps HBM busy (a wave that waits for its whole chunk before issuing the
-// next leaves gaps). Load block b of a chunk holds tokens b, b+8, b+16,
-// b+24 (4 rows x 256 B); blocks sit 1056 bytes apart, which makes the
-// transposing V reads conflict-free and the K reads at most 2-way.
+// of its kv head, 32 rows of 2*D bytes each) filled by direct-to-LDS loads,
+// and issues chunk j+2 as soon as chunk j is consumed (its K half right after
+// chunk j's S^T, its V half after the PV): one chunk is always in flight,
+// which is what keeps HBM busy (a wave that waits for its whole chunk before
+// issuing the next leaves gaps). A load writes 1 KB, i.e. 1024 / (2D) token
+// rows, so a chunk half is NB = D / 16 load blocks: block b holds tokens b,
+// b + NB, b + 2NB, ...; blocks sit 1056 bytes apart, which makes the
+// transposing V reads conflict-free at D = 128 and the K reads at most 2-way.
+// Workgroups hold 512 / D * 4 waves (8, 4, 2), so every head dim uses the same
+// LDS per CU and keeps the same bytes in flight per CU.
 //
 // Queries. The 16 MFMA columns of a wave are (query token, head) pairs of its
 // kv head's group: column n of chunk qc is token (16qc + n) / group, head
@@ -46,26 +50,44 @@
 namespace attn {
 namespace {
 
-constexpr int kSD = 128;
 constexpr int kSChunk = 32;
-constexpr int kSBlk = 1056;                  // 4 token rows (1 KB) + 32 B pad
-constexpr int kSHalf = 8 * kSBlk;            // K (or V) of one chunk
-constexpr int kSStage = 2 * kSHalf;          // K, then V
-constexpr int kSWaves = 4;                   // waves per workgroup (one workgroup per CU by LDS)
-constexpr int kSWaveLds = 2 * kSStage;       // two-stage ring per wave
-constexpr int kSLoads = 16;                  // direct-to-LDS loads per chunk per wave
+constexpr int kSBlk = 1056;                  // one 1 KB load block + 32 B pad
 constexpr int kMinSeg = 256;                 // shortest segment (positions)
 
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+// Per head dim: the chunk layout in LDS and the workgroup shape.
+template <int D>
+struct StreamShape {
+  static_assert(D == 64 || D == 128 || D == 256, "token rows must divide a 1 KB load block");
+  static constexpr int kRow = 2 * D;                   // bytes of one token row of one kv head
+  static constexpr int kLanesPerRow = kRow / 16;       // 16-byte pieces of a row: 8, 16, 32
+  static constexpr int kNB = D / 16;                   // load blocks per chunk half: 4, 8, 16
+  static constexpr int kHalf = kNB * kSBlk;            // K (or V) of one chunk
+  static constexpr int kStage = 2 * kHalf;             // K, then V
+  static constexpr int kWaveLds = 2 * kStage;          // two-stage ring per wave
+  static constexpr int kWaves = 4 * 128 / D;           // waves per workgroup (one workgroup per CU by LDS)
+  static constexpr int kLoads = 2 * kNB;               // direct-to-LDS loads per chunk per wave
+  // byte offset of token t (0..31) of a chunk half: block t % NB, row t / NB
+  __device__ __forceinline__ static uint32_t tok_off(uint32_t t) {
+    return (t % (uint32_t)kNB) * kSBlk + (t / (uint32_t)kNB) * (uint32_t)kRow;
+  }
+};
 
-__device__ __forceinline__ uint32_t tok_off(uint32_t t) { return (t & 7u) * kSBlk + (t >> 3) * 256u; }
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
+// sbase and lds are the same in every lane; readfirstlane tells the compiler
+// so where it cannot see it (it would otherwise hand the scalar operands a
+// vector register)
 __device__ __forceinline__ void load_lds16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(lds)
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint64_t bu = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"((const void*)(uintptr_t)bu), "s"(__builtin_amdgcn_readfirstlane(lds))
                : "memory", "m0");
 }
 
@@ -142,12 +164,16 @@ __device__ __forceinline__ int seg_len(int total, int n_seg) {
   return l > kMinSeg ? l : kMinSeg;
 }
 
-__global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
+template <int D>
+__global__ __launch_bounds__(64 * StreamShape<D>::kWaves) void paged_decode_stream_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ prefix, int num_seqs, int num_blocks, int max_blocks_per_seq, int hq, int hkv,
     int q_chunks, int n_seg, float c, uint16_t* __restrict__ out, float* __restrict__ lse,
     float* __restrict__ part_o, float* __restrict__ part_lse, const int32_t* __restrict__ cu_q, int max_q,
     int total_q, const int32_t* __restrict__ skip, int window) {
+  using S = StreamShape<D>;
+  constexpr int kSWaves = S::kWaves, kSWaveLds = S::kWaveLds, kSStage = S::kStage, kSHalf = S::kHalf;
+  constexpr int kSLoads = S::kLoads;
   __shared__ __attribute__((aligned(1024))) char smem[kSWaves * kSWaveLds];
   // every cursor below is wave-uniform (scalar registers, scalar loads): no
   // compiler-visible vector load may sit in the streaming loop, since the
@@ -174,7 +200,7 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
   const int qi = col_real ? col / group : 0;
   const int h = hk * group + (col_real ? col % group : 0);
 
-  const long row_elems = (long)hkv * kSD;                // elements between tokens of a block
+  const long row_elems = (long)hkv * D;                  // elements between tokens of a block
   const long blk_elems = 128L * row_elems;
   const long v_plane = (long)num_blocks * blk_elems;
   const uint32_t row_bytes = (uint32_t)row_elems * 2u;
@@ -183,8 +209,9 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
 
   // per-lane LDS offsets: K A operand (token 16kb + n16, d = 32b + 8G) and the
   // transposing V reads (token 4G + s/4, columns 16db + 4(s%4))
-  const uint32_t k_lane = tok_off((uint32_t)n16) + (uint32_t)G * 16u;
-  const uint32_t v_lane = tok_off(4u * (uint32_t)G + ((uint32_t)n16 >> 2)) + ((uint32_t)n16 & 3u) * 8u;
+  // (token 16kb + n16 sits 512 bytes after token n16 for every D)
+  const uint32_t k_lane = S::tok_off((uint32_t)n16) + (uint32_t)G * 16u;
+  const uint32_t v_lane = S::tok_off(4u * (uint32_t)G + ((uint32_t)n16 >> 2)) + ((uint32_t)n16 & 3u) * 8u;
 
   const int s0 = __builtin_amdgcn_readfirstlane(find_seq(prefix, num_seqs, seg_begin, lane));
   // the loader's cursor: sequence ls, chunk lc (32 tokens), its last chunk lc_end
@@ -200,20 +227,23 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
   // stage's K has been read (after this chunk's S^T), then V and the cursor
   // advance once its V has been read (after the PV)
   const uint16_t* lkb = kv;  // K base of the block being issued, kept between the halves
-  auto issue_half = [&](int stage, bool v_half) {
+  auto issue_half = [&](int stage, bool v_half) __attribute__((always_inline)) {
     const int t0 = lc * kSChunk;
     if (!v_half) {
       int blk = block_tables[(long)ls * max_blocks_per_seq + ((t0 + lskip) >> 7)];
       blk = clampi(blk, 0, num_blocks - 1);
-      lkb = kv + (long)blk * blk_elems + (long)hk * kSD;
+      lkb = kv + (long)blk * blk_elems + (long)hk * D;
     }
     const uint16_t* src = v_half ? lkb + v_plane : lkb;
     const uint32_t st = ring + stage * kSStage + (v_half ? kSHalf : 0);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      int t = t0 + b + 8 * (lane >> 4);
+    for (int b = 0; b < S::kNB; ++b) {
+      // lane l writes 16 bytes at st + b * kSBlk + 16 l: row l / kLanesPerRow
+      // of the block (token b + kNB * row), piece l % kLanesPerRow of it
+      int t = t0 + b + S::kNB * (lane / S::kLanesPerRow);
       t = t < lctx ? t : lctx - 1;  // rows past the context re-read the last one (same block)
-      const uint32_t voff = (uint32_t)((t + lskip) & 127) * row_bytes + (uint32_t)(lane & 15) * 16u;
+      const uint32_t voff =
+          (uint32_t)((t + lskip) & 127) * row_bytes + (uint32_t)(lane % S::kLanesPerRow) * 16u;
       load_lds16(src, voff, st + b * kSBlk);
     }
     if (!v_half) return;
@@ -234,7 +264,7 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
       }
     }
   };
-  auto issue = [&](int stage) {
+  auto issue = [&](int stage) __attribute__((always_inline)) {
     issue_half(stage, false);
     issue_half(stage, true);
   };
@@ -253,8 +283,10 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
   int cc_end = (t_hi - 1) / kSChunk;
   bool fresh = true;
 
-  bf16x8 qb[4];
-  f32x4 o[8];
+  constexpr int QB = D / 32;  // 32-wide d steps of S^T
+  constexpr int OB = D / 16;  // 16-wide d blocks of O^T
+  bf16x8 qb[QB];
+  f32x4 o[OB];
   float m = kNegInf, l = 0.f;
   int q_row = 0, lim = 0, lim_min = 0, lo_lim = 0, lo_max = 0;
   bool live = false;
@@ -277,15 +309,16 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
       // chunk may start up to 31 keys early); lo_max is the largest such bound
       lo_lim = window >= 0 ? lim - window : kNoLowerLimit;
       lo_max = window >= 0 ? cctx - 1 - window : kNoLowerLimit;
-      const uint16_t* qrow = q + ((long)q_row * hq + h) * kSD;
+      const uint16_t* qrow = q + ((long)q_row * hq + h) * D;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
+      for (int b = 0; b < QB; ++b) {
         const u32x4 x = ld_global16(qrow + b * 32 + G * 8);  // unconditional: no branch per load
         qb[b] = as_bf16x8(live ? x : u32x4{0u, 0u, 0u, 0u});
       }
-      asm volatile("" : : "v"(qb[0]), "v"(qb[1]), "v"(qb[2]), "v"(qb[3]));
 #pragma unroll
-      for (int b = 0; b < 8; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < QB; ++b) asm volatile("" : : "v"(qb[b]));
+#pragma unroll
+      for (int b = 0; b < OB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
       m = kNegInf;
       l = 0.f;
       fresh = false;
@@ -303,7 +336,7 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
+      for (int b = 0; b < QB; ++b) {
         const bf16x8 a = ld_lds16(kt, (int)(k_lane + (uint32_t)kb * 512u + (uint32_t)b * 64u));
         s[kb] = mfma16x16x32(a, qb[b], s[kb]);
       }
@@ -344,8 +377,8 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
     m = m_new;
     const lds_bf16x4* vb = (const lds_bf16x4*)(ring + stage * kSStage + kSHalf + v_lane);
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      // byte offsets 32db (columns) and tok_off(16) = 512 for tokens 16..31, in 8-byte units
+    for (int db = 0; db < OB; ++db) {
+      // byte offsets 32db (columns) and 512 for tokens 16..31, in 8-byte units
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 4 * db));
       const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 64 + 4 * db));
       const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -361,18 +394,18 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
       const float lse_p = lt > 0.f ? (m * c + hw_log2(lt)) * kLn2 : kNegInf;
       if (live) {
         if (t_lo == 0 && t_hi == cctx) {
-          uint16_t* orow = out + ((long)q_row * hq + h) * kSD;
+          uint16_t* orow = out + ((long)q_row * hq + h) * D;
 #pragma unroll
-          for (int db = 0; db < 8; ++db) {
+          for (int db = 0; db < OB; ++db) {
             const f32x4 t = o[db] * inv;
             *reinterpret_cast<bf16x4*>(orow + db * 16 + 4 * G) = to_bf16x4(t);
           }
           if (lse != nullptr && G == 0) lse[(long)h * total_q + q_row] = lse_p;
         } else {
           const long slot = ((long)(g + cs) * max_q + qi) * hq + h;
-          float* orow = part_o + slot * kSD;
+          float* orow = part_o + slot * D;
 #pragma unroll
-          for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * G) = o[db] * inv;
+          for (int db = 0; db < OB; ++db) *reinterpret_cast<f32x4*>(orow + db * 16 + 4 * G) = o[db] * inv;
           if (G == 0) part_lse[slot] = lse_p;
         }
       }
@@ -402,6 +435,7 @@ __global__ __launch_bounds__(64 * kSWaves) void paged_decode_stream_kernel(
 // order: LSE = ln sum_i exp(LSE_i), O = sum_i exp(LSE_i - LSE) O_i. A sequence
 // that lies in one segment was finished by the streaming kernel; an empty one
 // gets zeros and LSE = -inf.
+template <int D>
 __global__ __launch_bounds__(256) void paged_decode_stream_combine_kernel(
     const int32_t* __restrict__ prefix, int num_seqs, int hq, int n_seg, const float* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ out, float* __restrict__ lse,
@@ -422,9 +456,9 @@ __global__ __launch_bounds__(256) void paged_decode_stream_combine_kernel(
   const long row = q_first + qi;
   const int total = prefix[num_seqs];
   const int b0 = prefix[s], b1 = prefix[s + 1];
-  uint16_t* orow = out + (row * hq + h) * kSD;
+  uint16_t* orow = out + (row * hq + h) * D;
   if (b1 <= b0) {
-    for (int d = lane; d < kSD; d += 64) orow[d] = 0;
+    for (int d = lane; d < D; d += 64) orow[d] = 0;
     if (lse != nullptr && lane == 0) lse[(long)h * total_q + row] = kNegInf;
     return;
   }
@@ -444,7 +478,7 @@ __global__ __launch_bounds__(256) void paged_decode_stream_combine_kernel(
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = wave_xor_max(mx, o);
   if (mx == kNegInf) {  // no key visible to this query in any piece
-    for (int d = lane; d < kSD; d += 64) orow[d] = 0;
+    for (int d = lane; d < D; d += 64) orow[d] = 0;
     if (lse != nullptr && lane == 0) lse[(long)h * total_q + row] = kNegInf;
     return;
   }
@@ -456,43 +490,51 @@ __global__ __launch_bounds__(256) void paged_decode_stream_combine_kernel(
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) tot = wave_xor_sum(tot, o);
   const float lse_all = mx + hw_log2(tot) * kLn2;
-  float acc0 = 0.f, acc1 = 0.f;  // columns lane and lane + 64
+  constexpr int NC = D / 64;  // columns lane + 64k of the output row
+  float acc[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) acc[k] = 0.f;
   for (int c0 = first; c0 <= last; c0 += 64) {
     const int gg = c0 + lane;
     const float wl = gg <= last ? hw_exp2((part_lse[slot(gg)] - lse_all) * kLog2e) : 0.f;
     const int n = last - c0 + 1 < 64 ? last - c0 + 1 : 64;
     for (int i = 0; i < n; ++i) {
       const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
-      const float* po = part_o + slot(c0 + i) * kSD;
-      acc0 += wi * po[lane];
-      acc1 += wi * po[lane + 64];
+      const float* po = part_o + slot(c0 + i) * D;
+#pragma unroll
+      for (int k = 0; k < NC; ++k) acc[k] += wi * po[lane + 64 * k];
     }
   }
-  orow[lane] = __builtin_bit_cast(uint16_t, (__bf16)acc0);
-  orow[lane + 64] = __builtin_bit_cast(uint16_t, (__bf16)acc1);
+#pragma unroll
+  for (int k = 0; k < NC; ++k) orow[lane + 64 * k] = __builtin_bit_cast(uint16_t, (__bf16)acc[k]);
   if (lse != nullptr && lane == 0) lse[(long)h * total_q + row] = lse_all;
 }
 
 }  // namespace
 
-DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads, int max_q) {
+bool decode_stream_supported(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
+
+DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_q) {
   DecodeStreamPlan p{};
   const int group = num_heads / num_kv_heads;
   p.max_q = max_q > 1 ? max_q : 1;
   p.q_chunks = (p.max_q * group + 15) / 16;
   const int lanes = num_kv_heads * p.q_chunks;
-  p.n_seg = kDecodeStreamWaves / lanes > 1 ? kDecodeStreamWaves / lanes : 1;
+  // stream waves: 256 CUs x the workgroup's waves (8, 4, 2 for D = 64, 128, 256)
+  const int waves = kDecodeStreamWaves * 128 / head_dim;
+  p.n_seg = waves / lanes > 1 ? waves / lanes : 1;
   p.prefix_bytes = ((size_t)(num_seqs + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   p.skip_bytes = ((size_t)num_seqs * sizeof(int32_t) + 255) & ~(size_t)255;
   const size_t slots = (size_t)(p.n_seg + num_seqs) * p.max_q * num_heads;
   p.lse_bytes = (slots * sizeof(float) + 255) & ~(size_t)255;
-  p.o_bytes = slots * kSD * sizeof(float);
+  p.o_bytes = slots * (size_t)head_dim * sizeof(float);
   p.workspace_bytes = p.prefix_bytes + p.skip_bytes + p.lse_bytes + p.o_bytes;
   return p;
 }
 
-hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, hipStream_t stream) {
-  if (a.window >= 0 && a.cu_q != nullptr) return hipErrorInvalidValue;  // windows: one query token each
+template <int D>
+static hipError_t launch_decode_stream_d(const DecodeArgs& a, const DecodeStreamPlan& p, hipStream_t stream) {
+  constexpr int kSWaves = StreamShape<D>::kWaves;
   int32_t* prefix = (int32_t*)a.workspace;
   int32_t* skip = a.window >= 0 ? (int32_t*)((char*)a.workspace + p.prefix_bytes) : nullptr;
   float* part_lse = (float*)((char*)a.workspace + p.prefix_bytes + p.skip_bytes);
@@ -503,7 +545,7 @@ hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long waves = (long)p.n_seg * a.num_kv_heads * p.q_chunks;
-  hipLaunchKernelGGL(paged_decode_stream_kernel, dim3((unsigned)((waves + kSWaves - 1) / kSWaves)),
+  hipLaunchKernelGGL((paged_decode_stream_kernel<D>), dim3((unsigned)((waves + kSWaves - 1) / kSWaves)),
                      dim3(64 * kSWaves), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.kv_cache,
                      a.block_tables, prefix, a.num_seqs, a.num_blocks, a.max_blocks_per_seq, a.num_heads,
                      a.num_kv_heads, p.q_chunks, p.n_seg, a.scale * kLog2e, (uint16_t*)a.out, a.lse, part_o,
@@ -511,10 +553,20 @@ hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, 
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long pairs = (long)a.num_seqs * p.max_q * a.num_heads;
-  hipLaunchKernelGGL(paged_decode_stream_combine_kernel, dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, stream,
-                     prefix, a.num_seqs, a.num_heads, p.n_seg, part_o, part_lse, (uint16_t*)a.out, a.lse, a.cu_q,
-                     p.max_q, total_q);
+  hipLaunchKernelGGL((paged_decode_stream_combine_kernel<D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
+                     stream, prefix, a.num_seqs, a.num_heads, p.n_seg, part_o, part_lse, (uint16_t*)a.out, a.lse,
+                     a.cu_q, p.max_q, total_q);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, hipStream_t stream) {
+  if (a.window >= 0 && a.cu_q != nullptr) return hipErrorInvalidValue;  // windows: one query token each
+  switch (a.head_dim) {
+    case 64: return launch_decode_stream_d<64>(a, p, stream);
+    case 128: return launch_decode_stream_d<128>(a, p, stream);
+    case 256: return launch_decode_stream_d<256>(a, p, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace attn

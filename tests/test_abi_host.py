@@ -184,7 +184,13 @@ def test_paged_prefill_empty_is_noop(kw):
 def test_paged_prefill_workspace_query():
     # long query runs use the prefill kernels (no workspace); short ones stream like decode
     assert sav.attn_paged_prefill_workspace_size(16, 32, 8, 128, 1024, 16384) == 0
-    assert sav.attn_paged_prefill_workspace_size(16, 32, 8, 64, 4, 16384) == 0
+    # head dims 64, 128 and 256 stream short runs; 96 and 192 take the prefill kernels
+    assert sav.attn_paged_prefill_workspace_size(16, 32, 8, 96, 4, 16384) == 0
+    assert sav.attn_paged_prefill_workspace_size(16, 32, 8, 192, 4, 16384) == 0
+    for d in (64, 256):
+        assert sav.attn_paged_prefill_workspace_size(16, 32, 8, d, 4, 16384) > 0
+        assert sav.attn_paged_prefill_workspace_size(16, 32, 8, d, 1, 16384) == \
+            sav.attn_paged_decode_workspace_size(16, 32, 8, d, 16384)
     n4 = sav.attn_paged_prefill_workspace_size(64, 32, 8, 128, 4, 32768)
     n1 = sav.attn_paged_prefill_workspace_size(64, 32, 8, 128, 1, 32768)
     assert n4 > n1 > 0
