@@ -47,21 +47,27 @@ _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
 _SPARSE_SRC = ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"]
 TRAFFIC = {
     "tiny": {"kernel": "varlen_fwd_kernel<64,false,false>"},
+    "dense_d64": {"kernel": "varlen_fwd_kernel<64,false,false>"},
+    "dense_d96": {"kernel": "varlen_fwd_kernel<96,false,false>"},
+    "dense_d192": {"kernel": "varlen_fwd_kernel<192,false,false>"},
+    "dense_d256": {"kernel": "varlen_fwd_kernel<256,false,false>"},
+    "decode_d64": {"kernel": "paged_decode_stream_kernel<64>"},
+    "decode_d256": {"kernel": "paged_decode_stream_kernel<256>"},
     "dense": {"kernel": "prefill_d128_kernel<false,false,4,true>", "fetch_kib": 73853.1, "write_kib": 49952.6,
               "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
     "causal": {"kernel": "prefill_d128_kernel<true,false,4,true>", "fetch_kib": 111923.0, "write_kib": 142491.4,
                "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
-    "paged": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2443493.1, "write_kib": 3043.0,
+    "paged": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2443493.1, "write_kib": 3043.0,
               "sources": _DECODE_SRC, "sha256": "84ce7c15c1448e8c"},
     "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 235877.9, "write_kib": 49920.5,
                "sources": _SPARSE_SRC, "sha256": "b87edb9f712a3369"},
     "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,false>", "fetch_kib": 701680.5,
                       "write_kib": 87201.8, "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
-    "spec": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 2445730.6, "write_kib": 12163.8,
+    "spec": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2445730.6, "write_kib": 12163.8,
              "sources": _DECODE_SRC, "sha256": "84ce7c15c1448e8c"},
     "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 432763.5, "write_kib": 51482.8,
            "sources": _SPARSE_SRC, "sha256": "b87edb9f712a3369"},
-    "swa": {"kernel": "paged_decode_stream_kernel", "fetch_kib": 531366.6, "write_kib": 3081.4,
+    "swa": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 531366.6, "write_kib": 3081.4,
             "sources": _DECODE_SRC, "sha256": "84ce7c15c1448e8c"},
     "masked": {"kernel": "prefill_d128_kernel<false,false,4,true>", "fetch_kib": 28943.5, "write_kib": 50005.0,
                "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
@@ -404,11 +410,11 @@ def bench_sparse(case, steps, warmup):
 
 
 def bench_head_dims(steps, warmup):
-    """Head dims other than 128 (the first-generation kernels), opt-in with
-    --only head_dims and not part of the default line: dense non-causal prefill
-    of 2 x 4096 rows with 24 heads, and decode over workload 4's 64 contexts
-    (32 query / 8 kv heads, a random permutation of cache blocks), inputs drawn
-    on the device."""
+    """The head dims other than 128 that the pages list: dense non-causal
+    prefill of 2 x 4096 rows with 24 heads at D = 64, 96, 192, 256, and decode
+    over workload 4's 64 contexts (32 query / 8 kv heads, a random permutation
+    of cache blocks) at D = 64 and 256, inputs drawn on the device. Returns
+    (workload name, kind, StepTime, algorithmic work, bound) per line."""
     dev = torch.device("cuda")
     rows = []
     for d in (64, 96, 192, 256):
@@ -417,11 +423,9 @@ def bench_head_dims(steps, warmup):
         cu = torch.tensor([0, 4096, 8192], dtype=torch.int32, device=dev)
         out = torch.empty_like(q)
         lse = torch.empty((h, n), dtype=torch.float32, device=dev)
-        ms = time_steps(lambda: sav.attn_varlen_fwd(q, k, v, cu, cu, 4096, 4096, d ** -0.5, False, out=out, lse=lse),
-                        steps, warmup).mean
-        flops = 4.0 * 2 * h * d * 4096 * 4096
-        rows.append({"workload": f"dense-b2-s4096-h24-d{d}", "value": round(flops / (ms * 1e-3) / 1e12, 2),
-                     "unit": "TFLOP/s", "ms": round(ms, 4)})
+        t = time_steps(lambda: sav.attn_varlen_fwd(q, k, v, cu, cu, 4096, 4096, d ** -0.5, False, out=out, lse=lse),
+                       steps, warmup)
+        rows.append((f"dit-dense-b2-s4096-h24-d{d}", f"dense_d{d}", t, 4.0 * 2 * h * d * 4096 * 4096, "mfma"))
         del q, k, v, out
     ctx = workloads.config4_lengths()
     nblk = [(int(c) + 127) // 128 for c in ctx]
@@ -439,11 +443,11 @@ def bench_head_dims(steps, warmup):
         out = torch.empty_like(q)
         ws = torch.empty(max(sav.attn_paged_decode_workspace_size(len(ctx), 32, 8, d, int(max(ctx))), 1),
                          dtype=torch.uint8, device=dev)
-        ms = time_steps(lambda: sav.attn_paged_decode(q, cache, bt, cl, int(max(ctx)), d ** -0.5, out=out,
-                                                      workspace=ws), steps, warmup).mean
-        nbytes = float(sum(int(c) for c in ctx)) * 8 * d * 2 * 2
-        rows.append({"workload": f"paged-decode-64seq-ctx1k-32k-h32kv8-d{d}",
-                     "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s", "ms": round(ms, 4)})
+        t = time_steps(lambda: sav.attn_paged_decode(q, cache, bt, cl, int(max(ctx)), d ** -0.5, out=out,
+                                                     workspace=ws), steps, warmup)
+        # K and V of every context token, plus Q, O, tables and lengths
+        nbytes = float(sum(int(c) for c in ctx)) * 8 * d * 2 * 2 + 2.0 * len(ctx) * 32 * d * 2 + tables.nbytes + 256
+        rows.append((f"paged-decode-64seq-ctx1k-32k-h32kv8-d{d}", f"decode_d{d}", t, nbytes, "hbm"))
         del cache, q, out, ws
         torch.cuda.empty_cache()
     return rows
@@ -567,7 +571,7 @@ def main():
                     default=None,
                     help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
                          "copy, the reference that scales the HBM byte counters; 'head_dims' times the head "
-                         "dims other than 128 (not part of the default line)")
+                         "dims other than 128")
     ap.add_argument("--clock-warmup-ms", type=float, default=CLOCK_WARMUP_MS,
                     help="repeat each workload's step for this long before its warm-up steps (0: off)")
     ap.add_argument("--no-secondary", action="store_true")
@@ -597,12 +601,6 @@ def main():
                           "ms": round(ms, 5), "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
         return
 
-    if args.only == "head_dims":
-        rows = bench_head_dims(args.steps, args.warmup)
-        for r in rows:
-            log(f"{r['workload']}: {r['ms'] * 1e3:.1f} us/step, {r['value']} {r['unit']}")
-        print(json.dumps({"metric": "head dims other than 128", "workloads": rows}))
-        return
 
     secondary = []
     head = None
@@ -695,6 +693,10 @@ def main():
         del case
     del decode_case
     torch.cuda.empty_cache()
+    if want("head_dims"):
+        for name, kind, t, work, bound in bench_head_dims(args.steps, args.warmup):
+            KIND[name] = kind
+            line_for(name, t, work, bound)
     for name, cfg, masked in (("masked", workloads.config9, True), ("padded", workloads.config10, False)):
         if want(name):
             case = cfg()
