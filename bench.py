@@ -42,26 +42,26 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 FETCH_SCALE = 2.0
 WRITE_SCALE = 1.0
 CSRC = os.path.join(ROOT, "softmax_attention_varlen_amd", "csrc")
-_PREFILL_SRC = ["prefill_d128.hip", "pipe_d128.hpp", "attn_common.hpp", "key_rows.hpp"]
+_PREFILL_SRC = ["prefill_pipe.hip", "pipe.hpp", "attn_common.hpp", "key_rows.hpp"]
 _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
-_SPARSE_SRC = ["block_sparse_d128.hip", "pipe_d128.hpp", "attn_common.hpp"]
+_SPARSE_SRC = ["block_sparse_d128.hip", "pipe.hpp", "attn_common.hpp"]
 TRAFFIC = {
     "tiny": {"kernel": "varlen_fwd_kernel<64,false,false>"},
     "dense_d64": {"kernel": "varlen_fwd_kernel<64,false,false>"},
     "dense_d96": {"kernel": "varlen_fwd_kernel<96,false,false>"},
-    "dense_d192": {"kernel": "varlen_fwd_kernel<192,false,false>"},
-    "dense_d256": {"kernel": "varlen_fwd_kernel<256,false,false>"},
+    "dense_d192": {"kernel": "prefill_pipe_kernel<192,false,false,4,true>"},
+    "dense_d256": {"kernel": "prefill_pipe_kernel<256,false,false,4,true>"},
     "decode_d64": {"kernel": "paged_decode_stream_kernel<64>"},
     "decode_d256": {"kernel": "paged_decode_stream_kernel<256>"},
-    "dense": {"kernel": "prefill_d128_kernel<false,false,4,true>", "fetch_kib": 73853.1, "write_kib": 49952.6,
+    "dense": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 73853.1, "write_kib": 49952.6,
               "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
-    "causal": {"kernel": "prefill_d128_kernel<true,false,4,true>", "fetch_kib": 111923.0, "write_kib": 142491.4,
+    "causal": {"kernel": "prefill_pipe_kernel<128,true,false,4,true>", "fetch_kib": 111923.0, "write_kib": 142491.4,
                "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
     "paged": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2443493.1, "write_kib": 3043.0,
               "sources": _DECODE_SRC, "sha256": "84ce7c15c1448e8c"},
     "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 235877.9, "write_kib": 49920.5,
                "sources": _SPARSE_SRC, "sha256": "b87edb9f712a3369"},
-    "paged_prefill": {"kernel": "prefill_d128_kernel<true,true,8,false>", "fetch_kib": 701680.5,
+    "paged_prefill": {"kernel": "prefill_pipe_kernel<128,true,true,8,false>", "fetch_kib": 701680.5,
                       "write_kib": 87201.8, "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
     "spec": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2445730.6, "write_kib": 12163.8,
              "sources": _DECODE_SRC, "sha256": "84ce7c15c1448e8c"},
@@ -69,9 +69,9 @@ TRAFFIC = {
            "sources": _SPARSE_SRC, "sha256": "b87edb9f712a3369"},
     "swa": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 531366.6, "write_kib": 3081.4,
             "sources": _DECODE_SRC, "sha256": "84ce7c15c1448e8c"},
-    "masked": {"kernel": "prefill_d128_kernel<false,false,4,true>", "fetch_kib": 28943.5, "write_kib": 50005.0,
+    "masked": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 28943.5, "write_kib": 50005.0,
                "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
-    "padded": {"kernel": "prefill_d128_kernel<false,false,4,true>", "fetch_kib": 108036.1, "write_kib": 66235.8,
+    "padded": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 108036.1, "write_kib": 66235.8,
                "sources": _PREFILL_SRC, "sha256": "5fa4531d75d0eabb"},
 }
 

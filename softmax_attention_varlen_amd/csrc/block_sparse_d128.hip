@@ -10,7 +10,7 @@
 // The kept key tiles come from the block map as ascending lists with empty
 // tiles dropped, each entry packed as (size << 24) | tile. K and V stream
 // through separate two-stage LDS rings (direct-to-LDS loads, the
-// conflict-free layout of pipe_d128.hpp): step j runs the softmax of tile j
+// conflict-free layout of pipe.hpp): step j runs the softmax of tile j
 // under the S^T MFMAs of tile j+1 and the PV MFMAs of tile j-1, reading K of
 // tile j+1 and V of tile j-1, while K of tile j+2 and V of tile j are in
 // flight. With two workgroups per CU
@@ -31,13 +31,15 @@
 #include <type_traits>
 
 #include "launch.hpp"
-#include "pipe_d128.hpp"
+#include "pipe.hpp"
 
 namespace attn {
 namespace {
 
 using namespace pipe;
 
+constexpr int kD = 128;
+constexpr int kTileBytes = Geom<kD>::kTileBytes;
 constexpr int kSW = 4;                       // waves per workgroup
 constexpr int kSIPW = 16 / kSW;              // load blocks per wave per K (or V) tile
 constexpr int kSparseLds = 4 * kTileBytes;   // K stages 0, 1, then V stages 0, 1
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // the same in every lane of a wave
   const int rh = w & 1, kh = w >> 1;
-  const Lane L = make_lane(lane, 32 * kh);
+  const Lane L = make_lane<kD>(lane, 32 * kh);
   const int qsize = clampi(tile_sizes[a], 0, kBN);
   const int r = 32 * rh + L.n;
   const int r_c = r < qsize ? r : (qsize > 0 ? qsize - 1 : 0);
@@ -214,7 +216,7 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
 #pragma unroll
       for (int i = 0; i < kSIPW; ++i) load_lds16(tb, boff[i], stage_lds + (w * kSIPW + i) * kBlockBytes);
     } else {
-      issue_tile<kSIPW>(tb, stride_bytes, t.size, stage_lds, w * kSIPW, lane);
+      issue_tile<kD, kSIPW>(tb, stride_bytes, t.size, stage_lds, w * kSIPW, lane);
     }
   };
   auto issue_k = [&](const Entry& t, int stage) { issue(kbatch, t, ring + stage * kTileBytes); };
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
     } else {
       wait_loads_barrier<0>();
     }
-    if (wave_live) qk<1>(smem, L, qr, sa);
+    if (wave_live) qk<kD, 1>(smem, L, qr, sa);
   }
   settle_q(qr);
 
@@ -302,9 +304,9 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
     if (wave_live) {
       const uint32_t vt = ring + (2 + ((count - 1) & 1)) * kTileBytes;
       if ((count - 1) & 1) {
-        pv<1>(vt, L, pb, o);
+        pv<kD, 1>(vt, L, pb, o);
       } else {
-        pv<1>(vt, L, pa, o);
+        pv<kD, 1>(vt, L, pa, o);
       }
     }
   }
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   }
   st.m = mm;
   st.l = r < qsize ? st.l * a0 + ml.y * a1 : 0.f;  // padding rows: zeros, LSE = -inf
-  store_rows(o, st, L, c, true, out + ((qrow0 + r) * hq + h) * kD,
+  store_rows<4>(o, st, L, c, true, out + ((qrow0 + r) * hq + h) * kD,
              lse != nullptr ? lse + ((long)b * hq + h) * seq + (long)a * kBN + r : nullptr);
 }
 

@@ -1,15 +1,20 @@
-// Building blocks of the pipelined head_dim-128 attention kernels on gfx950
-// (dense/varlen prefill and 64-token block-sparse attention).
+// Building blocks of the pipelined attention kernels on gfx950 for head dims
+// 128, 192 and 256 (dense/varlen prefill; 64-token block-sparse attention at
+// head_dim 128).
 //
-// LDS tile layout. A K (or V) tile holds 64 keys x 128 bf16 columns and is
-// filled by direct-to-LDS 16-byte loads. Load block b (16 per tile) is one
-// contiguous 1 KB holding the four keys kappa(b) + {0, 16, 32, 48}; blocks sit
-// 1040 bytes apart (16 bytes = 4 banks of pad). Key k%16 = (b3 b2 b1 b0) lives
-// in block (b1 b0 b3 b2). A 16-lane slice of a K read then covers the 16
-// blocks (all 64 banks once), and a 32-lane slice of a transposing V read
+// LDS tile layout. A K (or V) tile holds 64 keys and is filled by
+// direct-to-LDS 16-byte loads, each writing one contiguous 1 KB load block.
+// A key's row takes 256 bytes in LDS at head_dim 128 and 512 at 192 and 256
+// (192 pads each row to 512), so a block holds 4 or 2 rows. Blocks sit 1040
+// bytes apart (16 bytes = 4 banks of pad). Keys go in groups of 16: within a
+// group, key k%16 = (b3 b2 b1 b0) lives in block (b1 b0 b3 b2) of a run of 16
+// blocks; at 128 the four groups are the four rows of those 16 blocks, at
+// 192/256 groups 0 and 1 take rows 0 of two runs of 16 blocks and groups 2
+// and 3 their rows 1. A 16-lane slice of a K read then covers 16 blocks of
+// one run (all 64 banks once), and a 32-lane slice of a transposing V read
 // (4 keys x 64 bytes) puts its 4 rows 16 banks apart: both conflict-free on
-// gfx950's 64-bank LDS, as measured. Every LDS address is a per-lane base plus
-// a compile-time offset.
+// gfx950's 64-bank LDS, as measured at head_dim 128. Every LDS address is a
+// per-lane base plus a compile-time offset.
 //
 // Per 32x32 block the orientation is S^T = K Q^T: a lane owns one query (its
 // row of S is spread over the lane and lane^32), K is read row-wise
@@ -17,29 +22,60 @@
 // transposing ds_read_b64_tr_b16, which hands each lane four keys of one
 // column: exactly the k-slot layout of the A operand of O^T += V^T P^T.
 #pragma once
+#include <utility>
+
 #include "attn_common.hpp"
 
 namespace attn {
 namespace pipe {
 
-constexpr int kD = 128;
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, in order, each call a
+// compile-time instance.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_seq(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_seq(f, std::make_integer_sequence<int, N>{});
+}
+
 constexpr int kBN = 64;                       // keys per LDS tile
-constexpr int kRowBytes = kD * 2;             // 256 B per K/V row
 constexpr int kBlockBytes = 1040;             // one 1 KB load block + 16 B pad
-constexpr int kTileBytes = 16 * kBlockBytes;  // 16 blocks of 4 rows per K (or V) tile
-constexpr int kHalfBytes = 2 * kRowBytes;     // keys 32..63 of a tile sit 512 B after keys 0..31
+constexpr int kHalfBytes = 512;               // keys 32..63 of a tile sit 512 B after keys 0..31
 constexpr float kRescaleThreshold = 8.f;      // log2 units
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 // LDS block of key k (0..15 within its group of 16): bits (b3 b2 b1 b0) -> (b1 b0 b3 b2).
-__device__ __forceinline__ uint32_t key_block(uint32_t k) { return ((k & 3u) << 2) | ((k >> 2) & 3u); }
+__device__ __forceinline__ constexpr uint32_t key_block(uint32_t k) { return ((k & 3u) << 2) | ((k >> 2) & 3u); }
 // The key held by LDS block b (the same 2-bit rotation undoes itself).
-__device__ __forceinline__ uint32_t block_key(uint32_t b) { return ((b & 3u) << 2) | ((b >> 2) & 3u); }
-// Byte offset of 16-byte chunk `ch` of key `key` inside a K or V tile.
-__device__ __forceinline__ uint32_t tile_off(uint32_t key, uint32_t ch) {
-  return key_block(key & 15u) * kBlockBytes + (key >> 4) * kRowBytes + ch * 16u;
-}
+__device__ __forceinline__ constexpr uint32_t block_key(uint32_t b) { return ((b & 3u) << 2) | ((b >> 2) & 3u); }
+// Tile geometry for head dim D.
+template <int D>
+struct Geom {
+  static_assert(D == 128 || D == 192 || D == 256, "pipelined tiles cover head dims 128, 192 and 256");
+  static constexpr int kRowLds = D <= 128 ? 256 : 512;     // LDS bytes of one key row (192 padded to 512)
+  static constexpr int kRowsPerBlock = 1024 / kRowLds;      // 4 or 2
+  static constexpr int kBlocks = 64 / kRowsPerBlock;        // load blocks per tile: 16 or 32
+  static constexpr int kRuns = kBlocks / 16;                // runs of 16 blocks: 1 or 2
+  static constexpr int kTileBytes = kBlocks * kBlockBytes;
+  static constexpr int kLanesPerRow = kRowLds / 16;         // 16-byte pieces of an LDS row: 16 or 32
+  static constexpr int kRowPieces = D / 8;                  // the real ones: 16, 24 or 32
+  static constexpr int kQB = D / 16;                        // 16-wide d steps of S^T (Q fragments)
+  static constexpr int kOB = D / 32;                        // 32-wide d blocks of O^T
+  // Byte offset of 16-byte piece `ch` of key `key` (0..63) inside a K or V tile.
+  __device__ __forceinline__ static constexpr uint32_t tile_off(uint32_t key, uint32_t ch) {
+    return ((key >> 4) % kRuns * 16u + key_block(key & 15u)) * kBlockBytes + (key >> 4) / kRuns * kRowLds +
+           ch * 16u;
+  }
+  // The key held by row r of load block b (block_key reads b's low 4 bits).
+  __device__ __forceinline__ static constexpr uint32_t block_row_key(uint32_t b, uint32_t r) {
+    return 16u * ((kRuns == 1 ? 0u : b / 16u) + kRuns * r) + block_key(b);
+  }
+  // Offset of keys 16c.. from keys 0.., in 8-byte units (transposing V reads).
+  __device__ __forceinline__ static constexpr int chunk_units(int c) { return (int)(tile_off(16u * c, 0) / 8u); }
+};
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -60,15 +96,20 @@ __device__ __forceinline__ void wait_loads_barrier() {
 
 // This wave's share (blocks [b0, b0 + NB)) of one K or V tile. base: first row
 // of the tile (this kv head); rows >= nvalid (nvalid >= 1) re-read row nvalid-1.
-template <int NB>
+// Lane l writes row l / kLanesPerRow of the block, piece l % kLanesPerRow; the
+// padding pieces of a head_dim-192 row re-read its last real piece.
+template <int D, int NB>
 __device__ __forceinline__ void issue_tile(const uint16_t* base, uint32_t stride_bytes, int nvalid,
                                            uint32_t tile_lds, int b0, int lane) {
+  using G = Geom<D>;
+  const int piece = lane % G::kLanesPerRow;
+  const uint32_t pc = (uint32_t)(piece < G::kRowPieces ? piece : G::kRowPieces - 1) * 16u;
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     const int blk = b0 + t;
-    const int key = (int)block_key((uint32_t)blk) + 16 * (lane >> 4);
+    const int key = (int)G::block_row_key((uint32_t)blk, (uint32_t)(lane / G::kLanesPerRow));
     const int kc = key < nvalid ? key : nvalid - 1;
-    const uint32_t voff = (uint32_t)kc * stride_bytes + (uint32_t)(lane & 15) * 16u;
+    const uint32_t voff = (uint32_t)kc * stride_bytes + pc;
     load_lds16(base, voff, __builtin_amdgcn_readfirstlane(tile_lds + blk * kBlockBytes));
   }
 }
@@ -77,8 +118,11 @@ __device__ __forceinline__ void issue_tile(const uint16_t* base, uint32_t stride
 // wait counters do not see the direct-to-LDS loads, so a wait for Q that it
 // placed inside the tile loop (where the first use is, on paths that skip the
 // prologue's S^T) would also hold back the ring's prefetches in every step.
-__device__ __forceinline__ void settle_q(const bf16x8 (&q)[8]) {
-  asm volatile("" : : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7]));
+template <int QB>
+__device__ __forceinline__ void settle_q(const bf16x8 (&q)[QB]) {
+  static_assert(QB % 8 == 0 || QB == 12, "Q fragments come in 8s (and 12 at head_dim 192)");
+#pragma unroll
+  for (int b = 0; b < QB; b += 4) asm volatile("" : : "v"(q[b]), "v"(q[b + 1]), "v"(q[b + 2]), "v"(q[b + 3]));
 }
 
 // max / sum of a lane's value and lane (l ^ 32)'s, via one lane swap.
@@ -99,42 +143,50 @@ struct Lane {
   int n, g;
 };
 
+template <int D>
 __device__ __forceinline__ Lane make_lane(int lane, int key_off = 0) {
+  using Gm = Geom<D>;
   Lane L;
   L.n = lane & 31;
   L.g = lane >> 5;
   const uint32_t half = (uint32_t)(key_off >> 5) * kHalfBytes;
-  L.k_base = tile_off((uint32_t)L.n, (uint32_t)L.g) + half;
+  L.k_base = Gm::tile_off((uint32_t)L.n, (uint32_t)L.g) + half;
   // source lane (G, s) of a transposing read points at key 16c + 8h + 4(G/2) + s/4,
   // columns 32b + 16(G%2) + 4(s%4) .. +3
   const uint32_t G = (uint32_t)lane >> 4, s = (uint32_t)lane & 15u;
-  L.v_base = tile_off(4u * (G >> 1) + (s >> 2), 2u * (G & 1u) + ((s & 3u) >> 1)) + (s & 1u) * 8u + half;
+  L.v_base = Gm::tile_off(4u * (G >> 1) + (s >> 2), 2u * (G & 1u) + ((s & 3u) >> 1)) + (s & 1u) * 8u + half;
   return L;
 }
 
-// O^T (128 d x 32 queries) += V^T P^T over KB blocks of 32 keys. P chunk c
+// V^T operand of PV MFMA (chunk c, d-block b) for the transposing reads: key
+// + 8 sits two LDS blocks further (+ 2080 bytes), the 32 columns of d-block b
+// 64 bytes further per block.
+template <int D>
+__device__ __forceinline__ bf16x8 read_vt(const lds_bf16x4* base, int c, int b) {
+  const int off = Geom<D>::chunk_units(c) + 8 * b;  // in 8-byte units
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + off));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 260 + off));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// O^T (D d x 32 queries) += V^T P^T over KB blocks of 32 keys. P chunk c
 // holds keys 16c + 8*(i/4) + 4g + i%4 in k-slot (g, i); the transposing reads
-// deliver the matching V columns (key + 8 sits two LDS blocks further:
-// + 2080 bytes).
-template <int KB>
-__device__ __forceinline__ void pv(uint32_t vt, const Lane& L, const bf16x8 (&p)[2 * KB], f32x16 (&o)[4]) {
+// deliver the matching V columns.
+template <int D, int KB>
+__device__ __forceinline__ void pv(uint32_t vt, const Lane& L, const bf16x8 (&p)[2 * KB],
+                                   f32x16 (&o)[Geom<D>::kOB]) {
   const lds_bf16x4* base = (const lds_bf16x4*)(vt + L.v_base);
 #pragma unroll
   for (int c = 0; c < 2 * KB; ++c) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      // byte offsets 2080h + 256c + 64b, in 8-byte units
-      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 32 * c + 8 * b));
-      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 260 + 32 * c + 8 * b));
-      const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[b] = mfma32x32x16(a, p[c], o[b]);
-    }
+    for (int b = 0; b < Geom<D>::kOB; ++b) o[b] = mfma32x32x16(read_vt<D>(base, c, b), p[c], o[b]);
   }
 }
 
 // S^T for one tile: s[kb] = keys 32kb..32kb+31 of the wave's share x its 32 queries.
-template <int KB>
-__device__ __forceinline__ void qk(const char* kt, const Lane& L, const bf16x8 (&q)[8], f32x16 (&s)[KB]) {
+template <int D, int KB>
+__device__ __forceinline__ void qk(const char* kt, const Lane& L, const bf16x8 (&q)[Geom<D>::kQB],
+                                   f32x16 (&s)[KB]) {
   const char* base = kt + L.k_base;
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
@@ -142,7 +194,7 @@ __device__ __forceinline__ void qk(const char* kt, const Lane& L, const bf16x8 (
     for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
   }
 #pragma unroll
-  for (int db = 0; db < 8; ++db) {
+  for (int db = 0; db < Geom<D>::kQB; ++db) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const bf16x8 a = ld_lds16(base, kb * kHalfBytes + db * 32);
@@ -156,25 +208,23 @@ struct Softmax {
   float l;  // lane-partial sum of the unrounded probabilities
 };
 
-// V^T operand of PV MFMA (chunk c, d-block b) for the transposing reads of pv().
-__device__ __forceinline__ bf16x8 read_vt(const lds_bf16x4* base, int c, int b) {
-  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 32 * c + 8 * b));
-  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + 260 + 32 * c + 8 * b));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
 // Software-pipelined step for tile j of 64 keys (two 32-key halves per wave):
-// the softmax of tile j (s) runs under 32 MFMAs, the S^T of tile j+1 (sn, K from
-// nk) on even slots and, when PV, the O^T += V^T P^T of tile j-1 (P in p_prev,
-// V^T from vt_prev) on odd slots, so every MFMA has VALU work beside it. Slots
-// 0-5 carry the row maximum, slot 6 the reference update, slots 7-31 the 32
-// exp2. P of tile j goes to p_cur. O and the row sum are rescaled at the end
-// (after the PV of tile j-1, which still belongs to the old reference).
-template <bool PV, bool PRIO = false>
+// the softmax of tile j (s) runs under NS = D/4 MFMAs (32 at head_dim 128), the
+// S^T of tile j+1 (sn, K from nk) on even slots and, when PV, the
+// O^T += V^T P^T of tile j-1 (P in p_prev, V^T from vt_prev) on odd slots, so
+// every MFMA has VALU work beside it. Slots 0-5 carry the row maximum, slot 6
+// the reference update, slots 7 on the 32 exp2 (spread over the step). P of
+// tile j goes to p_cur. O and the row sum are rescaled at the end (after the
+// PV of tile j-1, which still belongs to the old reference).
+template <int D, bool PV, bool PRIO = false>
 __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], const char* nk, uint32_t vt_prev,
-                                             const Lane& L, const bf16x8 (&q)[8], const bf16x8 (&p_prev)[4],
-                                             bf16x8 (&p_cur)[4], f32x16 (&o)[4], Softmax& st, float c, bool mask,
-                                             int key0, int len_k, int lim) {
+                                             const Lane& L, const bf16x8 (&q)[Geom<D>::kQB],
+                                             const bf16x8 (&p_prev)[4], bf16x8 (&p_cur)[4],
+                                             f32x16 (&o)[Geom<D>::kOB], Softmax& st, float c, bool mask, int key0,
+                                             int len_k, int lim) {
+  constexpr int OB = Geom<D>::kOB;
+  constexpr int NT = 2 * Geom<D>::kQB;  // S^T MFMAs per step = PV MFMAs per step
+  constexpr int NS = 2 * NT;            // MFMA slots
   if (mask) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -200,7 +250,7 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   bf16x8 va[PF];
   if (PV) {
 #pragma unroll
-    for (int i = 0; i < PF; ++i) va[i] = read_vt(vbase, i >> 2, i & 3);
+    for (int i = 0; i < PF; ++i) va[i] = read_vt<D>(vbase, i / OB, i % OB);
   }
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -216,16 +266,18 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   // level 1 after them (kernels that run two workgroups per CU out of phase)
   if constexpr (PRIO) __builtin_amdgcn_s_setprio(2);
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int slot = 0; slot < 32; ++slot) {
+  // one instance per slot (a counted loop this long exceeds the unroller's
+  // size limit at head_dims 192 and 256)
+  static_for<NS>([&](auto slot_c) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
     const int t = slot >> 1;
     if ((slot & 1) == 0) {  // S^T of tile j+1: step t = (d-block t/2, key half t%2)
       sn[t & 1] = mfma32x32x16(kr[t % PF], q[t >> 1], sn[t & 1]);
-      if (t + PF < 16) kr[t % PF] = ld_lds16(kbase, ((t + PF) % 2) * kHalfBytes + ((t + PF) / 2) * 32);
-    } else if (PV) {  // PV of tile j-1: chunk t/4, d-block t%4
+      if (t + PF < NT) kr[t % PF] = ld_lds16(kbase, ((t + PF) % 2) * kHalfBytes + ((t + PF) / 2) * 32);
+    } else if (PV) {  // PV of tile j-1: chunk t/OB, d-block t%OB
       const bf16x8 a = va[t % PF];
-      if (t + PF < 16) va[t % PF] = read_vt(vbase, (t + PF) >> 2, (t + PF) & 3);
-      o[t & 3] = mfma32x32x16(a, p_prev[t >> 2], o[t & 3]);
+      if (t + PF < NT) va[t % PF] = read_vt<D>(vbase, (t + PF) / OB, (t + PF) % OB);
+      o[t % OB] = mfma32x32x16(a, p_prev[t / OB], o[t % OB]);
     }
     if (slot < 4) {  // row maximum: chain slot over 8 keys (2 slots per chain pair)
 #pragma unroll
@@ -244,12 +296,13 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
       m_ref = need ? m_new : st.m;
       ms = (m_ref == kNegInf ? 0.f : m_ref) * c;
     } else if (slot >= 7) {
-      // element x's exp2 runs in slot 7 + 3x/4 (slots 7..30); its row-sum add,
-      // and the bf16 packing of a finished chunk, one slot later, so that no
-      // VALU op waits on the exp2 issued just before it
+      // element x's exp2 runs in slot 7 + (3x/4) * NS/32 (slots 7..30 at
+      // head_dim 128); its row-sum add, and the bf16 packing of a finished
+      // chunk, one slot later, so that no VALU op waits on the exp2 issued
+      // just before it
 #pragma unroll
       for (int x = 0; x < 32; ++x) {
-        if (8 + (3 * x) / 4 == slot) {
+        if (8 + ((3 * x) / 4) * NS / 32 == slot) {
           const int u = x & 7;
           if (u & 1) {
             rs1 += e[u];
@@ -267,14 +320,14 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
       }
 #pragma unroll
       for (int x = 0; x < 32; ++x) {
-        if (7 + (3 * x) / 4 == slot) {
+        if (7 + ((3 * x) / 4) * NS / 32 == slot) {
           const int ch = x >> 3, u = x & 7;
           e[u] = hw_exp2(__builtin_fmaf(s[ch >> 1][8 * (ch & 1) + u], c, -ms));
         }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-  }
+  });
   if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
   const float rs = rs0 + rs1;
   st.l = st.l * alpha + rs;
@@ -283,7 +336,7 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   // takes part in the condition so that the exp2 stay in their slots.
   if (__builtin_amdgcn_ballot_w64(need || rs != rs) != 0ull) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) o[b] *= alpha;
+    for (int b = 0; b < OB; ++b) o[b] *= alpha;
   }
 }
 
@@ -292,7 +345,7 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
 // tile j-1 (8 MFMAs, P in p_prev, V^T from vt_prev) on odd slots. Slots 0-1
 // carry the two row-maximum chains, slot 2 the reference update, slots 3-14
 // the 16 exp2 (each row-sum add and bf16 packing one slot after its exp2).
-template <bool PV>
+template <bool PV>  // head_dim 128
 __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], const char* nk, uint32_t vt_prev,
                                               const Lane& L, const bf16x8 (&q)[8], const bf16x8 (&p_prev)[2],
                                               bf16x8 (&p_cur)[2], f32x16 (&o)[4], Softmax& st, float c, bool mask,
@@ -312,8 +365,8 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
   kr[1] = ld_lds16(kbase, 32);
   bf16x8 va[2];
   if (PV) {
-    va[0] = read_vt(vbase, 0, 0);
-    va[1] = read_vt(vbase, 0, 1);
+    va[0] = read_vt<128>(vbase, 0, 0);
+    va[1] = read_vt<128>(vbase, 0, 1);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) sn[0][r] = 0.f;
@@ -336,7 +389,7 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
       if (t + 2 < 8) kr[t & 1] = ld_lds16(kbase, (t + 2) * 32);
     } else if (PV) {  // PV of tile j-1: chunk t/4, d-block t%4
       const bf16x8 a = va[t & 1];
-      if (t + 2 < 8) va[t & 1] = read_vt(vbase, (t + 2) >> 2, (t + 2) & 3);
+      if (t + 2 < 8) va[t & 1] = read_vt<128>(vbase, (t + 2) >> 2, (t + 2) & 3);
       o[t & 3] = mfma32x32x16(a, p_prev[t >> 2], o[t & 3]);
     }
     if (slot < 2) {  // row maximum: chain slot over elements 8*slot .. +7
@@ -389,13 +442,14 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
 // Write the wave's 32 normalised output rows (bf16) and their LSE. o holds
 // O^T (d = 32b + 8*grp + 4g + i for element 4*grp + i of block b); st.l is
 // lane-partial.
-__device__ __forceinline__ void store_rows(const f32x16 (&o)[4], const Softmax& st, const Lane& L, float c,
+template <int OB>
+__device__ __forceinline__ void store_rows(const f32x16 (&o)[OB], const Softmax& st, const Lane& L, float c,
                                            bool live, uint16_t* orow, float* lse_out) {
   const float lt = pair_sum(st.l);
   if (!live) return;
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < OB; ++b) {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       f32x4 t;

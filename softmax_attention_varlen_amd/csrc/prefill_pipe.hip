@@ -1,56 +1,66 @@
-// Pipelined varlen prefill for head_dim 128 on gfx950.
+// Pipelined varlen prefill for head dims 128, 192 and 256 on gfx950.
 //
 // Work unit: one workgroup of NW waves owns NW*32 query rows of one document
 // and one query head; wave w owns rows [32w, 32w+32). K/V tiles of 64 keys
 // stream through a 4-stage LDS ring filled by direct-to-LDS loads (no VGPR
 // staging, no transpose on the way in), in the bank-conflict-free layout of
-// pipe_d128.hpp. The loop is software-pipelined: it runs the softmax of tile j
+// pipe.hpp. The loop is software-pipelined: it runs the softmax of tile j
 // under the S^T MFMAs of tile j+1 and the PV MFMAs of tile j-1. One barrier
 // per tile guards the ring. SPLIT replaces the ring by separate two-stage K
 // and V rings (at step j, K of tile j+2 and V of tile j are in flight while K
 // of tile j+1 and V of tile j-1 are read), which fit two 4-wave workgroups
-// per CU, and raises the issue priority of the loop (1) and of its MFMA slots
-// (2) above the prologue and store (0).
+// per CU at head_dim 128, and raises the issue priority of the loop (1) and of
+// its MFMA slots (2) above the prologue and store (0). At head_dims 192 and
+// 256 a tile takes twice the LDS (512-byte rows), so the split rings (130 KB)
+// fit one 4-wave workgroup per CU, whose O (up to 8 accumulator blocks) and Q
+// fragments (up to 16) take the whole register file of one wave per SIMD.
 #include <type_traits>
 
 #include "key_rows.hpp"
 #include "launch.hpp"
-#include "pipe_d128.hpp"
+#include "pipe.hpp"
 
 namespace attn {
 namespace {
 
 using namespace pipe;
-constexpr int kStageBytes = 2 * kTileBytes;  // K tile, then V tile
 
-template <int NW>
+template <int D, int NW>
 struct Ring {
-  static constexpr int IPW = 16 / NW;    // load blocks per wave per K (or V) tile
-  static constexpr int LOADS = 2 * IPW;  // per wave per tile (K and V)
-  static_assert(IPW * NW == 16, "waves must split the 16 load blocks evenly");
+  static constexpr int kTileBytes = Geom<D>::kTileBytes;
+  static constexpr int kStageBytes = 2 * kTileBytes;     // K tile, then V tile
+  static constexpr int IPW = Geom<D>::kBlocks / NW;      // load blocks per wave per K (or V) tile
+  static constexpr int LOADS = 2 * IPW;                  // per wave per tile (K and V)
+  static_assert(IPW * NW == Geom<D>::kBlocks, "waves must split the load blocks evenly");
 
   // Issue this wave's share of one K/V tile. kbase/vbase: first key row of the
   // tile (this kv head); rows >= nvalid re-read row nvalid-1.
   __device__ __forceinline__ static void issue(const uint16_t* kbase, const uint16_t* vbase, uint32_t stride_bytes,
                                                int nvalid, uint32_t stage_lds, int w, int lane) {
-    issue_tile<IPW>(kbase, stride_bytes, nvalid, stage_lds, w * IPW, lane);
-    issue_tile<IPW>(vbase, stride_bytes, nvalid, stage_lds + kTileBytes, w * IPW, lane);
+    issue_tile<D, IPW>(kbase, stride_bytes, nvalid, stage_lds, w * IPW, lane);
+    issue_tile<D, IPW>(vbase, stride_bytes, nvalid, stage_lds + kTileBytes, w * IPW, lane);
   }
 };
+
+// Workgroups per CU: two at head_dim 128 on the split rings, else one.
+template <int D, bool SPLIT>
+constexpr int kWgPerCu = (SPLIT && D == 128) ? 2 : 1;
 
 // PAGED: keys come from a paged cache (k, v = its K and V planes) through
 // block_tables, with context_lens[doc] (clamped to max_len_k) keys per
 // document; otherwise from contiguous rows delimited by cu_k. q_used / k_used
 // (nullable) cut each document to a valid prefix of its rows.
-template <bool CAUSAL, bool PAGED, int NW, bool SPLIT>
-__global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
+template <int D, bool CAUSAL, bool PAGED, int NW, bool SPLIT>
+__global__ __launch_bounds__(64 * NW, (kWgPerCu<D, SPLIT>)) void prefill_pipe_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k, int batch, int total_q, int total_k,
     int tiles_per_doc, int hq, int hkv, int n_items, int per_xcd, float c, uint16_t* __restrict__ out,
     float* __restrict__ lse, const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     int max_blocks_per_seq, int num_blocks, int max_len_k, const int32_t* __restrict__ q_used,
     const int32_t* __restrict__ k_used) {
-  using R = Ring<NW>;
+  using R = Ring<D, NW>;
+  constexpr int kTileBytes = R::kTileBytes, kStageBytes = R::kStageBytes;
+  constexpr int QB = Geom<D>::kQB, OB = Geom<D>::kOB;
   constexpr int BM = 32 * NW;
   // the pipelined loop keeps tile j-1's V while tile j+2 loads: 4 stages of K
   // and V; SPLIT: separate two-stage K and V rings (K stages 0, 1, then V
@@ -93,7 +103,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
   if (m0 >= len_q) return;
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const Lane L = make_lane(lane);
+  const Lane L = make_lane<D>(lane);
   const int diag = len_k - len_q;
   const int row = m0 + w * 32 + L.n;
   const int row_c = row < len_q ? row : len_q - 1;
@@ -117,20 +127,20 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
   const int ntiles_w = (n_end_w + kBN - 1) / kBN;
   const int nomask_w = n_full_w < 0 ? 0 : n_full_w / kBN;
 
-  const uint32_t stride_bytes = (uint32_t)hkv * kD * 2u;
-  const uint16_t* kb0 = k + ((long)k0 * hkv + hk) * kD;
-  const uint16_t* vb0 = v + ((long)k0 * hkv + hk) * kD;
-  const KeyRows<PAGED> rows{(long)hkv * kD, PAGED ? block_tables + (long)doc * max_blocks_per_seq : nullptr,
+  const uint32_t stride_bytes = (uint32_t)hkv * D * 2u;
+  const uint16_t* kb0 = k + ((long)k0 * hkv + hk) * D;
+  const uint16_t* vb0 = v + ((long)k0 * hkv + hk) * D;
+  const KeyRows<PAGED> rows{(long)hkv * D, PAGED ? block_tables + (long)doc * max_blocks_per_seq : nullptr,
                             num_blocks};
   const uint32_t ring = lds_u32(smem);
 
   // Q into registers first (the compiler's wait for these also covers the
   // ring loads issued after them, which the first tile needs anyway)
-  bf16x8 qr[8];
+  bf16x8 qr[QB];
   {
-    const uint16_t* qp = q + ((long)(q0 + row_c) * hq + h) * kD + L.g * 8;
+    const uint16_t* qp = q + ((long)(q0 + row_c) * hq + h) * D + L.g * 8;
 #pragma unroll
-    for (int b = 0; b < 8; ++b) qr[b] = as_bf16x8(ld_global16(qp + b * 16));
+    for (int b = 0; b < QB; ++b) qr[b] = as_bf16x8(ld_global16(qp + b * 16));
   }
   // prologue: the first two tiles in flight
   constexpr int PRE = 2;
@@ -139,16 +149,16 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
     if (SPLIT) {
       if (s < ntiles) {
         const long off = rows.row(s * kBN);
-        issue_tile<R::IPW>(kb0 + off, stride_bytes, len_k - s * kBN, ring + s * kTileBytes, w * R::IPW, lane);
+        issue_tile<D, R::IPW>(kb0 + off, stride_bytes, len_k - s * kBN, ring + s * kTileBytes, w * R::IPW, lane);
       }
     } else if (s < ntiles) {
       const long off = rows.row(s * kBN);
       R::issue(kb0 + off, vb0 + off, stride_bytes, len_k - s * kBN, ring + s * kStageBytes, w, lane);
     }
   }
-  f32x16 o[4];
+  f32x16 o[OB];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < OB; ++b) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[b][r] = 0.f;
   }
@@ -169,7 +179,7 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
     } else {
       wait_loads_barrier<0>();
     }
-    if (ntiles_w > 0) qk<2>(smem, L, qr, sa);
+    if (ntiles_w > 0) qk<D, 2>(smem, L, qr, sa);
   }
   settle_q(qr);
 
@@ -189,13 +199,13 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
         wait_loads_barrier<0>();
         if (j + 2 < ntiles) {
           const long off = rows.row((j + 2) * kBN);
-          issue_tile<R::IPW>(kb0 + off, stride_bytes, len_k - (j + 2) * kBN, ring + (j & 1) * kTileBytes,
-                             w * R::IPW, lane);
+          issue_tile<D, R::IPW>(kb0 + off, stride_bytes, len_k - (j + 2) * kBN, ring + (j & 1) * kTileBytes,
+                                w * R::IPW, lane);
         }
         {
           const long off = rows.row(j * kBN);
-          issue_tile<R::IPW>(vb0 + off, stride_bytes, len_k - j * kBN, ring + (2 + (j & 1)) * kTileBytes,
-                             w * R::IPW, lane);
+          issue_tile<D, R::IPW>(vb0 + off, stride_bytes, len_k - j * kBN, ring + (2 + (j & 1)) * kTileBytes,
+                                w * R::IPW, lane);
         }
         vt_prev = ring + (2 + ((j + 1) & 1)) * kTileBytes;
         nk = smem + ((j + 1) & 1) * kTileBytes;
@@ -214,10 +224,10 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
       if (j < ntiles_w) {
         const int key0 = j * kBN;
         const bool mask = !(j < nomask_w && key0 + kBN <= len_k);
-        tile_step_pp<HAS_PV, SPLIT>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, mask, key0, len_k,
-                             CAUSAL ? row + diag : 0x7fffffff);
+        tile_step_pp<D, HAS_PV, SPLIT>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, mask, key0, len_k,
+                                       CAUSAL ? row + diag : 0x7fffffff);
       } else if (HAS_PV && j == ntiles_w) {
-        pv<2>(vt_prev, L, pp, o);  // this wave's last tile
+        pv<D, 2>(vt_prev, L, pp, o);  // this wave's last tile
       }
     };
     using yes = std::integral_constant<bool, true>;
@@ -236,38 +246,41 @@ __global__ __launch_bounds__(64 * NW, SPLIT ? 2 : 1) void prefill_d128_kernel(
         const uint32_t vt = SPLIT ? ring + (2 + ((ntiles - 1) & 1)) * kTileBytes
                                   : ring + ((ntiles - 1) % 4) * kStageBytes + kTileBytes;
         if ((ntiles - 1) & 1) {
-          pv<2>(vt, L, pb, o);
+          pv<D, 2>(vt, L, pb, o);
         } else {
-          pv<2>(vt, L, pa, o);
+          pv<D, 2>(vt, L, pa, o);
         }
       }
     }
     if constexpr (SPLIT) __builtin_amdgcn_s_setprio(0);
-    store_rows(o, st, L, c, row < len_q, out + ((long)(q0 + row_c) * hq + h) * kD,
+    store_rows<OB>(o, st, L, c, row < len_q, out + ((long)(q0 + row_c) * hq + h) * D,
                lse != nullptr ? lse + (long)h * total_q + q0 + row_c : nullptr);
   }
 }
 
 }  // namespace
 
-bool prefill_d128_supported(const VarlenArgs& a) { return a.head_dim == 128; }
+bool prefill_pipe_supported(const VarlenArgs& a) {
+  return a.head_dim == 128 || a.head_dim == 192 || a.head_dim == 256;
+}
 
-// Keys from contiguous rows: 4-wave workgroups (128 query rows) on split
-// two-stage K and V rings (66.5 KB), two workgroups per CU out of phase, so
-// one workgroup's prologue and store run under the other's loop, with the
-// loop at raised issue priority. Keys from the paged cache: 8-wave workgroups
-// (256 rows) on the 4-stage ring, one per CU, which copies each K/V tile into
-// LDS for twice as many rows.
-template <bool CAUSAL, bool PAGED>
-static void launch_prefill_d128_t(const VarlenArgs& a, hipStream_t stream) {
-  constexpr bool SPLIT = !PAGED;
+// head_dim 128, keys from contiguous rows: 4-wave workgroups (128 query rows)
+// on split two-stage K and V rings (66.5 KB), two workgroups per CU out of
+// phase, so one workgroup's prologue and store run under the other's loop,
+// with the loop at raised issue priority. head_dim 128, keys from the paged
+// cache: 8-wave workgroups (256 rows) on the 4-stage ring, one per CU, which
+// copies each K/V tile into LDS for twice as many rows. head_dims 192 and 256:
+// 4-wave workgroups on the split rings (130 KB), one per CU, for both.
+template <int D, bool CAUSAL, bool PAGED>
+static void launch_prefill_pipe_t(const VarlenArgs& a, hipStream_t stream) {
+  constexpr bool SPLIT = !PAGED || D != 128;
   constexpr int NW = SPLIT ? 4 : 8;
   constexpr int BM = 32 * NW;
   const int tiles = (a.max_seqlen_q + BM - 1) / BM;
   const long n_items = (long)tiles * a.batch * a.num_heads;
   const long per_xcd = (n_items + 7) / 8;
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((prefill_d128_kernel<CAUSAL, PAGED, NW, SPLIT>),
+  hipLaunchKernelGGL((prefill_pipe_kernel<D, CAUSAL, PAGED, NW, SPLIT>),
                      dim3((unsigned)(per_xcd * 8)), dim3(64 * NW), 0, stream, (const uint16_t*)a.q,
                      (const uint16_t*)a.k, (const uint16_t*)a.v, a.cu_q, a.cu_k, a.batch, a.total_q, a.total_k, tiles,
                      a.num_heads, a.num_kv_heads, (int)n_items, (int)per_xcd, c, (uint16_t*)a.out, a.lse,
@@ -275,17 +288,34 @@ static void launch_prefill_d128_t(const VarlenArgs& a, hipStream_t stream) {
                      PAGED ? nullptr : a.k_used);
 }
 
-hipError_t launch_prefill_d128(const VarlenArgs& a, hipStream_t stream) {
+template <int D>
+static void launch_prefill_pipe_d(const VarlenArgs& a, hipStream_t stream) {
   if (a.paged) {
     if (a.causal) {
-      launch_prefill_d128_t<true, true>(a, stream);
+      launch_prefill_pipe_t<D, true, true>(a, stream);
     } else {
-      launch_prefill_d128_t<false, true>(a, stream);
+      launch_prefill_pipe_t<D, false, true>(a, stream);
     }
   } else if (a.causal) {
-    launch_prefill_d128_t<true, false>(a, stream);
+    launch_prefill_pipe_t<D, true, false>(a, stream);
   } else {
-    launch_prefill_d128_t<false, false>(a, stream);
+    launch_prefill_pipe_t<D, false, false>(a, stream);
+  }
+}
+
+hipError_t launch_prefill_pipe(const VarlenArgs& a, hipStream_t stream) {
+  switch (a.head_dim) {
+    case 128:
+      launch_prefill_pipe_d<128>(a, stream);
+      break;
+    case 192:
+      launch_prefill_pipe_d<192>(a, stream);
+      break;
+    case 256:
+      launch_prefill_pipe_d<256>(a, stream);
+      break;
+    default:
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

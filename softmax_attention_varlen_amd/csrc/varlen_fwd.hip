@@ -1,4 +1,5 @@
-// Packed variable-length attention prefill for gfx950.
+// Packed variable-length attention prefill for gfx950 at head_dims 64 and 96
+// (128, 192 and 256 take the pipelined kernels of prefill_pipe.hip).
 //
 // Work unit: one workgroup of 4 waves owns a 128-row query tile of one
 // document and one query head; each wave owns 32 query rows. K/V tiles of 64
@@ -152,7 +153,7 @@ static hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_varlen_fwd(const VarlenArgs& a, hipStream_t stream) {
-  if (prefill_d128_supported(a)) return launch_prefill_d128(a, stream);
+  if (prefill_pipe_supported(a)) return launch_prefill_pipe(a, stream);
   const bool causal = a.causal != 0;
 #define ATTN_VARLEN_CASE(DIM)                                                              \
   case DIM:                                                                                \
@@ -160,9 +161,6 @@ hipError_t launch_varlen_fwd(const VarlenArgs& a, hipStream_t stream) {
   switch (a.head_dim) {
     ATTN_VARLEN_CASE(64)
     ATTN_VARLEN_CASE(96)
-    ATTN_VARLEN_CASE(128)
-    ATTN_VARLEN_CASE(192)
-    ATTN_VARLEN_CASE(256)
     default:
       return hipErrorInvalidValue;
   }

@@ -1,7 +1,7 @@
 """Bit-exact indexing probes through the kernels the full-size workloads run:
 the head_dim-128 streaming paged decode (plain, sliding-window and the
-speculative multi-token columns), the head_dim-128 prefill kernel reading keys
-from the paged cache, and the head_dim-128 block-sparse kernel with its packed
+speculative multi-token columns), the pipelined prefill kernel reading keys
+from the paged cache (head_dims 128, 192, 256), and the head_dim-128 block-sparse kernel with its packed
 kept-tile lists.
 
 Construction, shared by every probe: one selected key per unit (sequence or
@@ -37,8 +37,9 @@ SLOTS = [0, 31, 32, 33, 63, 64, 95, 96, 127, 1, 17, 100]
 
 def _probe_cache(tables, ctx, lo, num_blocks, hkv, d):
     """[2, NB, 128, hkv, d] bf16 on the GPU: value rows hold (block % 256,
-    block // 256, slot, head); keys are 0 on the visible tokens [lo[b], ctx[b])
-    of every sequence and 8 (poison) on every other slot."""
+    block // 256, slot, head) and then column index % 200 (so a row read with
+    its 16-byte pieces out of place differs); keys are 0 on the visible tokens
+    [lo[b], ctx[b]) of every sequence and 8 (poison) on every other slot."""
     nb = num_blocks
     kv = torch.zeros((2, nb, 128, hkv, d), dtype=BF16)
     blk = torch.arange(nb)
@@ -46,6 +47,7 @@ def _probe_cache(tables, ctx, lo, num_blocks, hkv, d):
     kv[1, :, :, :, 1] = (blk // 256).view(nb, 1, 1).to(BF16)
     kv[1, :, :, :, 2] = torch.arange(128).view(1, 128, 1).to(BF16)
     kv[1, :, :, :, 3] = torch.arange(hkv).view(1, 1, hkv).to(BF16)
+    kv[1, :, :, :, 4:] = (torch.arange(4, d) % 200).to(BF16)
     kv[0] = 8.0
     for b, L in enumerate(ctx):
         if L > lo[b]:
@@ -140,8 +142,7 @@ def test_sliding_window_decode_probe(window, d):
     _decode_probe(DECODE_CTX, 32, 8, d, seed=260 + window % 89 + d, window=window)
 
 
-def _paged_prefill_probe(ctx, qlens, hq, hkv, seed):
-    d = 128
+def _paged_prefill_probe(ctx, qlens, hq, hkv, seed, d=128):
     case = paged_case(ctx, num_heads=hq, num_kv_heads=hkv, head_dim=d, seed=seed, spare_blocks=5,
                       max_blocks_per_seq=-(-max(ctx) // 128) + 2, name=f"probe-pp-{seed}")
     group = hq // hkv
@@ -190,13 +191,16 @@ def test_speculative_columns_probe_every_block_position():
     assert exact > 0
 
 
-def test_paged_prefill_kernel_probe_every_block_position():
-    """Long query runs take the head_dim-128 prefill kernel with keys read
-    through the block table (64-key tiles, one table lookup each)."""
+@pytest.mark.parametrize("d", [128, 192, 256])
+def test_paged_prefill_kernel_probe_every_block_position(d):
+    """Long query runs take the pipelined prefill kernel with keys read
+    through the block table (64-key tiles, one table lookup each): the 8-wave
+    ring at head_dim 128, the 4-wave split rings with 512-byte LDS rows at 192
+    (rows padded) and 256."""
     ctx = [300, 1000, 4100, 129, 2000, 64]
     qlens = [300, 17, 100, 129, 64, 1]
-    announce("probe paged prefill")
-    exact = _paged_prefill_probe(ctx, qlens, 8, 2, seed=290)
+    announce("probe paged prefill", d)
+    exact = _paged_prefill_probe(ctx, qlens, 8, 2, seed=290 + d, d=d)
     assert exact > 0
 
 

@@ -96,14 +96,15 @@ def test_guard_canaries():
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 192, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_indexing_probe_bit_exact(causal, d):
     """K = 0 except one selected key per (doc, head) with a logit at least 512
     above the rest; every row that can see it must return that key's V
-    bit-exactly, and V encodes (doc, token) so a wrong cu_seqlens offset is
-    visible. head_dim 128 runs the pipelined kernels (128-row items with split
-    K/V rings under the causal mask, 256-row items without)."""
+    bit-exactly, and V encodes (doc, token) and then the column index, so a
+    wrong cu_seqlens offset or a misplaced 16-byte piece is visible. head_dims
+    128, 192 and 256 run the pipelined kernels (128-row items on split K/V
+    rings; 512-byte LDS rows at 192, padded, and 256)."""
     lens = [3, 129, 64, 250, 1, 385]
     hq = hkv = 3
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
@@ -122,6 +123,7 @@ def test_indexing_probe_bit_exact(causal, d):
             v[cu[b] + t, :, 1] = t % 128
             v[cu[b] + t, :, 2] = t // 128
             v[cu[b] + t, :, 3] = torch.arange(hkv)
+            v[cu[b] + t, :, 4:] = (torch.arange(4, d) % 200).to(torch.bfloat16)
     announce("varlen probe", causal, d)
     out = sav.attn_varlen_fwd(dev(q), dev(k), dev(v), dev(cu), dev(cu), max(lens), max(lens), 0.125, causal)
     torch.cuda.synchronize()
