@@ -98,21 +98,37 @@ __device__ __forceinline__ void wait_loads_barrier() {
 // of the tile (this kv head); rows >= nvalid (nvalid >= 1) re-read row nvalid-1.
 // Lane l writes row l / kLanesPerRow of the block, piece l % kLanesPerRow; the
 // padding pieces of a head_dim-192 row re-read its last real piece.
-template <int D, int NB>
-__device__ __forceinline__ void issue_tile(const uint16_t* base, uint32_t stride_bytes, int nvalid,
-                                           uint32_t tile_lds, int b0, int lane) {
+template <int D>
+__device__ __forceinline__ void issue_block(const uint16_t* base, uint32_t stride_bytes, int nvalid,
+                                            uint32_t tile_lds, int blk, int lane) {
   using G = Geom<D>;
   const int piece = lane % G::kLanesPerRow;
   const uint32_t pc = (uint32_t)(piece < G::kRowPieces ? piece : G::kRowPieces - 1) * 16u;
-#pragma unroll
-  for (int t = 0; t < NB; ++t) {
-    const int blk = b0 + t;
-    const int key = (int)G::block_row_key((uint32_t)blk, (uint32_t)(lane / G::kLanesPerRow));
-    const int kc = key < nvalid ? key : nvalid - 1;
-    const uint32_t voff = (uint32_t)kc * stride_bytes + pc;
-    load_lds16(base, voff, __builtin_amdgcn_readfirstlane(tile_lds + blk * kBlockBytes));
-  }
+  const int key = (int)G::block_row_key((uint32_t)blk, (uint32_t)(lane / G::kLanesPerRow));
+  const int kc = key < nvalid ? key : nvalid - 1;
+  const uint32_t voff = (uint32_t)kc * stride_bytes + pc;
+  load_lds16(base, voff, __builtin_amdgcn_readfirstlane(tile_lds + blk * kBlockBytes));
 }
+template <int D, int NB>
+__device__ __forceinline__ void issue_tile(const uint16_t* base, uint32_t stride_bytes, int nvalid,
+                                           uint32_t tile_lds, int b0, int lane) {
+#pragma unroll
+  for (int t = 0; t < NB; ++t) issue_block<D>(base, stride_bytes, nvalid, tile_lds, b0 + t, lane);
+}
+
+// p, which is the same in every lane, in scalar registers (for load bases the
+// compiler cannot prove uniform).
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t b = (uint64_t)(uintptr_t)p;
+  return (const uint16_t*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b));
+}
+
+// A per-slot hook of tile_step_pp that does nothing.
+struct NoHook {
+  template <typename S>
+  __device__ __forceinline__ void operator()(S) const {}
+};
 
 // Retire the loads of the Q fragments here, on every path. The compiler's
 // wait counters do not see the direct-to-LDS loads, so a wait for Q that it
@@ -215,13 +231,14 @@ struct Softmax {
 // every MFMA has VALU work beside it. Slots 0-5 carry the row maximum, slot 6
 // the reference update, slots 7 on the 32 exp2 (spread over the step). P of
 // tile j goes to p_cur. O and the row sum are rescaled at the end (after the
-// PV of tile j-1, which still belongs to the old reference).
-template <int D, bool PV, bool PRIO = false>
+// PV of tile j-1, which still belongs to the old reference). hook(slot) runs
+// at the start of every slot (the caller's load issue, say).
+template <int D, bool PV, bool PRIO = false, typename Hook = NoHook>
 __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], const char* nk, uint32_t vt_prev,
                                              const Lane& L, const bf16x8 (&q)[Geom<D>::kQB],
                                              const bf16x8 (&p_prev)[4], bf16x8 (&p_cur)[4],
                                              f32x16 (&o)[Geom<D>::kOB], Softmax& st, float c, bool mask, int key0,
-                                             int len_k, int lim) {
+                                             int len_k, int lim, Hook hook = Hook{}) {
   constexpr int OB = Geom<D>::kOB;
   constexpr int NT = 2 * Geom<D>::kQB;  // S^T MFMAs per step = PV MFMAs per step
   constexpr int NS = 2 * NT;            // MFMA slots
@@ -270,6 +287,7 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   // size limit at head_dims 192 and 256)
   static_for<NS>([&](auto slot_c) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
+    hook(slot_c);
     const int t = slot >> 1;
     if ((slot & 1) == 0) {  // S^T of tile j+1: step t = (d-block t/2, key half t%2)
       sn[t & 1] = mfma32x32x16(kr[t % PF], q[t >> 1], sn[t & 1]);

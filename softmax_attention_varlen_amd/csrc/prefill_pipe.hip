@@ -133,6 +133,7 @@ __global__ __launch_bounds__(64 * NW, (kWgPerCu<D, SPLIT>)) void prefill_pipe_ke
   const KeyRows<PAGED> rows{(long)hkv * D, PAGED ? block_tables + (long)doc * max_blocks_per_seq : nullptr,
                             num_blocks};
   const uint32_t ring = lds_u32(smem);
+  constexpr bool kLateLoads = SPLIT && D != 128;
 
   // Q into registers first (the compiler's wait for these also covers the
   // ring loads issued after them, which the first tile needs anyway)
@@ -193,10 +194,17 @@ __global__ __launch_bounds__(64 * NW, (kWgPerCu<D, SPLIT>)) void prefill_pipe_ke
       constexpr bool HAS_PV = decltype(pv_tag)::value;
       uint32_t vt_prev;
       const char* nk;
+      // SPLIT at head_dims 192/256 (one workgroup per CU): a wave with a tile
+      // to process issues its loads from inside the step, in its first slots,
+      // under the MFMAs (see below); before the step they had nothing to hide
+      // under (+3 % at 192, +8 % at 256)
+      const bool late = kLateLoads && j < ntiles_w;
       if (SPLIT) {
         // K of tile j+2 into the K stage of tile j (its S^T ran in step j-1),
         // V of tile j into the V stage of tile j-2 (its PV ran in step j-1)
         wait_loads_barrier<0>();
+      }
+      if (SPLIT && !late) {
         if (j + 2 < ntiles) {
           const long off = rows.row((j + 2) * kBN);
           issue_tile<D, R::IPW>(kb0 + off, stride_bytes, len_k - (j + 2) * kBN, ring + (j & 1) * kTileBytes,
@@ -207,6 +215,8 @@ __global__ __launch_bounds__(64 * NW, (kWgPerCu<D, SPLIT>)) void prefill_pipe_ke
           issue_tile<D, R::IPW>(vb0 + off, stride_bytes, len_k - j * kBN, ring + (2 + (j & 1)) * kTileBytes,
                                 w * R::IPW, lane);
         }
+      }
+      if (SPLIT) {
         vt_prev = ring + (2 + ((j + 1) & 1)) * kTileBytes;
         nk = smem + ((j + 1) & 1) * kTileBytes;
       } else {
@@ -224,8 +234,37 @@ __global__ __launch_bounds__(64 * NW, (kWgPerCu<D, SPLIT>)) void prefill_pipe_ke
       if (j < ntiles_w) {
         const int key0 = j * kBN;
         const bool mask = !(j < nomask_w && key0 + kBN <= len_k);
-        tile_step_pp<D, HAS_PV, SPLIT>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, mask, key0, len_k,
-                                       CAUSAL ? row + diag : 0x7fffffff);
+        if constexpr (kLateLoads) {
+          // past the last tile the K loads re-read tile j into its own stage
+          // (free, and read by nothing after), which keeps branches out of
+          // the slots
+          const int jk = j + 2 < ntiles ? j + 2 : j;
+          const uint16_t* kt = uniform_ptr(kb0 + rows.row(jk * kBN));
+          const uint16_t* vtile = uniform_ptr(vb0 + rows.row(j * kBN));
+          const int k_valid = len_k - jk * kBN, v_valid = len_k - j * kBN;
+          const uint32_t k_lds = ring + (j & 1) * kTileBytes, v_lds = ring + (2 + (j & 1)) * kTileBytes;
+          // load i (K blocks, then V blocks) in slot i at head_dim 192 and in
+          // slot 2i + 1 at 256 (measured against each other and against
+          // spreading the loads over the whole step, which left them too
+          // little time to land: -5 to -6 %)
+          constexpr int kGap = D == 256 ? 2 : 1;
+          auto loads = [&](auto slot_c) __attribute__((always_inline)) {
+            constexpr int slot = decltype(slot_c)::value;
+            constexpr int i = (slot - (kGap - 1)) / kGap;
+            if constexpr (slot >= kGap - 1 && (slot - (kGap - 1)) % kGap == 0 && i < 2 * R::IPW) {
+              if constexpr (i < R::IPW) {
+                issue_block<D>(kt, stride_bytes, k_valid, k_lds, w * R::IPW + i, lane);
+              } else {
+                issue_block<D>(vtile, stride_bytes, v_valid, v_lds, w * R::IPW + i - R::IPW, lane);
+              }
+            }
+          };
+          tile_step_pp<D, HAS_PV, SPLIT>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, mask, key0, len_k,
+                                         CAUSAL ? row + diag : 0x7fffffff, loads);
+        } else {
+          tile_step_pp<D, HAS_PV, SPLIT>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, mask, key0, len_k,
+                                         CAUSAL ? row + diag : 0x7fffffff);
+        }
       } else if (HAS_PV && j == ntiles_w) {
         pv<D, 2>(vt_prev, L, pp, o);  // this wave's last tile
       }
