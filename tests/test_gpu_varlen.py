@@ -158,6 +158,22 @@ def test_random_varlen_head_dim_128(seed):
     check_full(case, few_keys=True)
 
 
+@pytest.mark.parametrize("d,causal", [(192, False), (256, False), (256, True)])
+def test_head_dim_full_size_every_row(d, causal):
+    """Head dims 192 and 256 on the shape their throughput is measured on (2
+    documents of 4096 rows, 24 heads, N(0,1) inputs), every row and head
+    against the oracle: the pipelined kernel with 512-byte LDS rows and its
+    loads issued from inside the step."""
+    case = varlen_case([4096, 4096], num_heads=24, num_kv_heads=24, head_dim=d, causal=causal, seed=7700 + d + causal,
+                       name=f"dit-dense-b2-s4096-h24-d{d}" + ("-causal" if causal else ""))
+    announce("varlen full-size", case.name)
+    out, lse = run_case(case)
+    ref_o, ref_l = oracle.varlen_attention(case.q, case.k, case.v, case.cu_seqlens_q, case.cu_seqlens_k, case.scale,
+                                           case.causal)
+    assert_close("out", host(out), ref_o, OUT_TOL, bf16_output=True)
+    assert_close("lse", host(lse), ref_l, LSE_TOL)
+
+
 @pytest.mark.parametrize("make", [config2, config3])
 def test_full_size_config_every_row(make):
     """Configs 2 and 3 at full size, every row and head against the oracle."""
