@@ -46,11 +46,12 @@ def test_sweep_ragged(d, causal, hq, hkv):
     check_full(case, few_keys=True)
 
 
+@pytest.mark.parametrize("d", [128, 256])
 @pytest.mark.parametrize("causal", [False, True])
-def test_cross_lengths_bottom_right(causal):
+def test_cross_lengths_bottom_right(causal, d):
     # Lq != Lk per document, including Lq > Lk (rows with no key under causal)
-    case = varlen_case([5, 200, 130, 70], [77, 150, 130, 1], num_heads=4, num_kv_heads=2, head_dim=128,
-                       causal=causal, seed=41)
+    case = varlen_case([5, 200, 130, 70], [77, 150, 130, 1], num_heads=4, num_kv_heads=2, head_dim=d,
+                       causal=causal, seed=41 + (d - 128))
     check_full(case, few_keys=True)
 
 
@@ -60,16 +61,17 @@ def test_empty_documents():
     check_full(case, few_keys=True)
 
 
-@pytest.mark.parametrize("batch", [511, 512, 700])
+@pytest.mark.parametrize("batch,d", [(511, 128), (512, 128), (700, 128), (300, 192), (300, 256)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_many_documents(batch, causal):
+def test_many_documents(batch, causal, d):
     # hundreds of documents, most shorter than one 256-row query tile (many
     # empty workgroup slots), a few spanning several tiles, some empty
     rng = np.random.default_rng(batch + causal)
     lens = rng.integers(0, 96, batch)
     lens[rng.choice(batch, 5, replace=False)] = [257, 300, 513, 700, 1]
     lens[rng.choice(batch, 20, replace=False)] = 0
-    case = varlen_case(lens.tolist(), num_heads=4, num_kv_heads=2, head_dim=128, causal=causal, seed=44 + batch)
+    case = varlen_case(lens.tolist(), num_heads=4, num_kv_heads=2, head_dim=d, causal=causal,
+                       seed=44 + batch + (d - 128))
     check_full(case, few_keys=True)
 
 
