@@ -51,8 +51,7 @@ TRAFFIC = {
              "sources": _VARLEN_SRC, "sha256": "730fe5a387d4c6c3"},
     "dense_d64": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 66862.2, "write_kib": 25344.0,
                   "sources": _VARLEN_SRC, "sha256": "730fe5a387d4c6c3"},
-    "dense_d96": {"kernel": "varlen_fwd_kernel<96,false,false>", "fetch_kib": 172092.6, "write_kib": 37988.3,
-                  "sources": _VARLEN_SRC, "sha256": "730fe5a387d4c6c3"},
+    "dense_d96": {"kernel": "prefill_pipe_kernel<96,false,false,4,true>"},
     "dense_d192": {"kernel": "prefill_pipe_kernel<192,false,false,4,true>", "fetch_kib": 110851.1, "write_kib": 74496.2,
                    "sources": _PREFILL_SRC, "sha256": "1a9005f127bab94b"},
     "dense_d256": {"kernel": "prefill_pipe_kernel<256,false,false,4,true>", "fetch_kib": 149573.8,

@@ -54,7 +54,7 @@ __device__ __forceinline__ constexpr uint32_t block_key(uint32_t b) { return ((b
 // Tile geometry for head dim D.
 template <int D>
 struct Geom {
-  static_assert(D == 128 || D == 192 || D == 256, "pipelined tiles cover head dims 128, 192 and 256");
+  static_assert(D == 96 || D == 128 || D == 192 || D == 256, "pipelined tiles cover head dims 96 to 256");
   static constexpr int kRowLds = D <= 128 ? 256 : 512;     // LDS bytes of one key row (192 padded to 512)
   static constexpr int kRowsPerBlock = 1024 / kRowLds;      // 4 or 2
   static constexpr int kBlocks = 64 / kRowsPerBlock;        // load blocks per tile: 16 or 32
@@ -136,9 +136,13 @@ struct NoHook {
 // prologue's S^T) would also hold back the ring's prefetches in every step.
 template <int QB>
 __device__ __forceinline__ void settle_q(const bf16x8 (&q)[QB]) {
-  static_assert(QB % 8 == 0 || QB == 12, "Q fragments come in 8s (and 12 at head_dim 192)");
+  if constexpr (QB % 4 == 0) {
 #pragma unroll
-  for (int b = 0; b < QB; b += 4) asm volatile("" : : "v"(q[b]), "v"(q[b + 1]), "v"(q[b + 2]), "v"(q[b + 3]));
+    for (int b = 0; b < QB; b += 4) asm volatile("" : : "v"(q[b]), "v"(q[b + 1]), "v"(q[b + 2]), "v"(q[b + 3]));
+  } else {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) asm volatile("" : : "v"(q[b]));
+  }
 }
 
 // max / sum of a lane's value and lane (l ^ 32)'s, via one lane swap.
@@ -242,6 +246,10 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   constexpr int OB = Geom<D>::kOB;
   constexpr int NT = 2 * Geom<D>::kQB;  // S^T MFMAs per step = PV MFMAs per step
   constexpr int NS = 2 * NT;            // MFMA slots
+  // slot of element x's exp2: spread over slots 7 .. 7 + 23*NS/32 with 32 or
+  // more slots, two per slot over slots 7..22 with the 24 slots of head_dim 96
+  auto exp_slot = [](int x) constexpr { return NS >= 32 ? 7 + ((3 * x) / 4) * NS / 32 : 7 + x / 2; };
+  static_assert(NS >= 24, "the softmax needs 24 MFMA slots per step");
   if (mask) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -314,13 +322,12 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
       m_ref = need ? m_new : st.m;
       ms = (m_ref == kNegInf ? 0.f : m_ref) * c;
     } else if (slot >= 7) {
-      // element x's exp2 runs in slot 7 + (3x/4) * NS/32 (slots 7..30 at
-      // head_dim 128); its row-sum add, and the bf16 packing of a finished
-      // chunk, one slot later, so that no VALU op waits on the exp2 issued
-      // just before it
+      // element x's exp2 runs in slot exp_slot(x) (slots 7..30 at head_dim
+      // 128); its row-sum add, and the bf16 packing of a finished chunk, one
+      // slot later, so that no VALU op waits on the exp2 issued just before it
 #pragma unroll
       for (int x = 0; x < 32; ++x) {
-        if (8 + ((3 * x) / 4) * NS / 32 == slot) {
+        if (exp_slot(x) + 1 == slot) {
           const int u = x & 7;
           if (u & 1) {
             rs1 += e[u];
@@ -338,7 +345,7 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
       }
 #pragma unroll
       for (int x = 0; x < 32; ++x) {
-        if (7 + ((3 * x) / 4) * NS / 32 == slot) {
+        if (exp_slot(x) == slot) {
           const int ch = x >> 3, u = x & 7;
           e[u] = hw_exp2(__builtin_fmaf(s[ch >> 1][8 * (ch & 1) + u], c, -ms));
         }

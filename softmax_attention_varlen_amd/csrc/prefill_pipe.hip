@@ -1,4 +1,4 @@
-// Pipelined varlen prefill for head dims 128, 192 and 256 on gfx950.
+// Pipelined varlen prefill for head dims 96, 128, 192 and 256 on gfx950.
 //
 // Work unit: one workgroup of NW waves owns NW*32 query rows of one document
 // and one query head; wave w owns rows [32w, 32w+32). K/V tiles of 64 keys
@@ -9,11 +9,12 @@
 // per tile guards the ring. SPLIT replaces the ring by separate two-stage K
 // and V rings (at step j, K of tile j+2 and V of tile j are in flight while K
 // of tile j+1 and V of tile j-1 are read), which fit two 4-wave workgroups
-// per CU at head_dim 128, and raises the issue priority of the loop (1) and of
-// its MFMA slots (2) above the prologue and store (0). At head_dims 192 and
-// 256 a tile takes twice the LDS (512-byte rows), so the split rings (130 KB)
-// fit one 4-wave workgroup per CU, whose O (up to 8 accumulator blocks) and Q
-// fragments (up to 16) take the whole register file of one wave per SIMD.
+// per CU at head_dims 96 and 128 (96 pads its rows to 256 bytes in LDS), and
+// raises the issue priority of the loop (1) and of its MFMA slots (2) above
+// the prologue and store (0). At head_dims 192 and 256 a tile takes twice the
+// LDS (512-byte rows), so the split rings (130 KB) fit one 4-wave workgroup per
+// CU, whose O (up to 8 accumulator blocks) and Q fragments (up to 16) take the
+// whole register file of one wave per SIMD.
 #include <type_traits>
 
 #include "key_rows.hpp"
@@ -42,9 +43,9 @@ struct Ring {
   }
 };
 
-// Workgroups per CU: two at head_dim 128 on the split rings, else one.
+// Workgroups per CU: two at head_dims 96 and 128 on the split rings, else one.
 template <int D, bool SPLIT>
-constexpr int kWgPerCu = (SPLIT && D == 128) ? 2 : 1;
+constexpr int kWgPerCu = (SPLIT && D <= 128) ? 2 : 1;
 
 // PAGED: keys come from a paged cache (k, v = its K and V planes) through
 // block_tables, with context_lens[doc] (clamped to max_len_k) keys per
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(64 * NW, (kWgPerCu<D, SPLIT>)) void prefill_pipe_ke
   const KeyRows<PAGED> rows{(long)hkv * D, PAGED ? block_tables + (long)doc * max_blocks_per_seq : nullptr,
                             num_blocks};
   const uint32_t ring = lds_u32(smem);
-  constexpr bool kLateLoads = SPLIT && D != 128;
+  constexpr bool kLateLoads = SPLIT && D > 128;
 
   // Q into registers first (the compiler's wait for these also covers the
   // ring loads issued after them, which the first tile needs anyway)
@@ -300,19 +301,19 @@ __global__ __launch_bounds__(64 * NW, (kWgPerCu<D, SPLIT>)) void prefill_pipe_ke
 }  // namespace
 
 bool prefill_pipe_supported(const VarlenArgs& a) {
-  return a.head_dim == 128 || a.head_dim == 192 || a.head_dim == 256;
+  return a.head_dim == 96 || a.head_dim == 128 || a.head_dim == 192 || a.head_dim == 256;
 }
 
-// head_dim 128, keys from contiguous rows: 4-wave workgroups (128 query rows)
-// on split two-stage K and V rings (66.5 KB), two workgroups per CU out of
-// phase, so one workgroup's prologue and store run under the other's loop,
-// with the loop at raised issue priority. head_dim 128, keys from the paged
-// cache: 8-wave workgroups (256 rows) on the 4-stage ring, one per CU, which
-// copies each K/V tile into LDS for twice as many rows. head_dims 192 and 256:
-// 4-wave workgroups on the split rings (130 KB), one per CU, for both.
+// head_dims 96 and 128, keys from contiguous rows: 4-wave workgroups (128
+// query rows) on split two-stage K and V rings (66.5 KB), two workgroups per
+// CU out of phase, so one workgroup's prologue and store run under the other's
+// loop, with the loop at raised issue priority. Keys from the paged cache:
+// 8-wave workgroups (256 rows) on the 4-stage ring, one per CU, which copies
+// each K/V tile into LDS for twice as many rows. head_dims 192 and 256: 4-wave
+// workgroups on the split rings (130 KB), one per CU, for both.
 template <int D, bool CAUSAL, bool PAGED>
 static void launch_prefill_pipe_t(const VarlenArgs& a, hipStream_t stream) {
-  constexpr bool SPLIT = !PAGED || D != 128;
+  constexpr bool SPLIT = !PAGED || D > 128;
   constexpr int NW = SPLIT ? 4 : 8;
   constexpr int BM = 32 * NW;
   const int tiles = (a.max_seqlen_q + BM - 1) / BM;
@@ -344,6 +345,9 @@ static void launch_prefill_pipe_d(const VarlenArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill_pipe(const VarlenArgs& a, hipStream_t stream) {
   switch (a.head_dim) {
+    case 96:
+      launch_prefill_pipe_d<96>(a, stream);
+      break;
     case 128:
       launch_prefill_pipe_d<128>(a, stream);
       break;

@@ -1,5 +1,5 @@
-// Packed variable-length attention prefill for gfx950 at head_dims 64 and 96
-// (128, 192 and 256 take the pipelined kernels of prefill_pipe.hip).
+// Packed variable-length attention prefill for gfx950 at head_dim 64 (96, 128,
+// 192 and 256 take the pipelined kernels of prefill_pipe.hip).
 //
 // Work unit: one workgroup of 4 waves owns a 128-row query tile of one
 // document and one query head; each wave owns 32 query rows. K/V tiles of 64
@@ -160,7 +160,6 @@ hipError_t launch_varlen_fwd(const VarlenArgs& a, hipStream_t stream) {
     return causal ? launch_varlen<DIM, true>(a, stream) : launch_varlen<DIM, false>(a, stream);
   switch (a.head_dim) {
     ATTN_VARLEN_CASE(64)
-    ATTN_VARLEN_CASE(96)
     default:
       return hipErrorInvalidValue;
   }

@@ -191,7 +191,7 @@ def test_speculative_columns_probe_every_block_position():
     assert exact > 0
 
 
-@pytest.mark.parametrize("d", [128, 192, 256])
+@pytest.mark.parametrize("d", [96, 128, 192, 256])
 def test_paged_prefill_kernel_probe_every_block_position(d):
     """Long query runs take the pipelined prefill kernel with keys read
     through the block table (64-key tiles, one table lookup each): the 8-wave

@@ -98,15 +98,16 @@ def test_guard_canaries():
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
 
 
-@pytest.mark.parametrize("d", [64, 128, 192, 256])
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_indexing_probe_bit_exact(causal, d):
     """K = 0 except one selected key per (doc, head) with a logit at least 512
     above the rest; every row that can see it must return that key's V
     bit-exactly, and V encodes (doc, token) and then the column index, so a
     wrong cu_seqlens offset or a misplaced 16-byte piece is visible. head_dims
-    128, 192 and 256 run the pipelined kernels (128-row items on split K/V
-    rings; 512-byte LDS rows at 192, padded, and 256)."""
+    96 to 256 run the pipelined kernels (128-row items on split K/V rings;
+    256-byte LDS rows at 96, padded, and 128; 512-byte rows at 192, padded,
+    and 256)."""
     lens = [3, 129, 64, 250, 1, 385]
     hq = hkv = 3
     cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
