@@ -47,39 +47,40 @@ _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
 _SPARSE_SRC = ["block_sparse_d128.hip", "pipe.hpp", "attn_common.hpp"]
 _VARLEN_SRC = ["varlen_fwd.hip", "attn_common.hpp", "key_rows.hpp"]
 TRAFFIC = {
-    "tiny": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 246.5, "write_kib": 132.1,
-             "sources": _VARLEN_SRC, "sha256": "730fe5a387d4c6c3"},
-    "dense_d64": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 66862.2, "write_kib": 25344.0,
-                  "sources": _VARLEN_SRC, "sha256": "730fe5a387d4c6c3"},
-    "dense_d96": {"kernel": "prefill_pipe_kernel<96,false,false,4,true>"},
-    "dense_d192": {"kernel": "prefill_pipe_kernel<192,false,false,4,true>", "fetch_kib": 110851.1, "write_kib": 74496.2,
-                   "sources": _PREFILL_SRC, "sha256": "1a9005f127bab94b"},
-    "dense_d256": {"kernel": "prefill_pipe_kernel<256,false,false,4,true>", "fetch_kib": 149573.8,
-                   "write_kib": 116249.6, "sources": _PREFILL_SRC, "sha256": "1a9005f127bab94b"},
-    "decode_d64": {"kernel": "paged_decode_stream_kernel<64>", "fetch_kib": 1226024.5, "write_kib": 2601.7,
+    "tiny": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 247.6, "write_kib": 132.1,
+             "sources": _VARLEN_SRC, "sha256": "4f83bfe854bf432a"},
+    "dense_d64": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 67739.7, "write_kib": 25344.0,
+                  "sources": _VARLEN_SRC, "sha256": "4f83bfe854bf432a"},
+    "dense_d96": {"kernel": "prefill_pipe_kernel<96,false,false,4,true>", "fetch_kib": 73808.8, "write_kib": 37661.2,
+                  "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
+    "dense_d192": {"kernel": "prefill_pipe_kernel<192,false,false,4,true>", "fetch_kib": 110838.7,
+                   "write_kib": 74496.3, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
+    "dense_d256": {"kernel": "prefill_pipe_kernel<256,false,false,4,true>", "fetch_kib": 149842.2,
+                   "write_kib": 115987.4, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
+    "decode_d64": {"kernel": "paged_decode_stream_kernel<64>", "fetch_kib": 1226024.5, "write_kib": 2602.3,
                    "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "decode_d256": {"kernel": "paged_decode_stream_kernel<256>", "fetch_kib": 4878452.5, "write_kib": 3862.3,
+    "decode_d256": {"kernel": "paged_decode_stream_kernel<256>", "fetch_kib": 4878453.7, "write_kib": 3862.3,
                     "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "dense": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 73852.9, "write_kib": 49940.2,
-              "sources": _PREFILL_SRC, "sha256": "1a9005f127bab94b"},
-    "causal": {"kernel": "prefill_pipe_kernel<128,true,false,4,true>", "fetch_kib": 111810.3, "write_kib": 142483.2,
-               "sources": _PREFILL_SRC, "sha256": "1a9005f127bab94b"},
+    "dense": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 73859.1, "write_kib": 49937.4,
+              "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
+    "causal": {"kernel": "prefill_pipe_kernel<128,true,false,4,true>", "fetch_kib": 111842.3, "write_kib": 142480.5,
+               "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
     "paged": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2443513.0, "write_kib": 3042.6,
               "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 256166.0, "write_kib": 49921.2,
-               "sources": _SPARSE_SRC, "sha256": "189660875c16ee2d"},
-    "paged_prefill": {"kernel": "prefill_pipe_kernel<128,true,true,8,false>", "fetch_kib": 710153.3,
-                      "write_kib": 87201.9, "sources": _PREFILL_SRC, "sha256": "1a9005f127bab94b"},
+    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 251933.5, "write_kib": 49921.2,
+               "sources": _SPARSE_SRC, "sha256": "4500acdc4cc28950"},
+    "paged_prefill": {"kernel": "prefill_pipe_kernel<128,true,true,8,false>", "fetch_kib": 709416.2,
+                      "write_kib": 87201.4, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
     "spec": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2445751.0, "write_kib": 12163.3,
              "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 469258.1, "write_kib": 51487.9,
-           "sources": _SPARSE_SRC, "sha256": "189660875c16ee2d"},
+    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 468647.6, "write_kib": 51484.8,
+           "sources": _SPARSE_SRC, "sha256": "4500acdc4cc28950"},
     "swa": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 531392.9, "write_kib": 3081.2,
             "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "masked": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 28941.7, "write_kib": 50117.6,
-               "sources": _PREFILL_SRC, "sha256": "1a9005f127bab94b"},
-    "padded": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 107216.6, "write_kib": 66235.0,
-               "sources": _PREFILL_SRC, "sha256": "1a9005f127bab94b"},
+    "masked": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 28947.8, "write_kib": 50061.5,
+               "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
+    "padded": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 107378.2, "write_kib": 66236.1,
+               "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
 }
 
 
