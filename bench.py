@@ -57,6 +57,8 @@ TRAFFIC = {
                    "write_kib": 74496.3, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
     "dense_d256": {"kernel": "prefill_pipe_kernel<256,false,false,4,true>", "fetch_kib": 149842.2,
                    "write_kib": 115987.4, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
+    "decode_d96": {"kernel": "paged_decode_stream_kernel<96>"},
+    "decode_d192": {"kernel": "paged_decode_stream_kernel<192>"},
     "decode_d64": {"kernel": "paged_decode_stream_kernel<64>", "fetch_kib": 1226024.5, "write_kib": 2602.3,
                    "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
     "decode_d256": {"kernel": "paged_decode_stream_kernel<256>", "fetch_kib": 4878453.7, "write_kib": 3862.3,
@@ -421,7 +423,7 @@ def bench_head_dims(steps, warmup):
     """The head dims other than 128 that the pages list: dense non-causal
     prefill of 2 x 4096 rows with 24 heads at D = 64, 96, 192, 256, and decode
     over workload 4's 64 contexts (32 query / 8 kv heads, a random permutation
-    of cache blocks) at D = 64 and 256, inputs drawn on the device. Returns
+    of cache blocks) at D = 64, 96, 192 and 256, inputs drawn on the device. Returns
     (workload name, kind, StepTime, algorithmic work, bound) per line."""
     dev = torch.device("cuda")
     rows = []
@@ -445,7 +447,7 @@ def bench_head_dims(steps, warmup):
         o += nb
     bt = torch.from_numpy(tables).to(dev)
     cl = torch.from_numpy(np.asarray(ctx, dtype=np.int32)).to(dev)
-    for d in (64, 256):
+    for d in (64, 96, 192, 256):
         cache = workloads.randn_bf16_on((2, sum(nblk), 128, 8, d), 7800 + d, dev)
         q = workloads.randn_bf16_on((len(ctx), 32, d), 7801 + d, dev)
         out = torch.empty_like(q)

@@ -100,7 +100,12 @@ attn_status_t attn_varlen_fwd(const void* q, const void* k, const void* v,
 /*
  * Workspace bytes that attn_paged_decode needs for these host sizes
  * (the Ascend page sizes its paged-attention workspace with a query call,
- * _npu_paged_attention_get_workspace). Written to *bytes (host pointer).
+ * _npu_paged_attention_get_workspace). Written to *bytes (host pointer). The
+ * size does not depend on max_context_len (kept for that call's shape): two
+ * int32 arrays of num_seqs + 1 plus fp32 partials (O and LSE) for
+ * num_seqs + n_seg slots of every head, n_seg = 256 * W / (num_kv_heads *
+ * ceil(num_heads / num_kv_heads / 16)) with W = 8, 4, 4, 2, 2 waves per CU at
+ * head_dim 64, 96, 128, 192, 256.
  */
 attn_status_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                                int32_t head_dim, int32_t max_context_len, size_t* bytes);
@@ -120,14 +125,17 @@ attn_status_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_hea
  *   context_lens  [num_seqs] int32, 0 <= len <= max_blocks_per_seq * block_size
  *                 (the cache already holds the new token: the query attends all
  *                 context_lens[b] keys). len 0 gives O = 0, LSE = -inf.
- *   max_context_len (host) >= every context_lens[b]; plans the KV split.
+ *   max_context_len (host) >= every context_lens[b].
  *   block_size    must be 128.
  *   out           [num_seqs, num_heads, head_dim] bf16
  *   lse           nullable; [num_heads, num_seqs] fp32
  *   workspace     device buffer of at least attn_paged_decode_workspace_size()
- *                 bytes (split partials; contents on return are unspecified).
- * Long contexts are split over workgroups; partial (O, LSE) pairs are merged in
- * ascending split order by a second kernel, so the result is deterministic.
+ *                 bytes (token prefix sums and partials; contents on return
+ *                 are unspecified).
+ * The contexts of all sequences, end to end, are cut into equal segments, one
+ * per wave, whatever the mix of lengths; a sequence that spans segments has its
+ * partial (O, LSE) pairs merged in ascending segment order by a second kernel,
+ * so the result is deterministic.
  * num_seqs == 0 is a no-op.
  */
 attn_status_t attn_paged_decode(const void* q, const void* kv_cache,
@@ -170,24 +178,19 @@ attn_status_t attn_paged_decode_sliding_window(const void* q, const void* kv_cac
  * those of attn_paged_decode minus workspace / workspace_bytes; the call
  * allocates nothing.
  *
- * The split partials live in the library's own device array of
- * ATTN_DECODE_SCRATCH_BYTES, one per GPU, which stays allocated from the first
- * use until the process ends. Head dims 96 and 192 plan no more KV splits
- * than fit there (at most 64 per sequence, at least 1). A call whose partials
- * still do not fit returns ATTN_ERR_WORKSPACE_TOO_SMALL before any HIP call:
- * for head_dim 64, 128 and 256 that is 4 * num_heads * (head_dim + 1) *
- * (num_seqs + 1024 * 128 / head_dim / (num_kv_heads * ceil(num_heads /
- * num_kv_heads / 16))) bytes plus two int32 arrays of num_seqs + 1 above the
- * limit (about 1900 sequences at 32/8 heads and head_dim 128); for 96 and 192
- * one split of num_seqs * num_heads * (head_dim + 1) * 4 bytes above it. Nothing in the array needs clearing: every call writes each
- * partial before it reads it.
+ * The workspace of attn_paged_decode (token prefix sums and partials) lives in
+ * the library's own device array of ATTN_DECODE_SCRATCH_BYTES, one per GPU,
+ * which stays allocated from the first use until the process ends. A call
+ * whose workspace (attn_paged_decode_workspace_size) exceeds the array
+ * returns ATTN_ERR_WORKSPACE_TOO_SMALL before any HIP call (about 1900
+ * sequences at 32/8 heads and head_dim 128). Nothing in the array needs
+ * clearing: every call writes each partial before it reads it.
  * Every call on one GPU shares that GPU's array and leaves its partials there,
  * so calls that overlap on one GPU (other streams, other host threads) race:
  * issue them in order on one stream. The first call on each device looks the
  * array's device address up in the HIP runtime (no allocation) and caches it;
- * a failed lookup returns ATTN_ERR_LAUNCH. For head_dim 64, 128 and 256 the
- * result equals attn_paged_decode's bit for bit; for 96 and 192 it can differ
- * in the last bits where the split plan is capped.
+ * a failed lookup returns ATTN_ERR_LAUNCH. The result equals
+ * attn_paged_decode's bit for bit.
  */
 attn_status_t attn_paged_decode_scratch(const void* q, const void* kv_cache,
                                         const int32_t* block_tables, const int32_t* context_lens,

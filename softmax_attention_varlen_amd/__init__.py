@@ -258,8 +258,8 @@ def attn_paged_decode(q, kv_cache, block_tables, context_lens, max_context_len: 
 
 def attn_paged_decode_scratch(q, kv_cache, block_tables, context_lens, max_context_len: int, softmax_scale: float,
                               out=None, lse=None, return_lse: bool = False, stream=None):
-    """attn_paged_decode without a workspace: the split partials go to the
-    library's fixed per-GPU device array (ATTN_DECODE_SCRATCH_BYTES); nothing is
+    """attn_paged_decode without a workspace: its prefix sums and partials go to
+    the library's fixed per-GPU device array (ATTN_DECODE_SCRATCH_BYTES); nothing is
     allocated by the library. Calls that overlap on one GPU race."""
     dev = q.device
     nseq, hq, d = q.shape

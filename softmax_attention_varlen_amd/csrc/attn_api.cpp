@@ -83,7 +83,7 @@ attn_status_t attn_paged_decode_workspace_size(int32_t num_seqs, int32_t num_hea
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0) return ATTN_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
   if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
-  *bytes = attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len).workspace_bytes;
+  *bytes = attn::plan_decode_stream(num_seqs, num_heads, num_kv_heads, head_dim).workspace_bytes;
   return ATTN_OK;
 }
 
@@ -111,36 +111,22 @@ attn_status_t paged_decode_impl(const void* q, const void* kv_cache, const int32
   }
   if ((long long)num_blocks * block_size * num_kv_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
   if ((long long)num_seqs * max_context_len >= (1LL << 30)) return ATTN_ERR_UNSUPPORTED;  // int32 token prefix
+  const attn::DecodeStreamPlan plan = attn::plan_decode_stream(num_seqs, num_heads, num_kv_heads, head_dim);
   if (use_scratch) {
-    // the library's fixed scratch: plan no more partials than it holds, refuse
-    // what still does not fit, then resolve its address on this device
-    const attn::DecodePlan plan = attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                          max_context_len, attn::kDecodeScratchBytes);
+    // the library's fixed scratch: refuse what does not fit it, then resolve
+    // its address on this device
     if (plan.workspace_bytes > attn::kDecodeScratchBytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
-    void* ws = nullptr;
-    if (attn::decode_scratch_address(&ws) != hipSuccess) return ATTN_ERR_LAUNCH;
-    attn::DecodeArgs a{q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
-                       max_context_len, num_heads, num_kv_heads, head_dim, block_size, softmax_scale, out, lse, ws};
-    return from_hip(attn::launch_paged_decode(a, plan, (hipStream_t)stream));
-  }
-  const attn::DecodePlan need = attn::plan_paged_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len);
-  if (workspace_bytes < need.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
-  if (need.workspace_bytes > 0 && workspace == nullptr) return ATTN_ERR_INVALID_ARG;
-  // a window at least as long as the context is no window; a shorter one
-  // streams fewer keys per sequence, which sizes the splits (never beyond the
-  // workspace checked above)
-  const int win = window >= 0 && window < max_context_len ? window : -1;
-  const attn::DecodePlan plan =
-      win < 0 ? need
-              : attn::plan_paged_decode_window(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, win);
-  if (plan.o_bytes + plan.lse_bytes > workspace_bytes && !attn::decode_stream_supported(head_dim)) {
-    return ATTN_ERR_WORKSPACE_TOO_SMALL;
+    if (attn::decode_scratch_address(&workspace) != hipSuccess) return ATTN_ERR_LAUNCH;
+  } else {
+    if (workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;
+    if (plan.workspace_bytes > 0 && workspace == nullptr) return ATTN_ERR_INVALID_ARG;
   }
   attn::DecodeArgs a{q, kv_cache, block_tables, context_lens, num_seqs, num_blocks, max_blocks_per_seq,
                      max_context_len, num_heads, num_kv_heads, head_dim, block_size, softmax_scale, out, lse,
                      workspace};
-  a.window = win;
-  return from_hip(attn::launch_paged_decode(a, plan, (hipStream_t)stream));
+  // a window at least as long as the context is no window
+  a.window = window >= 0 && window < max_context_len ? window : -1;
+  return from_hip(attn::launch_decode_stream(a, plan, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -278,10 +264,8 @@ attn_status_t attn_paged_kv_write(const void* k, const void* v, const int32_t* s
 namespace {
 // Short multi-token queries (speculative decoding) stream the paged cache like
 // decode, with (query token, head) columns; longer ones run the prefill kernels.
-bool paged_prefill_streams(int batch, int num_heads, int num_kv_heads, int head_dim, int max_seqlen_q,
-                           int max_context_len) {
-  return attn::decode_stream_supported(head_dim) &&
-         (long long)max_seqlen_q * (num_heads / num_kv_heads) <= attn::kSpecMaxCols &&
+bool paged_prefill_streams(int batch, int num_heads, int num_kv_heads, int max_seqlen_q, int max_context_len) {
+  return (long long)max_seqlen_q * (num_heads / num_kv_heads) <= attn::kSpecMaxCols &&
          (long long)batch * max_context_len < (1LL << 30);
 }
 }  // namespace
@@ -297,7 +281,7 @@ attn_status_t attn_paged_prefill_workspace_size(int32_t batch, int32_t num_heads
   }
   if (!supported_head_dim(head_dim)) return ATTN_ERR_UNSUPPORTED;
   if (num_heads % num_kv_heads != 0) return ATTN_ERR_UNSUPPORTED;
-  *bytes = paged_prefill_streams(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q, max_context_len)
+  *bytes = paged_prefill_streams(batch, num_heads, num_kv_heads, max_seqlen_q, max_context_len)
                ? attn::plan_decode_stream(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q).workspace_bytes
                : 0;
   return ATTN_OK;
@@ -328,7 +312,7 @@ attn_status_t attn_paged_prefill(const void* q, const void* kv_cache, const int3
   if ((long long)total_q * num_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
   if ((long long)num_blocks * block_size * num_kv_heads > kMaxRows) return ATTN_ERR_UNSUPPORTED;
   if (attn::varlen_grid_size(batch, max_seqlen_q, num_heads) > kMaxRows) return ATTN_ERR_UNSUPPORTED;
-  if (paged_prefill_streams(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q, max_context_len)) {
+  if (paged_prefill_streams(batch, num_heads, num_kv_heads, max_seqlen_q, max_context_len)) {
     const attn::DecodeStreamPlan plan =
         attn::plan_decode_stream(batch, num_heads, num_kv_heads, head_dim, max_seqlen_q);
     if (workspace_bytes < plan.workspace_bytes) return ATTN_ERR_WORKSPACE_TOO_SMALL;

@@ -59,31 +59,6 @@ bool prefill_pipe_supported(const VarlenArgs& a);
 hipError_t launch_prefill_pipe(const VarlenArgs& a, hipStream_t stream);
 long varlen_grid_size(int batch, int max_seqlen_q, int num_heads);
 
-// Paged decode at head dims 96 and 192 (the others stream, below): the
-// context of each sequence is cut into splits of
-// split_tokens (a multiple of the 128-token block); split s of a sequence
-// writes a normalised fp32 partial (O_s, LSE_s) that a second kernel merges.
-struct DecodePlan {
-  int split_tokens;  // tokens per split
-  int max_splits;    // ceil(max_context_len / split_tokens)
-  int q_chunks;      // ceil(group / 16): query heads of one kv head per pass
-  size_t o_bytes;    // partial O   [num_seqs][max_splits][num_heads][head_dim] fp32
-  size_t lse_bytes;  // partial LSE [num_seqs][max_splits][num_heads] fp32
-  size_t workspace_bytes;
-};
-
-// max_partial_bytes (head dims 96 and 192): plan no more splits than fit
-// their fp32 partials in that many bytes (at least one split per sequence, so
-// workspace_bytes can still exceed it).
-DecodePlan plan_paged_decode(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
-                             size_t max_partial_bytes = SIZE_MAX);
-// The plan a sliding-window call runs (window >= 0 and < max_context_len;
-// otherwise the full plan): sized for the keys a sequence streams, with never
-// more splits, partial bytes or workspace than plan_paged_decode's for the
-// full max_context_len, so the workspace that plan reports always suffices.
-DecodePlan plan_paged_decode_window(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_context_len,
-                                    int window);
-
 struct DecodeArgs {
   const void* q;
   const void* kv_cache;
@@ -95,7 +70,7 @@ struct DecodeArgs {
   void* out;
   float* lse;
   void* workspace;
-  // multi-token queries (streaming path only): q is packed by cu_q, sequence b
+  // multi-token queries: q is packed by cu_q, sequence b
   // has cu_q[b+1] - cu_q[b] <= max_q new tokens; nullptr = one token each
   const int32_t* cu_q = nullptr;
   int total_q = 0;
@@ -104,8 +79,6 @@ struct DecodeArgs {
   int window = -1;
 };
 
-hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
-
 // The library's own decode scratch (decode_scratch.hip): a fixed device array
 // of kDecodeScratchBytes per GPU, held until the process ends, for the
 // allocation-free decode entry point. Its device address on the current
@@ -113,11 +86,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, const DecodePlan& plan, hipS
 constexpr size_t kDecodeScratchBytes = ATTN_DECODE_SCRATCH_BYTES;
 hipError_t decode_scratch_address(void** ptr);
 
-// head_dim 64, 128 and 256: balanced streaming decode (paged_decode_stream.hip).
-// The token stream of all sequences is cut into n_seg equal segments per kv
-// head (and query-head chunk); one wave streams one segment.
-constexpr int kDecodeStreamWaves = 1024;  // at head_dim 128: 4 waves on each of MI355X's 256 CUs
-bool decode_stream_supported(int head_dim);
+// Paged decode (every head dim): balanced streaming decode
+// (paged_decode_stream.hip). The token stream of all sequences is cut into
+// n_seg equal segments per kv head (and query-head chunk); one wave streams one
+// segment. The plan does not depend on the context lengths.
 struct DecodeStreamPlan {
   int max_q, q_chunks, n_seg;
   size_t prefix_bytes;  // int32 [num_seqs + 1] token prefix sums

@@ -1,5 +1,5 @@
-// Streaming single-token decode over a paged KV cache, head_dim 64, 128 or
-// 256, gfx950.
+// Streaming single-token decode over a paged KV cache, head_dims 64, 96, 128,
+// 192 and 256, gfx950.
 //
 // Work balance. The contexts of all sequences, laid end to end, form one token
 // stream of T = sum(context_lens) positions. For each kv head (and chunk of
@@ -20,12 +20,15 @@
 // and issues chunk j+2 as soon as chunk j is consumed (its K half right after
 // chunk j's S^T, its V half after the PV): one chunk is always in flight,
 // which is what keeps HBM busy (a wave that waits for its whole chunk before
-// issuing the next leaves gaps). A load writes 1 KB, i.e. 1024 / (2D) token
-// rows, so a chunk half is NB = D / 16 load blocks: block b holds tokens b,
-// b + NB, b + 2NB, ...; blocks sit 1056 bytes apart, which makes the
-// transposing V reads conflict-free at D = 128 and the K reads at most 2-way.
-// Workgroups hold 512 / D * 4 waves (8, 4, 2), so every head dim uses the same
-// LDS per CU and keeps the same bytes in flight per CU.
+// issuing the next leaves gaps). A token row takes R = 2D bytes of LDS, padded
+// to the next power of two at D = 96 and 192 (256 and 512 bytes; the pad lanes
+// of a load re-read the row's last real 16 bytes, in the same cache line). A
+// load writes 1 KB, i.e. 1024 / R token rows, so a chunk half is NB = R / 32
+// load blocks: block b holds tokens b, b + NB, b + 2NB, ...; blocks sit 1056
+// bytes apart, which makes the transposing V reads conflict-free at R = 256
+// and the K reads at most 2-way. Workgroups hold 1024 / R * 4 waves (8, 4, 4,
+// 2, 2 for D = 64, 96, 128, 192, 256), so every head dim uses about the same
+// LDS per CU and keeps the same row bytes in flight per CU.
 //
 // Queries. The 16 MFMA columns of a wave are (query token, head) pairs of its
 // kv head's group: column n of chunk qc is token (16qc + n) / group, head
@@ -57,14 +60,15 @@ constexpr int kMinSeg = 256;                 // shortest segment (positions)
 // Per head dim: the chunk layout in LDS and the workgroup shape.
 template <int D>
 struct StreamShape {
-  static_assert(D == 64 || D == 128 || D == 256, "token rows must divide a 1 KB load block");
-  static constexpr int kRow = 2 * D;                   // bytes of one token row of one kv head
-  static constexpr int kLanesPerRow = kRow / 16;       // 16-byte pieces of a row: 8, 16, 32
-  static constexpr int kNB = D / 16;                   // load blocks per chunk half: 4, 8, 16
+  static_assert(D == 64 || D == 96 || D == 128 || D == 192 || D == 256, "head dims 64, 96, 128, 192, 256");
+  static constexpr int kRow = D <= 64 ? 128 : D <= 128 ? 256 : 512;  // LDS bytes of one token row of one kv head
+  static constexpr int kLanesPerRow = kRow / 16;       // 16-byte pieces of an LDS row: 8, 16, 32
+  static constexpr int kRowPieces = D / 8;             // the real ones (fewer at D = 96, 192)
+  static constexpr int kNB = kRow / 32;                // load blocks per chunk half: 4, 8, 16
   static constexpr int kHalf = kNB * kSBlk;            // K (or V) of one chunk
   static constexpr int kStage = 2 * kHalf;             // K, then V
   static constexpr int kWaveLds = 2 * kStage;          // two-stage ring per wave
-  static constexpr int kWaves = 4 * 128 / D;           // waves per workgroup (one workgroup per CU by LDS)
+  static constexpr int kWaves = 4 * 256 / kRow;        // waves per workgroup (one workgroup per CU by LDS)
   static constexpr int kLoads = 2 * kNB;               // direct-to-LDS loads per chunk per wave
   // byte offset of token t (0..31) of a chunk half: block t % NB, row t / NB
   __device__ __forceinline__ static uint32_t tok_off(uint32_t t) {
@@ -239,11 +243,13 @@ __global__ __launch_bounds__(64 * StreamShape<D>::kWaves) void paged_decode_stre
 #pragma unroll
     for (int b = 0; b < S::kNB; ++b) {
       // lane l writes 16 bytes at st + b * kSBlk + 16 l: row l / kLanesPerRow
-      // of the block (token b + kNB * row), piece l % kLanesPerRow of it
+      // of the block (token b + kNB * row), piece l % kLanesPerRow of it (a
+      // pad piece re-reads the row's last real one)
       int t = t0 + b + S::kNB * (lane / S::kLanesPerRow);
       t = t < lctx ? t : lctx - 1;  // rows past the context re-read the last one (same block)
-      const uint32_t voff =
-          (uint32_t)((t + lskip) & 127) * row_bytes + (uint32_t)(lane % S::kLanesPerRow) * 16u;
+      const int piece = lane % S::kLanesPerRow;
+      const uint32_t voff = (uint32_t)((t + lskip) & 127) * row_bytes +
+                            (uint32_t)(piece < S::kRowPieces ? piece : S::kRowPieces - 1) * 16u;
       load_lds16(src, voff, st + b * kSBlk);
     }
     if (!v_half) return;
@@ -490,7 +496,7 @@ __global__ __launch_bounds__(256) void paged_decode_stream_combine_kernel(
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) tot = wave_xor_sum(tot, o);
   const float lse_all = mx + hw_log2(tot) * kLn2;
-  constexpr int NC = D / 64;  // columns lane + 64k of the output row
+  constexpr int NC = (D + 63) / 64;  // columns lane + 64k (< D) of the output row
   float acc[NC];
 #pragma unroll
   for (int k = 0; k < NC; ++k) acc[k] = 0.f;
@@ -502,17 +508,30 @@ __global__ __launch_bounds__(256) void paged_decode_stream_combine_kernel(
       const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), i));
       const float* po = part_o + slot(c0 + i) * D;
 #pragma unroll
-      for (int k = 0; k < NC; ++k) acc[k] += wi * po[lane + 64 * k];
+      for (int k = 0; k < NC; ++k) {
+        if (D % 64 == 0 || lane + 64 * k < D) acc[k] += wi * po[lane + 64 * k];
+      }
     }
   }
 #pragma unroll
-  for (int k = 0; k < NC; ++k) orow[lane + 64 * k] = __builtin_bit_cast(uint16_t, (__bf16)acc[k]);
+  for (int k = 0; k < NC; ++k) {
+    if (D % 64 == 0 || lane + 64 * k < D) orow[lane + 64 * k] = __builtin_bit_cast(uint16_t, (__bf16)acc[k]);
+  }
   if (lse != nullptr && lane == 0) lse[(long)h * total_q + row] = lse_all;
 }
 
 }  // namespace
 
-bool decode_stream_supported(int head_dim) { return head_dim == 64 || head_dim == 128 || head_dim == 256; }
+// stream waves: 256 CUs x the workgroup's waves
+static int decode_stream_waves(int head_dim) {
+  switch (head_dim) {
+    case 64: return 256 * StreamShape<64>::kWaves;
+    case 96: return 256 * StreamShape<96>::kWaves;
+    case 128: return 256 * StreamShape<128>::kWaves;
+    case 192: return 256 * StreamShape<192>::kWaves;
+    default: return 256 * StreamShape<256>::kWaves;
+  }
+}
 
 DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_heads, int head_dim, int max_q) {
   DecodeStreamPlan p{};
@@ -520,8 +539,7 @@ DecodeStreamPlan plan_decode_stream(int num_seqs, int num_heads, int num_kv_head
   p.max_q = max_q > 1 ? max_q : 1;
   p.q_chunks = (p.max_q * group + 15) / 16;
   const int lanes = num_kv_heads * p.q_chunks;
-  // stream waves: 256 CUs x the workgroup's waves (8, 4, 2 for D = 64, 128, 256)
-  const int waves = kDecodeStreamWaves * 128 / head_dim;
+  const int waves = decode_stream_waves(head_dim);
   p.n_seg = waves / lanes > 1 ? waves / lanes : 1;
   p.prefix_bytes = ((size_t)(num_seqs + 1) * sizeof(int32_t) + 255) & ~(size_t)255;
   p.skip_bytes = ((size_t)num_seqs * sizeof(int32_t) + 255) & ~(size_t)255;
@@ -563,7 +581,9 @@ hipError_t launch_decode_stream(const DecodeArgs& a, const DecodeStreamPlan& p, 
   if (a.window >= 0 && a.cu_q != nullptr) return hipErrorInvalidValue;  // windows: one query token each
   switch (a.head_dim) {
     case 64: return launch_decode_stream_d<64>(a, p, stream);
+    case 96: return launch_decode_stream_d<96>(a, p, stream);
     case 128: return launch_decode_stream_d<128>(a, p, stream);
+    case 192: return launch_decode_stream_d<192>(a, p, stream);
     case 256: return launch_decode_stream_d<256>(a, p, stream);
     default: return hipErrorInvalidValue;
   }

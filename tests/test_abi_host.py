@@ -87,12 +87,19 @@ def test_decode_empty_is_noop():
     assert _decode(nseq=0, q=None, out=None, ws=None, wsb=0) == OK
 
 
-def test_decode_workspace_query_is_monotone_and_covers_partials():
+def test_decode_workspace_query_covers_partials():
+    # the plan does not depend on the context length
     small = sav.attn_paged_decode_workspace_size(64, 32, 8, 128, 1024)
     big = sav.attn_paged_decode_workspace_size(64, 32, 8, 128, 32768)
-    assert 0 < small <= big
-    # at least one fp32 partial (O and LSE) per (seq, head) whenever a split is possible
-    assert big >= 64 * 32 * (128 + 1) * 4
+    assert 0 < small == big
+    # fp32 partials (O and LSE) for num_seqs + n_seg slots of every head, and two
+    # int32 arrays of num_seqs + 1; n_seg = 256 CUs x waves per CU / (kv heads x query chunks)
+    for d, waves in ((64, 8), (96, 4), (128, 4), (192, 2), (256, 2)):
+        n_seg = 256 * waves // 8
+        want = (64 + n_seg) * 32 * (d + 1) * 4
+        got = sav.attn_paged_decode_workspace_size(64, 32, 8, d, 4096)
+        # plus the two int32 arrays and alignment to 256 bytes: at most 1 KiB here
+        assert want <= got <= want + 1024, (d, got, want)
     with pytest.raises(sav.AttnError):
         sav.attn_paged_decode_workspace_size(64, 32, 8, 100, 1024)
 
@@ -184,10 +191,8 @@ def test_paged_prefill_empty_is_noop(kw):
 def test_paged_prefill_workspace_query():
     # long query runs use the prefill kernels (no workspace); short ones stream like decode
     assert sav.attn_paged_prefill_workspace_size(16, 32, 8, 128, 1024, 16384) == 0
-    # head dims 64, 128 and 256 stream short runs; 96 and 192 take the prefill kernels
-    assert sav.attn_paged_prefill_workspace_size(16, 32, 8, 96, 4, 16384) == 0
-    assert sav.attn_paged_prefill_workspace_size(16, 32, 8, 192, 4, 16384) == 0
-    for d in (64, 256):
+    # every head dim streams short runs
+    for d in (64, 96, 192, 256):
         assert sav.attn_paged_prefill_workspace_size(16, 32, 8, d, 4, 16384) > 0
         assert sav.attn_paged_prefill_workspace_size(16, 32, 8, d, 1, 16384) == \
             sav.attn_paged_decode_workspace_size(16, 32, 8, d, 16384)
@@ -343,8 +348,8 @@ def _decode_scratch(**kw):
     (dict(bs=64), UNSUPPORTED), (dict(d=100), UNSUPPORTED), (dict(hq=6, hkv=4), UNSUPPORTED),
     (dict(maxctx=513), INVALID), (dict(nseq=-1), INVALID), (dict(q=None), INVALID), (dict(out=None), INVALID),
     (dict(scale=0.0), INVALID),
-    # partials that do not fit the 32 MiB array: (128 + 4096) * 32 * 129 * 4 B at head_dim 128, and one split
-    # of 4096 * 32 * 65 * 4 B at head_dim 64
+    # partials that do not fit the 32 MiB array: (128 + 4096) * 32 * 129 * 4 B at head_dim 128 and
+    # (256 + 4096) * 32 * 65 * 4 B at head_dim 64
     (dict(nseq=4096, hq=32, hkv=8, d=128), WS_SMALL), (dict(nseq=4096, hq=32, hkv=8, d=64), WS_SMALL),
 ])
 def test_decode_scratch_validation(kw, code):

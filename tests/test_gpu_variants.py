@@ -58,14 +58,13 @@ def test_sliding_window_equals_plain_decode_when_it_covers_the_context():
     assert torch.equal(a, b) and torch.equal(la, lb)
 
 
-@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("d", [64, 96, 192, 256])
 @pytest.mark.parametrize("ctx,window", [([8193, 5, 8000, 100], 8160), ([8193, 8193, 1, 4097], 8100),
                                         ([20000, 300, 16385, 9], 16000), ([700, 129, 640, 2], 600)])
 def test_sliding_window_plan_fits_reported_workspace(d, ctx, window):
-    """The window's split plan streams fewer keys than the full context, and
-    rounding its splits up to whole blocks must never plan more partials than
-    the workspace the size query reported for max_context_len: the call gets
-    exactly that many bytes, followed by a poisoned guard."""
+    """A windowed call gets exactly the workspace the size query reported for
+    max_context_len, followed by a poisoned guard: the stream's prefix sums,
+    window starts and partials stay inside it."""
     from tests._gpu_helpers import guard_intact, guarded_empty
 
     case = paged_prefill_case([1] * len(ctx), ctx, num_heads=32, num_kv_heads=8, head_dim=d, seed=540 + d,
