@@ -1,8 +1,8 @@
 """Bit-exact indexing probes through the kernels the full-size workloads run:
-the head_dim-128 streaming paged decode (plain, sliding-window and the
-speculative multi-token columns), the pipelined prefill kernel reading keys
-from the paged cache (head_dims 128, 192, 256), and the head_dim-128 block-sparse kernel with its packed
-kept-tile lists.
+the streaming paged decode (plain at head_dims 96, 128, 192, sliding-window
+and the speculative multi-token columns), the pipelined prefill kernel reading
+keys from the paged cache (head_dims 96 to 256), and the head_dim-128
+block-sparse kernel with its packed kept-tile lists.
 
 Construction, shared by every probe: one selected key per unit (sequence or
 query tile, and head) scores thousands of logit units above every other key
@@ -126,10 +126,13 @@ def _decode_probe(ctx, hq, hkv, d, seed, window=None):
 DECODE_CTX = [1, 31, 32, 33, 127, 128, 129, 0, 255, 257, 300, 777, 2048, 4100, 9000, 3]
 
 
-@pytest.mark.parametrize("hq,hkv", [(32, 8), (40, 2)])
-def test_decode_stream_probe_every_block_position(hq, hkv):
-    announce("probe decode stream", hq, hkv)
-    checked = _decode_probe(DECODE_CTX, hq, hkv, 128, seed=240 + hq)
+@pytest.mark.parametrize("hq,hkv,d", [(32, 8, 128), (40, 2, 128), (32, 8, 96), (32, 8, 192)])
+def test_decode_stream_probe_every_block_position(hq, hkv, d):
+    """head_dims 96 and 192 stream with token rows padded in LDS (256 and 512
+    bytes); the probe's value rows encode every column, so a misplaced or
+    padded piece shows."""
+    announce("probe decode stream", hq, hkv, d)
+    checked = _decode_probe(DECODE_CTX, hq, hkv, d, seed=240 + hq + (d - 128))
     assert checked >= 71 * hq
 
 
