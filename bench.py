@@ -44,7 +44,7 @@ WRITE_SCALE = 1.0
 CSRC = os.path.join(ROOT, "softmax_attention_varlen_amd", "csrc")
 _PREFILL_SRC = ["prefill_pipe.hip", "pipe.hpp", "attn_common.hpp", "key_rows.hpp"]
 _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
-_SPARSE_SRC = ["block_sparse_d128.hip", "pipe.hpp", "attn_common.hpp"]
+_SPARSE_SRC = ["block_sparse_pipe.hip", "pipe.hpp", "attn_common.hpp"]
 _VARLEN_SRC = ["varlen_fwd.hip", "attn_common.hpp", "key_rows.hpp"]
 TRAFFIC = {
     "tiny": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 247.6, "write_kib": 132.1,
@@ -69,13 +69,13 @@ TRAFFIC = {
                "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
     "paged": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2443513.0, "write_kib": 3042.6,
               "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "sparse": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 251933.5, "write_kib": 49921.2,
+    "sparse": {"kernel": "block_sparse_pipe_kernel<128>", "fetch_kib": 251933.5, "write_kib": 49921.2,
                "sources": _SPARSE_SRC, "sha256": "4500acdc4cc28950"},
     "paged_prefill": {"kernel": "prefill_pipe_kernel<128,true,true,8,false>", "fetch_kib": 709416.2,
                       "write_kib": 87201.4, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
     "spec": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2445751.0, "write_kib": 12163.3,
              "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "h3": {"kernel": "block_sparse_d128_kernel", "fetch_kib": 468647.6, "write_kib": 51484.8,
+    "h3": {"kernel": "block_sparse_pipe_kernel<128>", "fetch_kib": 468647.6, "write_kib": 51484.8,
            "sources": _SPARSE_SRC, "sha256": "4500acdc4cc28950"},
     "swa": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 531392.9, "write_kib": 3081.2,
             "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},

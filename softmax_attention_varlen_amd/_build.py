@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_NAME = "libattn_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["attn_api.cpp", "varlen_fwd.hip", "prefill_pipe.hip", "paged_decode_stream.hip", "decode_scratch.hip", "paged_cache.hip", "padding.hip", "block_sparse.hip", "block_sparse_d128.hip", "vsa_prep.hip"]
+SOURCES = ["attn_api.cpp", "varlen_fwd.hip", "prefill_pipe.hip", "paged_decode_stream.hip", "decode_scratch.hip", "paged_cache.hip", "padding.hip", "block_sparse.hip", "block_sparse_pipe.hip", "vsa_prep.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -165,14 +165,15 @@ static hipError_t launch_sparse_d(const SparseArgs& a, hipStream_t stream) {
 
 hipError_t launch_block_sparse_fwd(const SparseArgs& a, hipStream_t stream) {
   const int rows = a.batch * a.num_heads * a.num_tiles;
-  const bool d128 = a.head_dim == 128 && a.num_tiles <= kSparseD128MaxTiles;
-  hipError_t e = launch_map_to_index(a.block_map, rows, a.num_tiles, d128 ? a.tile_sizes : nullptr, a.idx, a.num,
+  const bool pipe = sparse_pipe_supported(a.head_dim, a.num_tiles);
+  hipError_t e = launch_map_to_index(a.block_map, rows, a.num_tiles, pipe ? a.tile_sizes : nullptr, a.idx, a.num,
                                      stream);
   if (e != hipSuccess) return e;
-  switch (a.head_dim) {
+  if (pipe) return launch_block_sparse_pipe(a, stream);
+  switch (a.head_dim) {  // head_dim 64, and more than kSparsePipeMaxTiles tiles
     case 64: return launch_sparse_d<64>(a, stream);
     case 96: return launch_sparse_d<96>(a, stream);
-    case 128: return d128 ? launch_block_sparse_d128(a, stream) : launch_sparse_d<128>(a, stream);
+    case 128: return launch_sparse_d<128>(a, stream);
     case 192: return launch_sparse_d<192>(a, stream);
     case 256: return launch_sparse_d<256>(a, stream);
     default: return hipErrorInvalidValue;

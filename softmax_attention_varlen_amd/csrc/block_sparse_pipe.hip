@@ -1,4 +1,5 @@
-// Pipelined block-sparse attention over 64-token tiles, head_dim 128, gfx950.
+// Pipelined block-sparse attention over 64-token tiles, head_dims 96, 128, 192
+// and 256, gfx950.
 //
 // Work unit: one workgroup of 4 waves owns one (batch, head, query tile).
 // Wave w owns query rows 32*(w%2) .. +31 of the tile and key half w/2 (keys
@@ -13,8 +14,10 @@
 // conflict-free layout of pipe.hpp): step j runs the softmax of tile j
 // under the S^T MFMAs of tile j+1 and the PV MFMAs of tile j-1, reading K of
 // tile j+1 and V of tile j-1, while K of tile j+2 and V of tile j are in
-// flight. With two workgroups per CU
-// (66.5 KB of LDS each) a SIMD holds two waves.
+// flight. At head_dims 96 and 128 (256-byte LDS rows, 96 padded) two
+// workgroups share a CU (66.5 KB of LDS each), so a SIMD holds two waves; at
+// 192 and 256 (512-byte rows, 192 padded) the rings take 130 KB and one
+// workgroup runs per CU.
 //
 // Padding keys (at or past a tile's size) are masked; padding query rows are
 // written as zeros with LSE = -inf; a query tile with no kept key gets zeros
@@ -38,14 +41,18 @@ namespace {
 
 using namespace pipe;
 
-constexpr int kD = 128;
-constexpr int kTileBytes = Geom<kD>::kTileBytes;
-constexpr int kSW = 4;                       // waves per workgroup
-constexpr int kSIPW = 16 / kSW;              // load blocks per wave per K (or V) tile
-constexpr int kSparseLds = 4 * kTileBytes;   // K stages 0, 1, then V stages 0, 1
-constexpr int kMergeOBytes = 32 * 128 * 4;   // one wave's fp32 O^T block
-constexpr int kListCap = kSparseD128MaxTiles;  // the whole kept-tile list is staged in LDS
-static_assert(2 * kMergeOBytes + 2 * 512 <= kSparseLds, "merge area must fit in the ring");
+constexpr int kSW = 4;                             // waves per workgroup
+constexpr int kListCap = kSparsePipeMaxTiles;      // the whole kept-tile list is staged in LDS
+
+template <int D>
+struct SparseShape {
+  static constexpr int kTileBytes = Geom<D>::kTileBytes;
+  static constexpr int kSIPW = Geom<D>::kBlocks / kSW;  // load blocks per wave per K (or V) tile
+  static constexpr int kLds = 4 * kTileBytes;           // K stages 0, 1, then V stages 0, 1
+  static constexpr int kMergeOBytes = 32 * D * 4;        // one wave's fp32 O^T block
+  static constexpr int kWgPerCu = D <= 128 ? 2 : 1;
+  static_assert(2 * kMergeOBytes + 2 * 512 <= kLds, "merge area must fit in the ring");
+};
 
 constexpr int kOrderThreads = 1024;
 constexpr int kOrderWaves = kOrderThreads / 64;
@@ -145,12 +152,17 @@ __device__ __forceinline__ Entry unpack(int32_t v, int num_tiles) {
   return e;
 }
 
-__global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
+template <int D>
+__global__ __launch_bounds__(64 * kSW, SparseShape<D>::kWgPerCu) void block_sparse_pipe_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ tile_sizes, const int32_t* __restrict__ kidx, const int32_t* __restrict__ knum,
     const int32_t* __restrict__ order, int num_tiles, int hq, int hkv, int n_items, int per_xcd, float c,
     uint16_t* __restrict__ out, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(1024))) char smem[kSparseLds];
+  using SS = SparseShape<D>;
+  using G = Geom<D>;
+  constexpr int kD = D, kTileBytes = SS::kTileBytes, kSIPW = SS::kSIPW, kMergeOBytes = SS::kMergeOBytes;
+  constexpr int QB = G::kQB, OB = G::kOB;
+  __shared__ __attribute__((aligned(1024))) char smem[SS::kLds];
   __shared__ int32_t lst[kListCap];
 
   // XCD-aware order: XCD x runs the items of [x*per_xcd, (x+1)*per_xcd) (query
@@ -184,15 +196,15 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   const uint32_t ring = lds_u32(smem);
   const long qrow0 = (long)b * seq + (long)a * kBN;
 
-  bf16x8 qr[8];
+  bf16x8 qr[QB];
   {
     const uint16_t* qp = q + ((qrow0 + r_c) * hq + h) * kD + L.g * 8;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) qr[db] = as_bf16x8(ld_global16(qp + db * 16));
+    for (int db = 0; db < QB; ++db) qr[db] = as_bf16x8(ld_global16(qp + db * 16));
   }
-  f32x16 o[4];
+  f32x16 o[OB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < OB; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
   }
@@ -205,10 +217,13 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   // no per-tile vector arithmetic; a partial tile clamps its rows to the last
   // real key.
   uint32_t boff[kSIPW];
+  {
+    const int piece = lane % G::kLanesPerRow;  // a pad piece re-reads the row's last real one
+    const uint32_t pc = (uint32_t)(piece < G::kRowPieces ? piece : G::kRowPieces - 1) * 16u;
 #pragma unroll
-  for (int t = 0; t < kSIPW; ++t) {
-    boff[t] = (block_key((uint32_t)(w * kSIPW + t)) + 16u * (uint32_t)(lane >> 4)) * stride_bytes +
-              (uint32_t)(lane & 15) * 16u;
+    for (int t = 0; t < kSIPW; ++t) {
+      boff[t] = G::block_row_key((uint32_t)(w * kSIPW + t), (uint32_t)(lane / G::kLanesPerRow)) * stride_bytes + pc;
+    }
   }
   auto issue = [&](const uint16_t* plane, const Entry& t, uint32_t stage_lds) {
     const uint16_t* tb = plane + (long)t.tile * kBN * kv_stride;
@@ -283,8 +298,8 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
       // after the last tile the "next" K stage holds stale data; its S^T is unused
       const char* nk = smem + ((j + 1) & 1) * kTileBytes;
       const uint32_t vt_prev = ring + (2 + ((j + 1) & 1)) * kTileBytes;  // V of tile j-1
-      tile_step_pp1<HAS_PV>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, size < 32 * kh + 32, 32 * kh, size,
-                            0x7fffffff);
+      tile_step_pp1<D, HAS_PV>(s, sn, nk, vt_prev, L, qr, pp, pc, o, st, c, size < 32 * kh + 32, 32 * kh, size,
+                               0x7fffffff);
     }
   };
   using yes = std::integral_constant<bool, true>;
@@ -319,7 +334,7 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   float2* mml = reinterpret_cast<float2*>(smem + 2 * kMergeOBytes + rh * 512) + lane;
   if (kh == 1) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < OB; ++i) {
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         f32x4 t;
@@ -337,7 +352,7 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   const float a0 = st.m == kNegInf ? 0.f : hw_exp2((st.m - mm) * c);
   const float a1 = ml.x == kNegInf ? 0.f : hw_exp2((ml.x - mm) * c);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < OB; ++i) {
 #pragma unroll
     for (int grp = 0; grp < 4; ++grp) {
       const f32x4 t = mo[(4 * i + grp) * 64];
@@ -347,21 +362,45 @@ __global__ __launch_bounds__(64 * kSW, 2) void block_sparse_d128_kernel(
   }
   st.m = mm;
   st.l = r < qsize ? st.l * a0 + ml.y * a1 : 0.f;  // padding rows: zeros, LSE = -inf
-  store_rows<4>(o, st, L, c, true, out + ((qrow0 + r) * hq + h) * kD,
+  store_rows<OB>(o, st, L, c, true, out + ((qrow0 + r) * hq + h) * kD,
              lse != nullptr ? lse + ((long)b * hq + h) * seq + (long)a * kBN + r : nullptr);
 }
 
 }  // namespace
 
-hipError_t launch_block_sparse_d128(const SparseArgs& a, hipStream_t stream) {
+bool sparse_pipe_supported(int head_dim, int num_tiles) {
+  return (head_dim == 96 || head_dim == 128 || head_dim == 192 || head_dim == 256) && num_tiles <= kSparsePipeMaxTiles;
+}
+
+template <int D>
+static void launch_block_sparse_pipe_d(const SparseArgs& a, long n_items, long per_xcd, hipStream_t stream) {
+  hipLaunchKernelGGL((block_sparse_pipe_kernel<D>), dim3((unsigned)(per_xcd * 8)), dim3(64 * kSW), 0, stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.tile_sizes, a.idx, a.num,
+                     a.order, a.num_tiles, a.num_heads, a.num_kv_heads, (int)n_items, (int)per_xcd, a.scale * kLog2e,
+                     (uint16_t*)a.out, a.lse);
+}
+
+hipError_t launch_block_sparse_pipe(const SparseArgs& a, hipStream_t stream) {
   const long n_items = (long)a.batch * a.num_heads * a.num_tiles;
   const long per_xcd = (n_items + 7) / 8;
   hipLaunchKernelGGL(order_items_kernel, dim3(8), dim3(kOrderThreads), 0, stream, a.num, (int)n_items, (int)per_xcd,
                      a.order);
-  hipLaunchKernelGGL(block_sparse_d128_kernel, dim3((unsigned)(per_xcd * 8)), dim3(64 * kSW), 0, stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.tile_sizes, a.idx, a.num,
-                     a.order, a.num_tiles, a.num_heads, a.num_kv_heads, (int)n_items, (int)per_xcd, a.scale * kLog2e,
-                     (uint16_t*)a.out, a.lse);
+  switch (a.head_dim) {
+    case 96:
+      launch_block_sparse_pipe_d<96>(a, n_items, per_xcd, stream);
+      break;
+    case 128:
+      launch_block_sparse_pipe_d<128>(a, n_items, per_xcd, stream);
+      break;
+    case 192:
+      launch_block_sparse_pipe_d<192>(a, n_items, per_xcd, stream);
+      break;
+    case 256:
+      launch_block_sparse_pipe_d<256>(a, n_items, per_xcd, stream);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -127,15 +127,17 @@ struct SparseArgs {
   float* lse;
   int32_t* idx;  // workspace: [batch*num_heads*num_tiles][num_tiles]
   int32_t* num;  // workspace: [batch*num_heads*num_tiles]
-  int32_t* order;  // workspace: [batch*num_heads*num_tiles], the order the head_dim-128 kernel runs items in
+  int32_t* order;  // workspace: [batch*num_heads*num_tiles], the order the pipelined kernel runs items in
 };
 
 size_t sparse_workspace_bytes(int batch, int num_heads, int num_tiles);
 hipError_t launch_block_sparse_fwd(const SparseArgs& a, hipStream_t stream);
-// head_dim 128 with at most kSparseD128MaxTiles tiles (its kept-tile list is
-// staged in LDS); expects the packed, size-filtered lists in a.idx / a.num.
-constexpr int kSparseD128MaxTiles = 3072;
-hipError_t launch_block_sparse_d128(const SparseArgs& a, hipStream_t stream);
+// Pipelined block-sparse kernel (block_sparse_pipe.hip): head_dims 96 to 256
+// with at most kSparsePipeMaxTiles tiles (its kept-tile list is staged in
+// LDS); expects the packed, size-filtered lists in a.idx / a.num.
+constexpr int kSparsePipeMaxTiles = 3072;
+bool sparse_pipe_supported(int head_dim, int num_tiles);
+hipError_t launch_block_sparse_pipe(const SparseArgs& a, hipStream_t stream);
 
 // Video tile geometry (raster (t, h, w) cut into (tile_t, tile_h, tile_w) boxes),
 // optionally behind prefix segments (host array of num_segments lengths >= 0):

@@ -365,16 +365,24 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   }
 }
 
-// The same pipeline for a 32-key share per wave (KB = 1): 16 MFMA slots, the
-// S^T of tile j+1 (8 MFMAs, K from nk) on even slots and, when PV, the PV of
-// tile j-1 (8 MFMAs, P in p_prev, V^T from vt_prev) on odd slots. Slots 0-1
-// carry the two row-maximum chains, slot 2 the reference update, slots 3-14
-// the 16 exp2 (each row-sum add and bf16 packing one slot after its exp2).
-template <bool PV>  // head_dim 128
+// The same pipeline for a 32-key share per wave (KB = 1): NS = D/8 MFMA slots
+// (16 at head_dim 128), the S^T of tile j+1 (D/16 MFMAs, K from nk) on even
+// slots and, when PV, the PV of tile j-1 (D/16 MFMAs, P in p_prev, V^T from
+// vt_prev) on odd slots. Slots 0-1 carry the two row-maximum chains, slot 2 the
+// reference update, slots 3 on the 16 exp2 (each row-sum add and bf16 packing
+// one slot after its exp2): slot 3 + 3x/4 for element x at head_dim 128,
+// stretched over the step at 192 and 256, two per slot at 96.
+template <int D, bool PV>
 __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], const char* nk, uint32_t vt_prev,
-                                              const Lane& L, const bf16x8 (&q)[8], const bf16x8 (&p_prev)[2],
-                                              bf16x8 (&p_cur)[2], f32x16 (&o)[4], Softmax& st, float c, bool mask,
-                                              int key0, int len_k, int lim) {
+                                              const Lane& L, const bf16x8 (&q)[Geom<D>::kQB],
+                                              const bf16x8 (&p_prev)[2], bf16x8 (&p_cur)[2],
+                                              f32x16 (&o)[Geom<D>::kOB], Softmax& st, float c, bool mask, int key0,
+                                              int len_k, int lim) {
+  constexpr int OB = Geom<D>::kOB;
+  constexpr int NT = Geom<D>::kQB;  // S^T MFMAs per step = PV MFMAs per step (2 chunks x OB)
+  constexpr int NS = 2 * NT;        // MFMA slots
+  static_assert(NS >= 12, "the softmax needs 12 MFMA slots per step");
+  auto exp_slot = [](int x) constexpr { return NS >= 16 ? 3 + ((3 * x) / 4) * (NS - 4) / 12 : 3 + x / 2; };
   if (mask) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -390,8 +398,8 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
   kr[1] = ld_lds16(kbase, 32);
   bf16x8 va[2];
   if (PV) {
-    va[0] = read_vt<128>(vbase, 0, 0);
-    va[1] = read_vt<128>(vbase, 0, 1);
+    va[0] = read_vt<D>(vbase, 0, 0);
+    va[1] = read_vt<D>(vbase, 1 / OB, 1 % OB);
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) sn[0][r] = 0.f;
@@ -402,20 +410,20 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
   float rs0 = 0.f, rs1 = 0.f;
   // Issue priority 2 for the MFMA slots, back to 1 (the caller's loop level)
   // after them: the block-sparse kernel runs two workgroups per CU out of
-  // phase, and the other workgroup's ring refills (1) and prologue, merge and
-  // store (0) then yield the issue slot to these steps.
+  // phase (head_dims 96 and 128), and the other workgroup's ring refills (1)
+  // and prologue, merge and store (0) then yield the issue slot to these steps.
   __builtin_amdgcn_s_setprio(2);
   __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int slot = 0; slot < 16; ++slot) {
+  static_for<NS>([&](auto slot_c) __attribute__((always_inline)) {
+    constexpr int slot = decltype(slot_c)::value;
     const int t = slot >> 1;
     if ((slot & 1) == 0) {  // S^T of tile j+1, d-block t
       sn[0] = mfma32x32x16(kr[t & 1], q[t], sn[0]);
-      if (t + 2 < 8) kr[t & 1] = ld_lds16(kbase, (t + 2) * 32);
-    } else if (PV) {  // PV of tile j-1: chunk t/4, d-block t%4
+      if (t + 2 < NT) kr[t & 1] = ld_lds16(kbase, (t + 2) * 32);
+    } else if (PV) {  // PV of tile j-1: chunk t/OB, d-block t%OB
       const bf16x8 a = va[t & 1];
-      if (t + 2 < 8) va[t & 1] = read_vt<128>(vbase, (t + 2) >> 2, (t + 2) & 3);
-      o[t & 3] = mfma32x32x16(a, p_prev[t >> 2], o[t & 3]);
+      if (t + 2 < NT) va[t & 1] = read_vt<D>(vbase, (t + 2) / OB, (t + 2) % OB);
+      o[t % OB] = mfma32x32x16(a, p_prev[t / OB], o[t % OB]);
     }
     if (slot < 2) {  // row maximum: chain slot over elements 8*slot .. +7
       float m = fmaxf(s[0][8 * slot], s[0][8 * slot + 1]);
@@ -430,11 +438,11 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
       m_ref = need ? m_new : st.m;
       ms = (m_ref == kNegInf ? 0.f : m_ref) * c;
     } else {
-      // element x's exp2 runs in slot 3 + 3x/4 (slots 3..14); its row-sum add,
-      // and the packing of a finished chunk, one slot later
+      // element x's exp2 runs in slot exp_slot(x); its row-sum add, and the
+      // packing of a finished chunk, one slot later
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        if (4 + (3 * x) / 4 == slot) {
+        if (exp_slot(x) + 1 == slot) {
           const int u = x & 7;
           if (u & 1) {
             rs1 += e[u];
@@ -449,18 +457,18 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
       }
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        if (3 + (3 * x) / 4 == slot) e[x & 7] = hw_exp2(__builtin_fmaf(s[0][x], c, -ms));
+        if (exp_slot(x) == slot) e[x & 7] = hw_exp2(__builtin_fmaf(s[0][x], c, -ms));
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-  }
+  });
   __builtin_amdgcn_s_setprio(1);
   const float rs = rs0 + rs1;
   st.l = st.l * alpha + rs;
   st.m = m_ref;
   if (__builtin_amdgcn_ballot_w64(need || rs != rs) != 0ull) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) o[b] *= alpha;
+    for (int b = 0; b < OB; ++b) o[b] *= alpha;
   }
 }
 

@@ -1,8 +1,8 @@
 """Bit-exact indexing probes through the kernels the full-size workloads run:
 the streaming paged decode (plain at head_dims 96, 128, 192, sliding-window
 and the speculative multi-token columns), the pipelined prefill kernel reading
-keys from the paged cache (head_dims 96 to 256), and the head_dim-128
-block-sparse kernel with its packed kept-tile lists.
+keys from the paged cache (head_dims 96 to 256), and the pipelined
+block-sparse kernel with its packed kept-tile lists (head_dims 96 to 256).
 
 Construction, shared by every probe: one selected key per unit (sequence or
 query tile, and head) scores thousands of logit units above every other key
@@ -207,15 +207,15 @@ def test_paged_prefill_kernel_probe_every_block_position(d):
     assert exact > 0
 
 
-def _sparse_probe(nt, hq, hkv, seed, need_long=True):
+def _sparse_probe(nt, hq, hkv, seed, need_long=True, d=128):
     """Block-sparse probe. Query tile a of head h gets its own direction
     e = dir(h, a) (Q rows = 64 e). Real key rows of tile c hold 64 times the sum
     of the directions of every (head of the kv group, query tile) whose map
     drops c, and padding rows hold 64 times every direction: any read outside
     the kept tiles' real rows scores like the selected key. In each round every
     query tile picks one kept tile it has not yet picked and a free real row
-    there, which is set to 64 e."""
-    d = 128
+    there, which is set to 64 e. Value rows encode (tile, row, kv head) and
+    then the column index, so a misplaced 16-byte piece shows."""
     group = hq // hkv
     assert group * nt <= d
     rng = np.random.default_rng(seed)
@@ -249,6 +249,7 @@ def _sparse_probe(nt, hq, hkv, seed, need_long=True):
     v[0, :, :, 0] = (torch.arange(nt * 64) // 64).view(-1, 1).to(BF16)
     v[0, :, :, 1] = (torch.arange(nt * 64) % 64).view(-1, 1).to(BF16)
     v[0, :, :, 2] = torch.arange(hkv).view(1, hkv).to(BF16)
+    v[0, :, :, 3:] = (torch.arange(3, d) % 200).to(BF16)
 
     qd, kd, vd = q.cuda(), k.cuda(), v.cuda()
     md, sd = dev(bmap.astype(np.uint8)), dev(sizes)
@@ -301,19 +302,23 @@ def _sparse_probe(nt, hq, hkv, seed, need_long=True):
     return covered, longest
 
 
-def test_sparse_d128_kept_tile_probe_long_lists():
-    """100 tiles, two heads: kept lists up to about 100 entries (the kernel
-    holds 64 list entries in a register window at a time), partial, single-row
-    and empty tiles, an empty map row; every kept tile of every (head, query
-    tile) is selected in some round."""
-    announce("probe sparse d128 long lists")
-    covered, longest = _sparse_probe(100, 2, 2, seed=300)
-    assert longest > 64 and covered > 1000
+@pytest.mark.parametrize("d", [128, 96, 192, 256])
+def test_sparse_pipe_kept_tile_probe_long_lists(d):
+    """Up to 100 tiles, two heads: kept lists longer than 64 entries (the
+    kernel holds 64 list entries in a register window at a time), partial,
+    single-row and empty tiles, an empty map row; every kept tile of every
+    (head, query tile) is selected in some round. head_dims 96 and 192 pad
+    their LDS rows (256 and 512 bytes)."""
+    nt = 100 if d >= 100 else 90
+    announce("probe sparse long lists", d)
+    covered, longest = _sparse_probe(nt, 2, 2, seed=300 + (d - 128), d=d)
+    assert longest > 64 and covered > 900
 
 
-def test_sparse_d128_kept_tile_probe_grouped_heads():
+@pytest.mark.parametrize("d", [128, 256])
+def test_sparse_pipe_kept_tile_probe_grouped_heads(d):
     """Grouped heads (4 query heads on 2 kv heads, 60 tiles): query head h
     reads kv head h // 2."""
-    announce("probe sparse d128 gqa")
-    covered, _ = _sparse_probe(60, 4, 2, seed=301, need_long=False)
+    announce("probe sparse gqa", d)
+    covered, _ = _sparse_probe(60, 4, 2, seed=301 + (d - 128), need_long=False, d=d)
     assert covered > 1000

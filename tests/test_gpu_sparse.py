@@ -70,10 +70,11 @@ def test_partial_tiles_random_map(d, hq, hkv):
     assert_close("lse", host(lse), ref_l, LSE_TOL)
 
 
-def test_head_dim_128_beyond_staged_list_capacity():
-    # head_dim 128 stages each query tile's kept-tile list in LDS for up to
-    # 3072 tiles; a longer tile axis takes the general kernel
-    b, nt, h, d = 1, 3100, 1, 128
+@pytest.mark.parametrize("d", [128, 256])
+def test_pipe_beyond_staged_list_capacity(d):
+    # the pipelined kernel stages each query tile's kept-tile list in LDS for
+    # up to 3072 tiles; a longer tile axis takes the general kernel
+    b, nt, h = 1, 3100, 1
     q, k, v = (randn_bf16((b, nt * 64, h, d), 340 + j) for j in range(3))
     rng = np.random.default_rng(34)
     sizes = np.full(nt, 64, dtype=np.int32)
@@ -92,15 +93,16 @@ def test_head_dim_128_beyond_staged_list_capacity():
     assert_close("lse", host(lse)[:, :, rows], ref_l[:, :, rows], LSE_TOL)
 
 
-@pytest.mark.parametrize("density", [0.45, 0.9])
-def test_head_dim_128_long_kept_lists(density):
-    """Kept lists longer than 64 tiles (the D=128 kernel reads its list through a
-    64-entry window that moves forward), with partial and empty tiles that are
-    dropped from the lists, a row with every tile, one with none and one with 65."""
-    b, nt, hq, hkv, d = 1, 150, 4, 2, 128
+@pytest.mark.parametrize("density,d", [(0.45, 128), (0.9, 128), (0.9, 96), (0.45, 192), (0.9, 256)])
+def test_pipe_long_kept_lists(density, d):
+    """Kept lists longer than 64 tiles (the pipelined kernel reads its list
+    through a 64-entry window that moves forward), with partial and empty tiles
+    that are dropped from the lists, a row with every tile, one with none and
+    one with 65."""
+    b, nt, hq, hkv = 1, 150, 4, 2
     q = randn_bf16((b, nt * 64, hq, d), 350)
     k, v = (randn_bf16((b, nt * 64, hkv, d), 351 + j) for j in range(2))
-    rng = np.random.default_rng(35 + int(density * 100))
+    rng = np.random.default_rng(35 + int(density * 100) + (d - 128))
     sizes = np.full(nt, 64, dtype=np.int32)
     sizes[rng.choice(nt, 30, replace=False)] = rng.integers(0, 64, 30)  # some empty tiles
     bmap = rng.random((b, hq, nt, nt)) < density
@@ -120,8 +122,9 @@ def test_head_dim_128_long_kept_lists(density):
     assert_close("lse", host(lse)[:, :, rows][fin], ref_l[:, :, rows][fin], LSE_TOL)
 
 
-def test_full_map_matches_dense_oracle_and_is_deterministic():
-    b, nt, h, d = 1, 5, 3, 128
+@pytest.mark.parametrize("d", [128, 96, 256])
+def test_full_map_matches_dense_oracle_and_is_deterministic(d):
+    b, nt, h = 1, 5, 3
     q, k, v = (randn_bf16((b, nt * 64, h, d), 320 + j) for j in range(3))
     bmap = np.ones((b, h, nt, nt), dtype=bool)
     sizes = np.full(nt, 64, dtype=np.int32)
@@ -135,7 +138,7 @@ def test_full_map_matches_dense_oracle_and_is_deterministic():
 
 
 def test_item_order_longest_first_is_a_permutation():
-    # The head_dim-128 kernel runs the query tiles of each XCD chunk (8 equal
+    # The pipelined kernel runs the query tiles of each XCD chunk (8 equal
     # chunks of the (batch, head, tile) items) longest first. The order it
     # leaves in the workspace (after the index lists and their lengths) must
     # be a permutation of each chunk, non-increasing in the 16 count classes
