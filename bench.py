@@ -57,6 +57,10 @@ TRAFFIC = {
                    "write_kib": 74496.3, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
     "dense_d256": {"kernel": "prefill_pipe_kernel<256,false,false,4,true>", "fetch_kib": 149842.2,
                    "write_kib": 115987.4, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
+    "sparse_d64": {"kernel": "block_sparse_fwd_kernel<64>"},
+    "sparse_d96": {"kernel": "block_sparse_pipe_kernel<96>"},
+    "sparse_d192": {"kernel": "block_sparse_pipe_kernel<192>"},
+    "sparse_d256": {"kernel": "block_sparse_pipe_kernel<256>"},
     "decode_d96": {"kernel": "paged_decode_stream_kernel<96>"},
     "decode_d192": {"kernel": "paged_decode_stream_kernel<192>"},
     "decode_d64": {"kernel": "paged_decode_stream_kernel<64>", "fetch_kib": 1226024.5, "write_kib": 2602.3,
@@ -420,11 +424,12 @@ def bench_sparse(case, steps, warmup):
 
 
 def bench_head_dims(steps, warmup):
-    """The head dims other than 128 that the pages list: dense non-causal
-    prefill of 2 x 4096 rows with 24 heads at D = 64, 96, 192, 256, and decode
-    over workload 4's 64 contexts (32 query / 8 kv heads, a random permutation
-    of cache blocks) at D = 64, 96, 192 and 256, inputs drawn on the device. Returns
-    (workload name, kind, StepTime, algorithmic work, bound) per line."""
+    """The head dims other than 128 that the pages list (D = 64, 96, 192,
+    256): dense non-causal prefill of 2 x 4096 rows with 24 heads, decode over
+    workload 4's 64 contexts (32 query / 8 kv heads, a random permutation of
+    cache blocks), and block-sparse attention on workload 5's tile grid with
+    seeded random top-32 maps; inputs drawn on the device. Returns (workload
+    name, kind, StepTime, algorithmic work, bound) per line."""
     dev = torch.device("cuda")
     rows = []
     for d in (64, 96, 192, 256):
@@ -460,6 +465,25 @@ def bench_head_dims(steps, warmup):
         rows.append((f"paged-decode-64seq-ctx1k-32k-h32kv8-d{d}", f"decode_d{d}", t, nbytes, "hbm"))
         del cache, q, out, ws
         torch.cuda.empty_cache()
+    # block-sparse on workload 5's tile grid (256 full tiles, 12 heads), each
+    # query tile keeping 32 key tiles drawn at random (seeded)
+    nt, h = 256, 12
+    rng = np.random.default_rng(5)
+    kept = np.zeros((1, h, nt, nt), dtype=np.uint8)
+    for hh in range(h):
+        for a in range(nt):
+            kept[0, hh, a, rng.choice(nt, 32, replace=False)] = 1
+    bmap = torch.from_numpy(kept).to(dev)
+    sizes = torch.full((nt,), 64, dtype=torch.int32, device=dev)
+    ws = torch.empty(sav.attn_block_sparse_workspace_size(1, h, nt), dtype=torch.uint8, device=dev)
+    for d in (64, 96, 192, 256):
+        q, k, v = (workloads.randn_bf16_on((1, nt * 64, h, d), 7900 + 10 * d + j, dev) for j in range(3))
+        out = torch.empty_like(q)
+        t = time_steps(lambda: sav.attn_block_sparse_fwd(q, k, v, bmap, sizes, d ** -0.5, out=out, workspace=ws),
+                       steps, warmup)
+        flops = sparse_flops(kept, sizes.cpu().numpy(), d)
+        rows.append((f"block-sparse-256tiles-h12-top32-d{d}", f"sparse_d{d}", t, flops, "mfma"))
+        del q, k, v, out
     return rows
 
 
