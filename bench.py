@@ -46,47 +46,54 @@ _PREFILL_SRC = ["prefill_pipe.hip", "pipe.hpp", "attn_common.hpp", "key_rows.hpp
 _DECODE_SRC = ["paged_decode_stream.hip", "attn_common.hpp"]
 _SPARSE_SRC = ["block_sparse_pipe.hip", "pipe.hpp", "attn_common.hpp"]
 _VARLEN_SRC = ["varlen_fwd.hip", "attn_common.hpp", "key_rows.hpp"]
+_SPARSE_GEN_SRC = ["block_sparse.hip", "attn_common.hpp"]
 TRAFFIC = {
-    "tiny": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 247.6, "write_kib": 132.1,
+    "tiny": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 247.5, "write_kib": 132.1,
              "sources": _VARLEN_SRC, "sha256": "4f83bfe854bf432a"},
-    "dense_d64": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 67739.7, "write_kib": 25344.0,
+    "dense_d64": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 67762.5, "write_kib": 25344.0,
                   "sources": _VARLEN_SRC, "sha256": "4f83bfe854bf432a"},
-    "dense_d96": {"kernel": "prefill_pipe_kernel<96,false,false,4,true>", "fetch_kib": 73808.8, "write_kib": 37661.2,
-                  "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
-    "dense_d192": {"kernel": "prefill_pipe_kernel<192,false,false,4,true>", "fetch_kib": 110838.7,
-                   "write_kib": 74496.3, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
-    "dense_d256": {"kernel": "prefill_pipe_kernel<256,false,false,4,true>", "fetch_kib": 149842.2,
-                   "write_kib": 115987.4, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
-    "sparse_d64": {"kernel": "block_sparse_fwd_kernel<64>"},
-    "sparse_d96": {"kernel": "block_sparse_pipe_kernel<96>"},
-    "sparse_d192": {"kernel": "block_sparse_pipe_kernel<192>"},
-    "sparse_d256": {"kernel": "block_sparse_pipe_kernel<256>"},
-    "decode_d96": {"kernel": "paged_decode_stream_kernel<96>"},
-    "decode_d192": {"kernel": "paged_decode_stream_kernel<192>"},
-    "decode_d64": {"kernel": "paged_decode_stream_kernel<64>", "fetch_kib": 1226024.5, "write_kib": 2602.3,
-                   "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "decode_d256": {"kernel": "paged_decode_stream_kernel<256>", "fetch_kib": 4878453.7, "write_kib": 3862.3,
-                    "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "dense": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 73859.1, "write_kib": 49937.4,
-              "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
-    "causal": {"kernel": "prefill_pipe_kernel<128,true,false,4,true>", "fetch_kib": 111842.3, "write_kib": 142480.5,
-               "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
-    "paged": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2443513.0, "write_kib": 3042.6,
-              "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "sparse": {"kernel": "block_sparse_pipe_kernel<128>", "fetch_kib": 251933.5, "write_kib": 49921.2,
-               "sources": _SPARSE_SRC, "sha256": "4500acdc4cc28950"},
-    "paged_prefill": {"kernel": "prefill_pipe_kernel<128,true,true,8,false>", "fetch_kib": 709416.2,
-                      "write_kib": 87201.4, "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
-    "spec": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2445751.0, "write_kib": 12163.3,
-             "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "h3": {"kernel": "block_sparse_pipe_kernel<128>", "fetch_kib": 468647.6, "write_kib": 51484.8,
-           "sources": _SPARSE_SRC, "sha256": "4500acdc4cc28950"},
-    "swa": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 531392.9, "write_kib": 3081.2,
-            "sources": _DECODE_SRC, "sha256": "2ed61a3a26b6df66"},
-    "masked": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 28947.8, "write_kib": 50061.5,
-               "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
-    "padded": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 107378.2, "write_kib": 66236.1,
-               "sources": _PREFILL_SRC, "sha256": "091212d775dc6061"},
+    "dense_d96": {"kernel": "prefill_pipe_kernel<96,false,false,4,true>", "fetch_kib": 73828.9, "write_kib": 37654.2,
+                  "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+    "dense_d192": {"kernel": "prefill_pipe_kernel<192,false,false,4,true>", "fetch_kib": 110840.4,
+                   "write_kib": 74496.6, "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+    "dense_d256": {"kernel": "prefill_pipe_kernel<256,false,false,4,true>", "fetch_kib": 149568.1,
+                   "write_kib": 116445.9, "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+    "sparse_d64": {"kernel": "block_sparse_fwd_kernel<64>", "fetch_kib": 322502.6, "write_kib": 24576.2,
+                   "sources": _SPARSE_GEN_SRC, "sha256": "44f3ef3fc81f11ed"},
+    "sparse_d96": {"kernel": "block_sparse_pipe_kernel<96>", "fetch_kib": 254518.9, "write_kib": 36864.7,
+                   "sources": _SPARSE_SRC, "sha256": "6bc68b50e0b507a9"},
+    "sparse_d192": {"kernel": "block_sparse_pipe_kernel<192>", "fetch_kib": 644833.1, "write_kib": 73728.0,
+                    "sources": _SPARSE_SRC, "sha256": "6bc68b50e0b507a9"},
+    "sparse_d256": {"kernel": "block_sparse_pipe_kernel<256>", "fetch_kib": 992537.8, "write_kib": 98304.2,
+                    "sources": _SPARSE_SRC, "sha256": "6bc68b50e0b507a9"},
+    "decode_d96": {"kernel": "paged_decode_stream_kernel<96>", "fetch_kib": 1961229.5, "write_kib": 2284.5,
+                   "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
+    "decode_d192": {"kernel": "paged_decode_stream_kernel<192>", "fetch_kib": 3658876.8, "write_kib": 2901.1,
+                    "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
+    "decode_d64": {"kernel": "paged_decode_stream_kernel<64>", "fetch_kib": 1226021.5, "write_kib": 2602.5,
+                   "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
+    "decode_d256": {"kernel": "paged_decode_stream_kernel<256>", "fetch_kib": 4878549.4, "write_kib": 3862.2,
+                    "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
+    "dense": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 73859.3, "write_kib": 49939.0,
+              "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+    "causal": {"kernel": "prefill_pipe_kernel<128,true,false,4,true>", "fetch_kib": 111911.1, "write_kib": 142486.2,
+               "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+    "paged": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2443505.8, "write_kib": 3042.5,
+              "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
+    "sparse": {"kernel": "block_sparse_pipe_kernel<128>", "fetch_kib": 259852.9, "write_kib": 49920.8,
+               "sources": _SPARSE_SRC, "sha256": "6bc68b50e0b507a9"},
+    "paged_prefill": {"kernel": "prefill_pipe_kernel<128,true,true,8,false>", "fetch_kib": 708951.2,
+                      "write_kib": 87202.2, "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+    "spec": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2445743.6, "write_kib": 12164.9,
+             "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
+    "h3": {"kernel": "block_sparse_pipe_kernel<128>", "fetch_kib": 477754.3, "write_kib": 51488.2,
+           "sources": _SPARSE_SRC, "sha256": "6bc68b50e0b507a9"},
+    "swa": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 531385.8, "write_kib": 3081.3,
+            "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
+    "masked": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 28947.8, "write_kib": 50085.1,
+               "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+    "padded": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 107215.3, "write_kib": 66236.4,
+               "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
 }
 
 
