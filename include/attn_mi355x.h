@@ -311,10 +311,9 @@ attn_status_t attn_paged_kv_write(const void* k, const void* v, const int32_t* s
  *   lse           nullable; [num_heads, total_q] fp32
  *   workspace     device buffer of at least attn_paged_prefill_workspace_size()
  *                 bytes (nullable when that is 0). Short query runs (speculative
- *                 decoding: head_dim 64, 128 or 256 and max_seqlen_q *
- *                 num_heads/num_kv_heads <= 64) stream the cache once per kv
- *                 head like decode and keep fp32 partials there; longer ones
- *                 need none.
+ *                 decoding: max_seqlen_q * num_heads/num_kv_heads <= 64)
+ *                 stream the cache once per kv head like decode and keep fp32
+ *                 partials there; longer ones need none.
  * batch == 0 or total_q == 0 is a no-op.
  */
 attn_status_t attn_paged_prefill(const void* q, const void* kv_cache, const int32_t* block_tables,
