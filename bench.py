@@ -48,10 +48,8 @@ _SPARSE_SRC = ["block_sparse_pipe.hip", "pipe.hpp", "attn_common.hpp"]
 _VARLEN_SRC = ["varlen_fwd.hip", "attn_common.hpp", "key_rows.hpp"]
 _SPARSE_GEN_SRC = ["block_sparse.hip", "attn_common.hpp"]
 TRAFFIC = {
-    "tiny": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 247.5, "write_kib": 132.1,
-             "sources": _VARLEN_SRC, "sha256": "4f83bfe854bf432a"},
-    "dense_d64": {"kernel": "varlen_fwd_kernel<64,false,false>", "fetch_kib": 67762.5, "write_kib": 25344.0,
-                  "sources": _VARLEN_SRC, "sha256": "4f83bfe854bf432a"},
+    "tiny": {"kernel": "prefill_pipe_kernel<64,false,false,4,true>"},
+    "dense_d64": {"kernel": "prefill_pipe_kernel<64,false,false,4,true>"},
     "dense_d96": {"kernel": "prefill_pipe_kernel<96,false,false,4,true>", "fetch_kib": 73828.9, "write_kib": 37654.2,
                   "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
     "dense_d192": {"kernel": "prefill_pipe_kernel<192,false,false,4,true>", "fetch_kib": 110840.4,

@@ -54,7 +54,7 @@ __device__ __forceinline__ constexpr uint32_t block_key(uint32_t b) { return ((b
 // Tile geometry for head dim D.
 template <int D>
 struct Geom {
-  static_assert(D == 96 || D == 128 || D == 192 || D == 256, "pipelined tiles cover head dims 96 to 256");
+  static_assert(D == 64 || D == 96 || D == 128 || D == 192 || D == 256, "head dims 64 to 256");
   static constexpr int kRowLds = D <= 128 ? 256 : 512;     // LDS bytes of one key row (192 padded to 512)
   static constexpr int kRowsPerBlock = 1024 / kRowLds;      // 4 or 2
   static constexpr int kBlocks = 64 / kRowsPerBlock;        // load blocks per tile: 16 or 32
@@ -247,9 +247,12 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   constexpr int NT = 2 * Geom<D>::kQB;  // S^T MFMAs per step = PV MFMAs per step
   constexpr int NS = 2 * NT;            // MFMA slots
   // slot of element x's exp2: spread over slots 7 .. 7 + 23*NS/32 with 32 or
-  // more slots, two per slot over slots 7..22 with the 24 slots of head_dim 96
-  auto exp_slot = [](int x) constexpr { return NS >= 32 ? 7 + ((3 * x) / 4) * NS / 32 : 7 + x / 2; };
-  static_assert(NS >= 24, "the softmax needs 24 MFMA slots per step");
+  // more slots, two per slot over slots 7..22 with the 24 slots of head_dim
+  // 96, four per slot over slots 7..14 with the 16 slots of head_dim 64
+  auto exp_slot = [](int x) constexpr {
+    return NS >= 32 ? 7 + ((3 * x) / 4) * NS / 32 : NS >= 24 ? 7 + x / 2 : 7 + x / 4;
+  };
+  static_assert(NS >= 16, "the softmax needs 16 MFMA slots per step");
   if (mask) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {

@@ -1,5 +1,6 @@
-// Packed variable-length attention prefill for gfx950 at head_dim 64 (96, 128,
-// 192 and 256 take the pipelined kernels of prefill_pipe.hip).
+// Packed variable-length attention prefill for gfx950, register-staged: it
+// serves head_dim 64 under the causal mask (every other call takes the
+// pipelined kernels of prefill_pipe.hip, which measured faster there).
 //
 // Work unit: one workgroup of 4 waves owns a 128-row query tile of one
 // document and one query head; each wave owns 32 query rows. K/V tiles of 64
@@ -85,15 +86,8 @@ __global__ __launch_bounds__(kVarlenThreads, (D <= 128 ? 2 : 1)) void varlen_fwd
   Tile tl;
   if (ntiles > 0) tl.load(kb0 + rows.row(0), vb0 + rows.row(0), kv_stride, len_k, tid);
 
-  // Non-causal D <= 128 (two workgroups per CU): each tile's MFMA and softmax
-  // work runs at issue priority 1, the LDS store and next-tile loads at 0, so
-  // one workgroup's staging yields to the other's compute (+4 % at D=64, +7 %
-  // at D=96 on 2 x 4096 rows; the causal and larger-D kernels measured
-  // level or slower with it).
-  constexpr bool kPrio = !CAUSAL && D <= 128;
   for (int j = 0; j < ntiles; ++j) {
     const int n0 = j * kVarlenBN;
-    if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
     __syncthreads();
     tl.store(smem, tid);
     __syncthreads();
@@ -104,7 +98,6 @@ __global__ __launch_bounds__(kVarlenThreads, (D <= 128 ? 2 : 1)) void varlen_fwd
     // waves whose rows are all past the end or all above this tile's keys skip it
     bool active = wave_live;
     if (CAUSAL) active = active && (n0 <= wave_row0 + 31 + diag);
-    if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
     if (active) {
       f32x16 s[2];
       st.template scores<Tile::K_STRIDE>(smem, lane, s);
@@ -125,7 +118,6 @@ __global__ __launch_bounds__(kVarlenThreads, (D <= 128 ? 2 : 1)) void varlen_fwd
     }
   }
 
-  if constexpr (kPrio) __builtin_amdgcn_s_setprio(0);
   if (row < len_q) {
     float* lp = lse != nullptr ? lse + (long)h * total_q + q0 + row : nullptr;
     st.finish(out + ((long)(q0 + row) * hq + h) * D, lp, lane, c);
@@ -154,16 +146,9 @@ static hipError_t launch_varlen(const VarlenArgs& a, hipStream_t stream) {
 
 hipError_t launch_varlen_fwd(const VarlenArgs& a, hipStream_t stream) {
   if (prefill_pipe_supported(a)) return launch_prefill_pipe(a, stream);
-  const bool causal = a.causal != 0;
-#define ATTN_VARLEN_CASE(DIM)                                                              \
-  case DIM:                                                                                \
-    return causal ? launch_varlen<DIM, true>(a, stream) : launch_varlen<DIM, false>(a, stream);
-  switch (a.head_dim) {
-    ATTN_VARLEN_CASE(64)
-    default:
-      return hipErrorInvalidValue;
-  }
-#undef ATTN_VARLEN_CASE
+  // what the pipelined kernels leave: head_dim 64 under the causal mask
+  if (a.head_dim == 64 && a.causal) return launch_varlen<64, true>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 long varlen_grid_size(int batch, int max_seqlen_q, int num_heads) {

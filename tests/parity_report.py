@@ -23,6 +23,7 @@ FULL_SIZE = [
     ("8 sliding-window decode", "test_gpu_variants.py::test_sliding_window_decode_full_size_every_sequence"),
     ("9 masked cross-attention", "test_gpu_variants.py::test_masked_cross_full_size"),
     ("10 padded batch", "test_gpu_variants.py::test_padded_full_size"),
+    ("head_dim 64 dense 2 x 4096, 24 heads", "test_gpu_varlen.py::test_head_dim_full_size_every_row[64-False]"),
     ("head_dim 96 dense 2 x 4096, 24 heads", "test_gpu_varlen.py::test_head_dim_full_size_every_row[96-False]"),
     ("head_dim 192 dense 2 x 4096, 24 heads", "test_gpu_varlen.py::test_head_dim_full_size_every_row[192-False]"),
     ("head_dim 256 dense 2 x 4096, 24 heads", "test_gpu_varlen.py::test_head_dim_full_size_every_row[256-False]"),

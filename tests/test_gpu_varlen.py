@@ -161,13 +161,13 @@ def test_random_varlen_head_dim_128(seed):
     check_full(case, few_keys=True)
 
 
-@pytest.mark.parametrize("d,causal", [(96, False), (192, False), (256, False), (256, True)])
+@pytest.mark.parametrize("d,causal", [(64, False), (96, False), (192, False), (256, False), (256, True)])
 def test_head_dim_full_size_every_row(d, causal):
-    """Head dims 96, 192 and 256 on the shape their throughput is measured on
-    (2 documents of 4096 rows, 24 heads, N(0,1) inputs), every row and head
-    against the oracle: the pipelined kernel with padded LDS rows (96, 192),
-    512-byte rows (192, 256) and, at 192/256, its loads issued from inside the
-    step."""
+    """Head dims 64, 96, 192 and 256 on the shape their throughput is
+    measured on (2 documents of 4096 rows, 24 heads, N(0,1) inputs), every row
+    and head against the oracle: the pipelined kernel with padded LDS rows (64,
+    96, 192), 512-byte rows (192, 256) and, at 192/256, its loads issued from
+    inside the step."""
     case = varlen_case([4096, 4096], num_heads=24, num_kv_heads=24, head_dim=d, causal=causal, seed=7700 + d + causal,
                        name=f"dit-dense-b2-s4096-h24-d{d}" + ("-causal" if causal else ""))
     announce("varlen full-size", case.name)
