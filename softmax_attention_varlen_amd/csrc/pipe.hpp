@@ -299,32 +299,29 @@ __device__ __forceinline__ void tile_step_pp(f32x16 (&s)[2], f32x16 (&sn)[2], co
   static_for<NS>([&](auto slot_c) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
     hook(slot_c);
-    const int t = slot >> 1;
-    if ((slot & 1) == 0) {  // S^T of tile j+1: step t = (d-block t/2, key half t%2)
+    constexpr int t = slot >> 1;
+    if constexpr ((slot & 1) == 0) {  // S^T of tile j+1: step t = (d-block t/2, key half t%2)
       sn[t & 1] = mfma32x32x16(kr[t % PF], q[t >> 1], sn[t & 1]);
       if (t + PF < NT) kr[t % PF] = ld_lds16(kbase, ((t + PF) % 2) * kHalfBytes + ((t + PF) / 2) * 32);
-    } else if (PV) {  // PV of tile j-1: chunk t/OB, d-block t%OB
+    } else if constexpr (PV) {  // PV of tile j-1: chunk t/OB, d-block t%OB
       const bf16x8 a = va[t % PF];
       if (t + PF < NT) va[t % PF] = read_vt<D>(vbase, (t + PF) / OB, (t + PF) % OB);
       o[t % OB] = mfma32x32x16(a, p_prev[t / OB], o[t % OB]);
     }
-    if (slot < 4) {  // row maximum: chain slot over 8 keys (2 slots per chain pair)
+    if constexpr (slot < 4) {  // row maximum: chain slot over 8 keys (2 slots per chain pair)
+      constexpr int ch = slot;  // chain ch: half ch/2, elements 8(ch%2) .. +7
+      float m = fmaxf(s[ch >> 1][8 * (ch & 1)], s[ch >> 1][8 * (ch & 1) + 1]);
 #pragma unroll
-      for (int u = 0; u < 1; ++u) {
-        const int ch = slot;  // chain ch: half ch/2, elements 8(ch%2) .. +7
-        float m = fmaxf(s[ch >> 1][8 * (ch & 1)], s[ch >> 1][8 * (ch & 1) + 1]);
-#pragma unroll
-        for (int i = 2; i < 8; ++i) m = fmaxf(m, s[ch >> 1][8 * (ch & 1) + i]);
-        mx4[ch] = m;
-      }
-    } else if (slot == 5) {
+      for (int i = 2; i < 8; ++i) m = fmaxf(m, s[ch >> 1][8 * (ch & 1) + i]);
+      mx4[ch] = m;
+    } else if constexpr (slot == 5) {
       const float mx = pair_max(fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3])));
       const float m_new = fmaxf(st.m, mx);
       need = (m_new - st.m) * c > kRescaleThreshold;  // true on the first finite maximum
       alpha = need ? hw_exp2((st.m - m_new) * c) : 1.f;
       m_ref = need ? m_new : st.m;
       ms = (m_ref == kNegInf ? 0.f : m_ref) * c;
-    } else if (slot >= 7) {
+    } else if constexpr (slot >= 7) {
       // element x's exp2 runs in slot exp_slot(x) (slots 7..30 at head_dim
       // 128); its row-sum add, and the bf16 packing of a finished chunk, one
       // slot later, so that no VALU op waits on the exp2 issued just before it
@@ -419,21 +416,21 @@ __device__ __forceinline__ void tile_step_pp1(f32x16 (&s)[1], f32x16 (&sn)[1], c
   __builtin_amdgcn_sched_barrier(0);
   static_for<NS>([&](auto slot_c) __attribute__((always_inline)) {
     constexpr int slot = decltype(slot_c)::value;
-    const int t = slot >> 1;
-    if ((slot & 1) == 0) {  // S^T of tile j+1, d-block t
+    constexpr int t = slot >> 1;
+    if constexpr ((slot & 1) == 0) {  // S^T of tile j+1, d-block t
       sn[0] = mfma32x32x16(kr[t & 1], q[t], sn[0]);
       if (t + 2 < NT) kr[t & 1] = ld_lds16(kbase, (t + 2) * 32);
-    } else if (PV) {  // PV of tile j-1: chunk t/OB, d-block t%OB
+    } else if constexpr (PV) {  // PV of tile j-1: chunk t/OB, d-block t%OB
       const bf16x8 a = va[t & 1];
       if (t + 2 < NT) va[t & 1] = read_vt<D>(vbase, (t + 2) / OB, (t + 2) % OB);
       o[t % OB] = mfma32x32x16(a, p_prev[t / OB], o[t % OB]);
     }
-    if (slot < 2) {  // row maximum: chain slot over elements 8*slot .. +7
+    if constexpr (slot < 2) {  // row maximum: chain slot over elements 8*slot .. +7
       float m = fmaxf(s[0][8 * slot], s[0][8 * slot + 1]);
 #pragma unroll
       for (int i = 2; i < 8; ++i) m = fmaxf(m, s[0][8 * slot + i]);
       mx2[slot] = m;
-    } else if (slot == 2) {
+    } else if constexpr (slot == 2) {
       const float mx = pair_max(fmaxf(mx2[0], mx2[1]));
       const float m_new = fmaxf(st.m, mx);
       need = (m_new - st.m) * c > kRescaleThreshold;  // true on the first finite maximum
