@@ -48,50 +48,52 @@ _SPARSE_SRC = ["block_sparse_pipe.hip", "pipe.hpp", "attn_common.hpp"]
 _VARLEN_SRC = ["varlen_fwd.hip", "attn_common.hpp", "key_rows.hpp"]
 _SPARSE_GEN_SRC = ["block_sparse.hip", "attn_common.hpp"]
 TRAFFIC = {
-    "tiny": {"kernel": "prefill_pipe_kernel<64,false,false,4,true>"},
-    "dense_d64": {"kernel": "prefill_pipe_kernel<64,false,false,4,true>"},
-    "dense_d96": {"kernel": "prefill_pipe_kernel<96,false,false,4,true>", "fetch_kib": 73828.9, "write_kib": 37654.2,
-                  "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
-    "dense_d192": {"kernel": "prefill_pipe_kernel<192,false,false,4,true>", "fetch_kib": 110840.4,
-                   "write_kib": 74496.6, "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
-    "dense_d256": {"kernel": "prefill_pipe_kernel<256,false,false,4,true>", "fetch_kib": 149568.1,
-                   "write_kib": 116445.9, "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
-    "sparse_d64": {"kernel": "block_sparse_fwd_kernel<64>", "fetch_kib": 322502.6, "write_kib": 24576.2,
+    "tiny": {"kernel": "prefill_pipe_kernel<64,false,false,4,true>", "fetch_kib": 289.4, "write_kib": 132.1,
+             "sources": _PREFILL_SRC, "sha256": "0fdaca010aad7acb"},
+    "dense_d64": {"kernel": "prefill_pipe_kernel<64,false,false,4,true>", "fetch_kib": 36967.4, "write_kib": 25344.0,
+                  "sources": _PREFILL_SRC, "sha256": "0fdaca010aad7acb"},
+    "dense_d96": {"kernel": "prefill_pipe_kernel<96,false,false,4,true>", "fetch_kib": 73826.7, "write_kib": 37663.8,
+                  "sources": _PREFILL_SRC, "sha256": "0fdaca010aad7acb"},
+    "dense_d192": {"kernel": "prefill_pipe_kernel<192,false,false,4,true>", "fetch_kib": 110841.0,
+                   "write_kib": 74496.2, "sources": _PREFILL_SRC, "sha256": "0fdaca010aad7acb"},
+    "dense_d256": {"kernel": "prefill_pipe_kernel<256,false,false,4,true>", "fetch_kib": 149700.3,
+                   "write_kib": 116571.4, "sources": _PREFILL_SRC, "sha256": "0fdaca010aad7acb"},
+    "sparse_d64": {"kernel": "block_sparse_fwd_kernel<64>", "fetch_kib": 322495.8, "write_kib": 24576.7,
                    "sources": _SPARSE_GEN_SRC, "sha256": "44f3ef3fc81f11ed"},
-    "sparse_d96": {"kernel": "block_sparse_pipe_kernel<96>", "fetch_kib": 254518.9, "write_kib": 36864.7,
-                   "sources": _SPARSE_SRC, "sha256": "6bc68b50e0b507a9"},
-    "sparse_d192": {"kernel": "block_sparse_pipe_kernel<192>", "fetch_kib": 644833.1, "write_kib": 73728.0,
-                    "sources": _SPARSE_SRC, "sha256": "6bc68b50e0b507a9"},
-    "sparse_d256": {"kernel": "block_sparse_pipe_kernel<256>", "fetch_kib": 992537.8, "write_kib": 98304.2,
-                    "sources": _SPARSE_SRC, "sha256": "6bc68b50e0b507a9"},
-    "decode_d96": {"kernel": "paged_decode_stream_kernel<96>", "fetch_kib": 1961229.5, "write_kib": 2284.5,
+    "sparse_d96": {"kernel": "block_sparse_pipe_kernel<96>", "fetch_kib": 263609.2, "write_kib": 36864.7,
+                   "sources": _SPARSE_SRC, "sha256": "de8b74545248f2d3"},
+    "sparse_d192": {"kernel": "block_sparse_pipe_kernel<192>", "fetch_kib": 651084.4, "write_kib": 73728.0,
+                    "sources": _SPARSE_SRC, "sha256": "de8b74545248f2d3"},
+    "sparse_d256": {"kernel": "block_sparse_pipe_kernel<256>", "fetch_kib": 969442.6, "write_kib": 98304.1,
+                    "sources": _SPARSE_SRC, "sha256": "de8b74545248f2d3"},
+    "decode_d96": {"kernel": "paged_decode_stream_kernel<96>", "fetch_kib": 1962417.4, "write_kib": 2285.3,
                    "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
-    "decode_d192": {"kernel": "paged_decode_stream_kernel<192>", "fetch_kib": 3658876.8, "write_kib": 2901.1,
+    "decode_d192": {"kernel": "paged_decode_stream_kernel<192>", "fetch_kib": 3658877.8, "write_kib": 2901.3,
                     "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
-    "decode_d64": {"kernel": "paged_decode_stream_kernel<64>", "fetch_kib": 1226021.5, "write_kib": 2602.5,
+    "decode_d64": {"kernel": "paged_decode_stream_kernel<64>", "fetch_kib": 1226021.6, "write_kib": 2602.2,
                    "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
-    "decode_d256": {"kernel": "paged_decode_stream_kernel<256>", "fetch_kib": 4878549.4, "write_kib": 3862.2,
+    "decode_d256": {"kernel": "paged_decode_stream_kernel<256>", "fetch_kib": 4878550.5, "write_kib": 3862.3,
                     "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
     "dense": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 73859.3, "write_kib": 49939.0,
-              "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+              "sources": _PREFILL_SRC, "sha256": "0fdaca010aad7acb"},
     "causal": {"kernel": "prefill_pipe_kernel<128,true,false,4,true>", "fetch_kib": 111911.1, "write_kib": 142486.2,
-               "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+               "sources": _PREFILL_SRC, "sha256": "0fdaca010aad7acb"},
     "paged": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2443505.8, "write_kib": 3042.5,
               "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
     "sparse": {"kernel": "block_sparse_pipe_kernel<128>", "fetch_kib": 259852.9, "write_kib": 49920.8,
-               "sources": _SPARSE_SRC, "sha256": "6bc68b50e0b507a9"},
+               "sources": _SPARSE_SRC, "sha256": "de8b74545248f2d3"},
     "paged_prefill": {"kernel": "prefill_pipe_kernel<128,true,true,8,false>", "fetch_kib": 708951.2,
-                      "write_kib": 87202.2, "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+                      "write_kib": 87202.2, "sources": _PREFILL_SRC, "sha256": "0fdaca010aad7acb"},
     "spec": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 2445743.6, "write_kib": 12164.9,
              "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
     "h3": {"kernel": "block_sparse_pipe_kernel<128>", "fetch_kib": 477754.3, "write_kib": 51488.2,
-           "sources": _SPARSE_SRC, "sha256": "6bc68b50e0b507a9"},
+           "sources": _SPARSE_SRC, "sha256": "de8b74545248f2d3"},
     "swa": {"kernel": "paged_decode_stream_kernel<128>", "fetch_kib": 531385.8, "write_kib": 3081.3,
             "sources": _DECODE_SRC, "sha256": "867349d6b3aa0d47"},
     "masked": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 28947.8, "write_kib": 50085.1,
-               "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+               "sources": _PREFILL_SRC, "sha256": "0fdaca010aad7acb"},
     "padded": {"kernel": "prefill_pipe_kernel<128,false,false,4,true>", "fetch_kib": 107215.3, "write_kib": 66236.4,
-               "sources": _PREFILL_SRC, "sha256": "d5f9f1d5f7d1c8ce"},
+               "sources": _PREFILL_SRC, "sha256": "0fdaca010aad7acb"},
 }
 
 
