@@ -3,8 +3,9 @@
 // Step 1 (map -> index): each map row (batch, head, query tile) becomes the
 // ascending list of kept key tiles plus a count, built with a wave ballot and
 // a prefix popcount (bit-exact, no atomics).
-// Step 2 (attention, head_dim other than 128; head_dim 128 has its own
-// pipelined kernel): one workgroup of 2 waves owns one (batch, head, query
+// Step 2 (attention at head_dim 64, and beyond 3072 tiles; head_dims 96 to
+// 256 otherwise take the pipelined kernel of block_sparse_pipe.hip): one
+// workgroup of 2 waves owns one (batch, head, query
 // tile); each wave owns 32 query rows. It walks only the kept key tiles, each
 // staged through LDS exactly as in the varlen prefill (K row-major, V
 // transposed), with the same S^T = K Q^T MFMA / online softmax / O^T += V^T P^T
@@ -18,7 +19,7 @@ namespace attn {
 constexpr int kSparseTile = 64;
 constexpr int kSparseThreads = 128;
 
-// With `sizes` (the launch of the head_dim-128 kernel) tiles of size 0 are
+// With `sizes` (the launch of the pipelined kernel) tiles of size 0 are
 // dropped and each entry is packed as (size << 24) | tile, so the attention
 // loop reads one word per kept tile.
 __global__ __launch_bounds__(256) void map_to_index_kernel(const uint8_t* __restrict__ map, int rows, int n_cols,
