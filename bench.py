@@ -517,6 +517,31 @@ def _growing_sample(run, start, limit, budget_s):
         n = min(2 * n, limit)
 
 
+def gemm_reference(steps, warmup, n=8192, kinds=("randn", "constant")):
+    """Context for the MFMA roofline: the vendor's bf16 GEMM (torch.mm, which
+    runs hipBLASLt) on square n^3 products, timed like the workloads. On
+    seeded N(0,1) operands (the workloads' value distribution) and on constant
+    operands: the two run the same instructions, and the gap between them is
+    the clock the chip gives up for operand bit toggling. Not part of any
+    workload's step."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(8192)
+    out = {"kind": "torch.mm bf16 (hipBLASLt), m = n = k = %d" % n, "unit": "TFLOP/s"}
+    makers = {"randn": lambda: torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g),
+              "constant": lambda: torch.ones(n, n, device=dev, dtype=torch.bfloat16)}
+    for name in kinds:
+        a, b = makers[name](), makers[name]()
+        c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+        t = time_steps(lambda: torch.mm(a, b, out=c), steps, warmup)
+        out[name] = round(2.0 * n ** 3 / (t.mean * 1e-3) / 1e12, 1)
+        del a, b, c
+    if "randn" in out:
+        out["randn_frac_of_peak"] = round(out["randn"] / PEAK_BF16_TFLOPS, 4)
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline_varlen(case, budget_s):
     """The first n query rows of every document (all heads), n doubling until the
     oracle takes budget_s; rate in the GPU line's unit (algorithmic flops of the
@@ -608,15 +633,18 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["dense", "tiny", "causal", "paged", "sparse", "h3", "paged_prefill", "spec", "swa",
-                                       "masked", "padded", "copy", "head_dims"],
+                                       "masked", "padded", "copy", "head_dims", "gemm_ref", "gemm_ref_const"],
                     default=None,
                     help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
                          "copy, the reference that scales the HBM byte counters; 'head_dims' times the head "
-                         "dims other than 128")
+                         "dims other than 128; 'gemm_ref' / 'gemm_ref_const' time the vendor bf16 GEMM on "
+                         "N(0,1) / constant operands")
     ap.add_argument("--clock-warmup-ms", type=float, default=CLOCK_WARMUP_MS,
                     help="repeat each workload's step for this long before its warm-up steps (0: off)")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip timing the vendor bf16 GEMM that puts the MFMA roofline in context")
     ap.add_argument("--cpu-budget-s", type=float, default=4.0,
                     help="seconds of fp64 oracle work per workload for the cpu baselines (workloads 1-5)")
     args = ap.parse_args()
@@ -641,7 +669,10 @@ def main():
         print(json.dumps({"metric": "device copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n,
                           "ms": round(ms, 5), "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}))
         return
-
+    if args.only in ("gemm_ref", "gemm_ref_const"):
+        ref = gemm_reference(args.steps, args.warmup, kinds=("randn",) if args.only == "gemm_ref" else ("constant",))
+        print(json.dumps({"metric": "vendor bf16 GEMM", **ref}))
+        return
 
     secondary = []
     head = None
@@ -772,6 +803,11 @@ def main():
         "roofline": roofline("dense", "mfma", tf, flops),
         "secondary": secondary,
     }
+    if not args.no_gemm_reference:
+        ref = gemm_reference(args.steps, args.warmup)
+        ref["headline_over_randn"] = round(tf / ref["randn"], 4)
+        line["mfma_reference"] = ref
+        log(f"vendor bf16 GEMM: {ref['randn']} TFLOP/s on N(0,1) operands, {ref['constant']} on constant ones")
     if cpu:
         log("timing the fp64 oracle on a sample (cpu baseline)")
         line["cpu_baseline"] = cpu_baseline_varlen(case, budget)
