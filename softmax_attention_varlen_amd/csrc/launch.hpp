@@ -54,7 +54,8 @@ MaskedLayout plan_masked(int batch, int seqlen_q, int seqlen_k, int num_heads, i
                          bool mask_queries);
 hipError_t launch_masked_fwd(const VarlenArgs& base, const uint8_t* key_mask, int seqlen_q, int seqlen_k,
                              bool mask_queries, const MaskedLayout& l, void* workspace, hipStream_t stream);
-// head_dims 128, 192, 256: pipelined direct-to-LDS prefill (prefill_pipe.hip)
+// head_dims 96 to 256, and 64 without the causal mask: pipelined
+// direct-to-LDS prefill (prefill_pipe.hip)
 bool prefill_pipe_supported(const VarlenArgs& a);
 hipError_t launch_prefill_pipe(const VarlenArgs& a, hipStream_t stream);
 long varlen_grid_size(int batch, int max_seqlen_q, int num_heads);

@@ -1,16 +1,17 @@
-// Building blocks of the pipelined attention kernels on gfx950 for head dims
-// 128, 192 and 256 (dense/varlen prefill; 64-token block-sparse attention at
-// head_dim 128).
+// Building blocks of the pipelined attention kernels on gfx950: dense/varlen
+// prefill at head dims 64 (without the causal mask), 96, 128, 192 and 256, and
+// 64-token block-sparse attention at 96 to 256.
 //
 // LDS tile layout. A K (or V) tile holds 64 keys and is filled by
 // direct-to-LDS 16-byte loads, each writing one contiguous 1 KB load block.
-// A key's row takes 256 bytes in LDS at head_dim 128 and 512 at 192 and 256
-// (192 pads each row to 512), so a block holds 4 or 2 rows. Blocks sit 1040
+// A key's row takes 256 bytes in LDS at head dims up to 128 and 512 at 192
+// and 256 (64, 96 and 192 pad their rows; a pad piece re-reads the row's last
+// real 16 bytes), so a block holds 4 or 2 rows. Blocks sit 1040
 // bytes apart (16 bytes = 4 banks of pad). Keys go in groups of 16: within a
 // group, key k%16 = (b3 b2 b1 b0) lives in block (b1 b0 b3 b2) of a run of 16
-// blocks; at 128 the four groups are the four rows of those 16 blocks, at
-// 192/256 groups 0 and 1 take rows 0 of two runs of 16 blocks and groups 2
-// and 3 their rows 1. A 16-lane slice of a K read then covers 16 blocks of
+// blocks; with 256-byte rows the four groups are the four rows of those 16
+// blocks, with 512-byte rows groups 0 and 1 take rows 0 of two runs of 16
+// blocks and groups 2 and 3 their rows 1. A 16-lane slice of a K read then covers 16 blocks of
 // one run (all 64 banks once), and a 32-lane slice of a transposing V read
 // (4 keys x 64 bytes) puts its 4 rows 16 banks apart: both conflict-free on
 // gfx950's 64-bank LDS, as measured at head_dim 128. Every LDS address is a
