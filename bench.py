@@ -542,6 +542,49 @@ def gemm_reference(steps, warmup, n=8192, kinds=("randn", "constant")):
     return out
 
 
+def mfma_stream_reference(steps, warmup, iters=4096, kinds=("randn", "constant")):
+    """The sustained rate of the attention kernels' MFMA (32x32x16 bf16) in a
+    plain stream on operands held in registers (the calibration kernel in
+    softmax_attention_varlen_amd/calib), two 4-wave workgroups per CU, on
+    seeded N(0,1) operands and on constant ones. None when that library is not
+    built."""
+    import ctypes
+
+    path = os.path.join(ROOT, "softmax_attention_varlen_amd", "libattn_calib.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    fn = lib.attn_calib_mfma_stream
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    dev = torch.device("cuda")
+    wgs = 2 * torch.cuda.get_device_properties(dev).multi_processor_count
+    threads = wgs * 256
+    flops = float(wgs) * 4 * iters * 8 * 32768  # 4 waves, iters x 8 MFMAs each
+    sink = torch.empty(threads, device=dev, dtype=torch.float32)
+    g = torch.Generator(device=dev)
+    g.manual_seed(32)
+    out = {"kind": "v_mfma_f32_32x32x16_bf16 stream, operands in registers, %d workgroups of 4 waves" % wgs,
+           "unit": "TFLOP/s"}
+    for name in kinds:
+        shape = (16 * threads * 8,)
+        ops = (torch.randn(shape, device=dev, dtype=torch.bfloat16, generator=g) if name == "randn"
+               else torch.ones(shape, device=dev, dtype=torch.bfloat16))
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def step():
+            rc = fn(ops.data_ptr(), sink.data_ptr(), wgs, iters, stream)
+            if rc != 0:
+                raise RuntimeError(f"calibration kernel launch failed ({rc})")
+
+        t = time_steps(step, steps, warmup)
+        out[name] = round(flops / (t.mean * 1e-3) / 1e12, 1)
+        del ops
+    if "randn" in out:
+        out["randn_frac_of_peak"] = round(out["randn"] / PEAK_BF16_TFLOPS, 4)
+    return out
+
+
 def cpu_baseline_varlen(case, budget_s):
     """The first n query rows of every document (all heads), n doubling until the
     oracle takes budget_s; rate in the GPU line's unit (algorithmic flops of the
@@ -633,12 +676,14 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["dense", "tiny", "causal", "paged", "sparse", "h3", "paged_prefill", "spec", "swa",
-                                       "masked", "padded", "copy", "head_dims", "gemm_ref", "gemm_ref_const"],
+                                       "masked", "padded", "copy", "head_dims", "gemm_ref", "gemm_ref_const",
+                                       "mfma_stream", "mfma_stream_const"],
                     default=None,
                     help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
                          "copy, the reference that scales the HBM byte counters; 'head_dims' times the head "
                          "dims other than 128; 'gemm_ref' / 'gemm_ref_const' time the vendor bf16 GEMM on "
-                         "N(0,1) / constant operands")
+                         "N(0,1) / constant operands; 'mfma_stream' / 'mfma_stream_const' the MFMA "
+                         "calibration kernel on the same two")
     ap.add_argument("--clock-warmup-ms", type=float, default=CLOCK_WARMUP_MS,
                     help="repeat each workload's step for this long before its warm-up steps (0: off)")
     ap.add_argument("--no-secondary", action="store_true")
@@ -672,6 +717,10 @@ def main():
     if args.only in ("gemm_ref", "gemm_ref_const"):
         ref = gemm_reference(args.steps, args.warmup, kinds=("randn",) if args.only == "gemm_ref" else ("constant",))
         print(json.dumps({"metric": "vendor bf16 GEMM", **ref}))
+        return
+    if args.only in ("mfma_stream", "mfma_stream_const"):
+        kinds = ("randn",) if args.only == "mfma_stream" else ("constant",)
+        print(json.dumps({"metric": "MFMA stream", **(mfma_stream_reference(args.steps, args.warmup, kinds=kinds) or {})}))
         return
 
     secondary = []
@@ -806,8 +855,14 @@ def main():
     if not args.no_gemm_reference:
         ref = gemm_reference(args.steps, args.warmup)
         ref["headline_over_randn"] = round(tf / ref["randn"], 4)
-        line["mfma_reference"] = ref
         log(f"vendor bf16 GEMM: {ref['randn']} TFLOP/s on N(0,1) operands, {ref['constant']} on constant ones")
+        stream_ref = mfma_stream_reference(args.steps, args.warmup)
+        if stream_ref is not None:
+            stream_ref["headline_over_randn"] = round(tf / stream_ref["randn"], 4)
+            log(f"MFMA stream: {stream_ref['randn']} TFLOP/s on N(0,1) operands, {stream_ref['constant']} on "
+                f"constant ones")
+        ref["mfma_stream"] = stream_ref
+        line["mfma_reference"] = ref
     if cpu:
         log("timing the fp64 oracle on a sample (cpu baseline)")
         line["cpu_baseline"] = cpu_baseline_varlen(case, budget)

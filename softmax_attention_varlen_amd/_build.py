@@ -67,7 +67,21 @@ def build(verbose: bool = False, jobs: int | None = None, extra_flags=()) -> str
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB_PATH)
+    build_calib(verbose=verbose, extra_flags=extra_flags)
     return LIB_PATH
+
+
+# The MFMA calibration kernel that bench.py times beside the attention
+# roofline; a library of its own, not part of the attention C ABI.
+CALIB_SOURCE = os.path.join(HERE, "calib", "mfma_stream.hip")
+CALIB_LIB_PATH = os.path.join(HERE, "libattn_calib.so")
+
+
+def build_calib(verbose: bool = False, extra_flags=()) -> str:
+    tmp = CALIB_LIB_PATH + ".tmp"
+    _run([_hipcc(), "-x", "hip", *COMMON_FLAGS, *extra_flags, "-shared", CALIB_SOURCE, "-o", tmp], verbose)
+    os.replace(tmp, CALIB_LIB_PATH)
+    return CALIB_LIB_PATH
 
 
 if __name__ == "__main__":
