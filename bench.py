@@ -273,9 +273,15 @@ def time_steps(step, steps: int, warmup: int) -> StepTime:
     return StepTime(per_step, ev[0].elapsed_time(ev[-1]) / steps)
 
 
-def bench_varlen(case, steps, warmup, with_lse=True):
+def bench_varlen(case, steps, warmup, with_lse=True, operands="randn"):
+    """operands: "randn" (the workload's seeded inputs) or "ones" / "zeros"
+    (the same shapes filled with one constant, for the power measurement of
+    --only dense_const: the kernel runs the same instructions either way)."""
     dev = torch.device("cuda")
     q, k, v = case.q.to(dev), case.k.to(dev), case.v.to(dev)
+    if operands != "randn":
+        fill = torch.ones_like if operands == "ones" else torch.zeros_like
+        q, k, v = fill(q), fill(k), fill(v)
     cu_q = torch.from_numpy(case.cu_seqlens_q).to(dev)
     cu_k = torch.from_numpy(case.cu_seqlens_k).to(dev)
     out = torch.empty_like(q)
@@ -677,13 +683,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["dense", "tiny", "causal", "paged", "sparse", "h3", "paged_prefill", "spec", "swa",
                                        "masked", "padded", "copy", "head_dims", "gemm_ref", "gemm_ref_const",
-                                       "mfma_stream", "mfma_stream_const"],
+                                       "mfma_stream", "mfma_stream_const", "dense_const"],
                     default=None,
                     help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
                          "copy, the reference that scales the HBM byte counters; 'head_dims' times the head "
                          "dims other than 128; 'gemm_ref' / 'gemm_ref_const' time the vendor bf16 GEMM on "
                          "N(0,1) / constant operands; 'mfma_stream' / 'mfma_stream_const' the MFMA "
-                         "calibration kernel on the same two")
+                         "calibration kernel on the same two; 'dense_const' the dense workload on all-ones "
+                         "and all-zero inputs")
     ap.add_argument("--clock-warmup-ms", type=float, default=CLOCK_WARMUP_MS,
                     help="repeat each workload's step for this long before its warm-up steps (0: off)")
     ap.add_argument("--no-secondary", action="store_true")
@@ -717,6 +724,17 @@ def main():
     if args.only in ("gemm_ref", "gemm_ref_const"):
         ref = gemm_reference(args.steps, args.warmup, kinds=("randn",) if args.only == "gemm_ref" else ("constant",))
         print(json.dumps({"metric": "vendor bf16 GEMM", **ref}))
+        return
+    if args.only == "dense_const":
+        # the headline workload with all-ones, then all-zero Q, K and V: the same
+        # instructions as on N(0,1) inputs, less operand bit toggling
+        case = workloads.config2()
+        rec = {"metric": "dense attention on constant inputs", "workload": case.name, "unit": "TFLOP/s"}
+        for operands in ("ones", "zeros"):
+            t, flops = bench_varlen(case, args.steps, args.warmup, operands=operands)
+            rec[operands] = round(flops / (t.mean * 1e-3) / 1e12, 1)
+            rec[operands + "_ms"] = round(t.mean, 5)
+        print(json.dumps(rec))
         return
     if args.only in ("mfma_stream", "mfma_stream_const"):
         kinds = ("randn",) if args.only == "mfma_stream" else ("constant",)
