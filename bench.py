@@ -683,14 +683,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", choices=["dense", "tiny", "causal", "paged", "sparse", "h3", "paged_prefill", "spec", "swa",
                                        "masked", "padded", "copy", "head_dims", "gemm_ref", "gemm_ref_const",
-                                       "mfma_stream", "mfma_stream_const", "dense_const"],
+                                       "mfma_stream", "mfma_stream_const", "dense_const", "causal_const",
+                                       "sparse_const"],
                     default=None,
                     help="time one workload only (for profiling runs); 'copy' times a plain 1 GiB device "
                          "copy, the reference that scales the HBM byte counters; 'head_dims' times the head "
                          "dims other than 128; 'gemm_ref' / 'gemm_ref_const' time the vendor bf16 GEMM on "
                          "N(0,1) / constant operands; 'mfma_stream' / 'mfma_stream_const' the MFMA "
-                         "calibration kernel on the same two; 'dense_const' the dense workload on all-ones "
-                         "and all-zero inputs")
+                         "calibration kernel on the same two; 'dense_const' / 'causal_const' / 'sparse_const' "
+                         "workloads 2, 3 and 5 on constant inputs")
     ap.add_argument("--clock-warmup-ms", type=float, default=CLOCK_WARMUP_MS,
                     help="repeat each workload's step for this long before its warm-up steps (0: off)")
     ap.add_argument("--no-secondary", action="store_true")
@@ -725,16 +726,35 @@ def main():
         ref = gemm_reference(args.steps, args.warmup, kinds=("randn",) if args.only == "gemm_ref" else ("constant",))
         print(json.dumps({"metric": "vendor bf16 GEMM", **ref}))
         return
-    if args.only == "dense_const":
-        # the headline workload with all-ones, then all-zero Q, K and V: the same
+    if args.only in ("dense_const", "causal_const"):
+        # workload 2 (or 3) with all-ones, then all-zero Q, K and V: the same
         # instructions as on N(0,1) inputs, less operand bit toggling
-        case = workloads.config2()
-        rec = {"metric": "dense attention on constant inputs", "workload": case.name, "unit": "TFLOP/s"}
+        case = workloads.config2() if args.only == "dense_const" else workloads.config3()
+        rec = {"metric": "attention on constant inputs", "workload": case.name, "unit": "TFLOP/s"}
         for operands in ("ones", "zeros"):
             t, flops = bench_varlen(case, args.steps, args.warmup, operands=operands)
             rec[operands] = round(flops / (t.mean * 1e-3) / 1e12, 1)
             rec[operands + "_ms"] = round(t.mean, 5)
         print(json.dumps(rec))
+        return
+    if args.only == "sparse_const":
+        # workload 5's block-sparse call with the map built from its N(0,1)
+        # inputs, then run on all-ones tile-order Q, K and V (same items, same
+        # kept tiles, same instructions)
+        case = workloads.config5()
+        dev = torch.device("cuda")
+        prep = sav.vsa_prepare(case.q.to(dev), case.k.to(dev), case.v.to(dev), case.video_shape, case.tile_shape,
+                               case.topk, case.scale)
+        bmap, sizes = prep["block_map"], prep["tile_sizes"]
+        qt, kt, vt = (torch.ones_like(prep[n]) for n in ("q", "k", "v"))
+        out = torch.empty_like(qt)
+        ws = torch.empty(sav.attn_block_sparse_workspace_size(qt.shape[0], case.num_heads, sizes.numel()),
+                         dtype=torch.uint8, device=dev)
+        t = time_steps(lambda: sav.attn_block_sparse_fwd(qt, kt, vt, bmap, sizes, case.scale, out=out, workspace=ws),
+                       args.steps, args.warmup)
+        flops = sparse_flops(bmap.cpu().numpy(), sizes.cpu().numpy(), case.head_dim)
+        print(json.dumps({"metric": "attention on constant inputs", "workload": case.name, "unit": "TFLOP/s",
+                          "ones": round(flops / (t.mean * 1e-3) / 1e12, 1), "ones_ms": round(t.mean, 5)}))
         return
     if args.only in ("mfma_stream", "mfma_stream_const"):
         kinds = ("randn",) if args.only == "mfma_stream" else ("constant",)
