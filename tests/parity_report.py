@@ -5,7 +5,7 @@ runs with ATTN_PARITY_RECORD=<file> (tests/conftest.py writes one JSON object
 a line). This prints, for each full-size workload test, the plain max-abs
 error of the output and of the LSE, and a summary of the edge-case tests.
 
-    python tests/parity_report.py gpurun_out/parity_records.jsonl
+    python tests/parity_report.py parity_records.jsonl
 """
 
 import json
